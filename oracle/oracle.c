@@ -1,0 +1,218 @@
+/*
+ * oracle.c -- plain, slow, single-threaded CPU oracle of the 1-bit Adam
+ * compression-stage step.  TEST INFRASTRUCTURE ONLY (see oracle.h): nothing
+ * in the GPU library includes or calls it, and it includes nothing of that
+ * library.  Scalar loops, written in the order the method's steps are stated
+ * on the pages; page abbreviations [Tang], [AIMech], [CwP] are defined in
+ * oracle.h.
+ *
+ * Readings taken where the pages leave a step open (each is listed with its
+ * reason in the design notes of the repository):
+ *   R1  the broadcast server momentum replaces every worker's momentum
+ *       (m <- m_hat), so one momentum vector exists in the compression stage;
+ *   R2  no bias correction unless the caller passes bc1, bc2 != 1;
+ *   R3  the preconditioner divides by sqrt(v) + eta;
+ *   R4  the scale is ||c||_2 / ||sign(c)||_2 with sign(0) = +1, so the
+ *       denominator is sqrt(segment length);
+ *   R5  the server averages the n decompressed worker messages (mean), adds
+ *       its error, and recompresses with the same 1-bit compressor.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* IEEE 754 binary16 decoded from its definition: sign, 5-bit biased exponent
+ * (bias 15), 10-bit fraction; exponent 0 is subnormal (f * 2^-24).  Every
+ * binary16 value is exactly representable in binary32 and binary64. */
+double oracle_half_to_double(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 31;
+  int f = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -24);
+  else if (e == 31)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + f), e - 25);
+  return sign ? -v : v;
+}
+
+static float grad_at(const void* g, int g_is_f16, int64_t idx) {
+  if (g_is_f16) return (float)oracle_half_to_double(((const uint16_t*)g)[idx]);
+  return ((const float*)g)[idx];
+}
+
+/* ---------------------------------------------------------------------------
+ * Warm-up: one uncompressed Adam step on the mean gradient.
+ * [AIMech] definition paragraph: v_t = b2 v_{t-1} + (1-b2) g_t^2 and
+ * m_t = b1 m_{t-1} + (1-b1) g_t; [Tang] 1 and 4.3: plain Adam runs during the
+ * warm-up, with an uncompressed exchange, so g_t is the mean of the workers'
+ * gradients.  Per coordinate k, in this order:
+ *   gbar = (((0 + g_0) + g_1) + ... + g_{n-1}) / n
+ *   m = b1*m + (1-b1)*gbar
+ *   v = b2*v + (1-b2)*(gbar*gbar)
+ *   x = x - (lr*(m/bc1)) / (sqrt(v/bc2) + eta)
+ * The binary32 coefficients are the binary64 hyperparameters rounded once;
+ * (1-b1) and (1-b2) are formed in binary64 before that rounding.
+ * ------------------------------------------------------------------------- */
+void oracle_adam_warmup_step(int64_t d, int32_t n, int64_t ld, const void* g, int g_is_f16,
+                             float* x, float* m, float* v, double lr_, double beta1_,
+                             double beta2_, double eta_, double bc1_, double bc2_) {
+  const float lr = (float)lr_, beta1 = (float)beta1_, beta2 = (float)beta2_;
+  const float eta = (float)eta_, bc1 = (float)bc1_, bc2 = (float)bc2_;
+  const float omb1 = (float)(1.0 - beta1_);
+  const float omb2 = (float)(1.0 - beta2_);
+  for (int64_t k = 0; k < d; ++k) {
+    float sum = 0.0f;
+    for (int32_t i = 0; i < n; ++i) sum = sum + grad_at(g, g_is_f16, (int64_t)i * ld + k);
+    float gbar = sum / (float)n;
+    float mk = beta1 * m[k] + omb1 * gbar;
+    float vk = beta2 * v[k] + omb2 * (gbar * gbar);
+    m[k] = mk;
+    v[k] = vk;
+    x[k] = x[k] - (lr * (mk / bc1)) / (sqrtf(vk / bc2) + eta);
+  }
+}
+
+/* Freeze: the variance stops changing and becomes the fixed preconditioner
+ * V = diag(sqrt(v_Tw) + eta) ([AIMech] definition paragraph; [Tang] 3.3 and
+ * 5).  denom = sqrt(v/bc2) + eta, stored once. */
+void oracle_freeze_variance(int64_t d, const float* v, float* denom, double eta_, double bc2_) {
+  const float eta = (float)eta_, bc2 = (float)bc2_;
+  for (int64_t k = 0; k < d; ++k) denom[k] = sqrtf(v[k] / bc2) + eta;
+}
+
+/* ---------------------------------------------------------------------------
+ * The 1-bit compressor with error compensation ([Tang] 4.3: sign of each
+ * element plus one scale that keeps the magnitude; [CwP]: scale = magnitude
+ * of the compensated vector / magnitude of its sign vector; [AIMech]
+ * gather-broadcast mechanism: worker and server error memories).
+ * ------------------------------------------------------------------------- */
+
+/* sum of c^2 over a segment, each square exact in binary64 */
+double oracle_sumsq(int64_t len, const float* c) {
+  double s = 0.0;
+  for (int64_t k = 0; k < len; ++k) s += (double)c[k] * (double)c[k];
+  return s;
+}
+
+/* ||c||_2 / ||sign(c)||_2 where every sign is +-1, so ||sign(c)||_2^2 = len */
+float oracle_scale(double sumsq, int64_t len) { return (float)sqrt(sumsq / (double)len); }
+
+/* bit k (global index bit0+k) = 1 iff c[k] < 0; -0.0 and +0.0 give 0 (+1) */
+void oracle_pack_signs(int64_t len, const float* c, uint64_t* bits, int64_t bit0) {
+  for (int64_t k = 0; k < len; ++k) {
+    int64_t b = bit0 + k;
+    if (c[k] < 0.0f) bits[b >> 6] |= (uint64_t)1 << (b & 63);
+  }
+}
+
+int oracle_bit(const uint64_t* bits, int64_t k) { return (int)((bits[k >> 6] >> (k & 63)) & 1); }
+
+/* err = c - s*sign(c), sign(c) = -1 if c < 0 else +1 */
+void oracle_residual(int64_t len, const float* c, float s, float* err) {
+  for (int64_t k = 0; k < len; ++k) {
+    float sg = (c[k] < 0.0f) ? -1.0f : 1.0f;
+    err[k] = c[k] - s * sg;
+  }
+}
+
+/* Compress one vector c of length d with segment table seg: per segment a
+ * scale, signs into bits (row of W words, cleared here), residual into err. */
+static void ec_onebit(int64_t d, const int64_t* seg, int32_t n_seg, const float* c,
+                      uint64_t* bits, float* scale, float* err) {
+  int64_t W = (d + 63) / 64;
+  memset(bits, 0, (size_t)W * sizeof(uint64_t));
+  for (int32_t j = 0; j < n_seg; ++j) {
+    int64_t lo = seg[j], hi = seg[j + 1];
+    float s = oracle_scale(oracle_sumsq(hi - lo, c + lo), hi - lo);
+    scale[j] = s;
+    oracle_pack_signs(hi - lo, c + lo, bits, lo);
+    oracle_residual(hi - lo, c + lo, s, err + lo);
+  }
+}
+
+/* Worker side, per coordinate ([Tang] 11: each worker updates its momentum
+ * locally and applies error-compensated compression; [AIMech] definition
+ * paragraph for the momentum recurrence):
+ *   c = (b1*m + (1-b1)*g) + delta      two products, then two adds
+ * with b1 and (1-b1) rounded to binary32 from binary64 as in the warm-up. */
+void oracle_compensate(int64_t len, double beta1_, const float* m, const void* g, int g_is_f16,
+                       int64_t g_off, const float* delta, float* c) {
+  const float beta1 = (float)beta1_;
+  const float omb1 = (float)(1.0 - beta1_);
+  for (int64_t k = 0; k < len; ++k) {
+    float p = beta1 * m[k] + omb1 * grad_at(g, g_is_f16, g_off + k);
+    c[k] = p + delta[k];
+  }
+}
+
+void oracle_compress(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_wseg,
+                     const void* g, int g_is_f16, const float* m, float* delta, uint64_t* wbits,
+                     float* wscale, double beta1) {
+  int64_t W = (d + 63) / 64;
+  float* c = (float*)malloc((size_t)(d > 0 ? d : 1) * sizeof(float));
+  for (int32_t i = 0; i < n; ++i) {
+    float* di = delta + (int64_t)i * ld;
+    oracle_compensate(d, beta1, m, g, g_is_f16, (int64_t)i * ld, di, c);
+    ec_onebit(d, wseg, n_wseg, c, wbits + (int64_t)i * W, wscale + (int64_t)i * n_wseg, di);
+  }
+  free(c);
+}
+
+/* Server side, per coordinate k in [k0, k1) ([Tang] 11: the server averages
+ * the workers' messages, then compresses again; [AIMech] gather-broadcast
+ * mechanism: server error memory):
+ *   t = ((0 + s_0*sg_0) + s_1*sg_1) + ... + s_{n-1}*sg_{n-1}
+ *   a = t / n + eps
+ * where s_i is worker i's scale for the worker segment holding k and sg_i its
+ * decoded sign.  eps and a are indexed by the global coordinate. */
+void oracle_server_average(int64_t k0, int64_t k1, int64_t d, int32_t n, const int64_t* wseg,
+                           int32_t n_wseg, const uint64_t* wbits, const float* wscale,
+                           const float* eps, float* a) {
+  int64_t W = (d + 63) / 64;
+  int32_t j = 0;
+  for (int64_t k = k0; k < k1; ++k) {
+    while (wseg[j + 1] <= k) ++j;
+    float t = 0.0f;
+    for (int32_t i = 0; i < n; ++i) {
+      float s = wscale[(int64_t)i * n_wseg + j];
+      float sg = oracle_bit(wbits + (int64_t)i * W, k) ? -1.0f : 1.0f;
+      t = t + s * sg;
+    }
+    a[k] = t / (float)n + eps[k];
+  }
+}
+
+void oracle_server_reduce_recompress(int64_t d, int32_t n, const int64_t* wseg, int32_t n_wseg,
+                                     const int64_t* sseg, int32_t n_sseg, const uint64_t* wbits,
+                                     const float* wscale, float* eps, uint64_t* sbits,
+                                     float* sscale) {
+  float* a = (float*)malloc((size_t)(d > 0 ? d : 1) * sizeof(float));
+  oracle_server_average(0, d, d, n, wseg, n_wseg, wbits, wscale, eps, a);
+  ec_onebit(d, sseg, n_sseg, a, sbits, sscale, eps);
+  free(a);
+}
+
+/* Broadcast and update ([Tang] 11: the server broadcasts the momentum and
+ * workers update their models; [AIMech] definition paragraph:
+ * x_t = x_{t-1} - gamma V^{-1} m_hat_t), per coordinate k in [k0, k1):
+ *   m_hat = s_tau * sign        (s_tau: scale of the server segment of k)
+ *   m = m_hat                   (reading R1)
+ *   x = x - (lr*m_hat) / denom */
+void oracle_decompress_update(int64_t k0, int64_t k1, const int64_t* sseg, int32_t n_sseg,
+                              const uint64_t* sbits, const float* sscale, const float* denom,
+                              float* m, float* x, double lr_) {
+  const float lr = (float)lr_;
+  int32_t j = 0;
+  (void)n_sseg;
+  for (int64_t k = k0; k < k1; ++k) {
+    while (sseg[j + 1] <= k) ++j;
+    float mh = sscale[j] * (oracle_bit(sbits, k) ? -1.0f : 1.0f);
+    m[k] = mh;
+    x[k] = x[k] - (lr * mh) / denom[k];
+  }
+}
