@@ -1,0 +1,214 @@
+"""Benchmark: one 1-bit Adam compression step on one MI355X.
+
+A step is the whole hot path over one gradient set of the workload:
+oba_compress (n workers) -> oba_server_reduce_recompress -> oba_decompress_update.
+Default workload ``bert_large``: d = 336,000,000 binary32 parameters, n = 8
+simulated workers, binary16 gradients 1e-3 * Student-t(3) with a fixed 1 % of
+coordinates exactly zero, server error in n equal shards.  The state is
+prepared by 10 warm-up steps (the library's Adam kernel) and the freeze;
+the timed steps alternate two pre-generated gradient sets, all resident in
+HBM.  Prints one JSON line (rank 0, one GPU).
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+METRIC = "params updated/sec per 1-bit Adam step + achieved HBM GB/s vs peak"
+KERNEL_SRC = os.path.join(ROOT, "communication_compressed_optimizer_02_amd", "csrc",
+                          "kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gbytes(w):
+    """Algorithmic HBM bytes per parameter of each kernel: every buffer the
+    method defines is moved once per direction in that kernel."""
+    n, gb = w.n, (2 if w.g_dtype == "f16" else 4)
+    return {
+        # m read, g_i read, delta_i read (c written over it), packed bits written
+        "compress_p1": 4 + n * (gb + 4 + 4) + n / 8,
+        # c read, delta written
+        "compress_p2": 8 * n,
+        # worker bits read, eps read, a written over eps, server bits written
+        "server_p1": n / 8 + 8 + 1 / 8,
+        # a read, eps written
+        "server_p2": 8,
+        # server bits read, denom read, x read+written, m written
+        "decompress_update": 1 / 8 + 16,
+    }
+
+
+def source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(workload, kernel):
+    """HBM bytes per launch measured by rocprofv3 counters, if the committed
+    summary was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not val or src.group(1) != source_hash():
+        return None
+    return float(val.group(1))
+
+
+def make_state(w, torch, oba, synth):
+    L = oba.Layout(w.d, w.n, w.wseg, w.sseg)
+    S = oba.State(L, w.g_dtype)
+    gen = synth.device_generator(w.seed)
+    zero_idx = synth.device_zero_mask(gen, w.d) if w.name == "bert_large" else None
+    S.x.normal_(0.0, 0.02, generator=gen)
+    log(f"[bench] {w.name}: {w.warmup_steps} warm-up steps")
+    for _ in range(w.warmup_steps):
+        synth.device_grads(gen, w, S.g, zero_idx)
+        S.warmup(synth.LR, synth.BETA1, synth.BETA2, synth.ETA)
+    S.freeze(synth.ETA)
+    g_a = S.g
+    synth.device_grads(gen, w, g_a, zero_idx)
+    g_b = torch.empty_like(g_a)
+    synth.device_grads(gen, w, g_b, zero_idx)
+    del zero_idx
+    torch.cuda.synchronize()
+    return L, S, (g_a, g_b)
+
+
+def cpu_baseline(w, synth, d_sample):
+    """The oracle (single-threaded C) on a bounded sample of the same
+    workload: one compression step over d_sample coordinates, all n workers."""
+    import numpy as np
+
+    import oracle
+
+    ws = synth.scaled(w, d_sample)
+    rng = np.random.default_rng(w.seed)
+    st = synth.host_state(rng, ws.d, ws.n)
+    st["denom"] = oracle.freeze_variance(st["v"], synth.ETA)
+    zero = synth.zero_mask_host(rng, ws.d) if w.name == "bert_large" else None
+    g = synth.host_grads(rng, ws, zero_idx=zero)
+    t0 = time.perf_counter()
+    oracle.step(st, g, ws.wseg, ws.sseg, synth.BETA1, synth.LR)
+    dt = time.perf_counter() - t0
+    return {"value": ws.d / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"one compression step of the {w.name} recipe at d={ws.d:,} "
+                      f"(n={ws.n}, {ws.g_dtype} gradients), {dt:.2f} s on 1 thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bert_large",
+                    choices=["tiny", "bert_base", "bert_large", "gpt2_xl", "quadratic"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 23)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the n data-parallel workers are simulated as n "
+              "buffers on that GPU; runs over several GPUs are not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from communication_compressed_optimizer_02_amd import binding as oba
+    from communication_compressed_optimizer_02_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = synth.workload(args.workload)
+    L, S, gsets = make_state(w, torch, oba, synth)
+
+    def step(i):
+        S.step(synth.BETA1, synth.LR, g=gsets[i % 2])
+
+    log(f"[bench] {args.warmup} untimed steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    oba.timing_reset()
+    oba.timing_enable(True, capacity=16 * max(1, args.steps))
+    log(f"[bench] {args.steps} timed steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    oba.timing_enable(False, 1)
+    ms = (t1 - t0) * 1e3 / args.steps
+    per_kernel = {}
+    for k in ("compress_p1", "finalize_scales", "compress_p2", "server_p1", "server_p2",
+              "decompress_update"):
+        tot, cnt = oba.timing_read(k)
+        per_kernel[k] = (tot / cnt if cnt else 0.0, cnt)
+    oba.timing_reset()
+    alg = gbytes(w)
+    kernels = {}
+    for k, (avg_ms, cnt) in per_kernel.items():
+        ent = {"avg_ms": round(avg_ms, 4), "launches": cnt}
+        if k in alg and avg_ms > 0:
+            ent["alg_bytes_per_param"] = alg[k]
+            ent["alg_GBps"] = round(alg[k] * w.d / (avg_ms * 1e-3) / 1e9, 1)
+        kernels[k] = ent
+    dom = "compress_p1"
+    dom_ms = per_kernel[dom][0]
+    dom_bytes = alg[dom] * w.d
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles(w.name, dom)
+    step_alg = sum(alg.values()) * w.d
+    out = {
+        "metric": METRIC,
+        "value": w.d / (ms * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "d": w.d, "n_workers": w.n, "grad_dtype": w.g_dtype,
+                   "worker_segments": len(w.wseg) - 1, "server_segments": len(w.sseg) - 1,
+                   "parallelism": "dp%d simulated on one GPU" % w.n},
+        "step_alg_GBps": round(step_alg / (ms * 1e-3) / 1e9, 1),
+        "step_alg_bytes_per_param": round(sum(alg.values()), 3),
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "alg_bytes_per_launch": dom_bytes,
+                     "avg_launch_ms": round(dom_ms, 4)},
+        "kernels": kernels,
+        "kernel_source_sha256": source_hash(),
+    }
+    del S, gsets
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(w, synth, min(args.cpu_sample, w.d))
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,15 @@
+"""1-bit Adam compression-stage step on AMD MI355X (gfx950).
+
+The method runs in hand-written HIP kernels behind the C ABI of
+``include/oba.h`` (liboba.so, built in-tree); ``binding`` is its thin
+Python front end and ``synth`` holds the seeded synthetic workloads.
+"""
+from .binding import (OBA_F16, OBA_F32, Layout, ObaError, State, adam_warmup_step, compress,
+                      decompress_update, freeze_variance, server_reduce_recompress,
+                      timing_enable, timing_read, timing_reset, validate)
+
+__all__ = [
+    "OBA_F16", "OBA_F32", "Layout", "ObaError", "State", "adam_warmup_step", "compress",
+    "decompress_update", "freeze_variance", "server_reduce_recompress", "timing_enable",
+    "timing_read", "timing_reset", "validate",
+]

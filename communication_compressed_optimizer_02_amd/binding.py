@@ -1,0 +1,261 @@
+"""Python binding of liboba.so (the C ABI in include/oba.h).
+
+Argument marshalling only: every step of the method runs in the library's
+HIP kernels.  torch supplies device memory (``torch.Tensor.data_ptr``) and
+the stream (``torch.cuda.current_stream()``).  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+
+Buffers (all CUDA tensors on the layout's device, C-contiguous):
+  g      [n][ld]  float32 or float16     delta  [n][ld]  float32
+         (ld = row stride, a multiple of 8 >= d; default d rounded up to 8)
+  x, m, v, denom, eps  [d] float32
+  wbits  [n][W]  int64 (packed 64-bit words)   sbits [W] int64
+  wscale [n][n_wseg] float32                   sscale [n_sseg] float32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboba.so")
+
+OBA_F32, OBA_F16 = 0, 1
+_lib = None
+
+# name -> (restype, argtypes); mirrors include/oba.h
+_P, _I64, _I32, _D, _SZ, _I = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double,
+                               ctypes.c_size_t, ctypes.c_int)
+SIGNATURES = {
+    "oba_version": (_I, []),
+    "oba_status_string": (ctypes.c_char_p, [_I]),
+    "oba_layout_validate": (_I, [_I64, _I32, _I64, _P, _I32, _P, _I32]),
+    "oba_layout_create": (_I, [ctypes.POINTER(_P), _I64, _I32, _I64, _P, _I32, _P, _I32]),
+    "oba_layout_destroy": (None, [_P]),
+    "oba_workspace_bytes": (_SZ, [_P]),
+    "oba_adam_warmup_step": (_I, [_P, _P, _I, _P, _P, _P, _D, _D, _D, _D, _D, _D, _P]),
+    "oba_freeze_variance": (_I, [_P, _P, _P, _D, _D, _P]),
+    "oba_compress": (_I, [_P, _P, _I, _P, _P, _P, _P, _D, _P, _SZ, _P]),
+    "oba_server_reduce_recompress": (_I, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "oba_decompress_update": (_I, [_P, _P, _P, _P, _P, _P, _D, _P]),
+    "oba_timing_enable": (_I, [_I, _I32]),
+    "oba_timing_read": (_I, [ctypes.c_char_p, ctypes.POINTER(_D), ctypes.POINTER(_I64)]),
+    "oba_timing_reset": (_I, []),
+}
+
+
+class ObaError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load liboba.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
+                               "(python -c 'import __graft_entry__ as e; e.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(rc: int) -> str:
+    return lib().oba_status_string(rc).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ObaError(f"{what}: {status_string(rc)} (status {rc})")
+
+
+def _stream(stream=None):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t, name, dtypes, shape=None):
+    import torch
+
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name}: expected a CUDA tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _table(seg):
+    import numpy as np
+
+    a = np.ascontiguousarray(np.asarray(seg, dtype=np.int64))
+    return a, a.ctypes.data_as(ctypes.c_void_p), len(a) - 1
+
+
+def default_ld(d: int) -> int:
+    """Row stride of the [n][ld] buffers: d rounded up to a multiple of 8."""
+    return (int(d) + 7) // 8 * 8
+
+
+def validate(d, n, wseg, sseg, ld=None) -> int:
+    ld = default_ld(d) if ld is None else ld
+    w, wp, nw = _table(wseg)
+    s, sp, ns = _table(sseg)
+    return lib().oba_layout_validate(d, n, ld, wp, nw, sp, ns)
+
+
+class Layout:
+    """Owns an oba_layout handle and a workspace tensor on the current device."""
+
+    def __init__(self, d, n, wseg, sseg, ld=None):
+        import torch
+
+        self.d, self.n = int(d), int(n)
+        self.ld = default_ld(self.d) if ld is None else int(ld)
+        self.W = (self.d + 63) // 64
+        self.wseg, wp, self.n_wseg = _table(wseg)
+        self.sseg, sp, self.n_sseg = _table(sseg)
+        h = ctypes.c_void_p()
+        _check(lib().oba_layout_create(ctypes.byref(h), self.d, self.n, self.ld, wp, self.n_wseg,
+                                       sp, self.n_sseg), "oba_layout_create")
+        self.handle = h
+        self.device = torch.cuda.current_device()
+        self.ws_bytes = lib().oba_workspace_bytes(h)
+        self.ws = torch.empty(max(8, self.ws_bytes), dtype=torch.uint8, device="cuda")
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            lib().oba_layout_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _gdtype(g):
+    import torch
+
+    return OBA_F16 if g.dtype == torch.float16 else OBA_F32
+
+
+def adam_warmup_step(L: Layout, g, x, m, v, lr, beta1, beta2, eta, bc1=1.0, bc2=1.0, stream=None):
+    import torch
+
+    f32 = (torch.float32,)
+    rc = lib().oba_adam_warmup_step(
+        L.handle, _ptr(g, "g", (torch.float32, torch.float16), (L.n, L.ld)), _gdtype(g),
+        _ptr(x, "x", f32, (L.d,)), _ptr(m, "m", f32, (L.d,)), _ptr(v, "v", f32, (L.d,)),
+        lr, beta1, beta2, eta, bc1, bc2, _stream(stream))
+    _check(rc, "oba_adam_warmup_step")
+
+
+def freeze_variance(L: Layout, v, denom, eta, bc2=1.0, stream=None):
+    import torch
+
+    f32 = (torch.float32,)
+    rc = lib().oba_freeze_variance(L.handle, _ptr(v, "v", f32, (L.d,)),
+                                   _ptr(denom, "denom", f32, (L.d,)), eta, bc2, _stream(stream))
+    _check(rc, "oba_freeze_variance")
+
+
+def compress(L: Layout, g, m, delta, wbits, wscale, beta1, stream=None):
+    import torch
+
+    f32 = (torch.float32,)
+    rc = lib().oba_compress(
+        L.handle, _ptr(g, "g", (torch.float32, torch.float16), (L.n, L.ld)), _gdtype(g),
+        _ptr(m, "m", f32, (L.d,)), _ptr(delta, "delta", f32, (L.n, L.ld)),
+        _ptr(wbits, "wbits", (torch.int64,), (L.n, L.W)),
+        _ptr(wscale, "wscale", f32, (L.n, L.n_wseg)), beta1,
+        ctypes.c_void_p(L.ws.data_ptr()), L.ws_bytes, _stream(stream))
+    _check(rc, "oba_compress")
+
+
+def server_reduce_recompress(L: Layout, wbits, wscale, eps, sbits, sscale, stream=None):
+    import torch
+
+    f32 = (torch.float32,)
+    rc = lib().oba_server_reduce_recompress(
+        L.handle, _ptr(wbits, "wbits", (torch.int64,), (L.n, L.W)),
+        _ptr(wscale, "wscale", f32, (L.n, L.n_wseg)), _ptr(eps, "eps", f32, (L.d,)),
+        _ptr(sbits, "sbits", (torch.int64,), (L.W,)), _ptr(sscale, "sscale", f32, (L.n_sseg,)),
+        ctypes.c_void_p(L.ws.data_ptr()), L.ws_bytes, _stream(stream))
+    _check(rc, "oba_server_reduce_recompress")
+
+
+def decompress_update(L: Layout, sbits, sscale, denom, m, x, lr, stream=None):
+    import torch
+
+    f32 = (torch.float32,)
+    rc = lib().oba_decompress_update(
+        L.handle, _ptr(sbits, "sbits", (torch.int64,), (L.W,)),
+        _ptr(sscale, "sscale", f32, (L.n_sseg,)), _ptr(denom, "denom", f32, (L.d,)),
+        _ptr(m, "m", f32, (L.d,)), _ptr(x, "x", f32, (L.d,)), lr, _stream(stream))
+    _check(rc, "oba_decompress_update")
+
+
+def timing_enable(on=True, capacity=4096):
+    _check(lib().oba_timing_enable(1 if on else 0, capacity), "oba_timing_enable")
+
+
+def timing_read(kernel: str):
+    ms = ctypes.c_double()
+    cnt = ctypes.c_int64()
+    _check(lib().oba_timing_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(cnt)),
+           "oba_timing_read")
+    return ms.value, cnt.value
+
+
+def timing_reset():
+    _check(lib().oba_timing_reset(), "oba_timing_reset")
+
+
+class State:
+    """Device buffers of one simulated data-parallel job (allocation only)."""
+
+    def __init__(self, L: Layout, g_dtype="f32"):
+        import torch
+
+        dev = "cuda"
+        f = torch.float32
+        self.L = L
+        self.g = torch.zeros((L.n, L.ld), dtype=torch.float16 if g_dtype == "f16" else f, device=dev)
+        self.x = torch.zeros(L.d, dtype=f, device=dev)
+        self.m = torch.zeros(L.d, dtype=f, device=dev)
+        self.v = torch.zeros(L.d, dtype=f, device=dev)
+        self.denom = torch.zeros(L.d, dtype=f, device=dev)
+        self.eps = torch.zeros(L.d, dtype=f, device=dev)
+        self.delta = torch.zeros((L.n, L.ld), dtype=f, device=dev)
+        self.wbits = torch.zeros((L.n, L.W), dtype=torch.int64, device=dev)
+        self.wscale = torch.zeros((L.n, L.n_wseg), dtype=f, device=dev)
+        self.sbits = torch.zeros(L.W, dtype=torch.int64, device=dev)
+        self.sscale = torch.zeros(L.n_sseg, dtype=f, device=dev)
+
+    def warmup(self, lr, beta1, beta2, eta, bc1=1.0, bc2=1.0, g=None):
+        adam_warmup_step(self.L, self.g if g is None else g, self.x, self.m, self.v, lr, beta1,
+                         beta2, eta, bc1, bc2)
+
+    def freeze(self, eta, bc2=1.0):
+        freeze_variance(self.L, self.v, self.denom, eta, bc2)
+        self.delta.zero_()
+        self.eps.zero_()
+
+    def step(self, beta1, lr, g=None):
+        """One compression step: compress -> server -> decompress+update."""
+        compress(self.L, self.g if g is None else g, self.m, self.delta, self.wbits, self.wscale,
+                 beta1)
+        server_reduce_recompress(self.L, self.wbits, self.wscale, self.eps, self.sbits,
+                                 self.sscale)
+        decompress_update(self.L, self.sbits, self.sscale, self.denom, self.m, self.x, lr)

@@ -1,0 +1,386 @@
+// api.hip -- the C ABI declared in include/oba.h: argument checks on the
+// host, layout handles, kernel launches on the caller's stream, and the
+// optional per-kernel event timing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+#include "layout.hpp"
+#include "oba.h"
+
+struct oba_layout_s {
+  oba::Plan plan;
+  int device = -1;
+  void* dev_tables = nullptr;
+  oba::SegDev sig{}, tau{};
+  oba::Geo geo{};
+  size_t ws_worker = 0, ws_server = 0;
+};
+
+namespace {
+
+thread_local char g_hip_msg[256] = "HIP error";
+
+int hip_fail(hipError_t e, const char* what) {
+  std::snprintf(g_hip_msg, sizeof(g_hip_msg), "HIP error in %s: %s", what, hipGetErrorString(e));
+  return OBA_EHIP;
+}
+
+// ---- timing -------------------------------------------------------------
+struct TimingRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<hipEvent_t> g_pool;  // free events
+std::vector<TimingRec> g_recs;
+
+void timing_drop_all() {
+  for (auto& r : g_recs) {
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+}
+
+// Launch `fn` on `st`, bracketed by timing events when enabled; check launch.
+template <class F>
+int launch(const char* name, hipStream_t st, F&& fn) {
+  hipEvent_t a = nullptr, b = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (g_timing && g_pool.size() >= 2) {
+      a = g_pool.back();
+      g_pool.pop_back();
+      b = g_pool.back();
+      g_pool.pop_back();
+    }
+  }
+  if (a && hipEventRecord(a, st) != hipSuccess) a = nullptr;
+  fn();
+  hipError_t e = hipGetLastError();
+  if (a) {
+    if (hipEventRecord(b, st) == hipSuccess) {
+      std::lock_guard<std::mutex> lk(g_tmu);
+      g_recs.push_back({name, a, b});
+    } else {
+      std::lock_guard<std::mutex> lk(g_tmu);
+      g_pool.push_back(a);
+      g_pool.push_back(b);
+    }
+  } else if (b) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_pool.push_back(b);
+  }
+  if (e != hipSuccess) return hip_fail(e, name);
+  return OBA_OK;
+}
+
+// ---- argument checks ------------------------------------------------------
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_layout(oba_layout L) {
+  if (!L) return OBA_EINVAL;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != L->device) return OBA_EINVAL;
+  return OBA_OK;
+}
+
+int check_buf(const void* p, uintptr_t align) {
+  if (!p) return OBA_EINVAL;
+  if (!aligned(p, align)) return OBA_EALIGN;
+  return OBA_OK;
+}
+
+bool is_finite(double x) { return std::isfinite(x); }
+bool beta_ok(double b) { return is_finite(b) && b >= 0.0 && b < 1.0; }
+
+#define OBA_TRY(expr)          \
+  do {                         \
+    int rc_ = (expr);          \
+    if (rc_ != OBA_OK) return rc_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int oba_version(void) { return 100; }
+
+const char* oba_status_string(int status) {
+  switch (status) {
+    case OBA_OK: return "ok";
+    case OBA_EINVAL: return "invalid argument (null pointer, size, dtype, device or hyperparameter)";
+    case OBA_EALIGN: return "buffer misaligned (16 B for float/half, 8 B for packed words and workspace, 4 B for scales)";
+    case OBA_ESEG: return "segment table must rise strictly from 0 to d";
+    case OBA_EWORKSPACE: return "workspace smaller than oba_workspace_bytes()";
+    case OBA_EHIP: return g_hip_msg;
+    case OBA_ENOMEM: return "allocation failed";
+    default: return "unknown status";
+  }
+}
+
+int oba_layout_validate(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_wseg,
+                        const int64_t* sseg, int32_t n_sseg) {
+  return oba::validate(d, n, ld, wseg, n_wseg, sseg, n_sseg);
+}
+
+int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const int64_t* wseg,
+                      int32_t n_wseg, const int64_t* sseg, int32_t n_sseg) {
+  if (!out) return OBA_EINVAL;
+  oba_layout_s* L = new (std::nothrow) oba_layout_s();
+  if (!L) return OBA_ENOMEM;
+  int rc = oba::make_plan(d, n, ld, wseg, n_wseg, sseg, n_sseg, &L->plan);
+  if (rc) {
+    delete L;
+    return rc;
+  }
+  const oba::Plan& P = L->plan;
+  hipError_t e = hipGetDevice(&L->device);
+  if (e != hipSuccess) {
+    delete L;
+    return hip_fail(e, "hipGetDevice");
+  }
+  // one device allocation: int64 arrays first, then int32 arrays
+  const size_t nw_p = P.wp.lo.size(), ns_p = P.sp.lo.size();
+  std::vector<int64_t> h64;
+  std::vector<int32_t> h32;
+  auto put = [&](const oba::Pieces& pc, const std::vector<int64_t>& off, size_t o64[2],
+                 size_t o32[3]) {
+    o64[0] = h64.size();
+    h64.insert(h64.end(), off.begin(), off.end());
+    o64[1] = h64.size();
+    h64.insert(h64.end(), pc.hi.begin(), pc.hi.end());
+    o32[0] = h32.size();
+    h32.insert(h32.end(), pc.seg.begin(), pc.seg.end());
+    o32[1] = h32.size();
+    h32.insert(h32.end(), pc.blk_first.begin(), pc.blk_first.end());
+    o32[2] = h32.size();
+    h32.insert(h32.end(), pc.seg_first.begin(), pc.seg_first.end());
+  };
+  size_t w64[2], w32[3], s64[2], s32[3];
+  try {
+    put(P.wp, P.wseg, w64, w32);
+    put(P.sp, P.sseg, s64, s32);
+  } catch (...) {
+    delete L;
+    return OBA_ENOMEM;
+  }
+  const size_t bytes64 = h64.size() * sizeof(int64_t);
+  const size_t bytes = bytes64 + h32.size() * sizeof(int32_t);
+  if (bytes) {
+    e = hipMalloc(&L->dev_tables, bytes);
+    if (e != hipSuccess) {
+      delete L;
+      return OBA_ENOMEM;
+    }
+    e = hipMemcpy(L->dev_tables, h64.data(), bytes64, hipMemcpyHostToDevice);
+    if (e == hipSuccess && !h32.empty())
+      e = hipMemcpy(static_cast<char*>(L->dev_tables) + bytes64, h32.data(),
+                    h32.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(L->dev_tables);
+      delete L;
+      return hip_fail(e, "hipMemcpy (layout tables)");
+    }
+  }
+  const int64_t* d64 = static_cast<const int64_t*>(L->dev_tables);
+  const int32_t* d32 = reinterpret_cast<const int32_t*>(static_cast<const char*>(L->dev_tables) + bytes64);
+  auto view = [&](size_t o64[2], size_t o32[3], int32_t n_seg) {
+    oba::SegDev s;
+    s.off = d64 + o64[0];
+    s.phi = d64 + o64[1];
+    s.pseg = d32 + o32[0];
+    s.blk_first = d32 + o32[1];
+    s.seg_first = d32 + o32[2];
+    s.n_seg = n_seg;
+    return s;
+  };
+  L->sig = view(w64, w32, (int32_t)P.wseg.size() - 1);
+  L->tau = view(s64, s32, (int32_t)P.sseg.size() - 1);
+  L->geo = oba::Geo{P.d, P.ld, P.W, P.S, P.n, P.nblk};
+  L->ws_worker = nw_p * (size_t)P.n * sizeof(double);
+  L->ws_server = ns_p * sizeof(double);
+  *out = L;
+  return OBA_OK;
+}
+
+void oba_layout_destroy(oba_layout L) {
+  if (!L) return;
+  if (L->dev_tables) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(L->dev_tables);
+  }
+  delete L;
+}
+
+size_t oba_workspace_bytes(oba_layout L) {
+  if (!L) return 0;
+  return ((L->ws_worker + 255) / 256) * 256 + L->ws_server;
+}
+
+int oba_adam_warmup_step(oba_layout L, const void* g, int g_dtype, float* x, float* m, float* v,
+                         double lr, double beta1, double beta2, double eta, double bc1,
+                         double bc2, hipStream_t stream) {
+  OBA_TRY(check_layout(L));
+  if (g_dtype != OBA_F32 && g_dtype != OBA_F16) return OBA_EINVAL;
+  if (!is_finite(lr) || !beta_ok(beta1) || !beta_ok(beta2) || !is_finite(eta) || eta < 0.0 ||
+      !is_finite(bc1) || bc1 <= 0.0 || !is_finite(bc2) || bc2 <= 0.0)
+    return OBA_EINVAL;
+  if (L->geo.d == 0) return OBA_OK;
+  OBA_TRY(check_buf(g, 16));
+  OBA_TRY(check_buf(x, 16));
+  OBA_TRY(check_buf(m, 16));
+  OBA_TRY(check_buf(v, 16));
+  oba::AdamCoef C{(float)lr, (float)beta1, (float)(1.0 - beta1), (float)beta2,
+                  (float)(1.0 - beta2), (float)eta, (float)bc1, (float)bc2};
+  const oba::Geo G = L->geo;
+  return launch("adam_warmup", stream, [&] {
+    oba::launch_adam_warmup(G, g, g_dtype == OBA_F16, x, m, v, C, stream);
+  });
+}
+
+int oba_freeze_variance(oba_layout L, const float* v, float* denom, double eta, double bc2,
+                        hipStream_t stream) {
+  OBA_TRY(check_layout(L));
+  if (!is_finite(eta) || eta < 0.0 || !is_finite(bc2) || bc2 <= 0.0) return OBA_EINVAL;
+  if (L->geo.d == 0) return OBA_OK;
+  OBA_TRY(check_buf(v, 16));
+  OBA_TRY(check_buf(denom, 16));
+  if ((const void*)v == (const void*)denom) return OBA_EINVAL;
+  const oba::Geo G = L->geo;
+  return launch("freeze_variance", stream,
+                [&] { oba::launch_freeze(G, v, denom, (float)eta, (float)bc2, stream); });
+}
+
+int oba_compress(oba_layout L, const void* g, int g_dtype, const float* m, float* delta,
+                 uint64_t* wbits, float* wscale, double beta1, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  OBA_TRY(check_layout(L));
+  if (g_dtype != OBA_F32 && g_dtype != OBA_F16) return OBA_EINVAL;
+  if (!beta_ok(beta1)) return OBA_EINVAL;
+  if (L->geo.d == 0) return OBA_OK;
+  OBA_TRY(check_buf(g, 16));
+  OBA_TRY(check_buf(m, 16));
+  OBA_TRY(check_buf(delta, 16));
+  OBA_TRY(check_buf(wbits, 8));
+  OBA_TRY(check_buf(wscale, 4));
+  OBA_TRY(check_buf(ws, 8));
+  if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
+  const oba::Geo G = L->geo;
+  double* part = static_cast<double*>(ws);
+  const float b1 = (float)beta1, omb1 = (float)(1.0 - beta1);
+  uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
+  OBA_TRY(launch("compress_p1", stream, [&] {
+    oba::launch_compress_p1(G, g, g_dtype == OBA_F16, m, delta, wbytes, L->sig, part, b1, omb1,
+                            stream);
+  }));
+  OBA_TRY(launch("finalize_scales", stream,
+                 [&] { oba::launch_finalize(part, G.n, L->sig, wscale, stream); }));
+  return launch("compress_p2", stream,
+                [&] { oba::launch_residual(G, delta, G.ld, G.n, wscale, L->sig, stream); });
+}
+
+int oba_server_reduce_recompress(oba_layout L, const uint64_t* wbits, const float* wscale,
+                                 float* eps, uint64_t* sbits, float* sscale, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  OBA_TRY(check_layout(L));
+  if (L->geo.d == 0) return OBA_OK;
+  OBA_TRY(check_buf(wbits, 8));
+  OBA_TRY(check_buf(wscale, 4));
+  OBA_TRY(check_buf(eps, 16));
+  OBA_TRY(check_buf(sbits, 8));
+  OBA_TRY(check_buf(sscale, 4));
+  OBA_TRY(check_buf(ws, 8));
+  if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
+  const oba::Geo G = L->geo;
+  double* part = reinterpret_cast<double*>(static_cast<char*>(ws) +
+                                           ((L->ws_worker + 255) / 256) * 256);
+  const uint8_t* wbytes = reinterpret_cast<const uint8_t*>(wbits);
+  uint8_t* sbytes = reinterpret_cast<uint8_t*>(sbits);
+  OBA_TRY(launch("server_p1", stream, [&] {
+    oba::launch_server_p1(G, wbytes, wscale, eps, sbytes, L->sig, L->tau, part, stream);
+  }));
+  OBA_TRY(launch("finalize_scales", stream,
+                 [&] { oba::launch_finalize(part, 1, L->tau, sscale, stream); }));
+  return launch("server_p2", stream,
+                [&] { oba::launch_residual(G, eps, 0, 1, sscale, L->tau, stream); });
+}
+
+int oba_decompress_update(oba_layout L, const uint64_t* sbits, const float* sscale,
+                          const float* denom, float* m, float* x, double lr, hipStream_t stream) {
+  OBA_TRY(check_layout(L));
+  if (!is_finite(lr)) return OBA_EINVAL;
+  if (L->geo.d == 0) return OBA_OK;
+  OBA_TRY(check_buf(sbits, 8));
+  OBA_TRY(check_buf(sscale, 4));
+  OBA_TRY(check_buf(denom, 16));
+  OBA_TRY(check_buf(m, 16));
+  OBA_TRY(check_buf(x, 16));
+  const oba::Geo G = L->geo;
+  const uint8_t* sbytes = reinterpret_cast<const uint8_t*>(sbits);
+  return launch("decompress_update", stream, [&] {
+    oba::launch_decompress_update(G, sbytes, sscale, denom, m, x, L->tau, (float)lr, stream);
+  });
+}
+
+int oba_timing_enable(int on, int32_t capacity) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (on) {
+    if (capacity < 1 || capacity > (1 << 20)) return OBA_EINVAL;
+    const size_t want = 2 * (size_t)capacity;
+    size_t have = g_pool.size() + 2 * g_recs.size();
+    while (have < want) {
+      hipEvent_t ev;
+      hipError_t e = hipEventCreate(&ev);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+      g_pool.push_back(ev);
+      ++have;
+    }
+  }
+  g_timing = on != 0;
+  return OBA_OK;
+}
+
+int oba_timing_read(const char* kernel, double* total_ms, int64_t* launches) {
+  if (!kernel || !total_ms || !launches) return OBA_EINVAL;
+  std::vector<TimingRec> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    recs = g_recs;
+  }
+  double t = 0.0;
+  int64_t c = 0;
+  for (const auto& r : recs) {
+    if (std::strcmp(r.name, kernel) != 0) continue;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    t += ms;
+    ++c;
+  }
+  *total_ms = t;
+  *launches = c;
+  return OBA_OK;
+}
+
+int oba_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  timing_drop_all();
+  return OBA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// kernels.hpp -- launch interface between the C ABI and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "layout.hpp"
+
+namespace oba {
+
+// Grid geometry shared by all streaming kernels of a layout.
+struct Geo {
+  int64_t d, ld, W, S;
+  int32_t n, nblk;
+};
+
+// Device view of one segmentation (see layout.hpp for pieces).
+struct SegDev {
+  const int64_t* off;        // [n_seg+1] segment offsets
+  const int64_t* phi;        // [n_pieces] piece ends
+  const int32_t* pseg;       // [n_pieces] piece segment
+  const int32_t* blk_first;  // [nblk+1]
+  const int32_t* seg_first;  // [n_seg+1]
+  int32_t n_seg;
+};
+
+struct AdamCoef {
+  float lr, b1, omb1, b2, omb2, eta, bc1, bc2;
+};
+
+void launch_adam_warmup(const Geo& G, const void* g, bool f16, float* x, float* m, float* v,
+                        const AdamCoef& C, hipStream_t st);
+void launch_freeze(const Geo& G, const float* v, float* denom, float eta, float bc2,
+                   hipStream_t st);
+void launch_compress_p1(const Geo& G, const void* g, bool f16, const float* m, float* delta,
+                        uint8_t* wbytes, const SegDev& sig, double* part, float b1, float omb1,
+                        hipStream_t st);
+void launch_finalize(const double* part, int32_t rows, const SegDev& T, float* scale,
+                     hipStream_t st);
+void launch_residual(const Geo& G, float* buf, int64_t ld, int32_t rows, const float* scale,
+                     const SegDev& T, hipStream_t st);
+void launch_server_p1(const Geo& G, const uint8_t* wbytes, const float* wscale, float* eps,
+                      uint8_t* sbytes, const SegDev& sig, const SegDev& tau, double* part,
+                      hipStream_t st);
+void launch_decompress_update(const Geo& G, const uint8_t* sbytes, const float* sscale,
+                              const float* denom, float* m, float* x, const SegDev& tau, float lr,
+                              hipStream_t st);
+
+}  // namespace oba

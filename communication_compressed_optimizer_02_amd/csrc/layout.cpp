@@ -1,0 +1,90 @@
+// layout.cpp -- host-only validation and piece planning (see layout.hpp).
+#include "layout.hpp"
+
+#include <algorithm>
+#include <climits>
+
+namespace oba {
+
+namespace {
+
+constexpr int kOk = 0, kEInval = -1, kESeg = -3, kENoMem = -6;
+
+int check_table(int64_t d, const int64_t* seg, int32_t n_seg) {
+  if (!seg) return kEInval;
+  if (d == 0) return (n_seg == 0 && seg[0] == 0) ? kOk : kESeg;
+  if (n_seg < 1 || n_seg > INT32_MAX - 1) return kESeg;
+  if (seg[0] != 0 || seg[n_seg] != d) return kESeg;
+  for (int32_t j = 0; j < n_seg; ++j)
+    if (seg[j + 1] <= seg[j]) return kESeg;
+  return kOk;
+}
+
+// Cut segment table `off` at the block boundaries of the streaming grid.
+int cut(const Plan& P, const std::vector<int64_t>& off, Pieces* out) {
+  const int32_t n_seg = (int32_t)off.size() - 1;
+  out->lo.clear();
+  out->hi.clear();
+  out->seg.clear();
+  out->blk_first.assign((size_t)P.nblk + 1, 0);
+  out->seg_first.assign((size_t)n_seg + 1, 0);
+  int32_t j = 0;
+  for (int32_t b = 0; b < P.nblk; ++b) {
+    out->blk_first[b] = (int32_t)out->lo.size();
+    const int64_t r0 = span_begin(P.S, P.nblk, b) * kSpan;
+    const int64_t r1 = std::min(span_begin(P.S, P.nblk, b + 1) * kSpan, P.d);
+    while (off[j + 1] <= r0) ++j;
+    for (int32_t jj = j; jj < n_seg && off[jj] < r1; ++jj) {
+      if (out->lo.size() >= (size_t)INT32_MAX - 1) return kESeg;
+      out->lo.push_back(std::max(r0, off[jj]));
+      out->hi.push_back(std::min(r1, off[jj + 1]));
+      out->seg.push_back(jj);
+    }
+  }
+  out->blk_first[P.nblk] = (int32_t)out->lo.size();
+  // pieces are in coordinate order, so each segment's pieces are consecutive
+  int32_t q = 0;
+  for (int32_t s = 0; s < n_seg; ++s) {
+    while (out->seg[q] < s) ++q;
+    out->seg_first[s] = q;
+  }
+  out->seg_first[n_seg] = (int32_t)out->lo.size();
+  return kOk;
+}
+
+}  // namespace
+
+int validate(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_wseg,
+             const int64_t* sseg, int32_t n_sseg) {
+  if (d < 0 || d > ((int64_t)1 << 46)) return kEInval;
+  if (n < 1 || n > kMaxWorkers) return kEInval;
+  if (ld < d || ld % 8 != 0 || ld > ((int64_t)1 << 46)) return kEInval;
+  int rc = check_table(d, wseg, n_wseg);
+  if (rc) return rc;
+  return check_table(d, sseg, n_sseg);
+}
+
+int make_plan(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_wseg,
+              const int64_t* sseg, int32_t n_sseg, Plan* out) {
+  int rc = validate(d, n, ld, wseg, n_wseg, sseg, n_sseg);
+  if (rc) return rc;
+  try {
+    Plan P;
+    P.d = d;
+    P.n = n;
+    P.ld = ld;
+    P.W = (d + 63) / 64;
+    P.S = (d + kSpan - 1) / kSpan;
+    P.nblk = (int32_t)std::min<int64_t>(P.S, kMaxBlocks);
+    P.wseg.assign(wseg, wseg + n_wseg + 1);
+    P.sseg.assign(sseg, sseg + n_sseg + 1);
+    if ((rc = cut(P, P.wseg, &P.wp))) return rc;
+    if ((rc = cut(P, P.sseg, &P.sp))) return rc;
+    *out = std::move(P);
+  } catch (...) {
+    return kENoMem;
+  }
+  return kOk;
+}
+
+}  // namespace oba

@@ -1,0 +1,49 @@
+// layout.hpp -- host-only planning of the streaming grid and segment pieces.
+//
+// The streaming kernels cut [0, d) into spans of kSpan coordinates (one span
+// = one pass of a 256-thread block, 8 consecutive coordinates per lane) and
+// give block b the contiguous span range [b*S/nblk, (b+1)*S/nblk).  A segment
+// table is then cut at block boundaries into "pieces": each piece lies in one
+// block and one segment, so a block can reduce its part of a segment's sum of
+// squares into one binary64 partial per piece without atomics, and a segment's
+// pieces are consecutive (its partials are summed in a fixed order).
+//
+// No HIP here: this file is also compiled by the host compiler for tests.
+#pragma once
+#include <cstdint>
+#include <vector>
+
+namespace oba {
+
+constexpr int kBlock = 256;                 // threads per block (4 wave64)
+constexpr int kVec = 8;                     // consecutive coordinates per lane
+constexpr int64_t kSpan = kBlock * kVec;    // coordinates per block pass
+constexpr int kMaxBlocks = 2048;            // 8 resident blocks on each of 256 CUs
+constexpr int32_t kMaxWorkers = 4096;
+
+struct Pieces {
+  std::vector<int64_t> lo, hi;      // piece [lo, hi)
+  std::vector<int32_t> seg;         // segment of the piece
+  std::vector<int32_t> blk_first;   // [nblk+1] first piece of each block
+  std::vector<int32_t> seg_first;   // [n_seg+1] first piece of each segment
+};
+
+struct Plan {
+  int64_t d = 0, ld = 0, W = 0, S = 0;
+  int32_t n = 0, nblk = 0;
+  std::vector<int64_t> wseg, sseg;  // offsets, n_seg+1 each
+  Pieces wp, sp;
+};
+
+// Status codes mirror the C ABI (0 ok, negative error).
+int validate(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_wseg,
+             const int64_t* sseg, int32_t n_sseg);
+
+int make_plan(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_wseg,
+              const int64_t* sseg, int32_t n_sseg, Plan* out);
+
+inline int64_t span_begin(int64_t S, int32_t nblk, int32_t b) {
+  return (int64_t)b * S / nblk;
+}
+
+}  // namespace oba

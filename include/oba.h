@@ -1,0 +1,186 @@
+/*
+ * oba.h -- C ABI of the 1-bit Adam compression-stage step on AMD MI355X
+ * (gfx950).  All arithmetic runs in the library's HIP kernels; the caller
+ * owns every buffer and the stream.
+ *
+ * Method (pages cited by title and section):
+ *   [Tang]   "1-bit Adam: Communication Efficient Large-Scale Training with
+ *            Adam's Convergence Speed" (paper summary page), sections 3.3,
+ *            4.1-4.3, 5, 6, 11, 12 as numbered there.
+ *   [AIMech] "1-bit Adam (Two-Stage Preconditioner-Frozen Error-Compensated
+ *            Adam)" (curated algorithm page): definition paragraph and the
+ *            mechanism claims (preconditioner freeze; compressed
+ *            gather-broadcast allreduce with worker and server errors).
+ *   [CwP]    "1-bit Adam" (method description page): the scale factor and
+ *            the volume reduction of the packed message.
+ *
+ * Two stages: plain Adam for a warm-up ([Tang] 4.3), then the variance is
+ * frozen into a fixed preconditioner and the momentum is exchanged in a
+ * 1-bit, error-compensated form ([Tang] 4.3, 6; [AIMech] definition).  The
+ * n data-parallel workers are n rows of device buffers; the gather to the
+ * servers and the broadcast back become packed sign words in device memory.
+ *
+ * ---- Conventions (every entry point) ----------------------------------
+ * Sizes: d parameters, n workers, ld = row stride (elements) of the [n][ld]
+ *   buffers g and delta, W = ceil(d/64) packed words per row.
+ * Memory: every pointer named in a call is DEVICE memory of the current HIP
+ *   device, except the segment tables of oba_layout_create/validate, which
+ *   are HOST arrays copied by the call.  float/half buffers must be 16-byte
+ *   aligned, packed words 8-byte aligned, scales 4-byte aligned.
+ * Packed signs: bit j of word w is coordinate 64*w+j (least significant bit
+ *   first); bit 1 = negative, bit 0 = non-negative (sign(0) = +1, also for
+ *   -0.0); bits past d in the last word are written as 0.
+ * Segments: a segment table holds n_seg+1 strictly increasing offsets from 0
+ *   to d; each segment carries one scale.  Worker segments (sigma) give the
+ *   scales of the workers' messages, server segments (tau) those of the
+ *   server's.  Boundaries may fall anywhere, also inside a 64-bit word.
+ * Numerics: hyperparameters are binary64 and each binary32 coefficient is
+ *   rounded from them once (1-beta is formed in binary64 first).  Elementwise
+ *   work is binary32 in the order given per call, no fused multiply-add,
+ *   subnormals kept, division and square root correctly rounded.  Sums of
+ *   squares are binary64, reduced in a fixed order (results are bitwise
+ *   reproducible run to run on one device).
+ * Asynchrony: a call validates its arguments on the host, enqueues its
+ *   kernels on `stream` and returns; nothing is synchronised.  Faults from a
+ *   kernel surface at the caller's next synchronisation.
+ * Errors: 0 on success, a negative OBA_E* code otherwise; argument errors are
+ *   found before any HIP call and leave every buffer untouched.
+ *   oba_status_string gives a message (for OBA_EHIP it includes the HIP
+ *   error text of the failing launch on this thread).
+ * Aliasing: the in/out buffers named below are updated in place; no other
+ *   two buffer arguments of a call may overlap.
+ * Threads: calls are reentrant.  One workspace must not be used by two
+ *   calls that can run at the same time (two streams).
+ */
+#ifndef OBA_H
+#define OBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  OBA_OK = 0,
+  OBA_EINVAL = -1,     /* null pointer, bad size, bad dtype, bad hyperparameter */
+  OBA_EALIGN = -2,     /* a buffer is not aligned as required */
+  OBA_ESEG = -3,       /* a segment table is not 0 = o_0 < o_1 < ... < o_k = d */
+  OBA_EWORKSPACE = -4, /* workspace smaller than oba_workspace_bytes() */
+  OBA_EHIP = -5,       /* a HIP call failed (see oba_status_string) */
+  OBA_ENOMEM = -6      /* host or device allocation of the layout failed */
+};
+
+enum { OBA_F32 = 0, OBA_F16 = 1 }; /* gradient dtype: binary32 or binary16 */
+
+typedef struct oba_layout_s* oba_layout;
+
+/* Library version, 100*major + minor. */
+int oba_version(void);
+
+/* Message for a status code (static storage; OBA_EHIP's text is per thread). */
+const char* oba_status_string(int status);
+
+/* ---- layout --------------------------------------------------------------
+ * Checks, on the host only, that (d, n, ld) and both segment tables are
+ * valid: d >= 0, 1 <= n <= 4096, ld >= d, ld % 8 == 0, and each table rises
+ * strictly from 0 to d (for d = 0 the table is the single offset {0} and
+ * n_seg = 0).  Pure function: no HIP call, no allocation. */
+int oba_layout_validate(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_wseg,
+                        const int64_t* sseg, int32_t n_sseg);
+
+/* Validates as above, then builds the handle: small device copies of the
+ * segment tables and of the per-block piece lists the kernels walk (about
+ * 40 bytes per segment plus 80 bytes per thread block of the streaming
+ * grid).  Allocates on the current device; the handle must be used on that
+ * device only.  *out is set only on success. */
+int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const int64_t* wseg,
+                      int32_t n_wseg, const int64_t* sseg, int32_t n_sseg);
+
+/* Frees the handle's device tables (synchronises the device first). */
+void oba_layout_destroy(oba_layout layout);
+
+/* Bytes of device workspace that oba_compress and
+ * oba_server_reduce_recompress need (per-block binary64 partial sums). */
+size_t oba_workspace_bytes(oba_layout layout);
+
+/* ---- warm-up (plain Adam on the mean gradient) --------------------------
+ * [AIMech] definition paragraph (the two moment recurrences, the update
+ * x -= lr * m / (sqrt(v) + eta)); [Tang] 1 and 4.3 (Adam, uncompressed,
+ * during the warm-up).  g: [n][ld] of dtype g_dtype (rows are workers).
+ * x, m, v: [d] binary32, updated in place.  Per coordinate:
+ *   gbar = (((0 + g_0) + g_1) + ... + g_{n-1}) / n
+ *   m = b1*m + (1-b1)*gbar;  v = b2*v + (1-b2)*(gbar*gbar)
+ *   x = x - (lr*(m/bc1)) / (sqrt(v/bc2) + eta)
+ * bc1 = bc2 = 1 gives the bare recurrences; pass 1-b1^t, 1-b2^t for
+ * Kingma-Ba bias correction.  Requires 0 <= beta < 1, bc > 0, eta >= 0. */
+int oba_adam_warmup_step(oba_layout layout, const void* g, int g_dtype, float* x, float* m,
+                         float* v, double lr, double beta1, double beta2, double eta, double bc1,
+                         double bc2, hipStream_t stream);
+
+/* ---- variance freeze ------------------------------------------------------
+ * [AIMech] definition paragraph (V = diag(sqrt(v_Tw) + eps) is frozen);
+ * [Tang] 3.3, 5.  denom[k] = sqrt(v[k]/bc2) + eta, once, at the end of the
+ * warm-up.  v, denom: [d] binary32 (distinct buffers).  The caller zeroes
+ * the worker errors delta and the server error eps before the first
+ * compression step; the momentum m carries over. */
+int oba_freeze_variance(oba_layout layout, const float* v, float* denom, double eta, double bc2,
+                        hipStream_t stream);
+
+/* ---- worker side: momentum, error compensation, 1-bit compression -------
+ * [Tang] 4.3 and 11 (each worker updates its momentum and compresses it
+ * with error compensation, sign plus a magnitude-keeping scale); [CwP]
+ * (scale = ||c|| / ||sign(c)||); [AIMech] gather-broadcast mechanism
+ * (worker error memory delta_i).  For every worker i and coordinate k:
+ *   c = (b1*m + (1-b1)*g_i) + delta_i
+ *   s_{i,sigma} = sqrt(sum_{k in sigma} c^2 / |sigma|)   (binary64 sum)
+ *   bit = (c < 0);  delta_i = c - s*sign(c)
+ * g: [n][ld] (g_dtype); m: [d]; delta: [n][ld] in/out; wbits: [n][W] out;
+ * wscale: [n][n_wseg] out.  ws: workspace of at least
+ * oba_workspace_bytes(layout) bytes (contents on entry are ignored). */
+int oba_compress(oba_layout layout, const void* g, int g_dtype, const float* m, float* delta,
+                 uint64_t* wbits, float* wscale, double beta1, void* ws, size_t ws_bytes,
+                 hipStream_t stream);
+
+/* ---- server side: average, server error, recompression ------------------
+ * [Tang] 6 and 11 (the server averages the workers' compressed messages and
+ * compresses the result again); [AIMech] gather-broadcast mechanism (server
+ * error memory eps).  For every coordinate k (s_i = worker i's scale of the
+ * worker segment holding k, sg_i its sign):
+ *   a = (((0 + s_0*sg_0) + s_1*sg_1) + ... + s_{n-1}*sg_{n-1}) / n + eps
+ *   sbar_tau = sqrt(sum_{k in tau} a^2 / |tau|)          (binary64 sum)
+ *   sbit = (a < 0);  eps = a - sbar*sign(a)
+ * wbits: [n][W]; wscale: [n][n_wseg]; eps: [d] in/out; sbits: [W] out;
+ * sscale: [n_sseg] out.  ws as for oba_compress. */
+int oba_server_reduce_recompress(oba_layout layout, const uint64_t* wbits, const float* wscale,
+                                 float* eps, uint64_t* sbits, float* sscale, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/* ---- broadcast: decompress, precondition, update --------------------------
+ * [Tang] 11 (the server broadcasts the momentum, workers update their
+ * models); [AIMech] definition paragraph (x_t = x_{t-1} - gamma V^-1 m_hat).
+ * Every worker holds the same momentum afterwards.  Per coordinate:
+ *   m_hat = sbar_tau * sign;  m = m_hat;  x = x - (lr*m_hat) / denom
+ * sbits: [W]; sscale: [n_sseg]; denom: [d]; m, x: [d] in/out. */
+int oba_decompress_update(oba_layout layout, const uint64_t* sbits, const float* sscale,
+                          const float* denom, float* m, float* x, double lr, hipStream_t stream);
+
+/* ---- kernel timing (measurement aid) ---------------------------------------
+ * While enabled, every kernel the library launches is bracketed by two HIP
+ * events on the launch stream (up to `capacity` launches are kept).
+ * oba_timing_read synchronises on the recorded events and returns the summed
+ * duration in milliseconds and the launch count of the kernels whose name
+ * equals `kernel` ("compress_p1", "compress_p2", "finalize_scales",
+ * "server_p1", "server_p2", "decompress_update", "adam_warmup",
+ * "freeze_variance").  oba_timing_reset drops all records. */
+int oba_timing_enable(int on, int32_t capacity);
+int oba_timing_read(const char* kernel, double* total_ms, int64_t* launches);
+int oba_timing_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OBA_H */

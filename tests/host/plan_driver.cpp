@@ -1,0 +1,42 @@
+// plan_driver.cpp -- test driver for the host-only piece planner.
+// Usage: plan_driver d n ld n_wseg o_0 .. o_nw n_sseg o_0 .. o_ns
+// Prints "rc <status>", then "G d W S nblk", then for each segmentation
+// "T <n_pieces> <n_seg>", one "P lo hi seg" line per piece, "B" + blk_first,
+// "S" + seg_first.  Built by the test suite with the host compiler and
+// sanitizers; it calls nothing of HIP.
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "layout.hpp"
+
+static void dump(const oba::Pieces& p, int n_seg) {
+  std::printf("T %zu %d\n", p.lo.size(), n_seg);
+  for (size_t i = 0; i < p.lo.size(); ++i)
+    std::printf("P %lld %lld %d\n", (long long)p.lo[i], (long long)p.hi[i], p.seg[i]);
+  std::printf("B");
+  for (int v : p.blk_first) std::printf(" %d", v);
+  std::printf("\nS");
+  for (int v : p.seg_first) std::printf(" %d", v);
+  std::printf("\n");
+}
+
+int main(int argc, char** argv) {
+  int a = 1;
+  auto next = [&]() { return a < argc ? std::atoll(argv[a++]) : 0LL; };
+  const long long d = next(), n = next(), ld = next();
+  const int nw = (int)next();
+  std::vector<int64_t> w(nw + 1);
+  for (auto& x : w) x = next();
+  const int ns = (int)next();
+  std::vector<int64_t> s(ns + 1);
+  for (auto& x : s) x = next();
+  oba::Plan P;
+  int rc = oba::make_plan(d, (int32_t)n, ld, w.data(), nw, s.data(), ns, &P);
+  std::printf("rc %d\n", rc);
+  if (rc) return 0;
+  std::printf("G %lld %lld %lld %d\n", (long long)P.d, (long long)P.W, (long long)P.S, P.nblk);
+  dump(P.wp, nw);
+  dump(P.sp, ns);
+  return 0;
+}

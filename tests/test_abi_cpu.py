@@ -1,0 +1,160 @@
+"""CPU-only checks of the boundary: the C-ABI library loads and exports every
+entry point of include/oba.h, argument validation rejects bad layouts on the
+host, and the host planner (built with address and undefined-behaviour
+sanitizers) cuts segment tables into pieces that the kernels can walk."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from communication_compressed_optimizer_02_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "oba.h")
+CSRC = os.path.join(ROOT, "communication_compressed_optimizer_02_amd", "csrc")
+SPAN, MAXB = 2048, 2048
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(oba_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_entry_point():
+    L = ctypes.CDLL(binding.LIB_PATH)
+    syms = declared_symbols()
+    assert {"oba_compress", "oba_server_reduce_recompress", "oba_decompress_update",
+            "oba_adam_warmup_step", "oba_freeze_variance"} <= set(syms)
+    for s in syms:
+        assert hasattr(L, s), s
+    assert set(binding.SIGNATURES) == set(syms)
+    assert binding.lib().oba_version() == 100
+
+
+def test_status_strings():
+    for rc in (0, -1, -2, -3, -4, -5, -6):
+        assert binding.status_string(rc)
+    assert "segment" in binding.status_string(-3)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(d=100, n=2, wseg=[0, 100], sseg=[0, 50, 100]), 0),
+    (dict(d=100, n=2, wseg=[0, 100], sseg=[0, 50, 100], ld=104), 0),
+    (dict(d=0, n=1, wseg=[0], sseg=[0]), 0),
+    (dict(d=100, n=0, wseg=[0, 100], sseg=[0, 100]), -1),
+    (dict(d=100, n=4097, wseg=[0, 100], sseg=[0, 100]), -1),
+    (dict(d=-1, n=1, wseg=[0, 1], sseg=[0, 1]), -1),
+    (dict(d=100, n=2, wseg=[0, 100], sseg=[0, 100], ld=99), -1),
+    (dict(d=100, n=2, wseg=[0, 100], sseg=[0, 100], ld=100), -1),
+    (dict(d=100, n=2, wseg=[0, 100], sseg=[0, 100], ld=101), -1),
+    (dict(d=100, n=2, wseg=[0, 99], sseg=[0, 100]), -3),
+    (dict(d=100, n=2, wseg=[1, 100], sseg=[0, 100]), -3),
+    (dict(d=100, n=2, wseg=[0, 50, 50, 100], sseg=[0, 100]), -3),
+    (dict(d=100, n=2, wseg=[0, 60, 40, 100], sseg=[0, 100]), -3),
+    (dict(d=100, n=2, wseg=[0, 100], sseg=[0, 101]), -3),
+    (dict(d=0, n=1, wseg=[0, 0], sseg=[0]), -3),
+])
+def test_layout_validation_on_host(case, expect):
+    assert binding.validate(**case) == expect
+
+
+@pytest.fixture(scope="module")
+def driver(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("plan") / "plan_driver")
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-g", "-O1"]
+    subprocess.run(["g++", "-std=c++17", *san, f"-I{CSRC}",
+                    os.path.join(ROOT, "tests", "host", "plan_driver.cpp"),
+                    os.path.join(CSRC, "layout.cpp"), "-o", exe], check=True)
+    return exe
+
+
+def run_plan(exe, d, n, wseg, sseg, ld=None):
+    ld = binding.default_ld(d) if ld is None else ld
+    args = [exe, str(d), str(n), str(ld), str(len(wseg) - 1), *map(str, wseg),
+            str(len(sseg) - 1), *map(str, sseg)]
+    out = subprocess.run(args, check=True, capture_output=True, text=True).stdout.split("\n")
+    rc = int(out[0].split()[1])
+    if rc:
+        return rc, None
+    _, dd, W, S, nblk = out[1].split()
+    res = dict(d=int(dd), W=int(W), S=int(S), nblk=int(nblk), tabs=[])
+    i = 2
+    for _ in range(2):
+        _, npc, nseg = out[i].split()
+        i += 1
+        pcs = [tuple(map(int, out[i + k].split()[1:])) for k in range(int(npc))]
+        i += int(npc)
+        blk = list(map(int, out[i].split()[1:]))
+        seg = list(map(int, out[i + 1].split()[1:]))
+        i += 2
+        res["tabs"].append((pcs, blk, seg))
+    return 0, res
+
+
+def check_pieces(res, offs):
+    d, S, nblk = res["d"], res["S"], res["nblk"]
+    for (pcs, blk, segf), off in zip(res["tabs"], offs):
+        assert len(blk) == nblk + 1 and blk[0] == 0 and blk[-1] == len(pcs)
+        # pieces tile [0, d) in order
+        pos = 0
+        for lo, hi, s in pcs:
+            assert lo == pos and hi > lo
+            assert off[s] <= lo and hi <= off[s + 1]
+            pos = hi
+        assert pos == d
+        # each block's pieces cover exactly its span range
+        for b in range(nblk):
+            r0 = (b * S // nblk) * SPAN
+            r1 = min(((b + 1) * S // nblk) * SPAN, d)
+            mine = pcs[blk[b]:blk[b + 1]]
+            assert mine and mine[0][0] == r0 and mine[-1][1] == r1
+        # each segment's pieces are consecutive, first index recorded
+        assert len(segf) == len(off) and segf[-1] == len(pcs)
+        for j in range(len(off) - 1):
+            mine = pcs[segf[j]:segf[j + 1]]
+            assert mine and all(p[2] == j for p in mine)
+            assert mine[0][0] == off[j] and mine[-1][1] == off[j + 1]
+
+
+@pytest.mark.parametrize("d,n,wseg,sseg", [
+    (1, 1, [0, 1], [0, 1]),
+    (4096, 2, [0, 4096], [0, 2048, 4096]),
+    (2049, 3, [0, 7, 2048, 2049], [0, 1000, 2049]),
+    (110_000_000, 4, [0, 110_000_000], [j * 110_000_000 // 4 for j in range(5)]),
+    (5_000_003, 5, [0, 5_000_003], [j * 5_000_003 // 5 for j in range(6)]),
+    (300, 2, list(range(301)), [0, 150, 300]),
+])
+def test_planner_pieces_under_sanitizers(driver, d, n, wseg, sseg):
+    rc, res = run_plan(driver, d, n, wseg, sseg)
+    assert rc == 0
+    assert res["W"] == (d + 63) // 64 and res["S"] == -(-d // SPAN)
+    assert res["nblk"] == min(res["S"], MAXB)
+    check_pieces(res, [wseg, sseg])
+
+
+def test_planner_handles_the_tensor_list_and_random_tables(driver):
+    from communication_compressed_optimizer_02_amd import synth
+
+    t = synth.chunk_table(synth.gpt2_xl_tensor_sizes()).tolist()
+    assert len(t) - 1 == 392 and t[-1] == 1_556_920_000
+    rc, res = run_plan(driver, t[-1], 4, t, t)
+    assert rc == 0
+    check_pieces(res, [t, t])
+    rng = np.random.default_rng(0)
+    for _ in range(10):
+        d = int(rng.integers(1, 50_000))
+        cuts = sorted(set(rng.integers(1, d, size=rng.integers(0, 40)).tolist())) if d > 1 else []
+        w = [0] + cuts + [d]
+        s = [0] + sorted(set(rng.integers(1, d, size=3).tolist()) if d > 1 else []) + [d]
+        rc, res = run_plan(driver, d, 3, w, s)
+        assert rc == 0
+        check_pieces(res, [w, s])
+
+
+def test_planner_rejects_bad_tables(driver):
+    assert run_plan(driver, 100, 2, [0, 50, 50, 100], [0, 100])[0] == -3
+    assert run_plan(driver, 100, 2, [0, 100], [0, 100], ld=100)[0] == -1
