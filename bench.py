@@ -91,25 +91,57 @@ def make_state(w, torch, oba, synth):
     return L, S, (g_a, g_b)
 
 
-def cpu_baseline(w, synth, d_sample):
+def cpu_baseline(w, torch, synth, d_sample):
     """The oracle (single-threaded C) on a bounded sample of the same
-    workload: one compression step over d_sample coordinates, all n workers."""
+    workload: one compression step over d_sample coordinates for all n
+    workers.  The sample is drawn with the workload's device generators and
+    copied to the host (drawing it with numpy would take longer than the
+    timed oracle run)."""
     import numpy as np
 
     import oracle
 
     ws = synth.scaled(w, d_sample)
-    rng = np.random.default_rng(w.seed)
-    st = synth.host_state(rng, ws.d, ws.n)
-    st["denom"] = oracle.freeze_variance(st["v"], synth.ETA)
-    zero = synth.zero_mask_host(rng, ws.d) if w.name == "bert_large" else None
-    g = synth.host_grads(rng, ws, zero_idx=zero)
+    gen = synth.device_generator(w.seed + 1000)
+    dev = "cuda"
+    zero = synth.device_zero_mask(gen, ws.d) if w.name == "bert_large" else None
+    g = torch.empty((ws.n, ws.d), dtype=torch.float16 if ws.g_dtype == "f16" else torch.float32,
+                    device=dev)
+    synth.device_grads(gen, ws, g, zero)
+
+    def normal(shape, std):
+        return torch.empty(shape, device=dev).normal_(0.0, std, generator=gen).cpu().numpy()
+
+    st = {"x": normal(ws.d, 0.02), "m": normal(ws.d, 1e-3), "delta": normal((ws.n, ws.d), 1e-4),
+          "eps": normal(ws.d, 1e-4)}
+    v = normal(ws.d, 1e-3) ** 2
+    st["denom"] = oracle.freeze_variance(np.ascontiguousarray(v, dtype=np.float32), synth.ETA)
+    g = g.cpu().numpy()
     t0 = time.perf_counter()
     oracle.step(st, g, ws.wseg, ws.sseg, synth.BETA1, synth.LR)
     dt = time.perf_counter() - t0
     return {"value": ws.d / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"one compression step of the {w.name} recipe at d={ws.d:,} "
-                      f"(n={ws.n}, {ws.g_dtype} gradients), {dt:.2f} s on 1 thread"}
+            "sample": f"one compression step (compress, server, update) of the {w.name} recipe "
+                      f"at d={ws.d:,}, n={ws.n}, {ws.g_dtype} gradients: {dt:.2f} s on 1 thread"}
+
+
+def copy_reference(torch, nbytes=1 << 31, reps=5):
+    """Device-to-device copy of nbytes (read nbytes + write nbytes), the
+    plain streaming kernel that calibrates what HBM delivers on this machine."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return {"bytes_moved": 2 * nbytes, "avg_ms": round(ms, 4),
+            "GBps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
 def main():
@@ -120,7 +152,7 @@ def main():
     ap.add_argument("--workload", default="bert_large",
                     choices=["tiny", "bert_base", "bert_large", "gpt2_xl", "quadratic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 23)
+    ap.add_argument("--cpu-sample", type=int, default=128_000_000)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the n data-parallel workers are simulated as n "
@@ -202,9 +234,10 @@ def main():
     }
     del S, gsets
     torch.cuda.empty_cache()
+    out["copy_reference"] = copy_reference(torch)
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
-        out["cpu_baseline"] = cpu_baseline(w, synth, min(args.cpu_sample, w.d))
+        out["cpu_baseline"] = cpu_baseline(w, torch, synth, min(args.cpu_sample, w.d))
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
