@@ -35,14 +35,15 @@ def log(*a):
 
 
 def gbytes(w):
-    """Algorithmic HBM bytes per parameter of each kernel: every buffer the
-    method defines is moved once per direction in that kernel."""
+    """Algorithmic HBM bytes per parameter of each kernel of a step: every
+    buffer a kernel must touch, once per direction."""
     n, gb = w.n, (2 if w.g_dtype == "f16" else 4)
+    reads = 4 + n * (gb + 4)  # m, g_i, delta_i
     return {
-        # m read, g_i read, delta_i read (c written over it), packed bits written
-        "compress_p1": 4 + n * (gb + 4 + 4) + n / 8,
-        # c read, delta written
-        "compress_p2": 8 * n,
+        # norm pass: m, g_i, delta_i read
+        "compress_p1": reads,
+        # apply pass: m, g_i, delta_i read again; delta_i and packed bits written
+        "compress_p2": reads + 4 * n + n / 8,
         # worker bits read, eps read, a written over eps, server bits written
         "server_p1": n / 8 + 8 + 1 / 8,
         # a read, eps written
@@ -50,6 +51,13 @@ def gbytes(w):
         # server bits read, denom read, x read+written, m written
         "decompress_update": 1 / 8 + 16,
     }
+
+
+def method_bytes(w):
+    """Bytes per parameter if every buffer of the method is touched once per
+    direction per step: n(|g| + 8.25) + 28.25."""
+    gb = 2 if w.g_dtype == "f16" else 4
+    return w.n * (gb + 8.25) + 28.25
 
 
 def source_hash():
@@ -201,7 +209,8 @@ def main():
             ent["alg_bytes_per_param"] = alg[k]
             ent["alg_GBps"] = round(alg[k] * w.d / (avg_ms * 1e-3) / 1e9, 1)
         kernels[k] = ent
-    dom = "compress_p1"
+    # dominant kernel: the largest share of the step's time
+    dom = max(alg, key=lambda k: per_kernel[k][0])
     dom_ms = per_kernel[dom][0]
     dom_bytes = alg[dom] * w.d
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
@@ -225,6 +234,7 @@ def main():
                    "parallelism": "dp%d simulated on one GPU" % w.n},
         "step_alg_GBps": round(step_alg / (ms * 1e-3) / 1e9, 1),
         "step_alg_bytes_per_param": round(sum(alg.values()), 3),
+        "method_bytes_per_param": round(method_bytes(w), 3),
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": dom_bytes,

@@ -283,13 +283,14 @@ int oba_compress(oba_layout L, const void* g, int g_dtype, const float* m, float
   const float b1 = (float)beta1, omb1 = (float)(1.0 - beta1);
   uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
   OBA_TRY(launch("compress_p1", stream, [&] {
-    oba::launch_compress_p1(G, g, g_dtype == OBA_F16, m, delta, wbytes, L->sig, part, b1, omb1,
-                            stream);
+    oba::launch_compress_norm(G, g, g_dtype == OBA_F16, m, delta, L->sig, part, b1, omb1, stream);
   }));
   OBA_TRY(launch("finalize_scales", stream,
                  [&] { oba::launch_finalize(part, G.n, L->sig, wscale, stream); }));
-  return launch("compress_p2", stream,
-                [&] { oba::launch_residual(G, delta, G.ld, G.n, wscale, L->sig, stream); });
+  return launch("compress_p2", stream, [&] {
+    oba::launch_compress_apply(G, g, g_dtype == OBA_F16, m, delta, wbytes, L->sig, wscale, b1,
+                               omb1, stream);
+  });
 }
 
 int oba_server_reduce_recompress(oba_layout L, const uint64_t* wbits, const float* wscale,

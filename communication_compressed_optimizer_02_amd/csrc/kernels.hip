@@ -26,12 +26,26 @@ namespace {
 // 8-wide loads and stores with a guarded tail (coordinates >= d read as 0
 // and are never written).  Row bases are 32-byte aligned for binary32 and
 // 16-byte aligned for binary16 (16-byte-aligned base, ld % 8 == 0, k0 % 8 == 0).
+// Streamed inputs are read with the nontemporal hint: every byte is used once
+// per pass, so there is nothing for the caches to keep.
 // -------------------------------------------------------------------------
+#ifndef OBA_NT_LOADS
+#define OBA_NT_LOADS 1
+#endif
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename V>
+__device__ __forceinline__ V ldv(const V* p) {
+  if constexpr (OBA_NT_LOADS) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
 __device__ __forceinline__ void load8(const float* __restrict__ p, int64_t k0, int64_t d,
                                       float (&v)[8]) {
   if (k0 + 8 <= d) {
-    const float4 a = *reinterpret_cast<const float4*>(p + k0);
-    const float4 b = *reinterpret_cast<const float4*>(p + k0 + 4);
+    const f32x4 a = ldv(reinterpret_cast<const f32x4*>(p + k0));
+    const f32x4 b = ldv(reinterpret_cast<const f32x4*>(p + k0 + 4));
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   } else {
@@ -47,7 +61,7 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
 __device__ __forceinline__ void load8(const uint16_t* __restrict__ p, int64_t k0, int64_t d,
                                       float (&v)[8]) {
   if (k0 + 8 <= d) {
-    const uint4 a = *reinterpret_cast<const uint4*>(p + k0);
+    const u32x4 a = ldv(reinterpret_cast<const u32x4*>(p + k0));
     const uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -58,6 +72,38 @@ __device__ __forceinline__ void load8(const uint16_t* __restrict__ p, int64_t k0
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = (k0 + j < d) ? half_bits_to_float(p[k0 + j]) : 0.0f;
   }
+}
+
+__device__ __forceinline__ float grad_at(const float* p, int64_t k) { return p[k]; }
+__device__ __forceinline__ float grad_at(const uint16_t* p, int64_t k) {
+  return half_bits_to_float(p[k]);
+}
+
+// Full-span loaders: no tail check, so a kernel can issue every load of a
+// span before it uses any of them (a checked load is followed by its wait).
+__device__ __forceinline__ void load8_full(const float* __restrict__ p, int64_t k0,
+                                           float (&v)[8]) {
+  const f32x4 a = ldv(reinterpret_cast<const f32x4*>(p + k0));
+  const f32x4 b = ldv(reinterpret_cast<const f32x4*>(p + k0 + 4));
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ __forceinline__ void load8_full(const uint16_t* __restrict__ p, int64_t k0,
+                                           float (&v)[8]) {
+  const u32x4 a = ldv(reinterpret_cast<const u32x4*>(p + k0));
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = half_bits_to_float(w[j] & 0xFFFFu);
+    v[2 * j + 1] = half_bits_to_float(w[j] >> 16);
+  }
+}
+
+// c = (b1*m + (1-b1)*g) + delta: two products, then two adds (no contraction)
+__device__ __forceinline__ float compensate(float b1, float omb1, float m, float g, float dl) {
+  const float p = b1 * m + omb1 * g;
+  return p + dl;
 }
 
 __device__ __forceinline__ void store8(float* __restrict__ p, int64_t k0, int64_t d,
@@ -144,6 +190,23 @@ __device__ __forceinline__ double sumsq_range(const float* row, int64_t k0, int6
   return s;
 }
 
+// Same, recomputing c = compensate(m, g, delta) from the inputs.
+template <typename GT>
+__device__ __forceinline__ double sumsq_range_c(const float* m, const GT* grow, const float* drow,
+                                                float b1, float omb1, int64_t k0, int64_t a,
+                                                int64_t e) {
+  double s = 0.0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t k = k0 + j;
+    if (k >= a && k < e) {
+      const double x = (double)compensate(b1, omb1, m[k], grad_at(grow, k), drow[k]);
+      s = __builtin_fma(x, x, s);
+    }
+  }
+  return s;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -160,17 +223,37 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
   for (int64_t s = s_lo; s < s_hi; ++s) {
     const int64_t k0 = s * kSpan + (int64_t)threadIdx.x * kVec;
     if (k0 >= G.d) continue;
-    float sum[8], gv[8], mv[8], vv[8], xv[8];
+    const bool full = k0 + 8 <= G.d;
+    float sum[8], mv[8], vv[8], xv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) sum[j] = 0.0f;
-    for (int32_t i = 0; i < G.n; ++i) {
-      load8(g + (int64_t)i * G.ld, k0, G.d, gv);
+    for (int32_t i0 = 0; i0 < G.n; i0 += 4) {
+      // four rows loaded together (rows past n clamped, their terms skipped)
+      float gv[4][8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sum[j] = sum[j] + gv[j];
+      for (int u = 0; u < 4; ++u) {
+        const GT* row = g + (int64_t)min(i0 + u, G.n - 1) * G.ld;
+        if (full)
+          load8_full(row, k0, gv[u]);
+        else
+          load8(row, k0, G.d, gv[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + u < G.n) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sum[j] = sum[j] + gv[u][j];
+        }
     }
-    load8(m, k0, G.d, mv);
-    load8(v, k0, G.d, vv);
-    load8(x, k0, G.d, xv);
+    if (full) {
+      load8_full(m, k0, mv);
+      load8_full(v, k0, vv);
+      load8_full(x, k0, xv);
+    } else {
+      load8(m, k0, G.d, mv);
+      load8(v, k0, G.d, vv);
+      load8(x, k0, G.d, xv);
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float gb = sum[j] / nf;
@@ -198,7 +281,10 @@ __global__ __launch_bounds__(kBlock) void k_freeze(Geo G, const float* __restric
     const int64_t k0 = s * kSpan + (int64_t)threadIdx.x * kVec;
     if (k0 >= G.d) continue;
     float vv[8];
-    load8(v, k0, G.d, vv);
+    if (k0 + 8 <= G.d)
+      load8_full(v, k0, vv);
+    else
+      load8(v, k0, G.d, vv);
 #pragma unroll
     for (int j = 0; j < 8; ++j) vv[j] = __builtin_sqrtf(vv[j] / bc2) + eta;
     store8(denom, k0, G.d, vv);
@@ -206,22 +292,32 @@ __global__ __launch_bounds__(kBlock) void k_freeze(Geo G, const float* __restric
 }
 
 // ===========================================================================
-// Worker pass 1: c = (b1*m + (1-b1)*g_i) + delta_i for NB workers at once
-// (m is read once per coordinate), c stored over delta_i, sign byte stored,
-// binary64 sum of c^2 reduced per (piece, worker).
-// Grid: (nblk, ceil(n/NB)); block y handles workers [y*NB, y*NB+nw).
+// Worker side, for NB workers at once (m is read once per coordinate):
+//   c = (b1*m + (1-b1)*g_i) + delta_i
+// kNorm:  only reduce sum c^2 per (piece, worker) -- reads only;
+// kApply: recompute c bit for bit, store the sign byte and
+//         delta_i = c - s*sign(c) with the finished scales.
+// The scale needs the whole segment's norm before any residual can be
+// written, so c is needed twice.  Recomputing it reads g, m, delta twice but
+// never writes c: on this HBM, writes cost more than reads, and storing c in
+// a first pass to re-read it was measured 15 % slower per step.
+// NB is the exact number of workers of a block: a launch covers workers
+// [i0, i0 + gridDim.y*NB); n > 8 takes one launch of NB=8 groups and one
+// for the remainder.  Grid: (nblk, groups).
 // ===========================================================================
-template <typename GT, int NB>
-__global__ __launch_bounds__(kBlock) void k_compress_p1(Geo G, const GT* __restrict__ g,
-                                                        const float* __restrict__ m,
-                                                        float* __restrict__ delta,
-                                                        uint8_t* __restrict__ wbytes, SegDev sig,
-                                                        double* __restrict__ part, float b1,
-                                                        float omb1) {
+enum { kNorm = 1, kApply = 2 };
+
+template <typename GT, int NB, int MODE>
+__global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT* __restrict__ g,
+                                                     const float* __restrict__ m,
+                                                     float* __restrict__ delta,
+                                                     uint8_t* __restrict__ wbytes, SegDev sig,
+                                                     double* __restrict__ part,
+                                                     const float* __restrict__ wscale, float b1,
+                                                     float omb1) {
   __shared__ double lds[4 * NB];
   const int32_t b = blockIdx.x;
-  const int32_t i0 = blockIdx.y * NB;
-  const int nw = min(NB, G.n - i0);
+  i0 += blockIdx.y * NB;  // this block's workers: [i0, i0 + NB)
   const int64_t s_lo = dspan(G.S, G.nblk, b), s_hi = dspan(G.S, G.nblk, b + 1);
   const int32_t p_end = sig.blk_first[b + 1];
   int32_t p = sig.blk_first[b];
@@ -235,43 +331,83 @@ __global__ __launch_bounds__(kBlock) void k_compress_p1(Geo G, const GT* __restr
     const int64_t lo = s * kSpan;
     const int64_t hi = min(lo + kSpan, G.d);
     const int64_t k0 = lo + (int64_t)threadIdx.x * kVec;
-    float mv[8];
-    load8(m, k0, G.d, mv);
+    const bool uniform = hi <= p_hi;  // span inside the current piece
+    const bool full = lo + kSpan <= G.d;
+    int32_t jseg[8];
+    if (MODE == kApply && !uniform) {
+      int32_t js = sig.pseg[p];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (k0 + j < G.d) js = seg_walk(sig.off, js, k0 + j);
+        jseg[j] = js;
+      }
+    }
+    // every load of the span first (all NB workers), then the arithmetic
+    float mv[8], gv[NB][8], c[NB][8];
+    if (full) {
+      load8_full(m, k0, mv);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int64_t row = (int64_t)(i0 + i) * G.ld;
+        load8_full(g + row, k0, gv[i]);
+        load8_full(delta + row, k0, c[i]);
+      }
+    } else {
+      load8(m, k0, G.d, mv);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int64_t row = (int64_t)(i0 + i) * G.ld;
+        load8(g + row, k0, G.d, gv[i]);
+        load8(delta + row, k0, G.d, c[i]);
+      }
+    }
     double fs[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      fs[i] = 0.0;
-      if (i < nw) {
-        const int64_t row = (int64_t)(i0 + i) * G.ld;
-        float gv[8], c[8];
-        load8(g + row, k0, G.d, gv);
-        load8(delta + row, k0, G.d, c);
+      const int64_t row = (int64_t)(i0 + i) * G.ld;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float pj = b1 * mv[j] + omb1 * gv[j];
-          c[j] = pj + c[j];
+      for (int j = 0; j < 8; ++j) c[i][j] = compensate(b1, omb1, mv[j], gv[i][j], c[i][j]);
+      if (MODE != kNorm && k0 < 64 * G.W)
+        wbytes[(int64_t)(i0 + i) * rowbytes + (k0 >> 3)] = (uint8_t)sign_byte(c[i]);
+      fs[i] = (MODE == kNorm) ? sumsq8(c[i]) : 0.0;
+      if (MODE == kApply) {
+        const float* sc = wscale + (int64_t)(i0 + i) * sig.n_seg;
+        float sv[8];
+        if (uniform) {
+          const float s_ = sc[sig.pseg[p]];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sv[j] = s_;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sv[j] = sc[jseg[j]];
         }
-        store8(delta + row, k0, G.d, c);
-        if (k0 < 64 * G.W) wbytes[(int64_t)(i0 + i) * rowbytes + (k0 >> 3)] = (uint8_t)sign_byte(c);
-        fs[i] = sumsq8(c);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c[i][j] = (c[i][j] < 0.0f) ? c[i][j] + sv[j] : c[i][j] - sv[j];
+        store8(delta + row, k0, G.d, c[i]);
       }
     }
-    if (hi <= p_hi) {  // span inside the current piece
+    if (MODE == kApply) {
+      while (p < p_end && p_hi <= hi) {
+        if (++p < p_end) p_hi = sig.phi[p];
+      }
+    } else if (uniform) {
 #pragma unroll
       for (int i = 0; i < NB; ++i) acc[i] += fs[i];
       if (hi == p_hi) {
-        flush_rows<NB>(acc, nw, part + (int64_t)p * G.n + i0, lds);
+        flush_rows<NB>(acc, NB, part + (int64_t)p * G.n + i0, lds);
         if (++p < p_end) p_hi = sig.phi[p];
       }
-    } else {  // span crosses piece boundaries: re-read this lane's c from delta
+    } else {  // span crosses piece boundaries: sum this lane's c piece by piece
       int64_t cur = lo;
       while (cur < hi) {
         const int64_t e = min(p_hi, hi);
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
-          if (i < nw) acc[i] += sumsq_range(delta + (int64_t)(i0 + i) * G.ld, k0, cur, e);
+        for (int i = 0; i < NB; ++i) {
+          const int64_t row = (int64_t)(i0 + i) * G.ld;
+          acc[i] += sumsq_range_c(m, g + row, delta + row, b1, omb1, k0, cur, e);
+        }
         if (p_hi <= hi) {
-          flush_rows<NB>(acc, nw, part + (int64_t)p * G.n + i0, lds);
+          flush_rows<NB>(acc, NB, part + (int64_t)p * G.n + i0, lds);
           if (++p < p_end) p_hi = sig.phi[p];
         }
         cur = e;
@@ -284,19 +420,22 @@ __global__ __launch_bounds__(kBlock) void k_compress_p1(Geo G, const GT* __restr
 // Per-segment scale from the piece partials: s = sqrt(S / len) in binary64,
 // rounded once to binary32.  Grid: (n_seg, rows).  part: [n_pieces][rows].
 // ===========================================================================
-__global__ __launch_bounds__(kBlock) void k_finalize_scales(const double* __restrict__ part,
-                                                            int32_t rows, SegDev T,
-                                                            float* __restrict__ scale) {
-  __shared__ double lds[4];
+constexpr int kFinBlock = 1024;  // 16 waves: segments can have 65536 pieces
+
+__global__ __launch_bounds__(kFinBlock) void k_finalize_scales(const double* __restrict__ part,
+                                                               int32_t rows, SegDev T,
+                                                               float* __restrict__ scale) {
+  __shared__ double lds[kFinBlock / 64];
   const int32_t j = blockIdx.x, r = blockIdx.y;
   const int32_t q0 = T.seg_first[j], q1 = T.seg_first[j + 1];
   double t = 0.0;
-  for (int32_t q = q0 + threadIdx.x; q < q1; q += kBlock) t += part[(int64_t)q * rows + r];
+  for (int32_t q = q0 + threadIdx.x; q < q1; q += kFinBlock) t += part[(int64_t)q * rows + r];
   t = wave_sum(t);
   if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = t;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const double S = ((lds[0] + lds[1]) + lds[2]) + lds[3];
+    double S = 0.0;
+    for (int w = 0; w < kFinBlock / 64; ++w) S += lds[w];  // fixed order
     const double len = (double)(T.off[j + 1] - T.off[j]);
     scale[(int64_t)r * T.n_seg + j] = (float)__builtin_sqrt(S / len);
   }
@@ -321,7 +460,10 @@ __global__ __launch_bounds__(kBlock) void k_residual(Geo G, float* __restrict__ 
     const int64_t k0 = lo + (int64_t)threadIdx.x * kVec;
     if (k0 < G.d) {
       float c[8], sv[8];
-      load8(row, k0, G.d, c);
+      if (lo + kSpan <= G.d)
+        load8_full(row, k0, c);
+      else
+        load8(row, k0, G.d, c);
       if (hi <= p_hi) {
         const float s_ = sc[T.pseg[p]];
 #pragma unroll
@@ -347,8 +489,11 @@ __global__ __launch_bounds__(kBlock) void k_residual(Geo G, float* __restrict__ 
 // ===========================================================================
 // Server pass 1: a = (sum_i s_i*sign_i)/n + eps per coordinate (workers in
 // order), a stored over eps, server sign byte stored, binary64 sum of a^2
-// reduced per server piece.  Grid: nblk.
+// reduced per server piece.  The sign bytes and scales of NB workers are
+// loaded before any is used, so their loads overlap (NB = n for n <= 8, else
+// groups of 8).  Grid: nblk.
 // ===========================================================================
+template <int NB>
 __global__ __launch_bounds__(kBlock) void k_server_p1(Geo G, const uint8_t* __restrict__ wbytes,
                                                       const float* __restrict__ wscale,
                                                       float* __restrict__ eps,
@@ -368,46 +513,64 @@ __global__ __launch_bounds__(kBlock) void k_server_p1(Geo G, const uint8_t* __re
     const int64_t hi = min(lo + kSpan, G.d);
     const int64_t k0 = lo + (int64_t)threadIdx.x * kVec;
     double fs = 0.0;
-    if (k0 < G.d) {
+    const int64_t q = k0 >> 3;
+    if (hi <= ps_hi && lo + kSpan <= G.d) {
+      // fast path: full span, one worker segment; all loads first
+      const int32_t js0 = sig.pseg[ps];
       float ev[8], t[8];
-      load8(eps, k0, G.d, ev);
+      load8_full(eps, k0, ev);
 #pragma unroll
       for (int j = 0; j < 8; ++j) t[j] = 0.0f;
-      const int64_t q = k0 >> 3;
-      if (hi <= ps_hi) {  // one worker segment for the whole span
-        const int32_t js = sig.pseg[ps];
-        for (int32_t i = 0; i < G.n; ++i) {
-          const uint32_t byte = wbytes[(int64_t)i * rowbytes + q];
-          const float s_ = wscale[(int64_t)i * sig.n_seg + js];
+      for (int32_t i0 = 0; i0 < G.n; i0 += NB) {  // one pass when n <= NB
+        // rows past n are clamped to a valid row and their terms skipped
+        uint32_t byte[NB];
+        float sw[NB];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) t[j] = t[j] + (((byte >> j) & 1u) ? -s_ : s_);
+        for (int u = 0; u < NB; ++u) {
+          const int64_t r = min(i0 + u, G.n - 1);
+          byte[u] = wbytes[r * rowbytes + q];
+          sw[u] = wscale[r * sig.n_seg + js0];
         }
-      } else {
-        int32_t jseg[8];
-        int32_t js = sig.pseg[ps];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (k0 + j < G.d) js = seg_walk(sig.off, js, k0 + j);
-          jseg[j] = js;
-        }
-        for (int32_t i = 0; i < G.n; ++i) {
-          const uint32_t byte = wbytes[(int64_t)i * rowbytes + q];
-          const float* sc = wscale + (int64_t)i * sig.n_seg;
+        for (int u = 0; u < NB; ++u) {
+          if (i0 + u < G.n) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float s_ = sc[jseg[j]];
-            t[j] = t[j] + (((byte >> j) & 1u) ? -s_ : s_);
+            for (int j = 0; j < 8; ++j) t[j] = t[j] + (((byte[u] >> j) & 1u) ? -sw[u] : sw[u]);
           }
         }
       }
       float a[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) a[j] = (k0 + j < G.d) ? t[j] / nf + ev[j] : 0.0f;
+      for (int j = 0; j < 8; ++j) a[j] = t[j] / nf + ev[j];
       store8(eps, k0, G.d, a);
       sbytes[q] = (uint8_t)sign_byte(a);
       fs = sumsq8(a);
+    } else if (k0 < G.d) {
+      // general path (segment boundary in the span, or the tail): one
+      // coordinate at a time, same operations in the same order
+      uint32_t sb = 0;
+      int32_t js = sig.pseg[ps];
+#pragma unroll 1
+      for (int j = 0; j < 8; ++j) {
+        const int64_t k = k0 + j;
+        if (k < G.d) {
+          js = seg_walk(sig.off, js, k);
+          float t = 0.0f;
+          for (int32_t i = 0; i < G.n; ++i) {
+            const uint32_t byte = wbytes[(int64_t)i * rowbytes + q];
+            const float s_ = wscale[(int64_t)i * sig.n_seg + js];
+            t = t + (((byte >> j) & 1u) ? -s_ : s_);
+          }
+          const float a = t / nf + eps[k];
+          eps[k] = a;
+          sb |= (a < 0.0f ? 1u : 0u) << j;
+          const double x = (double)a;
+          fs = __builtin_fma(x, x, fs);
+        }
+      }
+      sbytes[q] = (uint8_t)sb;
     } else if (k0 < 64 * G.W) {
-      sbytes[k0 >> 3] = 0;
+      sbytes[q] = 0;
     }
     // advance the worker-segment cursor to the piece holding hi
     while (ps < ps_end && ps_hi <= hi) {
@@ -470,8 +633,13 @@ __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
         }
       }
       const uint32_t byte = sbytes[k0 >> 3];
-      load8(denom, k0, G.d, dv);
-      load8(x, k0, G.d, xv);
+      if (lo + kSpan <= G.d) {
+        load8_full(denom, k0, dv);
+        load8_full(x, k0, xv);
+      } else {
+        load8(denom, k0, G.d, dv);
+        load8(x, k0, G.d, xv);
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         mh[j] = ((byte >> j) & 1u) ? -sv[j] : sv[j];
@@ -509,42 +677,61 @@ void launch_freeze(const Geo& G, const float* v, float* denom, float eta, float 
   hipLaunchKernelGGL(k_freeze, dim3(G.nblk), dim3(kBlock), 0, st, G, v, denom, eta, bc2);
 }
 
-template <typename GT, int NB>
-static void launch_p1_nb(const Geo& G, const void* g, const float* m, float* delta,
-                         uint8_t* wbytes, const SegDev& sig, double* part, float b1, float omb1,
-                         hipStream_t st) {
-  const int groups = (G.n + NB - 1) / NB;
-  hipLaunchKernelGGL((k_compress_p1<GT, NB>), dim3(G.nblk, groups), dim3(kBlock), 0, st, G,
-                     static_cast<const GT*>(g), m, delta, wbytes, sig, part, b1, omb1);
+template <typename GT, int NB, int MODE>
+static void launch_cmp(const Geo& G, int32_t i0, int groups, const void* g, const float* m,
+                       float* delta, uint8_t* wbytes, const SegDev& sig, double* part,
+                       const float* wscale, float b1, float omb1, hipStream_t st) {
+  hipLaunchKernelGGL((k_compress<GT, NB, MODE>), dim3(G.nblk, groups), dim3(kBlock), 0, st, G,
+                     i0, static_cast<const GT*>(g), m, delta, wbytes, sig, part, wscale, b1,
+                     omb1);
 }
 
-template <typename GT>
-static void launch_p1_t(const Geo& G, const void* g, const float* m, float* delta,
-                        uint8_t* wbytes, const SegDev& sig, double* part, float b1, float omb1,
-                        hipStream_t st) {
-  if (G.n == 1)
-    launch_p1_nb<GT, 1>(G, g, m, delta, wbytes, sig, part, b1, omb1, st);
-  else if (G.n == 2)
-    launch_p1_nb<GT, 2>(G, g, m, delta, wbytes, sig, part, b1, omb1, st);
-  else if (G.n <= 4)
-    launch_p1_nb<GT, 4>(G, g, m, delta, wbytes, sig, part, b1, omb1, st);
-  else
-    launch_p1_nb<GT, 8>(G, g, m, delta, wbytes, sig, part, b1, omb1, st);
+// groups of 8 workers, then one launch for the n % 8 remainder
+template <typename GT, int MODE>
+static void launch_cmp_n(const Geo& G, const void* g, const float* m, float* delta,
+                         uint8_t* wbytes, const SegDev& sig, double* part, const float* wscale,
+                         float b1, float omb1, hipStream_t st) {
+  const int full = G.n / 8, rem = G.n % 8, i0 = full * 8;
+  if (full) launch_cmp<GT, 8, MODE>(G, 0, full, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st);
+  switch (rem) {
+    case 1: launch_cmp<GT, 1, MODE>(G, i0, 1, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st); break;
+    case 2: launch_cmp<GT, 2, MODE>(G, i0, 1, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st); break;
+    case 3: launch_cmp<GT, 3, MODE>(G, i0, 1, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st); break;
+    case 4: launch_cmp<GT, 4, MODE>(G, i0, 1, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st); break;
+    case 5: launch_cmp<GT, 5, MODE>(G, i0, 1, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st); break;
+    case 6: launch_cmp<GT, 6, MODE>(G, i0, 1, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st); break;
+    case 7: launch_cmp<GT, 7, MODE>(G, i0, 1, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st); break;
+    default: break;
+  }
 }
 
-void launch_compress_p1(const Geo& G, const void* g, bool f16, const float* m, float* delta,
-                        uint8_t* wbytes, const SegDev& sig, double* part, float b1, float omb1,
-                        hipStream_t st) {
+template <int MODE>
+static void launch_cmp_t(const Geo& G, const void* g, bool f16, const float* m, float* delta,
+                         uint8_t* wbytes, const SegDev& sig, double* part, const float* wscale,
+                         float b1, float omb1, hipStream_t st) {
   if (f16)
-    launch_p1_t<uint16_t>(G, g, m, delta, wbytes, sig, part, b1, omb1, st);
+    launch_cmp_n<uint16_t, MODE>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st);
   else
-    launch_p1_t<float>(G, g, m, delta, wbytes, sig, part, b1, omb1, st);
+    launch_cmp_n<float, MODE>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st);
+}
+
+void launch_compress_norm(const Geo& G, const void* g, bool f16, const float* m,
+                          const float* delta, const SegDev& sig, double* part, float b1,
+                          float omb1, hipStream_t st) {
+  launch_cmp_t<kNorm>(G, g, f16, m, const_cast<float*>(delta), nullptr, sig, part, nullptr, b1,
+                      omb1, st);
+}
+
+void launch_compress_apply(const Geo& G, const void* g, bool f16, const float* m, float* delta,
+                           uint8_t* wbytes, const SegDev& sig, const float* wscale, float b1,
+                           float omb1, hipStream_t st) {
+  launch_cmp_t<kApply>(G, g, f16, m, delta, wbytes, sig, nullptr, wscale, b1, omb1, st);
 }
 
 void launch_finalize(const double* part, int32_t rows, const SegDev& T, float* scale,
                      hipStream_t st) {
-  hipLaunchKernelGGL(k_finalize_scales, dim3(T.n_seg, rows), dim3(kBlock), 0, st, part, rows, T,
-                     scale);
+  hipLaunchKernelGGL(k_finalize_scales, dim3(T.n_seg, rows), dim3(kFinBlock), 0, st, part, rows,
+                     T, scale);
 }
 
 void launch_residual(const Geo& G, float* buf, int64_t ld, int32_t rows, const float* scale,
@@ -555,8 +742,20 @@ void launch_residual(const Geo& G, float* buf, int64_t ld, int32_t rows, const f
 void launch_server_p1(const Geo& G, const uint8_t* wbytes, const float* wscale, float* eps,
                       uint8_t* sbytes, const SegDev& sig, const SegDev& tau, double* part,
                       hipStream_t st) {
-  hipLaunchKernelGGL(k_server_p1, dim3(G.nblk), dim3(kBlock), 0, st, G, wbytes, wscale, eps,
-                     sbytes, sig, tau, part);
+#define OBA_SERVER_LAUNCH(NB)                                                              \
+  hipLaunchKernelGGL(k_server_p1<NB>, dim3(G.nblk), dim3(kBlock), 0, st, G, wbytes, wscale, eps, \
+                     sbytes, sig, tau, part)
+  switch (G.n) {
+    case 1: OBA_SERVER_LAUNCH(1); break;
+    case 2: OBA_SERVER_LAUNCH(2); break;
+    case 3: OBA_SERVER_LAUNCH(3); break;
+    case 4: OBA_SERVER_LAUNCH(4); break;
+    case 5: OBA_SERVER_LAUNCH(5); break;
+    case 6: OBA_SERVER_LAUNCH(6); break;
+    case 7: OBA_SERVER_LAUNCH(7); break;
+    default: OBA_SERVER_LAUNCH(8); break;
+  }
+#undef OBA_SERVER_LAUNCH
 }
 
 void launch_decompress_update(const Geo& G, const uint8_t* sbytes, const float* sscale,

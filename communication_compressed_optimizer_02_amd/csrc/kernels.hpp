@@ -32,9 +32,13 @@ void launch_adam_warmup(const Geo& G, const void* g, bool f16, float* x, float* 
                         const AdamCoef& C, hipStream_t st);
 void launch_freeze(const Geo& G, const float* v, float* denom, float eta, float bc2,
                    hipStream_t st);
-void launch_compress_p1(const Geo& G, const void* g, bool f16, const float* m, float* delta,
-                        uint8_t* wbytes, const SegDev& sig, double* part, float b1, float omb1,
-                        hipStream_t st);
+// Worker compression: read-only norm pass, then recompute c and store.
+void launch_compress_norm(const Geo& G, const void* g, bool f16, const float* m,
+                          const float* delta, const SegDev& sig, double* part, float b1,
+                          float omb1, hipStream_t st);
+void launch_compress_apply(const Geo& G, const void* g, bool f16, const float* m, float* delta,
+                           uint8_t* wbytes, const SegDev& sig, const float* wscale, float b1,
+                           float omb1, hipStream_t st);
 void launch_finalize(const double* part, int32_t rows, const SegDev& T, float* scale,
                      hipStream_t st);
 void launch_residual(const Geo& G, float* buf, int64_t ld, int32_t rows, const float* scale,

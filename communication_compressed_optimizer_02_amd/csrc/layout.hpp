@@ -18,7 +18,10 @@ namespace oba {
 constexpr int kBlock = 256;                 // threads per block (4 wave64)
 constexpr int kVec = 8;                     // consecutive coordinates per lane
 constexpr int64_t kSpan = kBlock * kVec;    // coordinates per block pass
-constexpr int kMaxBlocks = 2048;            // 8 resident blocks on each of 256 CUs
+#ifndef OBA_MAX_BLOCKS
+#define OBA_MAX_BLOCKS 65536
+#endif
+constexpr int kMaxBlocks = OBA_MAX_BLOCKS;  // cap on blocks of the streaming grid
 constexpr int32_t kMaxWorkers = 4096;
 
 struct Pieces {
