@@ -34,11 +34,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def gbytes(w):
+def gbytes(w, schedule="deferred"):
     """Algorithmic HBM bytes per parameter of each kernel of a step: every
     buffer a kernel must touch, once per direction."""
     n, gb = w.n, (2 if w.g_dtype == "f16" else 4)
-    reads = 4 + n * (gb + 4)  # m, g_i, delta_i
+    reads = 4 + n * (gb + 4)  # m, g_i, delta_i (or the last c_i)
+    if schedule == "deferred":
+        return {
+            # m, g_i, last c_i read; c_i and packed bits written
+            "compress_deferred": reads + 4 * n + n / 8,
+            # worker bits read, last a read, a written, server bits written
+            "server_deferred": n / 8 + 8 + 1 / 8,
+            # server bits read, denom read, x read+written, m written
+            "decompress_update": 1 / 8 + 16,
+        }
     return {
         # norm pass: m, g_i, delta_i read
         "compress_p1": reads,
@@ -177,41 +186,41 @@ def main():
     w = synth.workload(args.workload)
     L, S, gsets = make_state(w, torch, oba, synth)
 
-    def step(i):
-        S.step(synth.BETA1, synth.LR, g=gsets[i % 2])
+    def run(schedule):
+        """W untimed + K timed steps of one schedule from the freeze state."""
+        for t in (S.delta, S.eps, S.wscale, S.sscale):
+            t.zero_()
+        fn = S.step_deferred if schedule == "deferred" else S.step
+        log(f"[bench] {schedule}: {args.warmup} untimed steps, {args.steps} timed steps")
+        for i in range(args.warmup):
+            fn(synth.BETA1, synth.LR, g=gsets[i % 2])
+        torch.cuda.synchronize()
+        oba.timing_reset()
+        oba.timing_enable(True, capacity=16 * max(1, args.steps))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            fn(synth.BETA1, synth.LR, g=gsets[i % 2])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        oba.timing_enable(False, 1)
+        alg = gbytes(w, schedule)
+        kernels = {}
+        for k in list(alg) + ["finalize_scales"]:
+            tot, cnt = oba.timing_read(k)
+            ent = {"avg_ms": round(tot / cnt, 4) if cnt else 0.0, "launches": cnt}
+            if k in alg and cnt:
+                ent["alg_bytes_per_param"] = alg[k]
+                ent["alg_GBps"] = round(alg[k] * w.d / (tot / cnt * 1e-3) / 1e9, 1)
+            kernels[k] = ent
+        oba.timing_reset()
+        return (t1 - t0) * 1e3 / args.steps, alg, kernels
 
-    log(f"[bench] {args.warmup} untimed steps")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    oba.timing_reset()
-    oba.timing_enable(True, capacity=16 * max(1, args.steps))
-    log(f"[bench] {args.steps} timed steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    oba.timing_enable(False, 1)
-    ms = (t1 - t0) * 1e3 / args.steps
-    per_kernel = {}
-    for k in ("compress_p1", "finalize_scales", "compress_p2", "server_p1", "server_p2",
-              "decompress_update"):
-        tot, cnt = oba.timing_read(k)
-        per_kernel[k] = (tot / cnt if cnt else 0.0, cnt)
-    oba.timing_reset()
-    alg = gbytes(w)
-    kernels = {}
-    for k, (avg_ms, cnt) in per_kernel.items():
-        ent = {"avg_ms": round(avg_ms, 4), "launches": cnt}
-        if k in alg and avg_ms > 0:
-            ent["alg_bytes_per_param"] = alg[k]
-            ent["alg_GBps"] = round(alg[k] * w.d / (avg_ms * 1e-3) / 1e9, 1)
-        kernels[k] = ent
+    ms, alg, kernels = run("deferred")
+    ms_x, alg_x, kernels_x = run("explicit")
     # dominant kernel: the largest share of the step's time
-    dom = max(alg, key=lambda k: per_kernel[k][0])
-    dom_ms = per_kernel[dom][0]
+    dom = max(alg, key=lambda k: kernels[k]["avg_ms"])
+    dom_ms = kernels[dom]["avg_ms"]
     dom_bytes = alg[dom] * w.d
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = traffic_from_profiles(w.name, dom)
@@ -231,7 +240,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "d": w.d, "n_workers": w.n, "grad_dtype": w.g_dtype,
                    "worker_segments": len(w.wseg) - 1, "server_segments": len(w.sseg) - 1,
-                   "parallelism": "dp%d simulated on one GPU" % w.n},
+                   "parallelism": "dp%d simulated on one GPU" % w.n,
+                   "schedule": "deferred-residual state (c, a kept; residuals formed on use)"},
         "step_alg_GBps": round(step_alg / (ms * 1e-3) / 1e9, 1),
         "step_alg_bytes_per_param": round(sum(alg.values()), 3),
         "method_bytes_per_param": round(method_bytes(w), 3),
@@ -240,6 +250,11 @@ def main():
                      "traffic": traffic, "alg_bytes_per_launch": dom_bytes,
                      "avg_launch_ms": round(dom_ms, 4)},
         "kernels": kernels,
+        "explicit_schedule": {
+            "ms_per_step": round(ms_x, 4), "value": w.d / (ms_x * 1e-3),
+            "step_alg_bytes_per_param": round(sum(alg_x.values()), 3),
+            "step_alg_GBps": round(sum(alg_x.values()) * w.d / (ms_x * 1e-3) / 1e9, 1),
+            "kernels": kernels_x},
         "kernel_source_sha256": source_hash(),
     }
     del S, gsets

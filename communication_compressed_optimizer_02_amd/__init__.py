@@ -5,11 +5,13 @@ The method runs in hand-written HIP kernels behind the C ABI of
 Python front end and ``synth`` holds the seeded synthetic workloads.
 """
 from .binding import (OBA_F16, OBA_F32, Layout, ObaError, State, adam_warmup_step, compress,
-                      decompress_update, freeze_variance, server_reduce_recompress,
+                      compress_deferred, decompress_update, deferred_errors, freeze_variance,
+                      server_reduce_recompress, server_reduce_recompress_deferred,
                       timing_enable, timing_read, timing_reset, validate)
 
 __all__ = [
     "OBA_F16", "OBA_F32", "Layout", "ObaError", "State", "adam_warmup_step", "compress",
-    "decompress_update", "freeze_variance", "server_reduce_recompress", "timing_enable",
+    "compress_deferred", "decompress_update", "deferred_errors", "freeze_variance",
+    "server_reduce_recompress", "server_reduce_recompress_deferred", "timing_enable",
     "timing_read", "timing_reset", "validate",
 ]

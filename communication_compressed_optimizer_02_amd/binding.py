@@ -38,6 +38,9 @@ SIGNATURES = {
     "oba_compress": (_I, [_P, _P, _I, _P, _P, _P, _P, _D, _P, _SZ, _P]),
     "oba_server_reduce_recompress": (_I, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "oba_decompress_update": (_I, [_P, _P, _P, _P, _P, _P, _D, _P]),
+    "oba_compress_deferred": (_I, [_P, _P, _I, _P, _P, _P, _P, _D, _P, _SZ, _P]),
+    "oba_server_reduce_recompress_deferred": (_I, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "oba_deferred_errors": (_I, [_P, _P, _P, _P, _P, _P, _P, _P]),
     "oba_timing_enable": (_I, [_I, _I32]),
     "oba_timing_read": (_I, [ctypes.c_char_p, ctypes.POINTER(_D), ctypes.POINTER(_I64)]),
     "oba_timing_reset": (_I, []),
@@ -206,6 +209,51 @@ def decompress_update(L: Layout, sbits, sscale, denom, m, x, lr, stream=None):
     _check(rc, "oba_decompress_update")
 
 
+def compress_deferred(L: Layout, g, m, c, wbits, wscale, beta1, stream=None):
+    """c: last step's compensated vectors in, this step's out; wscale: last
+    step's worker scales in, this step's out."""
+    import torch
+
+    f32 = (torch.float32,)
+    rc = lib().oba_compress_deferred(
+        L.handle, _ptr(g, "g", (torch.float32, torch.float16), (L.n, L.ld)), _gdtype(g),
+        _ptr(m, "m", f32, (L.d,)), _ptr(c, "c", f32, (L.n, L.ld)),
+        _ptr(wbits, "wbits", (torch.int64,), (L.n, L.W)),
+        _ptr(wscale, "wscale", f32, (L.n, L.n_wseg)), beta1,
+        ctypes.c_void_p(L.ws.data_ptr()), L.ws_bytes, _stream(stream))
+    _check(rc, "oba_compress_deferred")
+
+
+def server_reduce_recompress_deferred(L: Layout, wbits, wscale, a, sbits, sscale, stream=None):
+    """a: last step's server vector in, this step's out; sscale: last step's
+    server scales in, this step's out."""
+    import torch
+
+    f32 = (torch.float32,)
+    rc = lib().oba_server_reduce_recompress_deferred(
+        L.handle, _ptr(wbits, "wbits", (torch.int64,), (L.n, L.W)),
+        _ptr(wscale, "wscale", f32, (L.n, L.n_wseg)), _ptr(a, "a", f32, (L.d,)),
+        _ptr(sbits, "sbits", (torch.int64,), (L.W,)), _ptr(sscale, "sscale", f32, (L.n_sseg,)),
+        ctypes.c_void_p(L.ws.data_ptr()), L.ws_bytes, _stream(stream))
+    _check(rc, "oba_server_reduce_recompress_deferred")
+
+
+def deferred_errors(L: Layout, c, wscale, a, sscale, delta=None, eps=None, stream=None):
+    """delta = c - s*sign(c) and/or eps = a - sbar*sign(a), out of place."""
+    import torch
+
+    f32 = (torch.float32,)
+    P = ctypes.c_void_p
+    dp = _ptr(delta, "delta", f32, (L.n, L.ld)) if delta is not None else P(None)
+    ep = _ptr(eps, "eps", f32, (L.d,)) if eps is not None else P(None)
+    cp = _ptr(c, "c", f32, (L.n, L.ld)) if delta is not None else P(None)
+    wp = _ptr(wscale, "wscale", f32, (L.n, L.n_wseg)) if delta is not None else P(None)
+    ap = _ptr(a, "a", f32, (L.d,)) if eps is not None else P(None)
+    sp = _ptr(sscale, "sscale", f32, (L.n_sseg,)) if eps is not None else P(None)
+    _check(lib().oba_deferred_errors(L.handle, cp, wp, ap, sp, dp, ep, _stream(stream)),
+           "oba_deferred_errors")
+
+
 def timing_enable(on=True, capacity=4096):
     _check(lib().oba_timing_enable(1 if on else 0, capacity), "oba_timing_enable")
 
@@ -248,9 +296,13 @@ class State:
                          beta2, eta, bc1, bc2)
 
     def freeze(self, eta, bc2=1.0):
+        """End of the warm-up: denom from v; errors (or, in the deferred
+        layout, the stored c, a and the scales) start at zero."""
         freeze_variance(self.L, self.v, self.denom, eta, bc2)
         self.delta.zero_()
         self.eps.zero_()
+        self.wscale.zero_()
+        self.sscale.zero_()
 
     def step(self, beta1, lr, g=None):
         """One compression step: compress -> server -> decompress+update."""
@@ -258,4 +310,13 @@ class State:
                  beta1)
         server_reduce_recompress(self.L, self.wbits, self.wscale, self.eps, self.sbits,
                                  self.sscale)
+        decompress_update(self.L, self.sbits, self.sscale, self.denom, self.m, self.x, lr)
+
+    def step_deferred(self, beta1, lr, g=None):
+        """The same step in the deferred-residual layout: `delta` holds the
+        last c and `eps` the last a (see oba_compress_deferred)."""
+        compress_deferred(self.L, self.g if g is None else g, self.m, self.delta, self.wbits,
+                          self.wscale, beta1)
+        server_reduce_recompress_deferred(self.L, self.wbits, self.wscale, self.eps, self.sbits,
+                                          self.sscale)
         decompress_update(self.L, self.sbits, self.sscale, self.denom, self.m, self.x, lr)

@@ -316,7 +316,86 @@ int oba_server_reduce_recompress(oba_layout L, const uint64_t* wbits, const floa
   OBA_TRY(launch("finalize_scales", stream,
                  [&] { oba::launch_finalize(part, 1, L->tau, sscale, stream); }));
   return launch("server_p2", stream,
-                [&] { oba::launch_residual(G, eps, 0, 1, sscale, L->tau, stream); });
+                [&] { oba::launch_residual(G, eps, 0, eps, 0, 1, sscale, L->tau, stream); });
+}
+
+int oba_compress_deferred(oba_layout L, const void* g, int g_dtype, const float* m, float* c,
+                          uint64_t* wbits, float* wscale, double beta1, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  OBA_TRY(check_layout(L));
+  if (g_dtype != OBA_F32 && g_dtype != OBA_F16) return OBA_EINVAL;
+  if (!beta_ok(beta1)) return OBA_EINVAL;
+  if (L->geo.d == 0) return OBA_OK;
+  OBA_TRY(check_buf(g, 16));
+  OBA_TRY(check_buf(m, 16));
+  OBA_TRY(check_buf(c, 16));
+  OBA_TRY(check_buf(wbits, 8));
+  OBA_TRY(check_buf(wscale, 4));
+  OBA_TRY(check_buf(ws, 8));
+  if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
+  const oba::Geo G = L->geo;
+  double* part = static_cast<double*>(ws);
+  const float b1 = (float)beta1, omb1 = (float)(1.0 - beta1);
+  uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
+  OBA_TRY(launch("compress_deferred", stream, [&] {
+    oba::launch_compress_deferred(G, g, g_dtype == OBA_F16, m, c, wbytes, L->sig, part, wscale, b1,
+                                  omb1, stream);
+  }));
+  return launch("finalize_scales", stream,
+                [&] { oba::launch_finalize(part, G.n, L->sig, wscale, stream); });
+}
+
+int oba_server_reduce_recompress_deferred(oba_layout L, const uint64_t* wbits,
+                                          const float* wscale, float* a, uint64_t* sbits,
+                                          float* sscale, void* ws, size_t ws_bytes,
+                                          hipStream_t stream) {
+  OBA_TRY(check_layout(L));
+  if (L->geo.d == 0) return OBA_OK;
+  OBA_TRY(check_buf(wbits, 8));
+  OBA_TRY(check_buf(wscale, 4));
+  OBA_TRY(check_buf(a, 16));
+  OBA_TRY(check_buf(sbits, 8));
+  OBA_TRY(check_buf(sscale, 4));
+  OBA_TRY(check_buf(ws, 8));
+  if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
+  const oba::Geo G = L->geo;
+  double* part = reinterpret_cast<double*>(static_cast<char*>(ws) +
+                                           ((L->ws_worker + 255) / 256) * 256);
+  const uint8_t* wbytes = reinterpret_cast<const uint8_t*>(wbits);
+  uint8_t* sbytes = reinterpret_cast<uint8_t*>(sbits);
+  OBA_TRY(launch("server_deferred", stream, [&] {
+    oba::launch_server_deferred(G, wbytes, wscale, a, sbytes, L->sig, L->tau, part, sscale,
+                                stream);
+  }));
+  return launch("finalize_scales", stream,
+                [&] { oba::launch_finalize(part, 1, L->tau, sscale, stream); });
+}
+
+int oba_deferred_errors(oba_layout L, const float* c, const float* wscale, const float* a,
+                        const float* sscale, float* delta, float* eps, hipStream_t stream) {
+  OBA_TRY(check_layout(L));
+  if (L->geo.d == 0) return OBA_OK;
+  if (!delta && !eps) return OBA_EINVAL;
+  const oba::Geo G = L->geo;
+  if (delta) {
+    OBA_TRY(check_buf(c, 16));
+    OBA_TRY(check_buf(wscale, 4));
+    OBA_TRY(check_buf(delta, 16));
+    if ((const void*)c == (const void*)delta) return OBA_EINVAL;
+    OBA_TRY(launch("deferred_errors", stream, [&] {
+      oba::launch_residual(G, c, G.ld, delta, G.ld, G.n, wscale, L->sig, stream);
+    }));
+  }
+  if (eps) {
+    OBA_TRY(check_buf(a, 16));
+    OBA_TRY(check_buf(sscale, 4));
+    OBA_TRY(check_buf(eps, 16));
+    if ((const void*)a == (const void*)eps) return OBA_EINVAL;
+    OBA_TRY(launch("deferred_errors", stream, [&] {
+      oba::launch_residual(G, a, 0, eps, 0, 1, sscale, L->tau, stream);
+    }));
+  }
+  return OBA_OK;
 }
 
 int oba_decompress_update(oba_layout L, const uint64_t* sbits, const float* sscale,

@@ -296,7 +296,12 @@ __global__ __launch_bounds__(kBlock) void k_freeze(Geo G, const float* __restric
 //   c = (b1*m + (1-b1)*g_i) + delta_i
 // kNorm:  only reduce sum c^2 per (piece, worker) -- reads only;
 // kApply: recompute c bit for bit, store the sign byte and
-//         delta_i = c - s*sign(c) with the finished scales.
+//         delta_i = c - s*sign(c) with the finished scales;
+// kDeferred: the state row holds the previous step's c (not delta) and the
+//         scale buffer its scales s'; the residual of the last step is formed
+//         where it is consumed, delta_i = c' - s'*sign(c'), then
+//         c = (b1*m + (1-b1)*g_i) + delta_i is stored over c' with its sign
+//         byte and its sum c^2 is reduced -- one pass instead of two.
 // The scale needs the whole segment's norm before any residual can be
 // written, so c is needed twice.  Recomputing it reads g, m, delta twice but
 // never writes c: on this HBM, writes cost more than reads, and storing c in
@@ -305,7 +310,7 @@ __global__ __launch_bounds__(kBlock) void k_freeze(Geo G, const float* __restric
 // [i0, i0 + gridDim.y*NB); n > 8 takes one launch of NB=8 groups and one
 // for the remainder.  Grid: (nblk, groups).
 // ===========================================================================
-enum { kNorm = 1, kApply = 2 };
+enum { kNorm = 1, kApply = 2, kDeferred = 3 };
 
 template <typename GT, int NB, int MODE>
 __global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT* __restrict__ g,
@@ -334,7 +339,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT
     const bool uniform = hi <= p_hi;  // span inside the current piece
     const bool full = lo + kSpan <= G.d;
     int32_t jseg[8];
-    if (MODE == kApply && !uniform) {
+    if ((MODE == kApply || MODE == kDeferred) && !uniform) {
       int32_t js = sig.pseg[p];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -365,11 +370,31 @@ __global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int64_t row = (int64_t)(i0 + i) * G.ld;
+      if (MODE == kDeferred) {  // c[i] holds c' of the last step: form its residual
+        const float* sc = wscale + (int64_t)(i0 + i) * sig.n_seg;
+        float sv[8];
+        if (uniform) {
+          const float s_ = sc[sig.pseg[p]];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sv[j] = s_;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sv[j] = sc[jseg[j]];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c[i][j] = (c[i][j] < 0.0f) ? c[i][j] + sv[j] : c[i][j] - sv[j];
+        if (!full) {  // coordinates past d read as 0 and must stay 0 (no bit, no c^2)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (k0 + j >= G.d) c[i][j] = 0.0f;
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) c[i][j] = compensate(b1, omb1, mv[j], gv[i][j], c[i][j]);
       if (MODE != kNorm && k0 < 64 * G.W)
         wbytes[(int64_t)(i0 + i) * rowbytes + (k0 >> 3)] = (uint8_t)sign_byte(c[i]);
-      fs[i] = (MODE == kNorm) ? sumsq8(c[i]) : 0.0;
+      if (MODE == kDeferred) store8(delta + row, k0, G.d, c[i]);
+      fs[i] = (MODE != kApply) ? sumsq8(c[i]) : 0.0;
       if (MODE == kApply) {
         const float* sc = wscale + (int64_t)(i0 + i) * sig.n_seg;
         float sv[8];
@@ -404,7 +429,10 @@ __global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
           const int64_t row = (int64_t)(i0 + i) * G.ld;
-          acc[i] += sumsq_range_c(m, g + row, delta + row, b1, omb1, k0, cur, e);
+          if (MODE == kDeferred)
+            acc[i] += sumsq_range(delta + row, k0, cur, e);  // c was stored there
+          else
+            acc[i] += sumsq_range_c(m, g + row, delta + row, b1, omb1, k0, cur, e);
         }
         if (p_hi <= hi) {
           flush_rows<NB>(acc, NB, part + (int64_t)p * G.n + i0, lds);
@@ -442,13 +470,16 @@ __global__ __launch_bounds__(kFinBlock) void k_finalize_scales(const double* __r
 }
 
 // ===========================================================================
-// Residual pass: err = c - s*sign(c) over one row, s = the row's scale of the
-// segment holding each coordinate.  Grid: (nblk, rows); row r at base + r*ld.
+// Residual pass: dst = c - s*sign(c) over one row of src, s = the row's scale
+// of the segment holding each coordinate (dst may be src: in place).
+// Grid: (nblk, rows); row r at src + r*src_ld and dst + r*dst_ld.
 // ===========================================================================
-__global__ __launch_bounds__(kBlock) void k_residual(Geo G, float* __restrict__ buf, int64_t ld,
+__global__ __launch_bounds__(kBlock) void k_residual(Geo G, const float* src, int64_t src_ld,
+                                                     float* dst, int64_t dst_ld,
                                                      const float* __restrict__ scale, SegDev T) {
   const int32_t b = blockIdx.x;
-  float* row = buf + (int64_t)blockIdx.y * ld;
+  const float* srow = src + (int64_t)blockIdx.y * src_ld;
+  float* drow = dst + (int64_t)blockIdx.y * dst_ld;
   const float* sc = scale + (int64_t)blockIdx.y * T.n_seg;
   const int64_t s_lo = dspan(G.S, G.nblk, b), s_hi = dspan(G.S, G.nblk, b + 1);
   const int32_t p_end = T.blk_first[b + 1];
@@ -461,9 +492,9 @@ __global__ __launch_bounds__(kBlock) void k_residual(Geo G, float* __restrict__ 
     if (k0 < G.d) {
       float c[8], sv[8];
       if (lo + kSpan <= G.d)
-        load8_full(row, k0, c);
+        load8_full(srow, k0, c);
       else
-        load8(row, k0, G.d, c);
+        load8(srow, k0, G.d, c);
       if (hi <= p_hi) {
         const float s_ = sc[T.pseg[p]];
 #pragma unroll
@@ -478,7 +509,7 @@ __global__ __launch_bounds__(kBlock) void k_residual(Geo G, float* __restrict__ 
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) c[j] = (c[j] < 0.0f) ? c[j] + sv[j] : c[j] - sv[j];
-      store8(row, k0, G.d, c);
+      store8(drow, k0, G.d, c);
     }
     while (p < p_end && p_hi <= hi) {
       if (++p < p_end) p_hi = T.phi[p];
@@ -491,14 +522,17 @@ __global__ __launch_bounds__(kBlock) void k_residual(Geo G, float* __restrict__ 
 // order), a stored over eps, server sign byte stored, binary64 sum of a^2
 // reduced per server piece.  The sign bytes and scales of NB workers are
 // loaded before any is used, so their loads overlap (NB = n for n <= 8, else
-// groups of 8).  Grid: nblk.
+// groups of 8).  DEFERRED: the buffer holds the last step's a' and
+// sscale_prev its server scales; the server error is formed where it is
+// consumed, eps = a' - s'*sign(a'), and a is stored over a'.  Grid: nblk.
 // ===========================================================================
-template <int NB>
+template <int NB, bool DEFERRED>
 __global__ __launch_bounds__(kBlock) void k_server_p1(Geo G, const uint8_t* __restrict__ wbytes,
                                                       const float* __restrict__ wscale,
                                                       float* __restrict__ eps,
                                                       uint8_t* __restrict__ sbytes, SegDev sig,
-                                                      SegDev tau, double* __restrict__ part) {
+                                                      SegDev tau, double* __restrict__ part,
+                                                      const float* __restrict__ sscale_prev) {
   __shared__ double lds[4];
   const int32_t b = blockIdx.x;
   const int64_t s_lo = dspan(G.S, G.nblk, b), s_hi = dspan(G.S, G.nblk, b + 1);
@@ -514,11 +548,16 @@ __global__ __launch_bounds__(kBlock) void k_server_p1(Geo G, const uint8_t* __re
     const int64_t k0 = lo + (int64_t)threadIdx.x * kVec;
     double fs = 0.0;
     const int64_t q = k0 >> 3;
-    if (hi <= ps_hi && lo + kSpan <= G.d) {
-      // fast path: full span, one worker segment; all loads first
+    if (hi <= ps_hi && hi <= pt_hi && lo + kSpan <= G.d) {
+      // fast path: full span, one worker and one server segment; loads first
       const int32_t js0 = sig.pseg[ps];
       float ev[8], t[8];
       load8_full(eps, k0, ev);
+      if (DEFERRED) {
+        const float sp = sscale_prev[tau.pseg[pt]];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ev[j] = (ev[j] < 0.0f) ? ev[j] + sp : ev[j] - sp;
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) t[j] = 0.0f;
       for (int32_t i0 = 0; i0 < G.n; i0 += NB) {  // one pass when n <= NB
@@ -550,18 +589,25 @@ __global__ __launch_bounds__(kBlock) void k_server_p1(Geo G, const uint8_t* __re
       // coordinate at a time, same operations in the same order
       uint32_t sb = 0;
       int32_t js = sig.pseg[ps];
+      int32_t jt = tau.pseg[pt];
 #pragma unroll 1
       for (int j = 0; j < 8; ++j) {
         const int64_t k = k0 + j;
         if (k < G.d) {
           js = seg_walk(sig.off, js, k);
+          float e = eps[k];
+          if (DEFERRED) {
+            jt = seg_walk(tau.off, jt, k);
+            const float sp = sscale_prev[jt];
+            e = (e < 0.0f) ? e + sp : e - sp;
+          }
           float t = 0.0f;
           for (int32_t i = 0; i < G.n; ++i) {
             const uint32_t byte = wbytes[(int64_t)i * rowbytes + q];
             const float s_ = wscale[(int64_t)i * sig.n_seg + js];
             t = t + (((byte >> j) & 1u) ? -s_ : s_);
           }
-          const float a = t / nf + eps[k];
+          const float a = t / nf + e;
           eps[k] = a;
           sb |= (a < 0.0f ? 1u : 0u) << j;
           const double x = (double)a;
@@ -722,6 +768,12 @@ void launch_compress_norm(const Geo& G, const void* g, bool f16, const float* m,
                       omb1, st);
 }
 
+void launch_compress_deferred(const Geo& G, const void* g, bool f16, const float* m, float* c,
+                              uint8_t* wbytes, const SegDev& sig, double* part,
+                              const float* wscale_prev, float b1, float omb1, hipStream_t st) {
+  launch_cmp_t<kDeferred>(G, g, f16, m, c, wbytes, sig, part, wscale_prev, b1, omb1, st);
+}
+
 void launch_compress_apply(const Geo& G, const void* g, bool f16, const float* m, float* delta,
                            uint8_t* wbytes, const SegDev& sig, const float* wscale, float b1,
                            float omb1, hipStream_t st) {
@@ -734,17 +786,19 @@ void launch_finalize(const double* part, int32_t rows, const SegDev& T, float* s
                      T, scale);
 }
 
-void launch_residual(const Geo& G, float* buf, int64_t ld, int32_t rows, const float* scale,
-                     const SegDev& T, hipStream_t st) {
-  hipLaunchKernelGGL(k_residual, dim3(G.nblk, rows), dim3(kBlock), 0, st, G, buf, ld, scale, T);
+void launch_residual(const Geo& G, const float* src, int64_t src_ld, float* dst, int64_t dst_ld,
+                     int32_t rows, const float* scale, const SegDev& T, hipStream_t st) {
+  hipLaunchKernelGGL(k_residual, dim3(G.nblk, rows), dim3(kBlock), 0, st, G, src, src_ld, dst,
+                     dst_ld, scale, T);
 }
 
-void launch_server_p1(const Geo& G, const uint8_t* wbytes, const float* wscale, float* eps,
-                      uint8_t* sbytes, const SegDev& sig, const SegDev& tau, double* part,
-                      hipStream_t st) {
-#define OBA_SERVER_LAUNCH(NB)                                                              \
-  hipLaunchKernelGGL(k_server_p1<NB>, dim3(G.nblk), dim3(kBlock), 0, st, G, wbytes, wscale, eps, \
-                     sbytes, sig, tau, part)
+template <bool DEFERRED>
+static void launch_server_t(const Geo& G, const uint8_t* wbytes, const float* wscale, float* eps,
+                            uint8_t* sbytes, const SegDev& sig, const SegDev& tau, double* part,
+                            const float* sscale_prev, hipStream_t st) {
+#define OBA_SERVER_LAUNCH(NB)                                                                  \
+  hipLaunchKernelGGL((k_server_p1<NB, DEFERRED>), dim3(G.nblk), dim3(kBlock), 0, st, G, wbytes, \
+                     wscale, eps, sbytes, sig, tau, part, sscale_prev)
   switch (G.n) {
     case 1: OBA_SERVER_LAUNCH(1); break;
     case 2: OBA_SERVER_LAUNCH(2); break;
@@ -756,6 +810,18 @@ void launch_server_p1(const Geo& G, const uint8_t* wbytes, const float* wscale, 
     default: OBA_SERVER_LAUNCH(8); break;
   }
 #undef OBA_SERVER_LAUNCH
+}
+
+void launch_server_p1(const Geo& G, const uint8_t* wbytes, const float* wscale, float* eps,
+                      uint8_t* sbytes, const SegDev& sig, const SegDev& tau, double* part,
+                      hipStream_t st) {
+  launch_server_t<false>(G, wbytes, wscale, eps, sbytes, sig, tau, part, nullptr, st);
+}
+
+void launch_server_deferred(const Geo& G, const uint8_t* wbytes, const float* wscale, float* a,
+                            uint8_t* sbytes, const SegDev& sig, const SegDev& tau, double* part,
+                            const float* sscale_prev, hipStream_t st) {
+  launch_server_t<true>(G, wbytes, wscale, a, sbytes, sig, tau, part, sscale_prev, st);
 }
 
 void launch_decompress_update(const Geo& G, const uint8_t* sbytes, const float* sscale,

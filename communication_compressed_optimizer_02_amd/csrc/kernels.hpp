@@ -41,8 +41,16 @@ void launch_compress_apply(const Geo& G, const void* g, bool f16, const float* m
                            float omb1, hipStream_t st);
 void launch_finalize(const double* part, int32_t rows, const SegDev& T, float* scale,
                      hipStream_t st);
-void launch_residual(const Geo& G, float* buf, int64_t ld, int32_t rows, const float* scale,
-                     const SegDev& T, hipStream_t st);
+void launch_residual(const Geo& G, const float* src, int64_t src_ld, float* dst, int64_t dst_ld,
+                     int32_t rows, const float* scale, const SegDev& T, hipStream_t st);
+// Deferred-residual state: rows hold the last step's c (worker) / a (server)
+// and the scale buffers its scales; see kernels.hip.
+void launch_compress_deferred(const Geo& G, const void* g, bool f16, const float* m, float* c,
+                              uint8_t* wbytes, const SegDev& sig, double* part,
+                              const float* wscale_prev, float b1, float omb1, hipStream_t st);
+void launch_server_deferred(const Geo& G, const uint8_t* wbytes, const float* wscale, float* a,
+                            uint8_t* sbytes, const SegDev& sig, const SegDev& tau, double* part,
+                            const float* sscale_prev, hipStream_t st);
 void launch_server_p1(const Geo& G, const uint8_t* wbytes, const float* wscale, float* eps,
                       uint8_t* sbytes, const SegDev& sig, const SegDev& tau, double* part,
                       hipStream_t st);

@@ -168,6 +168,48 @@ int oba_server_reduce_recompress(oba_layout layout, const uint64_t* wbits, const
 int oba_decompress_update(oba_layout layout, const uint64_t* sbits, const float* sscale,
                           const float* denom, float* m, float* x, double lr, hipStream_t stream);
 
+/* ---- deferred-residual state layout --------------------------------------
+ * The same step with a cheaper state: instead of the residuals delta_i and
+ * eps, the state keeps the last step's compensated vectors c_i and a, and the
+ * scale buffers keep the last step's scales.  A residual is formed only where
+ * it is consumed -- in the next step's pass -- as delta_i = c_i - s_i*sign(c_i)
+ * and eps = a - sbar*sign(a) ([Tang] 4.1: each step's compression error is
+ * fed back at the next step; [AIMech] limitations: the error buffers are the
+ * memory cost).  Every operation, its binary32 rounding and its order are
+ * those of oba_compress / oba_server_reduce_recompress, so the results are
+ * identical; the worker side is one pass over g, m, c instead of two, and the
+ * server residual pass disappears.
+ *
+ * Start of the compression stage: zero c, a, wscale and sscale (then every
+ * residual is 0, as after the freeze).  A step is oba_compress_deferred ->
+ * oba_server_reduce_recompress_deferred -> oba_decompress_update (unchanged).
+ * oba_deferred_errors writes delta and/or eps out of place (for checkpoints
+ * or inspection); it does not change the state. */
+
+/* c: [n][ld] in (last c) / out (this c); wscale: [n][n_wseg] in (last
+ * scales) / out (this step's); g, m, wbits, ws as for oba_compress.
+ *   delta_i = c_i - s_i*sign(c_i);  c_i = (b1*m + (1-b1)*g_i) + delta_i;
+ *   s_{i,sigma} = sqrt(sum c^2 / |sigma|);  bit = (c < 0). */
+int oba_compress_deferred(oba_layout layout, const void* g, int g_dtype, const float* m, float* c,
+                          uint64_t* wbits, float* wscale, double beta1, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* a: [d] in (last a) / out (this a); sscale: [n_sseg] in (last) / out (this);
+ * wbits, wscale: this step's worker messages; sbits, ws as for
+ * oba_server_reduce_recompress.
+ *   eps = a' - sbar'*sign(a');  a = (sum_i s_i*sg_i)/n + eps;
+ *   sbar_tau = sqrt(sum a^2 / |tau|);  sbit = (a < 0). */
+int oba_server_reduce_recompress_deferred(oba_layout layout, const uint64_t* wbits,
+                                          const float* wscale, float* a, uint64_t* sbits,
+                                          float* sscale, void* ws, size_t ws_bytes,
+                                          hipStream_t stream);
+
+/* delta = c - s*sign(c) ([n][ld], if delta != NULL) and eps = a - sbar*sign(a)
+ * ([d], if eps != NULL): the errors of the state (c, wscale, a, sscale), out
+ * of place.  At least one output must be given. */
+int oba_deferred_errors(oba_layout layout, const float* c, const float* wscale, const float* a,
+                        const float* sscale, float* delta, float* eps, hipStream_t stream);
+
 /* ---- kernel timing (measurement aid) ---------------------------------------
  * While enabled, every kernel the library launches is bracketed by two HIP
  * events on the launch stream (up to `capacity` launches are kept).
@@ -175,7 +217,8 @@ int oba_decompress_update(oba_layout layout, const uint64_t* sbits, const float*
  * duration in milliseconds and the launch count of the kernels whose name
  * equals `kernel` ("compress_p1", "compress_p2", "finalize_scales",
  * "server_p1", "server_p2", "decompress_update", "adam_warmup",
- * "freeze_variance").  oba_timing_reset drops all records. */
+ * "freeze_variance", "compress_deferred", "server_deferred",
+ * "deferred_errors").  oba_timing_reset drops all records. */
 int oba_timing_enable(int on, int32_t capacity);
 int oba_timing_read(const char* kernel, double* total_ms, int64_t* launches);
 int oba_timing_reset(void);

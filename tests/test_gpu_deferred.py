@@ -1,0 +1,153 @@
+"""GPU tests of the deferred-residual state layout (oba_compress_deferred,
+oba_server_reduce_recompress_deferred, oba_deferred_errors).
+
+The deferred layout performs the same operations in the same order as the
+explicit one, only at another time, so from the same start both must give
+bit-identical messages, scales, m and x, and the errors it materialises must
+equal the explicit layout's delta and eps bit for bit.  It is also run freely
+against the CPU oracle."""
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+import oracle
+from gpu_common import (B1, ETA, LR, assert_close, assert_words, cut_table, grads, padded,
+                        to_dev, to_host, torch)
+from communication_compressed_optimizer_02_amd import binding as oba
+from communication_compressed_optimizer_02_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def two_states(L, gdt, st):
+    out = []
+    for _ in range(2):
+        S = oba.State(L, gdt)
+        S.m.copy_(torch().from_numpy(st["m"]))
+        S.x.copy_(torch().from_numpy(st["x"]))
+        S.denom.copy_(torch().from_numpy(oracle.freeze_variance(st["v"], ETA)))
+        out.append(S)  # delta, eps, wscale, sscale start at zero (as after the freeze)
+    return out
+
+
+def same(a, b, what):
+    a, b = to_host(a), to_host(b)
+    assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{what} differs"
+
+
+@pytest.mark.parametrize("d,n,gdt,tab", [(4096, 2, "f32", "shards"), (2049, 3, "f16", "cuts"),
+                                         (300, 2, "f32", "singletons"),
+                                         (3_000_017, 8, "f16", "shards"),
+                                         (1_000_003, 11, "f32", "cuts")])
+def test_deferred_layout_is_bitwise_the_explicit_step(d, n, gdt, tab):
+    say(f"[deferred==explicit] d={d} n={n} g={gdt} tables={tab}")
+    rng = np.random.default_rng(d + 7 * n)
+    if tab == "shards":
+        wseg, sseg = synth.whole(d), synth.even_shards(d, n)
+    elif tab == "singletons":
+        wseg = sseg = np.arange(d + 1, dtype=np.int64)
+    else:
+        wseg, sseg = cut_table(rng, d, 6), cut_table(rng, d, 4)
+    L = oba.Layout(d, n, wseg, sseg)
+    st = synth.host_state(rng, d, n)
+    E, D = two_states(L, gdt, st)
+    delta = torch().zeros_like(D.delta)
+    eps = torch().zeros_like(D.eps)
+    for t in range(5):
+        g = to_dev(padded(grads(rng, n, d, gdt), L.ld))
+        E.step(B1, LR, g=g)
+        D.step_deferred(B1, LR, g=g)
+        oba.deferred_errors(L, D.delta, D.wscale, D.eps, D.sscale, delta, eps)
+        torch().cuda.synchronize()
+        for nm in ("wbits", "wscale", "sbits", "sscale", "m", "x"):
+            same(getattr(E, nm), getattr(D, nm), f"{nm} at step {t}")
+        same(E.delta[:, :d], delta[:, :d], f"delta at step {t}")
+        same(E.eps, eps, f"eps at step {t}")
+    L.close()
+
+
+def test_deferred_layout_free_running_tracks_oracle():
+    w = synth.workload("tiny")
+    say(f"[deferred free-run] tiny d={w.d} n={w.n}")
+    x0, G = synth.tiny_inputs(w.seed, w.d, w.n)
+    L = oba.Layout(w.d, w.n, w.wseg, w.sseg)
+    S = oba.State(L)
+    S.x.copy_(torch().from_numpy(x0))
+    x, m, v = x0.copy(), np.zeros(w.d, np.float32), np.zeros(w.d, np.float32)
+    for t in range(10):
+        oracle.adam_warmup_step(G[t], x, m, v, LR, B1, synth.BETA2, ETA)
+        S.warmup(LR, B1, synth.BETA2, ETA, g=to_dev(G[t]))
+    st = dict(x=x, m=m, delta=np.zeros((w.n, w.d), np.float32), eps=np.zeros(w.d, np.float32),
+              denom=oracle.freeze_variance(v, ETA))
+    S.freeze(ETA)
+    delta = torch().zeros_like(S.delta)
+    eps = torch().zeros_like(S.eps)
+    for t in range(10, 20):
+        wb, ws, sb, ss = oracle.step(st, G[t], w.wseg, w.sseg, B1, LR)
+        S.step_deferred(B1, LR, g=to_dev(G[t]))
+        oba.deferred_errors(L, S.delta, S.wscale, S.eps, S.sscale, delta, eps)
+        torch().cuda.synchronize()
+        assert_words(to_host(S.wbits, np.uint64), wb, f"worker words, step {t}")
+        assert_words(to_host(S.sbits, np.uint64), sb, f"server words, step {t}")
+        assert_close(to_host(S.wscale), ws, f"worker scales, step {t}")
+        assert_close(to_host(S.sscale), ss, f"server scales, step {t}")
+        assert_close(to_host(delta), st["delta"], f"delta, step {t}")
+        assert_close(to_host(eps), st["eps"], f"eps, step {t}")
+        assert_close(to_host(S.m), st["m"], f"m, step {t}")
+        assert_close(to_host(S.x), st["x"], f"x, step {t}")
+    L.close()
+
+
+def test_deferred_errors_rejects_bad_arguments():
+    L = oba.Layout(100, 2, synth.whole(100), synth.even_shards(100, 2))
+    S = oba.State(L)
+    import ctypes
+
+    P = ctypes.c_void_p
+    strm = P(torch().cuda.current_stream().cuda_stream)
+    lib = oba.lib()
+    # no output requested
+    assert lib.oba_deferred_errors(L.handle, P(S.delta.data_ptr()), P(S.wscale.data_ptr()),
+                                   P(S.eps.data_ptr()), P(S.sscale.data_ptr()), None, None,
+                                   strm) == -1
+    # in place is not allowed (the accessor never changes the state)
+    assert lib.oba_deferred_errors(L.handle, P(S.delta.data_ptr()), P(S.wscale.data_ptr()), None,
+                                   None, P(S.delta.data_ptr()), None, strm) == -1
+    torch().cuda.synchronize()
+    L.close()
+
+
+def test_bert_large_deferred_step_equals_explicit_step_on_device():
+    """Full size, bench launch configuration: one explicit and one deferred
+    step from the same state, compared bit for bit on the device."""
+    w = synth.workload("bert_large")
+    say(f"[deferred==explicit full size] {w.name} d={w.d} n={w.n}")
+    L, E, gsets = bench.make_state(w, torch(), oba, synth)
+    D = oba.State(L, w.g_dtype)
+    for nm in ("m", "x", "denom"):
+        getattr(D, nm).copy_(getattr(E, nm))
+    del D.g
+    # both start from the freeze state (errors, c, a and scales all zero)
+    for i in range(2):
+        E.step(B1, LR, g=gsets[i])
+        D.step_deferred(B1, LR, g=gsets[i])
+    torch().cuda.synchronize()
+    for nm in ("wbits", "wscale", "sbits", "sscale", "m", "x"):
+        assert torch().equal(getattr(E, nm), getattr(D, nm)), nm
+    delta = torch().empty_like(E.delta)
+    oba.deferred_errors(L, D.delta, D.wscale, D.eps, D.sscale, delta, None)
+    torch().cuda.synchronize()
+    assert torch().equal(delta, E.delta), "delta"
+    del delta
+    eps = torch().empty_like(E.eps)
+    oba.deferred_errors(L, D.delta, D.wscale, D.eps, D.sscale, None, eps)
+    torch().cuda.synchronize()
+    assert torch().equal(eps, E.eps), "eps"
+    L.close()
