@@ -1,15 +1,20 @@
 // kernels.hip -- HIP kernels of the 1-bit Adam compression-stage step, gfx950.
 //
 // All kernels are HBM-streaming: a few flops per byte, no contraction, so
-// no matrix cores.  Every lane owns 8 consecutive coordinates, loaded as
-// 16-byte vectors (two for binary32, one for binary16); the 8 sign bits of a
-// lane form exactly one byte of the packed little-endian word array, so each
-// lane writes its byte with one store and no cross-lane exchange.  A block
-// walks a contiguous range of 2048-coordinate spans.  Sums of squares are
-// binary64 per lane (the square of a binary32 value is exact there), reduced
-// across the wave by a butterfly and across the 4 waves through LDS into one
-// partial per (piece, row); a second tiny kernel sums a segment's partials in
-// piece order.  No atomics: results are bitwise reproducible.
+// no matrix cores.  A block walks a contiguous range of spans of
+// kSpan = 8*kBlock coordinates.  Inside a span, thread t owns two quads of
+// coordinates, A = [lo+4t, lo+4t+4) and B = [lo+4*kBlock+4t, +4): every
+// 16-byte vector instruction of a wave then covers one contiguous kilobyte
+// (measured 12-18 % faster on this HBM than 8 consecutive coordinates per
+// lane, whose two vectors leave every instruction half-line strided).  The
+// 8 sign bits of a lane are two nibbles; lanes 2u and 2u+1 swap theirs with
+// one cross-lane exchange, the even lane stores byte u of the A half and the
+// odd lane byte u of the B half, so every packed byte has one writer.
+// Sums of squares are binary64 per lane (the square of a binary32 value is
+// exact there), reduced across the wave by a butterfly and across the waves
+// through LDS into one partial per (piece, row); a second tiny kernel sums a
+// segment's partials in piece order.  No atomics: results are bitwise
+// reproducible.
 //
 // Method passages are cited in include/oba.h beside each entry point.
 #include <hip/hip_runtime.h>
@@ -23,17 +28,20 @@ namespace oba {
 namespace {
 
 // -------------------------------------------------------------------------
-// 8-wide loads and stores with a guarded tail (coordinates >= d read as 0
-// and are never written).  Row bases are 32-byte aligned for binary32 and
-// 16-byte aligned for binary16 (16-byte-aligned base, ld % 8 == 0, k0 % 8 == 0).
-// Streamed inputs are read with the nontemporal hint: every byte is used once
-// per pass, so there is nothing for the caches to keep.
+// Lane layout, loads and stores.  Row bases are 16-byte aligned and
+// ld % 8 == 0, so quad starts are 16-byte aligned for binary32 and 8-byte
+// aligned for binary16.  Full spans use unchecked vector loads (a checked
+// load is followed by its own wait); the tail span checks every element
+// (coordinates >= d read as 0 and are never written).
 // -------------------------------------------------------------------------
 #ifndef OBA_NT_LOADS
 #define OBA_NT_LOADS 1
 #endif
+#ifndef OBA_NT_STORES
+#define OBA_NT_STORES 1
+#endif
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <typename V>
 __device__ __forceinline__ V ldv(const V* p) {
@@ -41,62 +49,87 @@ __device__ __forceinline__ V ldv(const V* p) {
   else return *p;
 }
 
-__device__ __forceinline__ void load8(const float* __restrict__ p, int64_t k0, int64_t d,
-                                      float (&v)[8]) {
-  if (k0 + 8 <= d) {
-    const f32x4 a = ldv(reinterpret_cast<const f32x4*>(p + k0));
-    const f32x4 b = ldv(reinterpret_cast<const f32x4*>(p + k0 + 4));
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = (k0 + j < d) ? p[k0 + j] : 0.0f;
-  }
+template <typename V>
+__device__ __forceinline__ void stv(V v, V* p) {
+  if constexpr (OBA_NT_STORES) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+struct Quads {
+  int64_t kA, kB;  // first coordinates of the lane's two quads
+};
+
+__device__ __forceinline__ Quads quads(int64_t lo) {
+  const int64_t t = threadIdx.x;
+  return {lo + 4 * t, lo + 4 * (int64_t)kBlock + 4 * t};
+}
+
+// coordinate of the lane's element j (0..3: quad A, 4..7: quad B); increasing in j
+__device__ __forceinline__ int64_t coord(const Quads& q, int j) {
+  return j < 4 ? q.kA + j : q.kB + (j - 4);
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
 }
 
-__device__ __forceinline__ void load8(const uint16_t* __restrict__ p, int64_t k0, int64_t d,
-                                      float (&v)[8]) {
-  if (k0 + 8 <= d) {
-    const u32x4 a = ldv(reinterpret_cast<const u32x4*>(p + k0));
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[2 * j] = half_bits_to_float(w[j] & 0xFFFFu);
-      v[2 * j + 1] = half_bits_to_float(w[j] >> 16);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = (k0 + j < d) ? half_bits_to_float(p[k0 + j]) : 0.0f;
-  }
-}
-
-__device__ __forceinline__ float grad_at(const float* p, int64_t k) { return p[k]; }
-__device__ __forceinline__ float grad_at(const uint16_t* p, int64_t k) {
+__device__ __forceinline__ float elem(const float* p, int64_t k) { return p[k]; }
+__device__ __forceinline__ float elem(const uint16_t* p, int64_t k) {
   return half_bits_to_float(p[k]);
 }
 
-// Full-span loaders: no tail check, so a kernel can issue every load of a
-// span before it uses any of them (a checked load is followed by its wait).
-__device__ __forceinline__ void load8_full(const float* __restrict__ p, int64_t k0,
-                                           float (&v)[8]) {
-  const f32x4 a = ldv(reinterpret_cast<const f32x4*>(p + k0));
-  const f32x4 b = ldv(reinterpret_cast<const f32x4*>(p + k0 + 4));
+__device__ __forceinline__ void load_full(const float* __restrict__ p, const Quads& q,
+                                          float (&v)[8]) {
+  const f32x4 a = ldv(reinterpret_cast<const f32x4*>(p + q.kA));
+  const f32x4 b = ldv(reinterpret_cast<const f32x4*>(p + q.kB));
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-__device__ __forceinline__ void load8_full(const uint16_t* __restrict__ p, int64_t k0,
-                                           float (&v)[8]) {
-  const u32x4 a = ldv(reinterpret_cast<const u32x4*>(p + k0));
-  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+__device__ __forceinline__ void load_full(const uint16_t* __restrict__ p, const Quads& q,
+                                          float (&v)[8]) {
+  const u32x2 a = ldv(reinterpret_cast<const u32x2*>(p + q.kA));
+  const u32x2 b = ldv(reinterpret_cast<const u32x2*>(p + q.kB));
+  v[0] = half_bits_to_float(a.x & 0xFFFFu);
+  v[1] = half_bits_to_float(a.x >> 16);
+  v[2] = half_bits_to_float(a.y & 0xFFFFu);
+  v[3] = half_bits_to_float(a.y >> 16);
+  v[4] = half_bits_to_float(b.x & 0xFFFFu);
+  v[5] = half_bits_to_float(b.x >> 16);
+  v[6] = half_bits_to_float(b.y & 0xFFFFu);
+  v[7] = half_bits_to_float(b.y >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ void load_tail(const T* __restrict__ p, const Quads& q, int64_t d,
+                                          float (&v)[8]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    v[2 * j] = half_bits_to_float(w[j] & 0xFFFFu);
-    v[2 * j + 1] = half_bits_to_float(w[j] >> 16);
+  for (int j = 0; j < 8; ++j) {
+    const int64_t k = coord(q, j);
+    v[j] = (k < d) ? elem(p, k) : 0.0f;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* __restrict__ p, const Quads& q, int64_t d,
+                                      bool full, float (&v)[8]) {
+  if (full)
+    load_full(p, q, v);
+  else
+    load_tail(p, q, d, v);
+}
+
+__device__ __forceinline__ void store8(float* __restrict__ p, const Quads& q, int64_t d,
+                                       bool full, const float (&v)[8]) {
+  if (full) {
+    stv(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(p + q.kA));
+    stv(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4*>(p + q.kB));
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t k = coord(q, j);
+      if (k < d) p[k] = v[j];
+    }
   }
 }
 
@@ -106,23 +139,51 @@ __device__ __forceinline__ float compensate(float b1, float omb1, float m, float
   return p + dl;
 }
 
-__device__ __forceinline__ void store8(float* __restrict__ p, int64_t k0, int64_t d,
-                                       const float (&v)[8]) {
-  if (k0 + 8 <= d) {
-    *reinterpret_cast<float4*>(p + k0) = make_float4(v[0], v[1], v[2], v[3]);
-    *reinterpret_cast<float4*>(p + k0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (k0 + j < d) p[k0 + j] = v[j];
-  }
-}
-
-__device__ __forceinline__ uint32_t sign_byte(const float (&c)[8]) {
+// bit j = (v[j] < 0): -0.0 gives 0 (sign +1).  Bits 0-3 quad A, 4-7 quad B.
+__device__ __forceinline__ uint32_t sign_bits(const float (&v)[8]) {
   uint32_t b = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) b |= (c[j] < 0.0f ? 1u : 0u) << j;  // -0.0 gives 0 (+1)
+  for (int j = 0; j < 8; ++j) b |= (v[j] < 0.0f ? 1u : 0u) << j;
   return b;
+}
+
+// Store the lane's 8 sign bits into a packed row (little-endian bytes,
+// nbytes = 8*W).  Every lane of the wave must call this (cross-lane exchange).
+__device__ __forceinline__ void store_sign_bits(uint8_t* __restrict__ row, const Quads& q,
+                                                uint32_t b8, int64_t nbytes) {
+  const uint32_t p = (uint32_t)__shfl_xor((int)b8, 1, 64);
+  const bool odd = threadIdx.x & 1;
+  const uint32_t byte = odd ? ((p >> 4) | (b8 & 0xF0u)) : ((b8 & 0xFu) | ((p & 0xFu) << 4));
+  const int64_t qi = (odd ? q.kB : q.kA) >> 3;
+  if (qi < nbytes) row[qi] = (uint8_t)byte;
+}
+
+// The lane's 8 sign bits from a packed row.  FULL: both quads lie inside
+// [0, d) (no checks).  Otherwise bytes whose coordinates all lie at or past d
+// read as 0.  With OBA_SIGN_PAIRS each lane loads the two bytes holding its
+// quads; otherwise the even lane loads the A-half byte of the pair, the odd
+// lane the B-half byte (one distinct byte per lane), and they swap -- every
+// lane of the wave must then call this (cross-lane exchange).
+#ifndef OBA_SIGN_PAIRS
+#define OBA_SIGN_PAIRS 0
+#endif
+template <bool FULL>
+__device__ __forceinline__ uint32_t load_sign_bits(const uint8_t* __restrict__ row,
+                                                   const Quads& q, int64_t d) {
+  const bool odd = threadIdx.x & 1;
+  const uint32_t sh = odd ? 4u : 0u;
+  uint32_t byte_a, byte_b;
+  if constexpr (OBA_SIGN_PAIRS) {
+    byte_a = (FULL || q.kA < d) ? (uint32_t)row[q.kA >> 3] : 0u;
+    byte_b = (FULL || q.kB < d) ? (uint32_t)row[q.kB >> 3] : 0u;
+  } else {
+    const int64_t qi = (odd ? q.kB : q.kA) >> 3;
+    const uint32_t mine = (FULL || qi * 8 < d) ? (uint32_t)row[qi] : 0u;
+    const uint32_t other = (uint32_t)__shfl_xor((int)mine, 1, 64);
+    byte_a = odd ? other : mine;
+    byte_b = odd ? mine : other;
+  }
+  return ((byte_a >> sh) & 0xFu) | (((byte_b >> sh) & 0xFu) << 4);
 }
 
 __device__ __forceinline__ double sumsq8(const float (&c)[8]) {
@@ -157,7 +218,10 @@ __device__ __forceinline__ void flush_rows(double (&acc)[NB], int nw, double* __
   __syncthreads();
   if ((int)threadIdx.x < nw) {
     const int i = threadIdx.x;
-    dst[i] = ((lds[i] + lds[NB + i]) + lds[2 * NB + i]) + lds[3 * NB + i];
+    double t = lds[i];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) t += lds[w * NB + i];  // fixed order
+    dst[i] = t;
   }
   __syncthreads();
 }
@@ -175,13 +239,25 @@ __device__ __forceinline__ int32_t seg_walk(const int64_t* __restrict__ off, int
   return j;
 }
 
+// Segments of the lane's 8 coordinates (coordinates >= d keep the last one).
+__device__ __forceinline__ void lane_segs(const int64_t* __restrict__ off, int32_t j0,
+                                          const Quads& q, int64_t d, int32_t (&js)[8]) {
+  int32_t j = j0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int64_t k = coord(q, e);
+    if (k < d) j = seg_walk(off, j, k);
+    js[e] = j;
+  }
+}
+
 // Sum of squares of row[k] for the lane's coordinates k in [a, e).
-__device__ __forceinline__ double sumsq_range(const float* row, int64_t k0, int64_t a,
+__device__ __forceinline__ double sumsq_range(const float* row, const Quads& q, int64_t a,
                                               int64_t e) {
   double s = 0.0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int64_t k = k0 + j;
+    const int64_t k = coord(q, j);
     if (k >= a && k < e) {
       const double x = (double)row[k];
       s = __builtin_fma(x, x, s);
@@ -193,19 +269,22 @@ __device__ __forceinline__ double sumsq_range(const float* row, int64_t k0, int6
 // Same, recomputing c = compensate(m, g, delta) from the inputs.
 template <typename GT>
 __device__ __forceinline__ double sumsq_range_c(const float* m, const GT* grow, const float* drow,
-                                                float b1, float omb1, int64_t k0, int64_t a,
+                                                float b1, float omb1, const Quads& q, int64_t a,
                                                 int64_t e) {
   double s = 0.0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int64_t k = k0 + j;
+    const int64_t k = coord(q, j);
     if (k >= a && k < e) {
-      const double x = (double)compensate(b1, omb1, m[k], grad_at(grow, k), drow[k]);
+      const double x = (double)compensate(b1, omb1, m[k], elem(grow, k), drow[k]);
       s = __builtin_fma(x, x, s);
     }
   }
   return s;
 }
+
+// residual c - s*sign(c), sign(c) = -1 iff c < 0
+__device__ __forceinline__ float residual(float c, float s) { return (c < 0.0f) ? c + s : c - s; }
 
 }  // namespace
 
@@ -221,9 +300,9 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
   const int64_t s_hi = dspan(G.S, G.nblk, blockIdx.x + 1);
   const float nf = (float)G.n;
   for (int64_t s = s_lo; s < s_hi; ++s) {
-    const int64_t k0 = s * kSpan + (int64_t)threadIdx.x * kVec;
-    if (k0 >= G.d) continue;
-    const bool full = k0 + 8 <= G.d;
+    const int64_t lo = s * kSpan;
+    const Quads q = quads(lo);
+    const bool full = lo + kSpan <= G.d;
     float sum[8], mv[8], vv[8], xv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) sum[j] = 0.0f;
@@ -231,13 +310,8 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
       // four rows loaded together (rows past n clamped, their terms skipped)
       float gv[4][8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const GT* row = g + (int64_t)min(i0 + u, G.n - 1) * G.ld;
-        if (full)
-          load8_full(row, k0, gv[u]);
-        else
-          load8(row, k0, G.d, gv[u]);
-      }
+      for (int u = 0; u < 4; ++u)
+        load8(g + (int64_t)min(i0 + u, G.n - 1) * G.ld, q, G.d, full, gv[u]);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         if (i0 + u < G.n) {
@@ -245,15 +319,9 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
           for (int j = 0; j < 8; ++j) sum[j] = sum[j] + gv[u][j];
         }
     }
-    if (full) {
-      load8_full(m, k0, mv);
-      load8_full(v, k0, vv);
-      load8_full(x, k0, xv);
-    } else {
-      load8(m, k0, G.d, mv);
-      load8(v, k0, G.d, vv);
-      load8(x, k0, G.d, xv);
-    }
+    load8(m, q, G.d, full, mv);
+    load8(v, q, G.d, full, vv);
+    load8(x, q, G.d, full, xv);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float gb = sum[j] / nf;
@@ -263,9 +331,9 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
       vv[j] = vk;
       xv[j] = xv[j] - (C.lr * (mk / C.bc1)) / (__builtin_sqrtf(vk / C.bc2) + C.eta);
     }
-    store8(m, k0, G.d, mv);
-    store8(v, k0, G.d, vv);
-    store8(x, k0, G.d, xv);
+    store8(m, q, G.d, full, mv);
+    store8(v, q, G.d, full, vv);
+    store8(x, q, G.d, full, xv);
   }
 }
 
@@ -278,16 +346,14 @@ __global__ __launch_bounds__(kBlock) void k_freeze(Geo G, const float* __restric
   const int64_t s_lo = dspan(G.S, G.nblk, blockIdx.x);
   const int64_t s_hi = dspan(G.S, G.nblk, blockIdx.x + 1);
   for (int64_t s = s_lo; s < s_hi; ++s) {
-    const int64_t k0 = s * kSpan + (int64_t)threadIdx.x * kVec;
-    if (k0 >= G.d) continue;
+    const int64_t lo = s * kSpan;
+    const Quads q = quads(lo);
+    const bool full = lo + kSpan <= G.d;
     float vv[8];
-    if (k0 + 8 <= G.d)
-      load8_full(v, k0, vv);
-    else
-      load8(v, k0, G.d, vv);
+    load8(v, q, G.d, full, vv);
 #pragma unroll
     for (int j = 0; j < 8; ++j) vv[j] = __builtin_sqrtf(vv[j] / bc2) + eta;
-    store8(denom, k0, G.d, vv);
+    store8(denom, q, G.d, full, vv);
   }
 }
 
@@ -295,22 +361,27 @@ __global__ __launch_bounds__(kBlock) void k_freeze(Geo G, const float* __restric
 // Worker side, for NB workers at once (m is read once per coordinate):
 //   c = (b1*m + (1-b1)*g_i) + delta_i
 // kNorm:  only reduce sum c^2 per (piece, worker) -- reads only;
-// kApply: recompute c bit for bit, store the sign byte and
+// kApply: recompute c bit for bit, store the sign bits and
 //         delta_i = c - s*sign(c) with the finished scales;
 // kDeferred: the state row holds the previous step's c (not delta) and the
 //         scale buffer its scales s'; the residual of the last step is formed
 //         where it is consumed, delta_i = c' - s'*sign(c'), then
 //         c = (b1*m + (1-b1)*g_i) + delta_i is stored over c' with its sign
-//         byte and its sum c^2 is reduced -- one pass instead of two.
+//         bits and its sum c^2 is reduced -- one pass instead of two.
 // The scale needs the whole segment's norm before any residual can be
-// written, so c is needed twice.  Recomputing it reads g, m, delta twice but
-// never writes c: on this HBM, writes cost more than reads, and storing c in
-// a first pass to re-read it was measured 15 % slower per step.
+// written, so the explicit layout needs c twice.  Recomputing it reads g, m,
+// delta twice but never writes c: on this HBM, writes cost more than reads,
+// and storing c in a first pass to re-read it was measured 15 % slower per
+// step.
 // NB is the exact number of workers of a block: a launch covers workers
-// [i0, i0 + gridDim.y*NB); n > 8 takes one launch of NB=8 groups and one
+// [i0, i0 + gridDim.y*NB); larger n takes one launch of full groups and one
 // for the remainder.  Grid: (nblk, groups).
 // ===========================================================================
 enum { kNorm = 1, kApply = 2, kDeferred = 3 };
+#ifndef OBA_WORKER_BATCH
+#define OBA_WORKER_BATCH 4
+#endif
+constexpr int kWorkerBatch = OBA_WORKER_BATCH;
 
 template <typename GT, int NB, int MODE>
 __global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT* __restrict__ g,
@@ -320,7 +391,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT
                                                      double* __restrict__ part,
                                                      const float* __restrict__ wscale, float b1,
                                                      float omb1) {
-  __shared__ double lds[4 * NB];
+  __shared__ double lds[kWaves * NB];
   const int32_t b = blockIdx.x;
   i0 += blockIdx.y * NB;  // this block's workers: [i0, i0 + NB)
   const int64_t s_lo = dspan(G.S, G.nblk, b), s_hi = dspan(G.S, G.nblk, b + 1);
@@ -335,80 +406,78 @@ __global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT
   for (int64_t s = s_lo; s < s_hi; ++s) {
     const int64_t lo = s * kSpan;
     const int64_t hi = min(lo + kSpan, G.d);
-    const int64_t k0 = lo + (int64_t)threadIdx.x * kVec;
+    const Quads q = quads(lo);
     const bool uniform = hi <= p_hi;  // span inside the current piece
     const bool full = lo + kSpan <= G.d;
     int32_t jseg[8];
-    if ((MODE == kApply || MODE == kDeferred) && !uniform) {
-      int32_t js = sig.pseg[p];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (k0 + j < G.d) js = seg_walk(sig.off, js, k0 + j);
-        jseg[j] = js;
-      }
-    }
+    if ((MODE == kApply || MODE == kDeferred) && !uniform) lane_segs(sig.off, sig.pseg[p], q, G.d, jseg);
     // every load of the span first (all NB workers), then the arithmetic
-    float mv[8], gv[NB][8], c[NB][8];
-    if (full) {
-      load8_full(m, k0, mv);
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int64_t row = (int64_t)(i0 + i) * G.ld;
-        load8_full(g + row, k0, gv[i]);
-        load8_full(delta + row, k0, c[i]);
-      }
-    } else {
-      load8(m, k0, G.d, mv);
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int64_t row = (int64_t)(i0 + i) * G.ld;
-        load8(g + row, k0, G.d, gv[i]);
-        load8(delta + row, k0, G.d, c[i]);
-      }
-    }
+    float mv[8];
+    if (full)
+      load_full(m, q, mv);
+    else
+      load_tail(m, q, G.d, mv);
     double fs[NB];
+    // workers in batches of NBB: all loads of a batch, then its arithmetic
+    // and stores (NBB < NB trades loads in flight per wave for occupancy)
+    constexpr int NBB = NB < kWorkerBatch ? NB : kWorkerBatch;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int64_t row = (int64_t)(i0 + i) * G.ld;
-      if (MODE == kDeferred) {  // c[i] holds c' of the last step: form its residual
-        const float* sc = wscale + (int64_t)(i0 + i) * sig.n_seg;
-        float sv[8];
-        if (uniform) {
-          const float s_ = sc[sig.pseg[p]];
+    for (int ib = 0; ib < NB; ib += NBB) {
+      float gv[NBB][8], c[NBB][8];
+      // ib + u < NB is decided at compile time: a last batch may be partial
+      if (full) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) sv[j] = s_;
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) sv[j] = sc[jseg[j]];
+        for (int u = 0; u < NBB; ++u) {
+          if (ib + u >= NB) break;
+          const int64_t row = (int64_t)(i0 + ib + u) * G.ld;
+          load_full(g + row, q, gv[u]);
+          load_full(delta + row, q, c[u]);
         }
+      } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) c[i][j] = (c[i][j] < 0.0f) ? c[i][j] + sv[j] : c[i][j] - sv[j];
-        if (!full) {  // coordinates past d read as 0 and must stay 0 (no bit, no c^2)
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (k0 + j >= G.d) c[i][j] = 0.0f;
+        for (int u = 0; u < NBB; ++u) {
+          if (ib + u >= NB) break;
+          const int64_t row = (int64_t)(i0 + ib + u) * G.ld;
+          load_tail(g + row, q, G.d, gv[u]);
+          load_tail(delta + row, q, G.d, c[u]);
         }
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) c[i][j] = compensate(b1, omb1, mv[j], gv[i][j], c[i][j]);
-      if (MODE != kNorm && k0 < 64 * G.W)
-        wbytes[(int64_t)(i0 + i) * rowbytes + (k0 >> 3)] = (uint8_t)sign_byte(c[i]);
-      if (MODE == kDeferred) store8(delta + row, k0, G.d, c[i]);
-      fs[i] = (MODE != kApply) ? sumsq8(c[i]) : 0.0;
-      if (MODE == kApply) {
+      for (int u = 0; u < NBB; ++u) {
+        const int i = ib + u;
+        if (i >= NB) break;
+        const int64_t row = (int64_t)(i0 + i) * G.ld;
         const float* sc = wscale + (int64_t)(i0 + i) * sig.n_seg;
         float sv[8];
-        if (uniform) {
-          const float s_ = sc[sig.pseg[p]];
+        if (MODE == kApply || MODE == kDeferred) {
+          if (uniform) {
+            const float s_ = sc[sig.pseg[p]];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) sv[j] = s_;
-        } else {
+            for (int j = 0; j < 8; ++j) sv[j] = s_;
+          } else {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) sv[j] = sc[jseg[j]];
+            for (int j = 0; j < 8; ++j) sv[j] = sc[jseg[j]];
+          }
+        }
+        if (MODE == kDeferred) {  // c[u] holds c' of the last step: form its residual
+#pragma unroll
+          for (int j = 0; j < 8; ++j) c[u][j] = residual(c[u][j], sv[j]);
+          if (!full) {  // coordinates past d read as 0 and must stay 0 (no bit, no c^2)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (coord(q, j) >= G.d) c[u][j] = 0.0f;
+          }
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) c[i][j] = (c[i][j] < 0.0f) ? c[i][j] + sv[j] : c[i][j] - sv[j];
-        store8(delta + row, k0, G.d, c[i]);
+        for (int j = 0; j < 8; ++j) c[u][j] = compensate(b1, omb1, mv[j], gv[u][j], c[u][j]);
+        if (MODE != kNorm) store_sign_bits(wbytes + (int64_t)(i0 + i) * rowbytes, q, sign_bits(c[u]), rowbytes);
+        if (MODE == kDeferred) store8(delta + row, q, G.d, full, c[u]);
+        fs[i] = (MODE != kApply) ? sumsq8(c[u]) : 0.0;
+        if (MODE == kApply) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) c[u][j] = residual(c[u][j], sv[j]);
+          store8(delta + row, q, G.d, full, c[u]);
+        }
       }
     }
     if (MODE == kApply) {
@@ -430,9 +499,9 @@ __global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT
         for (int i = 0; i < NB; ++i) {
           const int64_t row = (int64_t)(i0 + i) * G.ld;
           if (MODE == kDeferred)
-            acc[i] += sumsq_range(delta + row, k0, cur, e);  // c was stored there
+            acc[i] += sumsq_range(delta + row, q, cur, e);  // c was stored there
           else
-            acc[i] += sumsq_range_c(m, g + row, delta + row, b1, omb1, k0, cur, e);
+            acc[i] += sumsq_range_c(m, g + row, delta + row, b1, omb1, q, cur, e);
         }
         if (p_hi <= hi) {
           flush_rows<NB>(acc, NB, part + (int64_t)p * G.n + i0, lds);
@@ -488,29 +557,23 @@ __global__ __launch_bounds__(kBlock) void k_residual(Geo G, const float* src, in
   for (int64_t s = s_lo; s < s_hi; ++s) {
     const int64_t lo = s * kSpan;
     const int64_t hi = min(lo + kSpan, G.d);
-    const int64_t k0 = lo + (int64_t)threadIdx.x * kVec;
-    if (k0 < G.d) {
-      float c[8], sv[8];
-      if (lo + kSpan <= G.d)
-        load8_full(srow, k0, c);
-      else
-        load8(srow, k0, G.d, c);
-      if (hi <= p_hi) {
-        const float s_ = sc[T.pseg[p]];
+    const Quads q = quads(lo);
+    const bool full = lo + kSpan <= G.d;
+    float c[8], sv[8];
+    load8(srow, q, G.d, full, c);
+    if (hi <= p_hi) {
+      const float s_ = sc[T.pseg[p]];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sv[j] = s_;
-      } else {
-        int32_t js = T.pseg[p];
+      for (int j = 0; j < 8; ++j) sv[j] = s_;
+    } else {
+      int32_t js[8];
+      lane_segs(T.off, T.pseg[p], q, G.d, js);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (k0 + j < G.d) js = seg_walk(T.off, js, k0 + j);
-          sv[j] = sc[js];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) c[j] = (c[j] < 0.0f) ? c[j] + sv[j] : c[j] - sv[j];
-      store8(drow, k0, G.d, c);
+      for (int j = 0; j < 8; ++j) sv[j] = sc[js[j]];
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = residual(c[j], sv[j]);
+    store8(drow, q, G.d, full, c);
     while (p < p_end && p_hi <= hi) {
       if (++p < p_end) p_hi = T.phi[p];
     }
@@ -518,9 +581,9 @@ __global__ __launch_bounds__(kBlock) void k_residual(Geo G, const float* src, in
 }
 
 // ===========================================================================
-// Server pass 1: a = (sum_i s_i*sign_i)/n + eps per coordinate (workers in
-// order), a stored over eps, server sign byte stored, binary64 sum of a^2
-// reduced per server piece.  The sign bytes and scales of NB workers are
+// Server pass: a = (sum_i s_i*sign_i)/n + eps per coordinate (workers in
+// order), a stored over eps, server sign bits stored, binary64 sum of a^2
+// reduced per server piece.  The sign bits and scales of NB workers are
 // loaded before any is used, so their loads overlap (NB = n for n <= 8, else
 // groups of 8).  DEFERRED: the buffer holds the last step's a' and
 // sscale_prev its server scales; the server error is formed where it is
@@ -533,7 +596,7 @@ __global__ __launch_bounds__(kBlock) void k_server_p1(Geo G, const uint8_t* __re
                                                       uint8_t* __restrict__ sbytes, SegDev sig,
                                                       SegDev tau, double* __restrict__ part,
                                                       const float* __restrict__ sscale_prev) {
-  __shared__ double lds[4];
+  __shared__ double lds[kWaves];
   const int32_t b = blockIdx.x;
   const int64_t s_lo = dspan(G.S, G.nblk, b), s_hi = dspan(G.S, G.nblk, b + 1);
   const int32_t ps_end = sig.blk_first[b + 1], pt_end = tau.blk_first[b + 1];
@@ -545,79 +608,71 @@ __global__ __launch_bounds__(kBlock) void k_server_p1(Geo G, const uint8_t* __re
   for (int64_t s = s_lo; s < s_hi; ++s) {
     const int64_t lo = s * kSpan;
     const int64_t hi = min(lo + kSpan, G.d);
-    const int64_t k0 = lo + (int64_t)threadIdx.x * kVec;
-    double fs = 0.0;
-    const int64_t q = k0 >> 3;
+    const Quads q = quads(lo);
+    float a[8];
     if (hi <= ps_hi && hi <= pt_hi && lo + kSpan <= G.d) {
       // fast path: full span, one worker and one server segment; loads first
       const int32_t js0 = sig.pseg[ps];
-      float ev[8], t[8];
-      load8_full(eps, k0, ev);
+      float t[8];
+      load_full(eps, q, a);
       if (DEFERRED) {
         const float sp = sscale_prev[tau.pseg[pt]];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ev[j] = (ev[j] < 0.0f) ? ev[j] + sp : ev[j] - sp;
+        for (int j = 0; j < 8; ++j) a[j] = residual(a[j], sp);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) t[j] = 0.0f;
       for (int32_t i0 = 0; i0 < G.n; i0 += NB) {  // one pass when n <= NB
         // rows past n are clamped to a valid row and their terms skipped
-        uint32_t byte[NB];
+        uint32_t bits[NB];
         float sw[NB];
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
           const int64_t r = min(i0 + u, G.n - 1);
-          byte[u] = wbytes[r * rowbytes + q];
+          bits[u] = load_sign_bits<true>(wbytes + r * rowbytes, q, G.d);
           sw[u] = wscale[r * sig.n_seg + js0];
         }
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
           if (i0 + u < G.n) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) t[j] = t[j] + (((byte[u] >> j) & 1u) ? -sw[u] : sw[u]);
+            for (int j = 0; j < 8; ++j) t[j] = t[j] + (((bits[u] >> j) & 1u) ? -sw[u] : sw[u]);
           }
         }
       }
-      float a[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) a[j] = t[j] / nf + ev[j];
-      store8(eps, k0, G.d, a);
-      sbytes[q] = (uint8_t)sign_byte(a);
-      fs = sumsq8(a);
-    } else if (k0 < G.d) {
-      // general path (segment boundary in the span, or the tail): one
+      for (int j = 0; j < 8; ++j) a[j] = t[j] / nf + a[j];
+      store8(eps, q, G.d, true, a);
+    } else {
+      // general path (a segment boundary in the span, or the tail): one
       // coordinate at a time, same operations in the same order
-      uint32_t sb = 0;
       int32_t js = sig.pseg[ps];
       int32_t jt = tau.pseg[pt];
 #pragma unroll 1
       for (int j = 0; j < 8; ++j) {
-        const int64_t k = k0 + j;
+        const int64_t k = coord(q, j);
+        a[j] = 0.0f;
         if (k < G.d) {
           js = seg_walk(sig.off, js, k);
           float e = eps[k];
           if (DEFERRED) {
             jt = seg_walk(tau.off, jt, k);
-            const float sp = sscale_prev[jt];
-            e = (e < 0.0f) ? e + sp : e - sp;
+            e = residual(e, sscale_prev[jt]);
           }
+          const uint32_t sh = (uint32_t)(k & 7);  // bit of k in its byte
           float t = 0.0f;
           for (int32_t i = 0; i < G.n; ++i) {
-            const uint32_t byte = wbytes[(int64_t)i * rowbytes + q];
+            const uint32_t byte = wbytes[(int64_t)i * rowbytes + (k >> 3)];
             const float s_ = wscale[(int64_t)i * sig.n_seg + js];
-            t = t + (((byte >> j) & 1u) ? -s_ : s_);
+            t = t + (((byte >> sh) & 1u) ? -s_ : s_);
           }
-          const float a = t / nf + e;
-          eps[k] = a;
-          sb |= (a < 0.0f ? 1u : 0u) << j;
-          const double x = (double)a;
-          fs = __builtin_fma(x, x, fs);
+          a[j] = t / nf + e;
+          eps[k] = a[j];
         }
       }
-      sbytes[q] = (uint8_t)sb;
-    } else if (k0 < 64 * G.W) {
-      sbytes[q] = 0;
     }
+    store_sign_bits(sbytes, q, sign_bits(a), rowbytes);
+    const double fs = sumsq8(a);  // coordinates past d hold 0
     // advance the worker-segment cursor to the piece holding hi
     while (ps < ps_end && ps_hi <= hi) {
       if (++ps < ps_end) ps_hi = sig.phi[ps];
@@ -633,7 +688,7 @@ __global__ __launch_bounds__(kBlock) void k_server_p1(Geo G, const uint8_t* __re
       int64_t cur = lo;
       while (cur < hi) {
         const int64_t e = min(pt_hi, hi);
-        acc[0] += sumsq_range(eps, k0, cur, e);
+        acc[0] += sumsq_range(eps, q, cur, e);
         if (pt_hi <= hi) {
           flush_rows<1>(acc, 1, part + pt, lds);
           if (++pt < pt_end) pt_hi = tau.phi[pt];
@@ -663,37 +718,30 @@ __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
   for (int64_t s = s_lo; s < s_hi; ++s) {
     const int64_t lo = s * kSpan;
     const int64_t hi = min(lo + kSpan, G.d);
-    const int64_t k0 = lo + (int64_t)threadIdx.x * kVec;
-    if (k0 < G.d) {
-      float sv[8], dv[8], xv[8], mh[8];
-      if (hi <= p_hi) {
-        const float s_ = sscale[tau.pseg[p]];
+    const Quads q = quads(lo);
+    const bool full = lo + kSpan <= G.d;
+    float sv[8], dv[8], xv[8], mh[8];
+    const uint32_t bits = full ? load_sign_bits<true>(sbytes, q, G.d)
+                               : load_sign_bits<false>(sbytes, q, G.d);
+    load8(denom, q, G.d, full, dv);
+    load8(x, q, G.d, full, xv);
+    if (hi <= p_hi) {
+      const float s_ = sscale[tau.pseg[p]];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sv[j] = s_;
-      } else {
-        int32_t js = tau.pseg[p];
+      for (int j = 0; j < 8; ++j) sv[j] = s_;
+    } else {
+      int32_t js[8];
+      lane_segs(tau.off, tau.pseg[p], q, G.d, js);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (k0 + j < G.d) js = seg_walk(tau.off, js, k0 + j);
-          sv[j] = sscale[js];
-        }
-      }
-      const uint32_t byte = sbytes[k0 >> 3];
-      if (lo + kSpan <= G.d) {
-        load8_full(denom, k0, dv);
-        load8_full(x, k0, xv);
-      } else {
-        load8(denom, k0, G.d, dv);
-        load8(x, k0, G.d, xv);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        mh[j] = ((byte >> j) & 1u) ? -sv[j] : sv[j];
-        xv[j] = xv[j] - (lr * mh[j]) / dv[j];
-      }
-      store8(m, k0, G.d, mh);
-      store8(x, k0, G.d, xv);
+      for (int j = 0; j < 8; ++j) sv[j] = sscale[js[j]];
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      mh[j] = ((bits >> j) & 1u) ? -sv[j] : sv[j];
+      xv[j] = xv[j] - (lr * mh[j]) / dv[j];
+    }
+    store8(m, q, G.d, full, mh);
+    store8(x, q, G.d, full, xv);
     while (p < p_end && p_hi <= hi) {
       if (++p < p_end) p_hi = tau.phi[p];
     }
@@ -732,13 +780,19 @@ static void launch_cmp(const Geo& G, int32_t i0, int groups, const void* g, cons
                      omb1);
 }
 
-// groups of 8 workers, then one launch for the n % 8 remainder
+// groups of kMaxNB workers, then one launch for the remainder
+#ifndef OBA_MAX_NB
+#define OBA_MAX_NB 8
+#endif
+constexpr int kMaxNB = OBA_MAX_NB;
+
 template <typename GT, int MODE>
 static void launch_cmp_n(const Geo& G, const void* g, const float* m, float* delta,
                          uint8_t* wbytes, const SegDev& sig, double* part, const float* wscale,
                          float b1, float omb1, hipStream_t st) {
-  const int full = G.n / 8, rem = G.n % 8, i0 = full * 8;
-  if (full) launch_cmp<GT, 8, MODE>(G, 0, full, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st);
+  const int full = G.n / kMaxNB, rem = G.n % kMaxNB, i0 = full * kMaxNB;
+  if (full)
+    launch_cmp<GT, kMaxNB, MODE>(G, 0, full, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st);
   switch (rem) {
     case 1: launch_cmp<GT, 1, MODE>(G, i0, 1, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st); break;
     case 2: launch_cmp<GT, 2, MODE>(G, i0, 1, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st); break;

@@ -15,7 +15,11 @@
 
 namespace oba {
 
-constexpr int kBlock = 256;                 // threads per block (4 wave64)
+#ifndef OBA_BLOCK
+#define OBA_BLOCK 256
+#endif
+constexpr int kBlock = OBA_BLOCK;           // threads per block of the streaming kernels
+constexpr int kWaves = kBlock / 64;         // wave64s per block
 constexpr int kVec = 8;                     // consecutive coordinates per lane
 constexpr int64_t kSpan = kBlock * kVec;    // coordinates per block pass
 #ifndef OBA_MAX_BLOCKS
