@@ -26,8 +26,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 METRIC = "params updated/sec per 1-bit Adam step + achieved HBM GB/s vs peak"
-KERNEL_SRC = os.path.join(ROOT, "communication_compressed_optimizer_02_amd", "csrc",
-                          "kernels.hip")
+CSRC = os.path.join(ROOT, "communication_compressed_optimizer_02_amd", "csrc")
 
 
 def log(*a):
@@ -70,8 +69,14 @@ def method_bytes(w):
 
 
 def source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel sources and of the code that picks their launch
+    grids (everything under csrc/)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(workload, kernel):

@@ -3,6 +3,7 @@
 // optional per-kernel event timing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -20,8 +21,11 @@ struct oba_layout_s {
   oba::Plan plan;
   int device = -1;
   void* dev_tables = nullptr;
-  oba::SegDev sig{}, tau{};
-  oba::Geo geo{};
+  oba::SegDev sig_w{};  // worker segments, worker grid (compress kernels)
+  oba::SegDev sig{};    // worker segments, server grid
+  oba::SegDev tau{};    // server segments, server grid
+  oba::Geo geo_w{};     // worker grid
+  oba::Geo geo{};       // server grid
   size_t ws_worker = 0, ws_server = 0;
 };
 
@@ -169,9 +173,10 @@ int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const i
     o32[2] = h32.size();
     h32.insert(h32.end(), pc.seg_first.begin(), pc.seg_first.end());
   };
-  size_t w64[2], w32[3], s64[2], s32[3];
+  size_t w64[2], w32[3], v64[2], v32[3], s64[2], s32[3];
   try {
     put(P.wp, P.wseg, w64, w32);
+    put(P.wp_s, P.wseg, v64, v32);
     put(P.sp, P.sseg, s64, s32);
   } catch (...) {
     delete L;
@@ -207,10 +212,12 @@ int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const i
     s.n_seg = n_seg;
     return s;
   };
-  L->sig = view(w64, w32, (int32_t)P.wseg.size() - 1);
+  L->sig_w = view(w64, w32, (int32_t)P.wseg.size() - 1);
+  L->sig = view(v64, v32, (int32_t)P.wseg.size() - 1);
   L->tau = view(s64, s32, (int32_t)P.sseg.size() - 1);
+  L->geo_w = oba::Geo{P.d, P.ld, P.W, P.S, P.n, P.nblk_w};
   L->geo = oba::Geo{P.d, P.ld, P.W, P.S, P.n, P.nblk};
-  L->ws_worker = nw_p * (size_t)P.n * sizeof(double);
+  L->ws_worker = std::max(nw_p, P.wp_s.lo.size()) * (size_t)P.n * sizeof(double);
   L->ws_server = ns_p * sizeof(double);
   *out = L;
   return OBA_OK;
@@ -278,17 +285,20 @@ int oba_compress(oba_layout L, const void* g, int g_dtype, const float* m, float
   OBA_TRY(check_buf(wscale, 4));
   OBA_TRY(check_buf(ws, 8));
   if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
-  const oba::Geo G = L->geo;
+  const oba::Geo G = L->geo_w;
   double* part = static_cast<double*>(ws);
   const float b1 = (float)beta1, omb1 = (float)(1.0 - beta1);
   uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
+  // the read-only norm pass runs on the server grid (a few spans per block:
+  // its per-block reduction would dominate at one span per block)
   OBA_TRY(launch("compress_p1", stream, [&] {
-    oba::launch_compress_norm(G, g, g_dtype == OBA_F16, m, delta, L->sig, part, b1, omb1, stream);
+    oba::launch_compress_norm(L->geo, g, g_dtype == OBA_F16, m, delta, L->sig, part, b1, omb1,
+                              stream);
   }));
   OBA_TRY(launch("finalize_scales", stream,
                  [&] { oba::launch_finalize(part, G.n, L->sig, wscale, stream); }));
   return launch("compress_p2", stream, [&] {
-    oba::launch_compress_apply(G, g, g_dtype == OBA_F16, m, delta, wbytes, L->sig, wscale, b1,
+    oba::launch_compress_apply(G, g, g_dtype == OBA_F16, m, delta, wbytes, L->sig_w, wscale, b1,
                                omb1, stream);
   });
 }
@@ -333,16 +343,16 @@ int oba_compress_deferred(oba_layout L, const void* g, int g_dtype, const float*
   OBA_TRY(check_buf(wscale, 4));
   OBA_TRY(check_buf(ws, 8));
   if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
-  const oba::Geo G = L->geo;
+  const oba::Geo G = L->geo_w;
   double* part = static_cast<double*>(ws);
   const float b1 = (float)beta1, omb1 = (float)(1.0 - beta1);
   uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
   OBA_TRY(launch("compress_deferred", stream, [&] {
-    oba::launch_compress_deferred(G, g, g_dtype == OBA_F16, m, c, wbytes, L->sig, part, wscale, b1,
+    oba::launch_compress_deferred(G, g, g_dtype == OBA_F16, m, c, wbytes, L->sig_w, part, wscale, b1,
                                   omb1, stream);
   }));
   return launch("finalize_scales", stream,
-                [&] { oba::launch_finalize(part, G.n, L->sig, wscale, stream); });
+                [&] { oba::launch_finalize(part, G.n, L->sig_w, wscale, stream); });
 }
 
 int oba_server_reduce_recompress_deferred(oba_layout L, const uint64_t* wbits,

@@ -20,19 +20,19 @@ int check_table(int64_t d, const int64_t* seg, int32_t n_seg) {
   return kOk;
 }
 
-// Cut segment table `off` at the block boundaries of the streaming grid.
-int cut(const Plan& P, const std::vector<int64_t>& off, Pieces* out) {
+// Cut segment table `off` at the block boundaries of a grid of nblk blocks.
+int cut(const Plan& P, int32_t nblk, const std::vector<int64_t>& off, Pieces* out) {
   const int32_t n_seg = (int32_t)off.size() - 1;
   out->lo.clear();
   out->hi.clear();
   out->seg.clear();
-  out->blk_first.assign((size_t)P.nblk + 1, 0);
+  out->blk_first.assign((size_t)nblk + 1, 0);
   out->seg_first.assign((size_t)n_seg + 1, 0);
   int32_t j = 0;
-  for (int32_t b = 0; b < P.nblk; ++b) {
+  for (int32_t b = 0; b < nblk; ++b) {
     out->blk_first[b] = (int32_t)out->lo.size();
-    const int64_t r0 = span_begin(P.S, P.nblk, b) * kSpan;
-    const int64_t r1 = std::min(span_begin(P.S, P.nblk, b + 1) * kSpan, P.d);
+    const int64_t r0 = span_begin(P.S, nblk, b) * kSpan;
+    const int64_t r1 = std::min(span_begin(P.S, nblk, b + 1) * kSpan, P.d);
     while (off[j + 1] <= r0) ++j;
     for (int32_t jj = j; jj < n_seg && off[jj] < r1; ++jj) {
       if (out->lo.size() >= (size_t)INT32_MAX - 1) return kESeg;
@@ -41,7 +41,7 @@ int cut(const Plan& P, const std::vector<int64_t>& off, Pieces* out) {
       out->seg.push_back(jj);
     }
   }
-  out->blk_first[P.nblk] = (int32_t)out->lo.size();
+  out->blk_first[nblk] = (int32_t)out->lo.size();
   // pieces are in coordinate order, so each segment's pieces are consecutive
   int32_t q = 0;
   for (int32_t s = 0; s < n_seg; ++s) {
@@ -76,10 +76,12 @@ int make_plan(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_w
     P.W = (d + 63) / 64;
     P.S = (d + kSpan - 1) / kSpan;
     P.nblk = (int32_t)std::min<int64_t>(P.S, kMaxBlocks);
+    P.nblk_w = (int32_t)std::min<int64_t>(P.S, kMaxBlocksWorker);
     P.wseg.assign(wseg, wseg + n_wseg + 1);
     P.sseg.assign(sseg, sseg + n_sseg + 1);
-    if ((rc = cut(P, P.wseg, &P.wp))) return rc;
-    if ((rc = cut(P, P.sseg, &P.sp))) return rc;
+    if ((rc = cut(P, P.nblk_w, P.wseg, &P.wp))) return rc;
+    if ((rc = cut(P, P.nblk, P.wseg, &P.wp_s))) return rc;
+    if ((rc = cut(P, P.nblk, P.sseg, &P.sp))) return rc;
     *out = std::move(P);
   } catch (...) {
     return kENoMem;

@@ -25,7 +25,14 @@ constexpr int64_t kSpan = kBlock * kVec;    // coordinates per block pass
 #ifndef OBA_MAX_BLOCKS
 #define OBA_MAX_BLOCKS 65536
 #endif
-constexpr int kMaxBlocks = OBA_MAX_BLOCKS;  // cap on blocks of the streaming grid
+#ifndef OBA_MAX_BLOCKS_WORKER
+#define OBA_MAX_BLOCKS_WORKER 131072
+#endif
+// Caps on blocks of the streaming grids: the worker-side kernels (many
+// streams, much work per span) run best with about one span per block, the
+// server and update kernels (little work per span) with a few spans each.
+constexpr int kMaxBlocks = OBA_MAX_BLOCKS;
+constexpr int kMaxBlocksWorker = OBA_MAX_BLOCKS_WORKER;
 constexpr int32_t kMaxWorkers = 4096;
 
 struct Pieces {
@@ -37,9 +44,13 @@ struct Pieces {
 
 struct Plan {
   int64_t d = 0, ld = 0, W = 0, S = 0;
-  int32_t n = 0, nblk = 0;
+  int32_t n = 0;
+  int32_t nblk = 0;    // grid of the server, update, residual, warm-up kernels
+  int32_t nblk_w = 0;  // grid of the worker-side compress kernels
   std::vector<int64_t> wseg, sseg;  // offsets, n_seg+1 each
-  Pieces wp, sp;
+  Pieces wp;    // worker segments cut on the worker grid (compress kernels)
+  Pieces wp_s;  // worker segments cut on the server grid (scale lookups there)
+  Pieces sp;    // server segments cut on the server grid
 };
 
 // Status codes mirror the C ABI (0 ok, negative error).

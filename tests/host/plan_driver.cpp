@@ -1,8 +1,9 @@
 // plan_driver.cpp -- test driver for the host-only piece planner.
 // Usage: plan_driver d n ld n_wseg o_0 .. o_nw n_sseg o_0 .. o_ns
-// Prints "rc <status>", then "G d W S nblk", then for each segmentation
-// "T <n_pieces> <n_seg>", one "P lo hi seg" line per piece, "B" + blk_first,
-// "S" + seg_first.  Built by the test suite with the host compiler and
+// Prints "rc <status>", then "G d W S nblk nblk_w", then for the worker
+// segments on the worker grid, the worker segments on the server grid and the
+// server segments on the server grid: "T <n_pieces> <n_seg>", one
+// "P lo hi seg" line per piece, "B" + blk_first, "S" + seg_first.  Built by the test suite with the host compiler and
 // sanitizers; it calls nothing of HIP.
 #include <cstdio>
 #include <cstdlib>
@@ -35,8 +36,10 @@ int main(int argc, char** argv) {
   int rc = oba::make_plan(d, (int32_t)n, ld, w.data(), nw, s.data(), ns, &P);
   std::printf("rc %d\n", rc);
   if (rc) return 0;
-  std::printf("G %lld %lld %lld %d\n", (long long)P.d, (long long)P.W, (long long)P.S, P.nblk);
+  std::printf("G %lld %lld %lld %d %d\n", (long long)P.d, (long long)P.W, (long long)P.S,
+              P.nblk, P.nblk_w);
   dump(P.wp, nw);
+  dump(P.wp_s, nw);
   dump(P.sp, ns);
   return 0;
 }
