@@ -299,6 +299,8 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
   const int64_t s_lo = dspan(G.S, G.nblk, blockIdx.x);
   const int64_t s_hi = dspan(G.S, G.nblk, blockIdx.x + 1);
   const float nf = (float)G.n;
+  const bool pow2 = (G.n & (G.n - 1)) == 0;
+  const float inv_n = 1.0f / nf;
   for (int64_t s = s_lo; s < s_hi; ++s) {
     const int64_t lo = s * kSpan;
     const Quads q = quads(lo);
@@ -324,7 +326,7 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
     load8(x, q, G.d, full, xv);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float gb = sum[j] / nf;
+      const float gb = pow2 ? sum[j] * inv_n : sum[j] / nf;  // identical for n = 2^k
       const float mk = C.b1 * mv[j] + C.omb1 * gb;
       const float vk = C.b2 * vv[j] + C.omb2 * (gb * gb);
       mv[j] = mk;
@@ -604,6 +606,8 @@ __global__ __launch_bounds__(kBlock) void k_server_p1(Geo G, const uint8_t* __re
   int64_t ps_hi = sig.phi[ps], pt_hi = tau.phi[pt];
   const int64_t rowbytes = G.W * 8;
   const float nf = (float)G.n;
+  const bool pow2 = (G.n & (G.n - 1)) == 0;
+  const float inv_n = 1.0f / nf;
   double acc[1] = {0.0};
   for (int64_t s = s_lo; s < s_hi; ++s) {
     const int64_t lo = s * kSpan;
@@ -640,8 +644,13 @@ __global__ __launch_bounds__(kBlock) void k_server_p1(Geo G, const uint8_t* __re
           }
         }
       }
+      if (pow2) {  // t * (1/n) is t / n exactly when n is a power of two
 #pragma unroll
-      for (int j = 0; j < 8; ++j) a[j] = t[j] / nf + a[j];
+        for (int j = 0; j < 8; ++j) a[j] = t[j] * inv_n + a[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] = t[j] / nf + a[j];
+      }
       store8(eps, q, G.d, true, a);
     } else {
       // general path (a segment boundary in the span, or the tail): one
