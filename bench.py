@@ -37,16 +37,17 @@ def gbytes(w, schedule="deferred"):
     """Algorithmic HBM bytes per parameter of each kernel of a step: every
     buffer a kernel must touch, once per direction."""
     n, gb = w.n, (2 if w.g_dtype == "f16" else 4)
-    reads = 4 + n * (gb + 4)  # m, g_i, delta_i (or the last c_i)
     if schedule == "deferred":
         return {
-            # m, g_i, last c_i read; c_i and packed bits written
-            "compress_deferred": reads + 4 * n + n / 8,
+            # last server bits read (the momentum), g_i and last c_i read;
+            # c_i and packed bits written
+            "compress_deferred": 1 / 8 + n * (gb + 4) + 4 * n + n / 8,
             # worker bits read, last a read, a written, server bits written
             "server_deferred": n / 8 + 8 + 1 / 8,
-            # server bits read, denom read, x read+written, m written
-            "decompress_update": 1 / 8 + 16,
+            # server bits read, denom read, x read+written (m stays implicit)
+            "decompress_update": 1 / 8 + 12,
         }
+    reads = 4 + n * (gb + 4)  # m, g_i, delta_i
     return {
         # norm pass: m, g_i, delta_i read
         "compress_p1": reads,
@@ -63,9 +64,12 @@ def gbytes(w, schedule="deferred"):
 
 def method_bytes(w):
     """Bytes per parameter if every buffer of the method is touched once per
-    direction per step: n(|g| + 8.25) + 28.25."""
+    direction per step, the momentum being carried by the server message:
+    g_i read, error read and written, worker bits written and read, server
+    error read and written, server bits written and read, denom read, x read
+    and written: n(|g| + 8.25) + 20.25."""
     gb = 2 if w.g_dtype == "f16" else 4
-    return w.n * (gb + 8.25) + 28.25
+    return w.n * (gb + 8.25) + 20.25
 
 
 def source_hash():
@@ -147,6 +151,58 @@ def cpu_baseline(w, torch, synth, d_sample):
                       f"at d={ws.d:,}, n={ws.n}, {ws.g_dtype} gradients: {dt:.2f} s on 1 thread"}
 
 
+def one_gpu_share(w, torch, oba, synth, steps, warmup):
+    """The kernels one GPU of an n-GPU job would run per step, at their real
+    shapes: its own worker's compression over all d coordinates, the server
+    pass over its shard of d/n coordinates (reading the n workers' messages
+    for that shard), and the update over d.  The exchanges between GPUs are
+    not modelled.  The inputs are the workload's gradient recipe; the shard's
+    worker messages are those of n compressions of the same recipe."""
+    d, n = w.d, w.n
+    ds = d // n
+    L1 = oba.Layout(d, 1, synth.whole(d), synth.whole(d))
+    Ls = oba.Layout(ds, n, synth.whole(ds), synth.whole(ds))
+    S1 = oba.State(L1, w.g_dtype)
+    Ss = oba.State(Ls, w.g_dtype)
+    gen = synth.device_generator(w.seed + 2000)
+    wl1 = synth.Workload(w.name, d, 1, w.g_dtype, w.seed, 0, L1.wseg, L1.sseg, w.grad_std)
+    wls = synth.Workload(w.name, ds, n, w.g_dtype, w.seed, 0, Ls.wseg, Ls.sseg, w.grad_std)
+    synth.device_grads(gen, wl1, S1.g)
+    synth.device_grads(gen, wls, Ss.g)
+    S1.x.normal_(0.0, 0.02, generator=gen)
+    S1.denom.uniform_(1e-3, 2e-3, generator=gen)
+    S1.m.normal_(0.0, 1e-3, generator=gen)
+    Ss.denom.fill_(1.0)
+    # the shard's n worker messages (and scales) come from n real compressions
+    Ss.step_deferred(synth.BETA1, synth.LR)
+    S1.step_deferred(synth.BETA1, synth.LR)
+
+    def step():
+        oba.compress_deferred(L1, S1.g, None, S1.delta, S1.wbits, S1.wscale, synth.BETA1,
+                              S1.sbits, S1.sscale)
+        oba.server_reduce_recompress_deferred(Ls, Ss.wbits, Ss.wscale, Ss.eps, Ss.sbits,
+                                              Ss.sscale)
+        oba.decompress_update(L1, S1.sbits, S1.sscale, S1.denom, None, S1.x, synth.LR)
+
+    for _ in range(max(1, warmup)):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    gb = 2 if w.g_dtype == "f16" else 4
+    alg = d * (1 / 8 + (gb + 4) + 4 + 1 / 8) + ds * (n / 8 + 8 + 1 / 8) + d * (1 / 8 + 12)
+    del S1, Ss
+    L1.close()
+    Ls.close()
+    return {"ms_per_step": round(ms, 4), "params_per_s": d / (ms * 1e-3),
+            "alg_bytes": alg, "alg_GBps": round(alg / (ms * 1e-3) / 1e9, 1),
+            "shape": f"1 worker over d={d:,}, 1 server shard of {ds:,} coordinates with "
+                     f"{n} workers' messages, update over d"}
+
+
 def copy_reference(torch, nbytes=1 << 31, reps=5):
     """Device-to-device copy of nbytes (read nbytes + write nbytes), the
     plain streaming kernel that calibrates what HBM delivers on this machine."""
@@ -192,11 +248,14 @@ def main():
     L, S, gsets = make_state(w, torch, oba, synth)
 
     def run(schedule):
-        """W untimed + K timed steps of one schedule from the freeze state."""
-        for t in (S.delta, S.eps, S.wscale, S.sscale):
-            t.zero_()
+        """W untimed + K timed steps of one schedule from the freeze state.
+        The deferred schedule's first step, which reads the warm-up's m
+        instead of the server message, is never timed."""
+        S.start_compression()
         fn = S.step_deferred if schedule == "deferred" else S.step
         log(f"[bench] {schedule}: {args.warmup} untimed steps, {args.steps} timed steps")
+        if schedule == "deferred" and args.warmup == 0:
+            fn(synth.BETA1, synth.LR, g=gsets[1])
         for i in range(args.warmup):
             fn(synth.BETA1, synth.LR, g=gsets[i % 2])
         torch.cuda.synchronize()
@@ -246,7 +305,8 @@ def main():
         "config": {"workload": w.name, "d": w.d, "n_workers": w.n, "grad_dtype": w.g_dtype,
                    "worker_segments": len(w.wseg) - 1, "server_segments": len(w.sseg) - 1,
                    "parallelism": "dp%d simulated on one GPU" % w.n,
-                   "schedule": "deferred-residual state (c, a kept; residuals formed on use)"},
+                   "schedule": "deferred-residual state (c, a kept; residuals formed on use; "
+                               "momentum rebuilt from the server message)"},
         "step_alg_GBps": round(step_alg / (ms * 1e-3) / 1e9, 1),
         "step_alg_bytes_per_param": round(sum(alg.values()), 3),
         "method_bytes_per_param": round(method_bytes(w), 3),
@@ -263,6 +323,10 @@ def main():
         "kernel_source_sha256": source_hash(),
     }
     del S, gsets
+    L.close()
+    torch.cuda.empty_cache()
+    log("[bench] one-GPU share")
+    out["one_gpu_share"] = one_gpu_share(w, torch, oba, synth, args.steps, args.warmup)
     torch.cuda.empty_cache()
     out["copy_reference"] = copy_reference(torch)
     if not args.no_cpu_baseline:

@@ -6,12 +6,13 @@ Python front end and ``synth`` holds the seeded synthetic workloads.
 """
 from .binding import (OBA_F16, OBA_F32, Layout, ObaError, State, adam_warmup_step, compress,
                       compress_deferred, decompress_update, deferred_errors, freeze_variance,
-                      server_reduce_recompress, server_reduce_recompress_deferred,
-                      timing_enable, timing_read, timing_reset, validate)
+                      server_momentum, server_reduce_recompress,
+                      server_reduce_recompress_deferred, timing_enable, timing_read, timing_reset, validate)
 
 __all__ = [
     "OBA_F16", "OBA_F32", "Layout", "ObaError", "State", "adam_warmup_step", "compress",
     "compress_deferred", "decompress_update", "deferred_errors", "freeze_variance",
-    "server_reduce_recompress", "server_reduce_recompress_deferred", "timing_enable",
+    "server_momentum", "server_reduce_recompress", "server_reduce_recompress_deferred",
+    "timing_enable",
     "timing_read", "timing_reset", "validate",
 ]

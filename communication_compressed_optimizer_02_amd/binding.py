@@ -38,7 +38,8 @@ SIGNATURES = {
     "oba_compress": (_I, [_P, _P, _I, _P, _P, _P, _P, _D, _P, _SZ, _P]),
     "oba_server_reduce_recompress": (_I, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "oba_decompress_update": (_I, [_P, _P, _P, _P, _P, _P, _D, _P]),
-    "oba_compress_deferred": (_I, [_P, _P, _I, _P, _P, _P, _P, _D, _P, _SZ, _P]),
+    "oba_server_momentum": (_I, [_P, _P, _P, _P, _P]),
+    "oba_compress_deferred": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _D, _P, _SZ, _P]),
     "oba_server_reduce_recompress_deferred": (_I, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "oba_deferred_errors": (_I, [_P, _P, _P, _P, _P, _P, _P, _P]),
     "oba_timing_enable": (_I, [_I, _I32]),
@@ -199,25 +200,46 @@ def server_reduce_recompress(L: Layout, wbits, wscale, eps, sbits, sscale, strea
 
 
 def decompress_update(L: Layout, sbits, sscale, denom, m, x, lr, stream=None):
+    """m=None: the momentum is not stored (implicit in sbits, sscale)."""
     import torch
 
     f32 = (torch.float32,)
+    mp = _ptr(m, "m", f32, (L.d,)) if m is not None else ctypes.c_void_p(None)
     rc = lib().oba_decompress_update(
         L.handle, _ptr(sbits, "sbits", (torch.int64,), (L.W,)),
         _ptr(sscale, "sscale", f32, (L.n_sseg,)), _ptr(denom, "denom", f32, (L.d,)),
-        _ptr(m, "m", f32, (L.d,)), _ptr(x, "x", f32, (L.d,)), lr, _stream(stream))
+        mp, _ptr(x, "x", f32, (L.d,)), lr, _stream(stream))
     _check(rc, "oba_decompress_update")
 
 
-def compress_deferred(L: Layout, g, m, c, wbits, wscale, beta1, stream=None):
-    """c: last step's compensated vectors in, this step's out; wscale: last
-    step's worker scales in, this step's out."""
+def server_momentum(L: Layout, sbits, sscale, m, stream=None):
+    """m = sbar*sign from the server message."""
     import torch
 
     f32 = (torch.float32,)
+    rc = lib().oba_server_momentum(
+        L.handle, _ptr(sbits, "sbits", (torch.int64,), (L.W,)),
+        _ptr(sscale, "sscale", f32, (L.n_sseg,)), _ptr(m, "m", f32, (L.d,)), _stream(stream))
+    _check(rc, "oba_server_momentum")
+
+
+def compress_deferred(L: Layout, g, m, c, wbits, wscale, beta1, sbits_prev=None,
+                      sscale_prev=None, stream=None):
+    """c: last step's compensated vectors in, this step's out; wscale: last
+    step's worker scales in, this step's out.  The momentum is m, or (m=None)
+    the last server message (sbits_prev, sscale_prev)."""
+    import torch
+
+    f32 = (torch.float32,)
+    P = ctypes.c_void_p
+    mp = _ptr(m, "m", f32, (L.d,)) if m is not None else P(None)
+    bp = (_ptr(sbits_prev, "sbits_prev", (torch.int64,), (L.W,)) if sbits_prev is not None
+          else P(None))
+    sp = (_ptr(sscale_prev, "sscale_prev", f32, (L.n_sseg,)) if sscale_prev is not None
+          else P(None))
     rc = lib().oba_compress_deferred(
         L.handle, _ptr(g, "g", (torch.float32, torch.float16), (L.n, L.ld)), _gdtype(g),
-        _ptr(m, "m", f32, (L.d,)), _ptr(c, "c", f32, (L.n, L.ld)),
+        mp, bp, sp, _ptr(c, "c", f32, (L.n, L.ld)),
         _ptr(wbits, "wbits", (torch.int64,), (L.n, L.W)),
         _ptr(wscale, "wscale", f32, (L.n, L.n_wseg)), beta1,
         ctypes.c_void_p(L.ws.data_ptr()), L.ws_bytes, _stream(stream))
@@ -291,7 +313,22 @@ class State:
         self.sbits = torch.zeros(L.W, dtype=torch.int64, device=dev)
         self.sscale = torch.zeros(L.n_sseg, dtype=f, device=dev)
 
+        # True while m is implicit: the momentum is sbar*sign of (sbits,
+        # sscale) and the buffer m is stale (see oba_compress_deferred)
+        self.m_implicit = False
+
+    def momentum(self):
+        """The momentum every worker holds, written to self.m if implicit."""
+        if self.m_implicit:
+            server_momentum(self.L, self.sbits, self.sscale, self.m)
+        return self.m
+
+    def _explicit_m(self):
+        self.momentum()
+        self.m_implicit = False
+
     def warmup(self, lr, beta1, beta2, eta, bc1=1.0, bc2=1.0, g=None):
+        self._explicit_m()
         adam_warmup_step(self.L, self.g if g is None else g, self.x, self.m, self.v, lr, beta1,
                          beta2, eta, bc1, bc2)
 
@@ -299,6 +336,12 @@ class State:
         """End of the warm-up: denom from v; errors (or, in the deferred
         layout, the stored c, a and the scales) start at zero."""
         freeze_variance(self.L, self.v, self.denom, eta, bc2)
+        self.start_compression()
+
+    def start_compression(self):
+        """State of the first compression step: m explicit, errors (or the
+        stored c, a) and scales zero."""
+        self._explicit_m()
         self.delta.zero_()
         self.eps.zero_()
         self.wscale.zero_()
@@ -306,17 +349,26 @@ class State:
 
     def step(self, beta1, lr, g=None):
         """One compression step: compress -> server -> decompress+update."""
+        self._explicit_m()
         compress(self.L, self.g if g is None else g, self.m, self.delta, self.wbits, self.wscale,
                  beta1)
         server_reduce_recompress(self.L, self.wbits, self.wscale, self.eps, self.sbits,
                                  self.sscale)
         decompress_update(self.L, self.sbits, self.sscale, self.denom, self.m, self.x, lr)
 
-    def step_deferred(self, beta1, lr, g=None):
+    def step_deferred(self, beta1, lr, g=None, implicit_m=True):
         """The same step in the deferred-residual layout: `delta` holds the
-        last c and `eps` the last a (see oba_compress_deferred)."""
-        compress_deferred(self.L, self.g if g is None else g, self.m, self.delta, self.wbits,
-                          self.wscale, beta1)
+        last c and `eps` the last a (see oba_compress_deferred).  With
+        implicit_m the update does not store m and the next step rebuilds it
+        from the server message; momentum() writes it out."""
+        g = self.g if g is None else g
+        if self.m_implicit:
+            compress_deferred(self.L, g, None, self.delta, self.wbits, self.wscale, beta1,
+                              self.sbits, self.sscale)
+        else:
+            compress_deferred(self.L, g, self.m, self.delta, self.wbits, self.wscale, beta1)
         server_reduce_recompress_deferred(self.L, self.wbits, self.wscale, self.eps, self.sbits,
                                           self.sscale)
-        decompress_update(self.L, self.sbits, self.sscale, self.denom, self.m, self.x, lr)
+        decompress_update(self.L, self.sbits, self.sscale, self.denom,
+                          None if implicit_m else self.m, self.x, lr)
+        self.m_implicit = implicit_m

@@ -24,6 +24,7 @@ struct oba_layout_s {
   oba::SegDev sig_w{};  // worker segments, worker grid (compress kernels)
   oba::SegDev sig{};    // worker segments, server grid
   oba::SegDev tau{};    // server segments, server grid
+  oba::SegDev tau_w{};  // server segments, worker grid (implicit momentum)
   oba::Geo geo_w{};     // worker grid
   oba::Geo geo{};       // server grid
   size_t ws_worker = 0, ws_server = 0;
@@ -173,11 +174,12 @@ int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const i
     o32[2] = h32.size();
     h32.insert(h32.end(), pc.seg_first.begin(), pc.seg_first.end());
   };
-  size_t w64[2], w32[3], v64[2], v32[3], s64[2], s32[3];
+  size_t w64[2], w32[3], v64[2], v32[3], s64[2], s32[3], t64[2], t32[3];
   try {
     put(P.wp, P.wseg, w64, w32);
     put(P.wp_s, P.wseg, v64, v32);
     put(P.sp, P.sseg, s64, s32);
+    put(P.sp_w, P.sseg, t64, t32);
   } catch (...) {
     delete L;
     return OBA_ENOMEM;
@@ -215,6 +217,7 @@ int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const i
   L->sig_w = view(w64, w32, (int32_t)P.wseg.size() - 1);
   L->sig = view(v64, v32, (int32_t)P.wseg.size() - 1);
   L->tau = view(s64, s32, (int32_t)P.sseg.size() - 1);
+  L->tau_w = view(t64, t32, (int32_t)P.sseg.size() - 1);
   L->geo_w = oba::Geo{P.d, P.ld, P.W, P.S, P.n, P.nblk_w};
   L->geo = oba::Geo{P.d, P.ld, P.W, P.S, P.n, P.nblk};
   L->ws_worker = std::max(nw_p, P.wp_s.lo.size()) * (size_t)P.n * sizeof(double);
@@ -329,15 +332,24 @@ int oba_server_reduce_recompress(oba_layout L, const uint64_t* wbits, const floa
                 [&] { oba::launch_residual(G, eps, 0, eps, 0, 1, sscale, L->tau, stream); });
 }
 
-int oba_compress_deferred(oba_layout L, const void* g, int g_dtype, const float* m, float* c,
+int oba_compress_deferred(oba_layout L, const void* g, int g_dtype, const float* m,
+                          const uint64_t* sbits_prev, const float* sscale_prev, float* c,
                           uint64_t* wbits, float* wscale, double beta1, void* ws, size_t ws_bytes,
                           hipStream_t stream) {
   OBA_TRY(check_layout(L));
   if (g_dtype != OBA_F32 && g_dtype != OBA_F16) return OBA_EINVAL;
   if (!beta_ok(beta1)) return OBA_EINVAL;
+  const bool implicit_m = !m;
+  if (implicit_m != (sbits_prev != nullptr) || implicit_m != (sscale_prev != nullptr))
+    return OBA_EINVAL;
   if (L->geo.d == 0) return OBA_OK;
   OBA_TRY(check_buf(g, 16));
-  OBA_TRY(check_buf(m, 16));
+  if (implicit_m) {
+    OBA_TRY(check_buf(sbits_prev, 8));
+    OBA_TRY(check_buf(sscale_prev, 4));
+  } else {
+    OBA_TRY(check_buf(m, 16));
+  }
   OBA_TRY(check_buf(c, 16));
   OBA_TRY(check_buf(wbits, 8));
   OBA_TRY(check_buf(wscale, 4));
@@ -347,9 +359,10 @@ int oba_compress_deferred(oba_layout L, const void* g, int g_dtype, const float*
   double* part = static_cast<double*>(ws);
   const float b1 = (float)beta1, omb1 = (float)(1.0 - beta1);
   uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
+  const oba::MomSrc ms{reinterpret_cast<const uint8_t*>(sbits_prev), sscale_prev, L->tau_w};
   OBA_TRY(launch("compress_deferred", stream, [&] {
-    oba::launch_compress_deferred(G, g, g_dtype == OBA_F16, m, c, wbytes, L->sig_w, part, wscale, b1,
-                                  omb1, stream);
+    oba::launch_compress_deferred(G, g, g_dtype == OBA_F16, m, c, wbytes, L->sig_w, part, wscale,
+                                  b1, omb1, ms, stream);
   }));
   return launch("finalize_scales", stream,
                 [&] { oba::launch_finalize(part, G.n, L->sig_w, wscale, stream); });
@@ -416,13 +429,26 @@ int oba_decompress_update(oba_layout L, const uint64_t* sbits, const float* ssca
   OBA_TRY(check_buf(sbits, 8));
   OBA_TRY(check_buf(sscale, 4));
   OBA_TRY(check_buf(denom, 16));
-  OBA_TRY(check_buf(m, 16));
+  if (m) OBA_TRY(check_buf(m, 16));
   OBA_TRY(check_buf(x, 16));
   const oba::Geo G = L->geo;
   const uint8_t* sbytes = reinterpret_cast<const uint8_t*>(sbits);
   return launch("decompress_update", stream, [&] {
     oba::launch_decompress_update(G, sbytes, sscale, denom, m, x, L->tau, (float)lr, stream);
   });
+}
+
+int oba_server_momentum(oba_layout L, const uint64_t* sbits, const float* sscale, float* m,
+                        hipStream_t stream) {
+  OBA_TRY(check_layout(L));
+  if (L->geo.d == 0) return OBA_OK;
+  OBA_TRY(check_buf(sbits, 8));
+  OBA_TRY(check_buf(sscale, 4));
+  OBA_TRY(check_buf(m, 16));
+  const oba::Geo G = L->geo;
+  const uint8_t* sbytes = reinterpret_cast<const uint8_t*>(sbits);
+  return launch("server_momentum", stream,
+                [&] { oba::launch_server_momentum(G, sbytes, sscale, m, L->tau, stream); });
 }
 
 int oba_timing_enable(int on, int32_t capacity) {

@@ -369,7 +369,11 @@ __global__ __launch_bounds__(kBlock) void k_freeze(Geo G, const float* __restric
 //         scale buffer its scales s'; the residual of the last step is formed
 //         where it is consumed, delta_i = c' - s'*sign(c'), then
 //         c = (b1*m + (1-b1)*g_i) + delta_i is stored over c' with its sign
-//         bits and its sum c^2 is reduced -- one pass instead of two.
+//         bits and its sum c^2 is reduced -- one pass instead of two;
+// kDeferredM: as kDeferred, but m is not read: after a compression step
+//         every worker's momentum is the server's m_hat = sbar*sign, so it is
+//         rebuilt from the last packed server bits and scales (1/8 byte
+//         instead of 4 bytes per coordinate).
 // The scale needs the whole segment's norm before any residual can be
 // written, so the explicit layout needs c twice.  Recomputing it reads g, m,
 // delta twice but never writes c: on this HBM, writes cost more than reads,
@@ -379,7 +383,7 @@ __global__ __launch_bounds__(kBlock) void k_freeze(Geo G, const float* __restric
 // [i0, i0 + gridDim.y*NB); larger n takes one launch of full groups and one
 // for the remainder.  Grid: (nblk, groups).
 // ===========================================================================
-enum { kNorm = 1, kApply = 2, kDeferred = 3 };
+enum { kNorm = 1, kApply = 2, kDeferred = 3, kDeferredM = 4 };
 #ifndef OBA_WORKER_BATCH
 #define OBA_WORKER_BATCH 4
 #endif
@@ -392,7 +396,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT
                                                      uint8_t* __restrict__ wbytes, SegDev sig,
                                                      double* __restrict__ part,
                                                      const float* __restrict__ wscale, float b1,
-                                                     float omb1) {
+                                                     float omb1, MomSrc ms) {
   __shared__ double lds[kWaves * NB];
   const int32_t b = blockIdx.x;
   i0 += blockIdx.y * NB;  // this block's workers: [i0, i0 + NB)
@@ -400,6 +404,14 @@ __global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT
   const int32_t p_end = sig.blk_first[b + 1];
   int32_t p = sig.blk_first[b];
   int64_t p_hi = sig.phi[p];
+  // kDeferredM: cursor over the server segments (on this grid) for sbar
+  int32_t pt = 0, pt_end = 0;
+  int64_t pt_hi = 0;
+  if (MODE == kDeferredM) {
+    pt = ms.tau.blk_first[b];
+    pt_end = ms.tau.blk_first[b + 1];
+    pt_hi = ms.tau.phi[pt];
+  }
   const int64_t rowbytes = G.W * 8;
   double acc[NB];
 #pragma unroll
@@ -412,13 +424,34 @@ __global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT
     const bool uniform = hi <= p_hi;  // span inside the current piece
     const bool full = lo + kSpan <= G.d;
     int32_t jseg[8];
-    if ((MODE == kApply || MODE == kDeferred) && !uniform) lane_segs(sig.off, sig.pseg[p], q, G.d, jseg);
+    if (MODE != kNorm && !uniform) lane_segs(sig.off, sig.pseg[p], q, G.d, jseg);
     // every load of the span first (all NB workers), then the arithmetic
     float mv[8];
-    if (full)
+    if (MODE == kDeferredM) {  // m = sbar*sign from the last server message
+      const uint32_t bits = full ? load_sign_bits<true>(ms.sbytes, q, G.d)
+                                 : load_sign_bits<false>(ms.sbytes, q, G.d);
+      float sb[8];
+      if (hi <= pt_hi) {
+        const float s_ = ms.sscale[ms.tau.pseg[pt]];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sb[j] = s_;
+      } else {
+        int32_t jt[8];
+        lane_segs(ms.tau.off, ms.tau.pseg[pt], q, G.d, jt);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sb[j] = ms.sscale[jt[j]];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        mv[j] = (!full && coord(q, j) >= G.d) ? 0.0f : (((bits >> j) & 1u) ? -sb[j] : sb[j]);
+      while (pt < pt_end && pt_hi <= hi) {
+        if (++pt < pt_end) pt_hi = ms.tau.phi[pt];
+      }
+    } else if (full) {
       load_full(m, q, mv);
-    else
+    } else {
       load_tail(m, q, G.d, mv);
+    }
     double fs[NB];
     // workers in batches of NBB: all loads of a batch, then its arithmetic
     // and stores (NBB < NB trades loads in flight per wave for occupancy)
@@ -451,7 +484,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT
         const int64_t row = (int64_t)(i0 + i) * G.ld;
         const float* sc = wscale + (int64_t)(i0 + i) * sig.n_seg;
         float sv[8];
-        if (MODE == kApply || MODE == kDeferred) {
+        if (MODE != kNorm) {
           if (uniform) {
             const float s_ = sc[sig.pseg[p]];
 #pragma unroll
@@ -461,7 +494,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT
             for (int j = 0; j < 8; ++j) sv[j] = sc[jseg[j]];
           }
         }
-        if (MODE == kDeferred) {  // c[u] holds c' of the last step: form its residual
+        if (MODE == kDeferred || MODE == kDeferredM) {  // c[u] holds c' of the last step
 #pragma unroll
           for (int j = 0; j < 8; ++j) c[u][j] = residual(c[u][j], sv[j]);
           if (!full) {  // coordinates past d read as 0 and must stay 0 (no bit, no c^2)
@@ -473,7 +506,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT
 #pragma unroll
         for (int j = 0; j < 8; ++j) c[u][j] = compensate(b1, omb1, mv[j], gv[u][j], c[u][j]);
         if (MODE != kNorm) store_sign_bits(wbytes + (int64_t)(i0 + i) * rowbytes, q, sign_bits(c[u]), rowbytes);
-        if (MODE == kDeferred) store8(delta + row, q, G.d, full, c[u]);
+        if (MODE == kDeferred || MODE == kDeferredM) store8(delta + row, q, G.d, full, c[u]);
         fs[i] = (MODE != kApply) ? sumsq8(c[u]) : 0.0;
         if (MODE == kApply) {
 #pragma unroll
@@ -500,7 +533,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
           const int64_t row = (int64_t)(i0 + i) * G.ld;
-          if (MODE == kDeferred)
+          if (MODE == kDeferred || MODE == kDeferredM)
             acc[i] += sumsq_range(delta + row, q, cur, e);  // c was stored there
           else
             acc[i] += sumsq_range_c(m, g + row, delta + row, b1, omb1, q, cur, e);
@@ -709,9 +742,10 @@ __global__ __launch_bounds__(kBlock) void k_server_p1(Geo G, const uint8_t* __re
 }
 
 // ===========================================================================
-// Decompress + precondition + update: m_hat = sbar*sign; m = m_hat;
-// x = x - (lr*m_hat)/denom.  Grid: nblk.
+// Decompress + precondition + update: m_hat = sbar*sign; m = m_hat (when
+// WRITE_M); x = x - (lr*m_hat)/denom (when UPDATE_X).  Grid: nblk.
 // ===========================================================================
+template <bool WRITE_M, bool UPDATE_X>
 __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
                                                               const uint8_t* __restrict__ sbytes,
                                                               const float* __restrict__ sscale,
@@ -732,8 +766,10 @@ __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
     float sv[8], dv[8], xv[8], mh[8];
     const uint32_t bits = full ? load_sign_bits<true>(sbytes, q, G.d)
                                : load_sign_bits<false>(sbytes, q, G.d);
-    load8(denom, q, G.d, full, dv);
-    load8(x, q, G.d, full, xv);
+    if (UPDATE_X) {
+      load8(denom, q, G.d, full, dv);
+      load8(x, q, G.d, full, xv);
+    }
     if (hi <= p_hi) {
       const float s_ = sscale[tau.pseg[p]];
 #pragma unroll
@@ -747,10 +783,10 @@ __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       mh[j] = ((bits >> j) & 1u) ? -sv[j] : sv[j];
-      xv[j] = xv[j] - (lr * mh[j]) / dv[j];
+      if (UPDATE_X) xv[j] = xv[j] - (lr * mh[j]) / dv[j];
     }
-    store8(m, q, G.d, full, mh);
-    store8(x, q, G.d, full, xv);
+    if (WRITE_M) store8(m, q, G.d, full, mh);
+    if (UPDATE_X) store8(x, q, G.d, full, xv);
     while (p < p_end && p_hi <= hi) {
       if (++p < p_end) p_hi = tau.phi[p];
     }
@@ -783,10 +819,11 @@ void launch_freeze(const Geo& G, const float* v, float* denom, float eta, float 
 template <typename GT, int NB, int MODE>
 static void launch_cmp(const Geo& G, int32_t i0, int groups, const void* g, const float* m,
                        float* delta, uint8_t* wbytes, const SegDev& sig, double* part,
-                       const float* wscale, float b1, float omb1, hipStream_t st) {
+                       const float* wscale, float b1, float omb1, const MomSrc& ms,
+                       hipStream_t st) {
   hipLaunchKernelGGL((k_compress<GT, NB, MODE>), dim3(G.nblk, groups), dim3(kBlock), 0, st, G,
                      i0, static_cast<const GT*>(g), m, delta, wbytes, sig, part, wscale, b1,
-                     omb1);
+                     omb1, ms);
 }
 
 // groups of kMaxNB workers, then one launch for the remainder
@@ -798,49 +835,56 @@ constexpr int kMaxNB = OBA_MAX_NB;
 template <typename GT, int MODE>
 static void launch_cmp_n(const Geo& G, const void* g, const float* m, float* delta,
                          uint8_t* wbytes, const SegDev& sig, double* part, const float* wscale,
-                         float b1, float omb1, hipStream_t st) {
+                         float b1, float omb1, const MomSrc& ms, hipStream_t st) {
   const int full = G.n / kMaxNB, rem = G.n % kMaxNB, i0 = full * kMaxNB;
-  if (full)
-    launch_cmp<GT, kMaxNB, MODE>(G, 0, full, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st);
+#define OBA_CMP(NB_, I0, GROUPS) \
+  launch_cmp<GT, NB_, MODE>(G, I0, GROUPS, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms, st)
+  if (full) OBA_CMP(kMaxNB, 0, full);
   switch (rem) {
-    case 1: launch_cmp<GT, 1, MODE>(G, i0, 1, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st); break;
-    case 2: launch_cmp<GT, 2, MODE>(G, i0, 1, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st); break;
-    case 3: launch_cmp<GT, 3, MODE>(G, i0, 1, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st); break;
-    case 4: launch_cmp<GT, 4, MODE>(G, i0, 1, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st); break;
-    case 5: launch_cmp<GT, 5, MODE>(G, i0, 1, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st); break;
-    case 6: launch_cmp<GT, 6, MODE>(G, i0, 1, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st); break;
-    case 7: launch_cmp<GT, 7, MODE>(G, i0, 1, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st); break;
+    case 1: OBA_CMP(1, i0, 1); break;
+    case 2: OBA_CMP(2, i0, 1); break;
+    case 3: OBA_CMP(3, i0, 1); break;
+    case 4: OBA_CMP(4, i0, 1); break;
+    case 5: OBA_CMP(5, i0, 1); break;
+    case 6: OBA_CMP(6, i0, 1); break;
+    case 7: OBA_CMP(7, i0, 1); break;
     default: break;
   }
+#undef OBA_CMP
 }
 
 template <int MODE>
 static void launch_cmp_t(const Geo& G, const void* g, bool f16, const float* m, float* delta,
                          uint8_t* wbytes, const SegDev& sig, double* part, const float* wscale,
-                         float b1, float omb1, hipStream_t st) {
+                         float b1, float omb1, const MomSrc& ms, hipStream_t st) {
   if (f16)
-    launch_cmp_n<uint16_t, MODE>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st);
+    launch_cmp_n<uint16_t, MODE>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms, st);
   else
-    launch_cmp_n<float, MODE>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, st);
+    launch_cmp_n<float, MODE>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms, st);
 }
 
 void launch_compress_norm(const Geo& G, const void* g, bool f16, const float* m,
                           const float* delta, const SegDev& sig, double* part, float b1,
                           float omb1, hipStream_t st) {
   launch_cmp_t<kNorm>(G, g, f16, m, const_cast<float*>(delta), nullptr, sig, part, nullptr, b1,
-                      omb1, st);
+                      omb1, MomSrc{}, st);
 }
 
 void launch_compress_deferred(const Geo& G, const void* g, bool f16, const float* m, float* c,
                               uint8_t* wbytes, const SegDev& sig, double* part,
-                              const float* wscale_prev, float b1, float omb1, hipStream_t st) {
-  launch_cmp_t<kDeferred>(G, g, f16, m, c, wbytes, sig, part, wscale_prev, b1, omb1, st);
+                              const float* wscale_prev, float b1, float omb1, const MomSrc& ms,
+                              hipStream_t st) {
+  if (ms.sbytes)
+    launch_cmp_t<kDeferredM>(G, g, f16, nullptr, c, wbytes, sig, part, wscale_prev, b1, omb1, ms,
+                             st);
+  else
+    launch_cmp_t<kDeferred>(G, g, f16, m, c, wbytes, sig, part, wscale_prev, b1, omb1, ms, st);
 }
 
 void launch_compress_apply(const Geo& G, const void* g, bool f16, const float* m, float* delta,
                            uint8_t* wbytes, const SegDev& sig, const float* wscale, float b1,
                            float omb1, hipStream_t st) {
-  launch_cmp_t<kApply>(G, g, f16, m, delta, wbytes, sig, nullptr, wscale, b1, omb1, st);
+  launch_cmp_t<kApply>(G, g, f16, m, delta, wbytes, sig, nullptr, wscale, b1, omb1, MomSrc{}, st);
 }
 
 void launch_finalize(const double* part, int32_t rows, const SegDev& T, float* scale,
@@ -890,8 +934,18 @@ void launch_server_deferred(const Geo& G, const uint8_t* wbytes, const float* ws
 void launch_decompress_update(const Geo& G, const uint8_t* sbytes, const float* sscale,
                               const float* denom, float* m, float* x, const SegDev& tau, float lr,
                               hipStream_t st) {
-  hipLaunchKernelGGL(k_decompress_update, dim3(G.nblk), dim3(kBlock), 0, st, G, sbytes, sscale,
-                     denom, m, x, tau, lr);
+  if (m)
+    hipLaunchKernelGGL((k_decompress_update<true, true>), dim3(G.nblk), dim3(kBlock), 0, st, G,
+                       sbytes, sscale, denom, m, x, tau, lr);
+  else
+    hipLaunchKernelGGL((k_decompress_update<false, true>), dim3(G.nblk), dim3(kBlock), 0, st, G,
+                       sbytes, sscale, denom, m, x, tau, lr);
+}
+
+void launch_server_momentum(const Geo& G, const uint8_t* sbytes, const float* sscale, float* m,
+                            const SegDev& tau, hipStream_t st) {
+  hipLaunchKernelGGL((k_decompress_update<true, false>), dim3(G.nblk), dim3(kBlock), 0, st, G,
+                     sbytes, sscale, nullptr, m, nullptr, tau, 0.0f);
 }
 
 }  // namespace oba

@@ -24,6 +24,15 @@ struct SegDev {
   int32_t n_seg;
 };
 
+// Momentum source of the deferred worker pass: null sbytes = read m;
+// otherwise m = sbar*sign from the last packed server bits and scales, with
+// the server segments cut on the worker pass's grid.
+struct MomSrc {
+  const uint8_t* sbytes;
+  const float* sscale;
+  SegDev tau;
+};
+
 struct AdamCoef {
   float lr, b1, omb1, b2, omb2, eta, bc1, bc2;
 };
@@ -47,13 +56,17 @@ void launch_residual(const Geo& G, const float* src, int64_t src_ld, float* dst,
 // and the scale buffers its scales; see kernels.hip.
 void launch_compress_deferred(const Geo& G, const void* g, bool f16, const float* m, float* c,
                               uint8_t* wbytes, const SegDev& sig, double* part,
-                              const float* wscale_prev, float b1, float omb1, hipStream_t st);
+                              const float* wscale_prev, float b1, float omb1, const MomSrc& ms,
+                              hipStream_t st);
 void launch_server_deferred(const Geo& G, const uint8_t* wbytes, const float* wscale, float* a,
                             uint8_t* sbytes, const SegDev& sig, const SegDev& tau, double* part,
                             const float* sscale_prev, hipStream_t st);
 void launch_server_p1(const Geo& G, const uint8_t* wbytes, const float* wscale, float* eps,
                       uint8_t* sbytes, const SegDev& sig, const SegDev& tau, double* part,
                       hipStream_t st);
+// m == nullptr: m is not written (the momentum stays implicit in sbits, sscale)
+void launch_server_momentum(const Geo& G, const uint8_t* sbytes, const float* sscale, float* m,
+                            const SegDev& tau, hipStream_t st);
 void launch_decompress_update(const Geo& G, const uint8_t* sbytes, const float* sscale,
                               const float* denom, float* m, float* x, const SegDev& tau, float lr,
                               hipStream_t st);

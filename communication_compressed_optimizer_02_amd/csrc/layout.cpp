@@ -82,6 +82,7 @@ int make_plan(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_w
     if ((rc = cut(P, P.nblk_w, P.wseg, &P.wp))) return rc;
     if ((rc = cut(P, P.nblk, P.wseg, &P.wp_s))) return rc;
     if ((rc = cut(P, P.nblk, P.sseg, &P.sp))) return rc;
+    if ((rc = cut(P, P.nblk_w, P.sseg, &P.sp_w))) return rc;
     *out = std::move(P);
   } catch (...) {
     return kENoMem;

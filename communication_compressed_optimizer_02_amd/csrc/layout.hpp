@@ -51,6 +51,7 @@ struct Plan {
   Pieces wp;    // worker segments cut on the worker grid (compress kernels)
   Pieces wp_s;  // worker segments cut on the server grid (scale lookups there)
   Pieces sp;    // server segments cut on the server grid
+  Pieces sp_w;  // server segments cut on the worker grid (momentum from sbar*sign)
 };
 
 // Status codes mirror the C ABI (0 ok, negative error).

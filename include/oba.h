@@ -93,9 +93,10 @@ int oba_layout_validate(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, i
                         const int64_t* sseg, int32_t n_sseg);
 
 /* Validates as above, then builds the handle: small device copies of the
- * segment tables and of the per-block piece lists the kernels walk (about
- * 40 bytes per segment plus 80 bytes per thread block of the streaming
- * grid).  Allocates on the current device; the handle must be used on that
+ * segment tables and of the per-block piece lists the kernels walk (four
+ * tables, each about 16 bytes per thread block of its grid plus 20 bytes per
+ * segment; the grids have at most 131072 and 65536 blocks, so about 6 MB at
+ * 336M parameters).  Allocates on the current device; the handle must be used on that
  * device only.  *out is set only on success. */
 int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const int64_t* wseg,
                       int32_t n_wseg, const int64_t* sseg, int32_t n_sseg);
@@ -164,9 +165,18 @@ int oba_server_reduce_recompress(oba_layout layout, const uint64_t* wbits, const
  * models); [AIMech] definition paragraph (x_t = x_{t-1} - gamma V^-1 m_hat).
  * Every worker holds the same momentum afterwards.  Per coordinate:
  *   m_hat = sbar_tau * sign;  m = m_hat;  x = x - (lr*m_hat) / denom
- * sbits: [W]; sscale: [n_sseg]; denom: [d]; m, x: [d] in/out. */
+ * sbits: [W]; sscale: [n_sseg]; denom: [d]; m: [d] out; x: [d] in/out.
+ * m may be NULL: the momentum is then not stored, since it is fully given by
+ * (sbits, sscale) -- the implicit momentum of oba_compress_deferred. */
 int oba_decompress_update(oba_layout layout, const uint64_t* sbits, const float* sscale,
                           const float* denom, float* m, float* x, double lr, hipStream_t stream);
+
+/* m[k] = sbar_tau * sign (the momentum every worker holds after a step,
+ * [Tang] 11), materialised from the server message: for checkpoints,
+ * inspection, or to return to a layout that reads m.  sbits: [W]; sscale:
+ * [n_sseg]; m: [d] out. */
+int oba_server_momentum(oba_layout layout, const uint64_t* sbits, const float* sscale, float* m,
+                        hipStream_t stream);
 
 /* ---- deferred-residual state layout --------------------------------------
  * The same step with a cheaper state: instead of the residuals delta_i and
@@ -182,15 +192,27 @@ int oba_decompress_update(oba_layout layout, const uint64_t* sbits, const float*
  *
  * Start of the compression stage: zero c, a, wscale and sscale (then every
  * residual is 0, as after the freeze).  A step is oba_compress_deferred ->
- * oba_server_reduce_recompress_deferred -> oba_decompress_update (unchanged).
+ * oba_server_reduce_recompress_deferred -> oba_decompress_update.  With the
+ * implicit momentum, the first step reads the warm-up's m and every later
+ * one the last server message, and the update is called with m = NULL;
+ * oba_server_momentum writes m out when it is wanted.
  * oba_deferred_errors writes delta and/or eps out of place (for checkpoints
  * or inspection); it does not change the state. */
 
 /* c: [n][ld] in (last c) / out (this c); wscale: [n][n_wseg] in (last
- * scales) / out (this step's); g, m, wbits, ws as for oba_compress.
+ * scales) / out (this step's); g, wbits, ws as for oba_compress.
  *   delta_i = c_i - s_i*sign(c_i);  c_i = (b1*m + (1-b1)*g_i) + delta_i;
- *   s_{i,sigma} = sqrt(sum c^2 / |sigma|);  bit = (c < 0). */
-int oba_compress_deferred(oba_layout layout, const void* g, int g_dtype, const float* m, float* c,
+ *   s_{i,sigma} = sqrt(sum c^2 / |sigma|);  bit = (c < 0).
+ * The momentum m comes from exactly one source:
+ *   - m != NULL, sbits_prev = sscale_prev = NULL: m is read ([d]); the first
+ *     step after the freeze, whose m is the warm-up's;
+ *   - m == NULL, sbits_prev: [W] and sscale_prev: [n_sseg] the last step's
+ *     server message: m[k] = sscale_prev[tau] * sign, which is what
+ *     oba_decompress_update stored (implicit momentum: 1/8 byte per
+ *     coordinate read instead of 4, and the update need not write m).
+ * Any other combination is OBA_EINVAL. */
+int oba_compress_deferred(oba_layout layout, const void* g, int g_dtype, const float* m,
+                          const uint64_t* sbits_prev, const float* sscale_prev, float* c,
                           uint64_t* wbits, float* wscale, double beta1, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 
@@ -218,7 +240,7 @@ int oba_deferred_errors(oba_layout layout, const float* c, const float* wscale, 
  * equals `kernel` ("compress_p1", "compress_p2", "finalize_scales",
  * "server_p1", "server_p2", "decompress_update", "adam_warmup",
  * "freeze_variance", "compress_deferred", "server_deferred",
- * "deferred_errors").  oba_timing_reset drops all records. */
+ * "deferred_errors", "server_momentum").  oba_timing_reset drops all records. */
 int oba_timing_enable(int on, int32_t capacity);
 int oba_timing_read(const char* kernel, double* total_ms, int64_t* launches);
 int oba_timing_reset(void);

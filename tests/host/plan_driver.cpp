@@ -1,8 +1,9 @@
 // plan_driver.cpp -- test driver for the host-only piece planner.
 // Usage: plan_driver d n ld n_wseg o_0 .. o_nw n_sseg o_0 .. o_ns
 // Prints "rc <status>", then "G d W S nblk nblk_w", then for the worker
-// segments on the worker grid, the worker segments on the server grid and the
-// server segments on the server grid: "T <n_pieces> <n_seg>", one
+// segments on the worker grid, the worker segments on the server grid, the
+// server segments on the server grid and the server segments on the worker
+// grid: "T <n_pieces> <n_seg>", one
 // "P lo hi seg" line per piece, "B" + blk_first, "S" + seg_first.  Built by the test suite with the host compiler and
 // sanitizers; it calls nothing of HIP.
 #include <cstdio>
@@ -41,5 +42,6 @@ int main(int argc, char** argv) {
   dump(P.wp, nw);
   dump(P.wp_s, nw);
   dump(P.sp, ns);
+  dump(P.sp_w, ns);
   return 0;
 }

@@ -83,7 +83,7 @@ def run_plan(exe, d, n, wseg, sseg, ld=None):
     _, dd, W, S, nblk, nblk_w = out[1].split()
     res = dict(d=int(dd), W=int(W), S=int(S), nblk=int(nblk), nblk_w=int(nblk_w), tabs=[])
     i = 2
-    for _ in range(3):
+    for _ in range(4):
         _, npc, nseg = out[i].split()
         i += 1
         pcs = [tuple(map(int, out[i + k].split()[1:])) for k in range(int(npc))]
@@ -98,10 +98,11 @@ def run_plan(exe, d, n, wseg, sseg, ld=None):
 def check_pieces(res, offs):
     """offs: (worker table, server table); tables: worker segments on the
     worker grid, worker segments on the server grid, server segments on the
-    server grid."""
+    server grid, server segments on the worker grid."""
     d, S = res["d"], res["S"]
-    grids = (res["nblk_w"], res["nblk"], res["nblk"])
-    for (pcs, blk, segf), off, nblk in zip(res["tabs"], (offs[0], offs[0], offs[1]), grids):
+    grids = (res["nblk_w"], res["nblk"], res["nblk"], res["nblk_w"])
+    for (pcs, blk, segf), off, nblk in zip(res["tabs"], (offs[0], offs[0], offs[1], offs[1]),
+                                           grids):
         assert len(blk) == nblk + 1 and blk[0] == 0 and blk[-1] == len(pcs)
         # pieces tile [0, d) in order
         pos = 0

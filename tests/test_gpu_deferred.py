@@ -1,5 +1,7 @@
 """GPU tests of the deferred-residual state layout (oba_compress_deferred,
-oba_server_reduce_recompress_deferred, oba_deferred_errors).
+oba_server_reduce_recompress_deferred, oba_deferred_errors) and of the
+implicit momentum (m rebuilt from the last server message,
+oba_server_momentum).
 
 The deferred layout performs the same operations in the same order as the
 explicit one, only at another time, so from the same start both must give
@@ -66,8 +68,9 @@ def test_deferred_layout_is_bitwise_the_explicit_step(d, n, gdt, tab):
         D.step_deferred(B1, LR, g=g)
         oba.deferred_errors(L, D.delta, D.wscale, D.eps, D.sscale, delta, eps)
         torch().cuda.synchronize()
-        for nm in ("wbits", "wscale", "sbits", "sscale", "m", "x"):
+        for nm in ("wbits", "wscale", "sbits", "sscale", "x"):
             same(getattr(E, nm), getattr(D, nm), f"{nm} at step {t}")
+        same(E.m, D.momentum(), f"m at step {t}")
         same(E.delta[:, :d], delta[:, :d], f"delta at step {t}")
         same(E.eps, eps, f"eps at step {t}")
     L.close()
@@ -100,8 +103,66 @@ def test_deferred_layout_free_running_tracks_oracle():
         assert_close(to_host(S.sscale), ss, f"server scales, step {t}")
         assert_close(to_host(delta), st["delta"], f"delta, step {t}")
         assert_close(to_host(eps), st["eps"], f"eps, step {t}")
-        assert_close(to_host(S.m), st["m"], f"m, step {t}")
+        assert_close(to_host(S.momentum()), st["m"], f"m, step {t}")
         assert_close(to_host(S.x), st["x"], f"x, step {t}")
+    L.close()
+
+
+@pytest.mark.parametrize("d,n,tab", [(2049, 3, "cuts"), (5_000_011, 8, "shards"),
+                                     (300, 2, "singletons")])
+def test_implicit_momentum_is_the_stored_momentum(d, n, tab):
+    """A deferred run that stores m and one that rebuilds it from the last
+    server message give the same bits every step; the update leaves m
+    untouched when it is implicit, and oba_server_momentum writes it out."""
+    say(f"[implicit momentum] d={d} n={n} tables={tab}")
+    rng = np.random.default_rng(d + n)
+    if tab == "shards":
+        wseg, sseg = synth.whole(d), synth.even_shards(d, n)
+    elif tab == "singletons":
+        wseg = sseg = np.arange(d + 1, dtype=np.int64)
+    else:
+        wseg, sseg = cut_table(rng, d, 5), cut_table(rng, d, 7)
+    L = oba.Layout(d, n, wseg, sseg)
+    st = synth.host_state(rng, d, n)
+    A, B = two_states(L, "f32", st)
+    for t in range(4):
+        g = to_dev(padded(grads(rng, n, d, "f32"), L.ld))
+        A.step_deferred(B1, LR, g=g, implicit_m=False)
+        before = B.m.clone()
+        B.step_deferred(B1, LR, g=g, implicit_m=True)
+        torch().cuda.synchronize()
+        assert B.m_implicit
+        same(B.m, before, f"m written by the implicit update at step {t}")
+        for nm in ("wbits", "wscale", "sbits", "sscale", "delta", "eps", "x"):
+            same(getattr(A, nm), getattr(B, nm), f"{nm} at step {t}")
+        if t % 2:
+            same(A.m, B.momentum(), f"m at step {t}")
+    L.close()
+
+
+def test_implicit_momentum_rejects_mixed_sources():
+    L = oba.Layout(100, 2, synth.whole(100), synth.even_shards(100, 2))
+    S = oba.State(L)
+    import ctypes
+
+    P = ctypes.c_void_p
+    strm = P(torch().cuda.current_stream().cuda_stream)
+    lib = oba.lib()
+
+    def call(m, sb, ss):
+        return lib.oba_compress_deferred(L.handle, P(S.g.data_ptr()), 0, m, sb, ss,
+                                         P(S.delta.data_ptr()), P(S.wbits.data_ptr()),
+                                         P(S.wscale.data_ptr()), B1, P(L.ws.data_ptr()),
+                                         L.ws_bytes, strm)
+    m, sb, ss = P(S.m.data_ptr()), P(S.sbits.data_ptr()), P(S.sscale.data_ptr())
+    assert call(m, sb, ss) == -1  # two sources
+    assert call(None, None, None) == -1  # none
+    assert call(None, sb, None) == -1
+    assert call(None, None, ss) == -1
+    assert call(m, None, ss) == -1
+    assert call(m, None, None) == 0
+    assert call(None, sb, ss) == 0
+    torch().cuda.synchronize()
     L.close()
 
 
@@ -139,8 +200,9 @@ def test_bert_large_deferred_step_equals_explicit_step_on_device():
         E.step(B1, LR, g=gsets[i])
         D.step_deferred(B1, LR, g=gsets[i])
     torch().cuda.synchronize()
-    for nm in ("wbits", "wscale", "sbits", "sscale", "m", "x"):
+    for nm in ("wbits", "wscale", "sbits", "sscale", "x"):
         assert torch().equal(getattr(E, nm), getattr(D, nm)), nm
+    assert torch().equal(E.m, D.momentum()), "m"
     delta = torch().empty_like(E.delta)
     oba.deferred_errors(L, D.delta, D.wscale, D.eps, D.sscale, delta, None)
     torch().cuda.synchronize()

@@ -60,7 +60,7 @@ def test_quadratic_gpu_and_oracle_run_together():
         torch().cuda.synchronize()
         xg = to_host(S.x)
         assert_close(xg, st["x"], f"x, step {t}")
-        assert_close(to_host(S.m), st["m"], f"m, step {t}")
+        assert_close(to_host(S.momentum()), st["m"], f"m, step {t}")
         exact.append(float(np.mean(xg == st["x"])))
     say(f"  fraction of x bit-exact per step: min {min(exact):.6f}, last {exact[-1]:.6f}")
     L.close()
