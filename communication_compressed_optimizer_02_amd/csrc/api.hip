@@ -24,7 +24,7 @@ struct oba_layout_s {
   oba::SegDev sig_w{};  // worker segments, worker grid (compress kernels)
   oba::SegDev sig{};    // worker segments, server grid
   oba::SegDev tau{};    // server segments, server grid
-  oba::SegDev tau_w{};  // server segments, worker grid (implicit momentum)
+  oba::SegDev tau_w{};  // server segments, worker grid (implicit momentum, update)
   oba::Geo geo_w{};     // worker grid
   oba::Geo geo{};       // server grid
   size_t ws_worker = 0, ws_server = 0;
@@ -158,11 +158,10 @@ int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const i
     return hip_fail(e, "hipGetDevice");
   }
   // one device allocation: int64 arrays first, then int32 arrays
-  const size_t nw_p = P.wp.lo.size(), ns_p = P.sp.lo.size();
   std::vector<int64_t> h64;
   std::vector<int32_t> h32;
   auto put = [&](const oba::Pieces& pc, const std::vector<int64_t>& off, size_t o64[2],
-                 size_t o32[3]) {
+                 size_t o32[5]) {
     o64[0] = h64.size();
     h64.insert(h64.end(), off.begin(), off.end());
     o64[1] = h64.size();
@@ -173,8 +172,12 @@ int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const i
     h32.insert(h32.end(), pc.blk_first.begin(), pc.blk_first.end());
     o32[2] = h32.size();
     h32.insert(h32.end(), pc.seg_first.begin(), pc.seg_first.end());
+    o32[3] = h32.size();
+    h32.insert(h32.end(), pc.item_q.begin(), pc.item_q.end());
+    o32[4] = h32.size();
+    h32.insert(h32.end(), pc.seg_item.begin(), pc.seg_item.end());
   };
-  size_t w64[2], w32[3], v64[2], v32[3], s64[2], s32[3], t64[2], t32[3];
+  size_t w64[2], w32[5], v64[2], v32[5], s64[2], s32[5], t64[2], t32[5];
   try {
     put(P.wp, P.wseg, w64, w32);
     put(P.wp_s, P.wseg, v64, v32);
@@ -204,24 +207,28 @@ int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const i
   }
   const int64_t* d64 = static_cast<const int64_t*>(L->dev_tables);
   const int32_t* d32 = reinterpret_cast<const int32_t*>(static_cast<const char*>(L->dev_tables) + bytes64);
-  auto view = [&](size_t o64[2], size_t o32[3], int32_t n_seg) {
+  auto view = [&](const oba::Pieces& pc, size_t o64[2], size_t o32[5], int32_t n_seg) {
     oba::SegDev s;
     s.off = d64 + o64[0];
     s.phi = d64 + o64[1];
     s.pseg = d32 + o32[0];
     s.blk_first = d32 + o32[1];
     s.seg_first = d32 + o32[2];
+    s.item_q = pc.item_q.empty() ? nullptr : d32 + o32[3];
+    s.seg_item = pc.item_q.empty() ? nullptr : d32 + o32[4];
     s.n_seg = n_seg;
+    s.n_pieces = (int32_t)pc.lo.size();
+    s.n_items = pc.item_q.empty() ? 0 : (int32_t)pc.item_q.size() - 1;
     return s;
   };
-  L->sig_w = view(w64, w32, (int32_t)P.wseg.size() - 1);
-  L->sig = view(v64, v32, (int32_t)P.wseg.size() - 1);
-  L->tau = view(s64, s32, (int32_t)P.sseg.size() - 1);
-  L->tau_w = view(t64, t32, (int32_t)P.sseg.size() - 1);
+  L->sig_w = view(P.wp, w64, w32, (int32_t)P.wseg.size() - 1);
+  L->sig = view(P.wp_s, v64, v32, (int32_t)P.wseg.size() - 1);
+  L->tau = view(P.sp, s64, s32, (int32_t)P.sseg.size() - 1);
+  L->tau_w = view(P.sp_w, t64, t32, (int32_t)P.sseg.size() - 1);
   L->geo_w = oba::Geo{P.d, P.ld, P.W, P.S, P.n, P.nblk_w};
   L->geo = oba::Geo{P.d, P.ld, P.W, P.S, P.n, P.nblk};
-  L->ws_worker = std::max(nw_p, P.wp_s.lo.size()) * (size_t)P.n * sizeof(double);
-  L->ws_server = ns_p * sizeof(double);
+  L->ws_worker = std::max(oba::partial_bytes(L->sig_w, P.n), oba::partial_bytes(L->sig, P.n));
+  L->ws_server = oba::partial_bytes(L->tau, 1);
   *out = L;
   return OBA_OK;
 }
@@ -431,10 +438,11 @@ int oba_decompress_update(oba_layout L, const uint64_t* sbits, const float* ssca
   OBA_TRY(check_buf(denom, 16));
   if (m) OBA_TRY(check_buf(m, 16));
   OBA_TRY(check_buf(x, 16));
-  const oba::Geo G = L->geo;
+  // one span per block (the worker grid): the update streams best that way
+  const oba::Geo G = L->geo_w;
   const uint8_t* sbytes = reinterpret_cast<const uint8_t*>(sbits);
   return launch("decompress_update", stream, [&] {
-    oba::launch_decompress_update(G, sbytes, sscale, denom, m, x, L->tau, (float)lr, stream);
+    oba::launch_decompress_update(G, sbytes, sscale, denom, m, x, L->tau_w, (float)lr, stream);
   });
 }
 
@@ -445,10 +453,10 @@ int oba_server_momentum(oba_layout L, const uint64_t* sbits, const float* sscale
   OBA_TRY(check_buf(sbits, 8));
   OBA_TRY(check_buf(sscale, 4));
   OBA_TRY(check_buf(m, 16));
-  const oba::Geo G = L->geo;
+  const oba::Geo G = L->geo_w;
   const uint8_t* sbytes = reinterpret_cast<const uint8_t*>(sbits);
   return launch("server_momentum", stream,
-                [&] { oba::launch_server_momentum(G, sbytes, sscale, m, L->tau, stream); });
+                [&] { oba::launch_server_momentum(G, sbytes, sscale, m, L->tau_w, stream); });
 }
 
 int oba_timing_enable(int on, int32_t capacity) {

@@ -160,20 +160,26 @@ __device__ __forceinline__ void store_sign_bits(uint8_t* __restrict__ row, const
 
 // The lane's 8 sign bits from a packed row.  FULL: both quads lie inside
 // [0, d) (no checks).  Otherwise bytes whose coordinates all lie at or past d
-// read as 0.  With OBA_SIGN_PAIRS each lane loads the two bytes holding its
-// quads; otherwise the even lane loads the A-half byte of the pair, the odd
-// lane the B-half byte (one distinct byte per lane), and they swap -- every
-// lane of the wave must then call this (cross-lane exchange).
-#ifndef OBA_SIGN_PAIRS
-#define OBA_SIGN_PAIRS 0
+// read as 0.  PAIRS: each lane loads the two bytes holding its quads (no
+// cross-lane step, so the bits are not needed until used).  Otherwise the
+// even lane loads the A-half byte of the pair, the odd lane the B-half byte
+// (one distinct byte per lane), and they swap -- every lane of the wave must
+// then call this (cross-lane exchange).  The worker and update passes load
+// one row per span and take pairs; the server pass loads n rows and takes the
+// exchange (half the load instructions).
+#ifndef OBA_PAIRS_CMP
+#define OBA_PAIRS_CMP 1
 #endif
-template <bool FULL>
+#ifndef OBA_PAIRS_UPD
+#define OBA_PAIRS_UPD 1
+#endif
+template <bool FULL, bool PAIRS>
 __device__ __forceinline__ uint32_t load_sign_bits(const uint8_t* __restrict__ row,
                                                    const Quads& q, int64_t d) {
   const bool odd = threadIdx.x & 1;
   const uint32_t sh = odd ? 4u : 0u;
   uint32_t byte_a, byte_b;
-  if constexpr (OBA_SIGN_PAIRS) {
+  if constexpr (PAIRS) {
     byte_a = (FULL || q.kA < d) ? (uint32_t)row[q.kA >> 3] : 0u;
     byte_b = (FULL || q.kB < d) ? (uint32_t)row[q.kB >> 3] : 0u;
   } else {
@@ -389,8 +395,15 @@ enum { kNorm = 1, kApply = 2, kDeferred = 3, kDeferredM = 4 };
 #endif
 constexpr int kWorkerBatch = OBA_WORKER_BATCH;
 
+// Optional occupancy target of the worker pass (waves per SIMD), a tuning knob.
+#ifdef OBA_CMP_WAVES
+#define OBA_CMP_ATTR __attribute__((amdgpu_waves_per_eu(OBA_CMP_WAVES, OBA_CMP_WAVES)))
+#else
+#define OBA_CMP_ATTR
+#endif
+
 template <typename GT, int NB, int MODE>
-__global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT* __restrict__ g,
+__global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t i0, const GT* __restrict__ g,
                                                      const float* __restrict__ m,
                                                      float* __restrict__ delta,
                                                      uint8_t* __restrict__ wbytes, SegDev sig,
@@ -428,8 +441,8 @@ __global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT
     // every load of the span first (all NB workers), then the arithmetic
     float mv[8];
     if (MODE == kDeferredM) {  // m = sbar*sign from the last server message
-      const uint32_t bits = full ? load_sign_bits<true>(ms.sbytes, q, G.d)
-                                 : load_sign_bits<false>(ms.sbytes, q, G.d);
+      const uint32_t bits = full ? load_sign_bits<true, OBA_PAIRS_CMP>(ms.sbytes, q, G.d)
+                                 : load_sign_bits<false, OBA_PAIRS_CMP>(ms.sbytes, q, G.d);
       float sb[8];
       if (hi <= pt_hi) {
         const float s_ = ms.sscale[ms.tau.pseg[pt]];
@@ -549,17 +562,21 @@ __global__ __launch_bounds__(kBlock) void k_compress(Geo G, int32_t i0, const GT
 }
 
 // ===========================================================================
-// Per-segment scale from the piece partials: s = sqrt(S / len) in binary64,
-// rounded once to binary32.  Grid: (n_seg, rows).  part: [n_pieces][rows].
+// Per-segment scale from the binary64 partials: s = sqrt(S / len) in
+// binary64, rounded once to binary32.  part: [n_parts][rows]; the parts of
+// segment j are [first[j], first[j+1]) (pieces, or items of the two-stage
+// sum).  Grid: (n_seg, rows).
 // ===========================================================================
-constexpr int kFinBlock = 1024;  // 16 waves: segments can have 65536 pieces
+constexpr int kFinBlock = 1024;  // 16 waves: at most 8192 parts per segment
 
 __global__ __launch_bounds__(kFinBlock) void k_finalize_scales(const double* __restrict__ part,
-                                                               int32_t rows, SegDev T,
+                                                               int32_t rows,
+                                                               const int32_t* __restrict__ first,
+                                                               SegDev T,
                                                                float* __restrict__ scale) {
   __shared__ double lds[kFinBlock / 64];
   const int32_t j = blockIdx.x, r = blockIdx.y;
-  const int32_t q0 = T.seg_first[j], q1 = T.seg_first[j + 1];
+  const int32_t q0 = first[j], q1 = first[j + 1];
   double t = 0.0;
   for (int32_t q = q0 + threadIdx.x; q < q1; q += kFinBlock) t += part[(int64_t)q * rows + r];
   t = wave_sum(t);
@@ -570,6 +587,29 @@ __global__ __launch_bounds__(kFinBlock) void k_finalize_scales(const double* __r
     for (int w = 0; w < kFinBlock / 64; ++w) S += lds[w];  // fixed order
     const double len = (double)(T.off[j + 1] - T.off[j]);
     scale[(int64_t)r * T.n_seg + j] = (float)__builtin_sqrt(S / len);
+  }
+}
+
+// First stage of a two-stage sum: item it (at most kItem consecutive pieces
+// of one segment) of row r.  Grid: (n_items, rows).  out: [n_items][rows].
+constexpr int kItemBlock = 256;
+
+__global__ __launch_bounds__(kItemBlock) void k_sum_items(const double* __restrict__ part,
+                                                          int32_t rows,
+                                                          const int32_t* __restrict__ item_q,
+                                                          double* __restrict__ out) {
+  __shared__ double lds[kItemBlock / 64];
+  const int32_t it = blockIdx.x, r = blockIdx.y;
+  const int32_t q0 = item_q[it], q1 = item_q[it + 1];
+  double t = 0.0;
+  for (int32_t q = q0 + threadIdx.x; q < q1; q += kItemBlock) t += part[(int64_t)q * rows + r];
+  t = wave_sum(t);
+  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = t;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double S = 0.0;
+    for (int w = 0; w < kItemBlock / 64; ++w) S += lds[w];  // fixed order
+    out[(int64_t)it * rows + r] = S;
   }
 }
 
@@ -666,7 +706,7 @@ __global__ __launch_bounds__(kBlock) void k_server_p1(Geo G, const uint8_t* __re
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
           const int64_t r = min(i0 + u, G.n - 1);
-          bits[u] = load_sign_bits<true>(wbytes + r * rowbytes, q, G.d);
+          bits[u] = load_sign_bits<true, false>(wbytes + r * rowbytes, q, G.d);
           sw[u] = wscale[r * sig.n_seg + js0];
         }
 #pragma unroll
@@ -743,7 +783,7 @@ __global__ __launch_bounds__(kBlock) void k_server_p1(Geo G, const uint8_t* __re
 
 // ===========================================================================
 // Decompress + precondition + update: m_hat = sbar*sign; m = m_hat (when
-// WRITE_M); x = x - (lr*m_hat)/denom (when UPDATE_X).  Grid: nblk.
+// WRITE_M); x = x - (lr*m_hat)/denom (when UPDATE_X).  Grid: the worker grid.
 // ===========================================================================
 template <bool WRITE_M, bool UPDATE_X>
 __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
@@ -764,8 +804,8 @@ __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
     const Quads q = quads(lo);
     const bool full = lo + kSpan <= G.d;
     float sv[8], dv[8], xv[8], mh[8];
-    const uint32_t bits = full ? load_sign_bits<true>(sbytes, q, G.d)
-                               : load_sign_bits<false>(sbytes, q, G.d);
+    const uint32_t bits = full ? load_sign_bits<true, OBA_PAIRS_UPD>(sbytes, q, G.d)
+                               : load_sign_bits<false, OBA_PAIRS_UPD>(sbytes, q, G.d);
     if (UPDATE_X) {
       load8(denom, q, G.d, full, dv);
       load8(x, q, G.d, full, xv);
@@ -826,20 +866,30 @@ static void launch_cmp(const Geo& G, int32_t i0, int groups, const void* g, cons
                      omb1, ms);
 }
 
-// groups of kMaxNB workers, then one launch for the remainder
+// Groups of GROUP workers per block, then one launch for the remainder.  A
+// pass that reads m shares it across the block's workers (4 bytes per
+// coordinate per group); the implicit momentum costs 1/8 byte per group, so
+// that pass can take smaller groups (fewer registers, more blocks).
 #ifndef OBA_MAX_NB
 #define OBA_MAX_NB 8
 #endif
+#ifndef OBA_IMPLICIT_NB
+#define OBA_IMPLICIT_NB 4
+#endif
 constexpr int kMaxNB = OBA_MAX_NB;
+constexpr int kImplicitNB = OBA_IMPLICIT_NB;
+static_assert(kMaxNB >= 1 && kMaxNB <= 8 && kImplicitNB >= 1 && kImplicitNB <= 8,
+              "worker groups hold 1 to 8 workers");
 
 template <typename GT, int MODE>
 static void launch_cmp_n(const Geo& G, const void* g, const float* m, float* delta,
                          uint8_t* wbytes, const SegDev& sig, double* part, const float* wscale,
                          float b1, float omb1, const MomSrc& ms, hipStream_t st) {
-  const int full = G.n / kMaxNB, rem = G.n % kMaxNB, i0 = full * kMaxNB;
+  constexpr int GROUP = MODE == kDeferredM ? kImplicitNB : kMaxNB;
+  const int full = G.n / GROUP, rem = G.n % GROUP, i0 = full * GROUP;
 #define OBA_CMP(NB_, I0, GROUPS) \
   launch_cmp<GT, NB_, MODE>(G, I0, GROUPS, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms, st)
-  if (full) OBA_CMP(kMaxNB, 0, full);
+  if (full) OBA_CMP(GROUP, 0, full);
   switch (rem) {
     case 1: OBA_CMP(1, i0, 1); break;
     case 2: OBA_CMP(2, i0, 1); break;
@@ -887,10 +937,18 @@ void launch_compress_apply(const Geo& G, const void* g, bool f16, const float* m
   launch_cmp_t<kApply>(G, g, f16, m, delta, wbytes, sig, nullptr, wscale, b1, omb1, MomSrc{}, st);
 }
 
-void launch_finalize(const double* part, int32_t rows, const SegDev& T, float* scale,
+void launch_finalize(double* part, int32_t rows, const SegDev& T, float* scale,
                      hipStream_t st) {
-  hipLaunchKernelGGL(k_finalize_scales, dim3(T.n_seg, rows), dim3(kFinBlock), 0, st, part, rows,
-                     T, scale);
+  if (T.n_items == 0) {
+    hipLaunchKernelGGL(k_finalize_scales, dim3(T.n_seg, rows), dim3(kFinBlock), 0, st, part,
+                       rows, T.seg_first, T, scale);
+    return;
+  }
+  double* items = part + ((size_t)T.n_pieces * rows * 8 + 255) / 256 * 32;
+  hipLaunchKernelGGL(k_sum_items, dim3(T.n_items, rows), dim3(kItemBlock), 0, st, part, rows,
+                     T.item_q, items);
+  hipLaunchKernelGGL(k_finalize_scales, dim3(T.n_seg, rows), dim3(kFinBlock), 0, st, items, rows,
+                     T.seg_item, T, scale);
 }
 
 void launch_residual(const Geo& G, const float* src, int64_t src_ld, float* dst, int64_t dst_ld,

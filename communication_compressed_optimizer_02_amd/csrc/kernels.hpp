@@ -21,8 +21,19 @@ struct SegDev {
   const int32_t* pseg;       // [n_pieces] piece segment
   const int32_t* blk_first;  // [nblk+1]
   const int32_t* seg_first;  // [n_seg+1]
+  const int32_t* item_q;     // [n_items+1] (two-stage sums only)
+  const int32_t* seg_item;   // [n_seg+1] (two-stage sums only)
   int32_t n_seg;
+  int32_t n_pieces;
+  int32_t n_items;           // 0: one-stage sums
 };
+
+// Bytes of binary64 partials for table T with `rows` rows: pieces, then
+// (two-stage) items, each part 256-byte aligned.
+inline size_t partial_bytes(const SegDev& T, int32_t rows) {
+  auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+  return al((size_t)T.n_pieces * rows * 8) + al((size_t)T.n_items * rows * 8);
+}
 
 // Momentum source of the deferred worker pass: null sbytes = read m;
 // otherwise m = sbar*sign from the last packed server bits and scales, with
@@ -48,7 +59,7 @@ void launch_compress_norm(const Geo& G, const void* g, bool f16, const float* m,
 void launch_compress_apply(const Geo& G, const void* g, bool f16, const float* m, float* delta,
                            uint8_t* wbytes, const SegDev& sig, const float* wscale, float b1,
                            float omb1, hipStream_t st);
-void launch_finalize(const double* part, int32_t rows, const SegDev& T, float* scale,
+void launch_finalize(double* part, int32_t rows, const SegDev& T, float* scale,
                      hipStream_t st);
 void launch_residual(const Geo& G, const float* src, int64_t src_ld, float* dst, int64_t dst_ld,
                      int32_t rows, const float* scale, const SegDev& T, hipStream_t st);

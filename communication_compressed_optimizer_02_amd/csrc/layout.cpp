@@ -49,6 +49,21 @@ int cut(const Plan& P, int32_t nblk, const std::vector<int64_t>& off, Pieces* ou
     out->seg_first[s] = q;
   }
   out->seg_first[n_seg] = (int32_t)out->lo.size();
+  out->item_q.clear();
+  out->seg_item.clear();
+  int32_t most = 0;
+  for (int32_t s = 0; s < n_seg; ++s)
+    most = std::max(most, out->seg_first[s + 1] - out->seg_first[s]);
+  if (most > kSplitAbove) {
+    out->seg_item.assign((size_t)n_seg + 1, 0);
+    for (int32_t s = 0; s < n_seg; ++s) {
+      out->seg_item[s] = (int32_t)out->item_q.size();
+      for (int32_t q = out->seg_first[s]; q < out->seg_first[s + 1]; q += kItem)
+        out->item_q.push_back(q);
+    }
+    out->seg_item[n_seg] = (int32_t)out->item_q.size();
+    out->item_q.push_back((int32_t)out->lo.size());
+  }
   return kOk;
 }
 

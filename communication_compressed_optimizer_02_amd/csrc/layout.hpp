@@ -26,32 +26,41 @@ constexpr int64_t kSpan = kBlock * kVec;    // coordinates per block pass
 #define OBA_MAX_BLOCKS 65536
 #endif
 #ifndef OBA_MAX_BLOCKS_WORKER
-#define OBA_MAX_BLOCKS_WORKER 131072
+#define OBA_MAX_BLOCKS_WORKER 262144
 #endif
-// Caps on blocks of the streaming grids: the worker-side kernels (many
-// streams, much work per span) run best with about one span per block, the
-// server and update kernels (little work per span) with a few spans each.
+// Caps on blocks of the streaming grids: the worker-side kernels and the
+// update run best with one span per block, the server pass (n packed rows
+// per span) with a few spans per block.
 constexpr int kMaxBlocks = OBA_MAX_BLOCKS;
 constexpr int kMaxBlocksWorker = OBA_MAX_BLOCKS_WORKER;
 constexpr int32_t kMaxWorkers = 4096;
+
+// A segment cut into more than kSplitAbove pieces has its partials summed in
+// two stages: runs of at most kItem consecutive pieces ("items") first, in
+// parallel, then the items of each segment.  Both orders are fixed.
+constexpr int32_t kItem = 2048;
+constexpr int32_t kSplitAbove = 8192;
 
 struct Pieces {
   std::vector<int64_t> lo, hi;      // piece [lo, hi)
   std::vector<int32_t> seg;         // segment of the piece
   std::vector<int32_t> blk_first;   // [nblk+1] first piece of each block
   std::vector<int32_t> seg_first;   // [n_seg+1] first piece of each segment
+  // empty unless some segment has more than kSplitAbove pieces:
+  std::vector<int32_t> item_q;      // [n_items+1] first piece of each item
+  std::vector<int32_t> seg_item;    // [n_seg+1] first item of each segment
 };
 
 struct Plan {
   int64_t d = 0, ld = 0, W = 0, S = 0;
   int32_t n = 0;
-  int32_t nblk = 0;    // grid of the server, update, residual, warm-up kernels
-  int32_t nblk_w = 0;  // grid of the worker-side compress kernels
+  int32_t nblk = 0;    // grid of the server, residual, warm-up, freeze, norm kernels
+  int32_t nblk_w = 0;  // grid of the worker-side compress kernels and the update
   std::vector<int64_t> wseg, sseg;  // offsets, n_seg+1 each
   Pieces wp;    // worker segments cut on the worker grid (compress kernels)
   Pieces wp_s;  // worker segments cut on the server grid (scale lookups there)
   Pieces sp;    // server segments cut on the server grid
-  Pieces sp_w;  // server segments cut on the worker grid (momentum from sbar*sign)
+  Pieces sp_w;  // server segments cut on the worker grid (update, implicit momentum)
 };
 
 // Status codes mirror the C ABI (0 ok, negative error).

@@ -4,7 +4,8 @@
 // segments on the worker grid, the worker segments on the server grid, the
 // server segments on the server grid and the server segments on the worker
 // grid: "T <n_pieces> <n_seg>", one
-// "P lo hi seg" line per piece, "B" + blk_first, "S" + seg_first.  Built by the test suite with the host compiler and
+// "P lo hi seg" line per piece, "B" + blk_first, "S" + seg_first, "I" +
+// item_q, "J" + seg_item (the last two empty for one-stage sums).  Built by the test suite with the host compiler and
 // sanitizers; it calls nothing of HIP.
 #include <cstdio>
 #include <cstdlib>
@@ -20,6 +21,10 @@ static void dump(const oba::Pieces& p, int n_seg) {
   for (int v : p.blk_first) std::printf(" %d", v);
   std::printf("\nS");
   for (int v : p.seg_first) std::printf(" %d", v);
+  std::printf("\nI");
+  for (int v : p.item_q) std::printf(" %d", v);
+  std::printf("\nJ");
+  for (int v : p.seg_item) std::printf(" %d", v);
   std::printf("\n");
 }
 
