@@ -173,23 +173,34 @@ __device__ __forceinline__ void store_sign_bits(uint8_t* __restrict__ row, const
 #ifndef OBA_PAIRS_UPD
 #define OBA_PAIRS_UPD 1
 #endif
+// The exchange form in two halves: this lane's byte (a load only) ...
+template <bool FULL>
+__device__ __forceinline__ uint32_t sign_byte(const uint8_t* __restrict__ row, const Quads& q,
+                                              int64_t d) {
+  const int64_t qi = ((threadIdx.x & 1) ? q.kB : q.kA) >> 3;
+  return (FULL || qi * 8 < d) ? (uint32_t)row[qi] : 0u;
+}
+
+// ... and the swap with the neighbour lane that yields the 8 bits.
+__device__ __forceinline__ uint32_t sign_bits_of(uint32_t mine) {
+  const bool odd = threadIdx.x & 1;
+  const uint32_t sh = odd ? 4u : 0u;
+  const uint32_t other = (uint32_t)__shfl_xor((int)mine, 1, 64);
+  const uint32_t byte_a = odd ? other : mine, byte_b = odd ? mine : other;
+  return ((byte_a >> sh) & 0xFu) | (((byte_b >> sh) & 0xFu) << 4);
+}
+
 template <bool FULL, bool PAIRS>
 __device__ __forceinline__ uint32_t load_sign_bits(const uint8_t* __restrict__ row,
                                                    const Quads& q, int64_t d) {
-  const bool odd = threadIdx.x & 1;
-  const uint32_t sh = odd ? 4u : 0u;
-  uint32_t byte_a, byte_b;
   if constexpr (PAIRS) {
-    byte_a = (FULL || q.kA < d) ? (uint32_t)row[q.kA >> 3] : 0u;
-    byte_b = (FULL || q.kB < d) ? (uint32_t)row[q.kB >> 3] : 0u;
+    const uint32_t sh = (threadIdx.x & 1) ? 4u : 0u;
+    const uint32_t byte_a = (FULL || q.kA < d) ? (uint32_t)row[q.kA >> 3] : 0u;
+    const uint32_t byte_b = (FULL || q.kB < d) ? (uint32_t)row[q.kB >> 3] : 0u;
+    return ((byte_a >> sh) & 0xFu) | (((byte_b >> sh) & 0xFu) << 4);
   } else {
-    const int64_t qi = (odd ? q.kB : q.kA) >> 3;
-    const uint32_t mine = (FULL || qi * 8 < d) ? (uint32_t)row[qi] : 0u;
-    const uint32_t other = (uint32_t)__shfl_xor((int)mine, 1, 64);
-    byte_a = odd ? other : mine;
-    byte_b = odd ? mine : other;
+    return sign_bits_of(sign_byte<FULL>(row, q, d));
   }
-  return ((byte_a >> sh) & 0xFu) | (((byte_b >> sh) & 0xFu) << 4);
 }
 
 __device__ __forceinline__ double sumsq8(const float (&c)[8]) {
@@ -208,10 +219,11 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;  // every lane holds the same value (commutative butterfly)
 }
 
-// Block-reduce acc[0..nw) and write dst[0..nw); resets acc.  Uniform call.
+// Block-reduce acc[0..nw) and write dst[i*stride], i < nw; resets acc.
+// Uniform call.
 template <int NB>
 __device__ __forceinline__ void flush_rows(double (&acc)[NB], int nw, double* __restrict__ dst,
-                                           double* lds) {
+                                           int64_t stride, double* lds) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
@@ -227,7 +239,7 @@ __device__ __forceinline__ void flush_rows(double (&acc)[NB], int nw, double* __
     double t = lds[i];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) t += lds[w * NB + i];  // fixed order
-    dst[i] = t;
+    dst[i * stride] = t;
   }
   __syncthreads();
 }
@@ -536,7 +548,7 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
 #pragma unroll
       for (int i = 0; i < NB; ++i) acc[i] += fs[i];
       if (hi == p_hi) {
-        flush_rows<NB>(acc, NB, part + (int64_t)p * G.n + i0, lds);
+        flush_rows<NB>(acc, NB, part + (int64_t)i0 * sig.n_pieces + p, sig.n_pieces, lds);
         if (++p < p_end) p_hi = sig.phi[p];
       }
     } else {  // span crosses piece boundaries: sum this lane's c piece by piece
@@ -552,7 +564,7 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
             acc[i] += sumsq_range_c(m, g + row, delta + row, b1, omb1, q, cur, e);
         }
         if (p_hi <= hi) {
-          flush_rows<NB>(acc, NB, part + (int64_t)p * G.n + i0, lds);
+          flush_rows<NB>(acc, NB, part + (int64_t)i0 * sig.n_pieces + p, sig.n_pieces, lds);
           if (++p < p_end) p_hi = sig.phi[p];
         }
         cur = e;
@@ -563,22 +575,23 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
 
 // ===========================================================================
 // Per-segment scale from the binary64 partials: s = sqrt(S / len) in
-// binary64, rounded once to binary32.  part: [n_parts][rows]; the parts of
+// binary64, rounded once to binary32.  part: [rows][n_parts]; the parts of
 // segment j are [first[j], first[j+1]) (pieces, or items of the two-stage
 // sum).  Grid: (n_seg, rows).
 // ===========================================================================
 constexpr int kFinBlock = 1024;  // 16 waves: at most 8192 parts per segment
 
 __global__ __launch_bounds__(kFinBlock) void k_finalize_scales(const double* __restrict__ part,
-                                                               int32_t rows,
+                                                               int32_t n_parts,
                                                                const int32_t* __restrict__ first,
                                                                SegDev T,
                                                                float* __restrict__ scale) {
   __shared__ double lds[kFinBlock / 64];
   const int32_t j = blockIdx.x, r = blockIdx.y;
+  const double* row = part + (int64_t)r * n_parts;
   const int32_t q0 = first[j], q1 = first[j + 1];
   double t = 0.0;
-  for (int32_t q = q0 + threadIdx.x; q < q1; q += kFinBlock) t += part[(int64_t)q * rows + r];
+  for (int32_t q = q0 + threadIdx.x; q < q1; q += kFinBlock) t += row[q];
   t = wave_sum(t);
   if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = t;
   __syncthreads();
@@ -591,25 +604,28 @@ __global__ __launch_bounds__(kFinBlock) void k_finalize_scales(const double* __r
 }
 
 // First stage of a two-stage sum: item it (at most kItem consecutive pieces
-// of one segment) of row r.  Grid: (n_items, rows).  out: [n_items][rows].
+// of one segment) of row r.  Grid: (n_items, rows).  part: [rows][n_pieces];
+// out: [rows][n_items].
 constexpr int kItemBlock = 256;
 
 __global__ __launch_bounds__(kItemBlock) void k_sum_items(const double* __restrict__ part,
-                                                          int32_t rows,
+                                                          int32_t n_pieces,
                                                           const int32_t* __restrict__ item_q,
+                                                          int32_t n_items,
                                                           double* __restrict__ out) {
   __shared__ double lds[kItemBlock / 64];
   const int32_t it = blockIdx.x, r = blockIdx.y;
+  const double* row = part + (int64_t)r * n_pieces;
   const int32_t q0 = item_q[it], q1 = item_q[it + 1];
   double t = 0.0;
-  for (int32_t q = q0 + threadIdx.x; q < q1; q += kItemBlock) t += part[(int64_t)q * rows + r];
+  for (int32_t q = q0 + threadIdx.x; q < q1; q += kItemBlock) t += row[q];
   t = wave_sum(t);
   if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = t;
   __syncthreads();
   if (threadIdx.x == 0) {
     double S = 0.0;
     for (int w = 0; w < kItemBlock / 64; ++w) S += lds[w];  // fixed order
-    out[(int64_t)it * rows + r] = S;
+    out[(int64_t)r * n_items + it] = S;
   }
 }
 
@@ -664,8 +680,15 @@ __global__ __launch_bounds__(kBlock) void k_residual(Geo G, const float* src, in
 // sscale_prev its server scales; the server error is formed where it is
 // consumed, eps = a' - s'*sign(a'), and a is stored over a'.  Grid: nblk.
 // ===========================================================================
+// Optional occupancy target of the server pass (waves per SIMD), a tuning knob.
+#ifdef OBA_SRV_WAVES
+#define OBA_SRV_ATTR __attribute__((amdgpu_waves_per_eu(OBA_SRV_WAVES, OBA_SRV_WAVES)))
+#else
+#define OBA_SRV_ATTR
+#endif
+
 template <int NB, bool DEFERRED>
-__global__ __launch_bounds__(kBlock) void k_server_p1(Geo G, const uint8_t* __restrict__ wbytes,
+__global__ __launch_bounds__(kBlock) OBA_SRV_ATTR void k_server_p1(Geo G, const uint8_t* __restrict__ wbytes,
                                                       const float* __restrict__ wscale,
                                                       float* __restrict__ eps,
                                                       uint8_t* __restrict__ sbytes, SegDev sig,
@@ -763,7 +786,7 @@ __global__ __launch_bounds__(kBlock) void k_server_p1(Geo G, const uint8_t* __re
     if (hi <= pt_hi) {
       acc[0] += fs;
       if (hi == pt_hi) {
-        flush_rows<1>(acc, 1, part + pt, lds);
+        flush_rows<1>(acc, 1, part + pt, 0, lds);
         if (++pt < pt_end) pt_hi = tau.phi[pt];
       }
     } else {
@@ -772,7 +795,7 @@ __global__ __launch_bounds__(kBlock) void k_server_p1(Geo G, const uint8_t* __re
         const int64_t e = min(pt_hi, hi);
         acc[0] += sumsq_range(eps, q, cur, e);
         if (pt_hi <= hi) {
-          flush_rows<1>(acc, 1, part + pt, lds);
+          flush_rows<1>(acc, 1, part + pt, 0, lds);
           if (++pt < pt_end) pt_hi = tau.phi[pt];
         }
         cur = e;
@@ -941,14 +964,14 @@ void launch_finalize(double* part, int32_t rows, const SegDev& T, float* scale,
                      hipStream_t st) {
   if (T.n_items == 0) {
     hipLaunchKernelGGL(k_finalize_scales, dim3(T.n_seg, rows), dim3(kFinBlock), 0, st, part,
-                       rows, T.seg_first, T, scale);
+                       T.n_pieces, T.seg_first, T, scale);
     return;
   }
   double* items = part + ((size_t)T.n_pieces * rows * 8 + 255) / 256 * 32;
-  hipLaunchKernelGGL(k_sum_items, dim3(T.n_items, rows), dim3(kItemBlock), 0, st, part, rows,
-                     T.item_q, items);
-  hipLaunchKernelGGL(k_finalize_scales, dim3(T.n_seg, rows), dim3(kFinBlock), 0, st, items, rows,
-                     T.seg_item, T, scale);
+  hipLaunchKernelGGL(k_sum_items, dim3(T.n_items, rows), dim3(kItemBlock), 0, st, part,
+                     T.n_pieces, T.item_q, T.n_items, items);
+  hipLaunchKernelGGL(k_finalize_scales, dim3(T.n_seg, rows), dim3(kFinBlock), 0, st, items,
+                     T.n_items, T.seg_item, T, scale);
 }
 
 void launch_residual(const Geo& G, const float* src, int64_t src_ld, float* dst, int64_t dst_ld,

@@ -28,8 +28,8 @@ struct SegDev {
   int32_t n_items;           // 0: one-stage sums
 };
 
-// Bytes of binary64 partials for table T with `rows` rows: pieces, then
-// (two-stage) items, each part 256-byte aligned.
+// Bytes of binary64 partials for table T with `rows` rows: [rows][pieces],
+// then (two-stage) [rows][items], each part 256-byte aligned.
 inline size_t partial_bytes(const SegDev& T, int32_t rows) {
   auto al = [](size_t b) { return (b + 255) / 256 * 256; };
   return al((size_t)T.n_pieces * rows * 8) + al((size_t)T.n_items * rows * 8);
