@@ -173,34 +173,23 @@ __device__ __forceinline__ void store_sign_bits(uint8_t* __restrict__ row, const
 #ifndef OBA_PAIRS_UPD
 #define OBA_PAIRS_UPD 1
 #endif
-// The exchange form in two halves: this lane's byte (a load only) ...
-template <bool FULL>
-__device__ __forceinline__ uint32_t sign_byte(const uint8_t* __restrict__ row, const Quads& q,
-                                              int64_t d) {
-  const int64_t qi = ((threadIdx.x & 1) ? q.kB : q.kA) >> 3;
-  return (FULL || qi * 8 < d) ? (uint32_t)row[qi] : 0u;
-}
-
-// ... and the swap with the neighbour lane that yields the 8 bits.
-__device__ __forceinline__ uint32_t sign_bits_of(uint32_t mine) {
-  const bool odd = threadIdx.x & 1;
-  const uint32_t sh = odd ? 4u : 0u;
-  const uint32_t other = (uint32_t)__shfl_xor((int)mine, 1, 64);
-  const uint32_t byte_a = odd ? other : mine, byte_b = odd ? mine : other;
-  return ((byte_a >> sh) & 0xFu) | (((byte_b >> sh) & 0xFu) << 4);
-}
-
 template <bool FULL, bool PAIRS>
 __device__ __forceinline__ uint32_t load_sign_bits(const uint8_t* __restrict__ row,
                                                    const Quads& q, int64_t d) {
+  const bool odd = threadIdx.x & 1;
+  const uint32_t sh = odd ? 4u : 0u;
+  uint32_t byte_a, byte_b;
   if constexpr (PAIRS) {
-    const uint32_t sh = (threadIdx.x & 1) ? 4u : 0u;
-    const uint32_t byte_a = (FULL || q.kA < d) ? (uint32_t)row[q.kA >> 3] : 0u;
-    const uint32_t byte_b = (FULL || q.kB < d) ? (uint32_t)row[q.kB >> 3] : 0u;
-    return ((byte_a >> sh) & 0xFu) | (((byte_b >> sh) & 0xFu) << 4);
+    byte_a = (FULL || q.kA < d) ? (uint32_t)row[q.kA >> 3] : 0u;
+    byte_b = (FULL || q.kB < d) ? (uint32_t)row[q.kB >> 3] : 0u;
   } else {
-    return sign_bits_of(sign_byte<FULL>(row, q, d));
+    const int64_t qi = (odd ? q.kB : q.kA) >> 3;
+    const uint32_t mine = (FULL || qi * 8 < d) ? (uint32_t)row[qi] : 0u;
+    const uint32_t other = (uint32_t)__shfl_xor((int)mine, 1, 64);
+    byte_a = odd ? other : mine;
+    byte_b = odd ? mine : other;
   }
+  return ((byte_a >> sh) & 0xFu) | (((byte_b >> sh) & 0xFu) << 4);
 }
 
 __device__ __forceinline__ double sumsq8(const float (&c)[8]) {
