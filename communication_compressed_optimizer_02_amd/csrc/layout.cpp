@@ -90,7 +90,7 @@ int make_plan(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_w
     P.ld = ld;
     P.W = (d + 63) / 64;
     P.S = (d + kSpan - 1) / kSpan;
-    P.nblk = (int32_t)std::min<int64_t>(P.S, kMaxBlocks);
+    P.nblk = (int32_t)std::min<int64_t>((P.S + kServerSpans - 1) / kServerSpans, kMaxBlocks);
     P.nblk_w = (int32_t)std::min<int64_t>(P.S, kMaxBlocksWorker);
     P.wseg.assign(wseg, wseg + n_wseg + 1);
     P.sseg.assign(sseg, sseg + n_sseg + 1);

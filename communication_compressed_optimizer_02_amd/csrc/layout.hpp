@@ -26,12 +26,16 @@ constexpr int64_t kSpan = kBlock * kVec;    // coordinates per block pass
 #define OBA_MAX_BLOCKS 65536
 #endif
 #ifndef OBA_MAX_BLOCKS_WORKER
-#define OBA_MAX_BLOCKS_WORKER 262144
+#define OBA_MAX_BLOCKS_WORKER 2097152
 #endif
-// Caps on blocks of the streaming grids: the worker-side kernels and the
-// update run best with one span per block, the server pass (n packed rows
-// per span) with a few spans per block.
+// Streaming grids: the worker-side kernels and the update run best with one
+// span per block (up to 2^21 blocks, 4.3e9 coordinates), the server pass (n
+// packed rows per span) with at least four spans per block.
+#ifndef OBA_SERVER_SPANS
+#define OBA_SERVER_SPANS 4
+#endif
 constexpr int kMaxBlocks = OBA_MAX_BLOCKS;
+constexpr int kServerSpans = OBA_SERVER_SPANS;  // least spans per block of the server grid
 constexpr int kMaxBlocksWorker = OBA_MAX_BLOCKS_WORKER;
 constexpr int32_t kMaxWorkers = 4096;
 

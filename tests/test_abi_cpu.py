@@ -15,7 +15,7 @@ from communication_compressed_optimizer_02_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "oba.h")
 CSRC = os.path.join(ROOT, "communication_compressed_optimizer_02_amd", "csrc")
-SPAN, MAXB, MAXB_W = 2048, 65536, 262144
+SPAN, MAXB, MAXB_W, SRV_SPANS = 2048, 65536, 1 << 21, 4
 
 
 def declared_symbols():
@@ -157,7 +157,8 @@ def test_planner_pieces_under_sanitizers(driver, d, n, wseg, sseg):
     rc, res = run_plan(driver, d, n, wseg, sseg)
     assert rc == 0
     assert res["W"] == (d + 63) // 64 and res["S"] == -(-d // SPAN)
-    assert res["nblk"] == min(res["S"], MAXB) and res["nblk_w"] == min(res["S"], MAXB_W)
+    assert res["nblk"] == min(-(-res["S"] // SRV_SPANS), MAXB)
+    assert res["nblk_w"] == min(res["S"], MAXB_W)
     check_pieces(res, [wseg, sseg])
 
 
