@@ -97,16 +97,36 @@ def traffic_from_profiles(workload, kernel):
     return float(val.group(1))
 
 
-def make_state(w, torch, oba, synth):
+def make_state(w, torch, oba, synth, warmup_timing=None):
+    """The workload's state after its warm-up (Adam steps with the fused
+    variance norm, as a run watching for the plateau makes them) and the
+    freeze, plus two gradient sets.  warmup_timing (a dict) receives the
+    warm-up kernels' mean time per step (gradient generation excluded) and
+    the last variance norm."""
     L = oba.Layout(w.d, w.n, w.wseg, w.sseg)
     S = oba.State(L, w.g_dtype)
     gen = synth.device_generator(w.seed)
     zero_idx = synth.device_zero_mask(gen, w.d) if w.name == "bert_large" else None
     S.x.normal_(0.0, 0.02, generator=gen)
+    vnorm = torch.zeros(1, dtype=torch.float64, device="cuda")
     log(f"[bench] {w.name}: {w.warmup_steps} warm-up steps")
+    oba.timing_reset()
+    oba.timing_enable(True, 64)
     for _ in range(w.warmup_steps):
         synth.device_grads(gen, w, S.g, zero_idx)
-        S.warmup(synth.LR, synth.BETA1, synth.BETA2, synth.ETA)
+        S.warmup(synth.LR, synth.BETA1, synth.BETA2, synth.ETA, vnorm=vnorm)
+    torch.cuda.synchronize()
+    oba.timing_enable(False, 1)
+    tot, cnt = oba.timing_read("adam_warmup")
+    oba.timing_reset()
+    if warmup_timing is not None and cnt:
+        gb = 2 if w.g_dtype == "f16" else 4
+        alg = w.n * gb + 24  # g_i read; m, v, x read and written
+        warmup_timing.update({
+            "avg_ms": round(tot / cnt, 4), "steps": cnt, "alg_bytes_per_param": alg,
+            "alg_GBps": round(alg * w.d / (tot / cnt * 1e-3) / 1e9, 1),
+            "variance_norm": float(vnorm.item()),
+            "note": "Adam warm-up step with the fused variance norm (two kernels)"})
     S.freeze(synth.ETA)
     g_a = S.g
     synth.device_grads(gen, w, g_a, zero_idx)
@@ -245,7 +265,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = synth.workload(args.workload)
-    L, S, gsets = make_state(w, torch, oba, synth)
+    warm = {}
+    L, S, gsets = make_state(w, torch, oba, synth, warm)
 
     def run(schedule):
         """W untimed + K timed steps of one schedule from the freeze state.
@@ -315,6 +336,7 @@ def main():
                      "traffic": traffic, "alg_bytes_per_launch": dom_bytes,
                      "avg_launch_ms": round(dom_ms, 4)},
         "kernels": kernels,
+        "warmup_step": warm,
         "explicit_schedule": {
             "ms_per_step": round(ms_x, 4), "value": w.d / (ms_x * 1e-3),
             "step_alg_bytes_per_param": round(sum(alg_x.values()), 3),

@@ -34,6 +34,10 @@ SIGNATURES = {
     "oba_layout_destroy": (None, [_P]),
     "oba_workspace_bytes": (_SZ, [_P]),
     "oba_adam_warmup_step": (_I, [_P, _P, _I, _P, _P, _P, _D, _D, _D, _D, _D, _D, _P]),
+    "oba_adam_warmup_step_vnorm": (_I, [_P, _P, _I, _P, _P, _P, _D, _D, _D, _D, _D, _D, _P, _P,
+                                         _SZ, _P]),
+    "oba_plateau_init": (_I, [_P, _I32, _D, _I32]),
+    "oba_plateau_observe": (_I, [_P, _D]),
     "oba_freeze_variance": (_I, [_P, _P, _P, _D, _D, _P]),
     "oba_compress": (_I, [_P, _P, _I, _P, _P, _P, _P, _D, _P, _SZ, _P]),
     "oba_server_reduce_recompress": (_I, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -163,6 +167,49 @@ def adam_warmup_step(L: Layout, g, x, m, v, lr, beta1, beta2, eta, bc1=1.0, bc2=
         _ptr(x, "x", f32, (L.d,)), _ptr(m, "m", f32, (L.d,)), _ptr(v, "v", f32, (L.d,)),
         lr, beta1, beta2, eta, bc1, bc2, _stream(stream))
     _check(rc, "oba_adam_warmup_step")
+
+
+def adam_warmup_step_vnorm(L: Layout, g, x, m, v, lr, beta1, beta2, eta, vnorm, bc1=1.0,
+                           bc2=1.0, stream=None):
+    """The warm-up step; vnorm (a float64 CUDA tensor of one element) gets
+    ||v||_2 of the updated v."""
+    import torch
+
+    f32 = (torch.float32,)
+    rc = lib().oba_adam_warmup_step_vnorm(
+        L.handle, _ptr(g, "g", (torch.float32, torch.float16), (L.n, L.ld)), _gdtype(g),
+        _ptr(x, "x", f32, (L.d,)), _ptr(m, "m", f32, (L.d,)), _ptr(v, "v", f32, (L.d,)),
+        lr, beta1, beta2, eta, bc1, bc2, _ptr(vnorm, "vnorm", (torch.float64,), (1,)),
+        ctypes.c_void_p(L.ws.data_ptr()), L.ws_bytes, _stream(stream))
+    _check(rc, "oba_adam_warmup_step_vnorm")
+
+
+PLATEAU_MAX_WINDOW = 1024
+
+
+class _PlateauState(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("min_steps", ctypes.c_int32),
+                ("steps", ctypes.c_int32), ("fired", ctypes.c_int32), ("rtol", ctypes.c_double),
+                ("ring", ctypes.c_double * PLATEAU_MAX_WINDOW)]
+
+
+class Plateau:
+    """The library's plateau test on a scalar series (oba_plateau_*)."""
+
+    def __init__(self, window, rtol, min_steps=0):
+        self._s = _PlateauState()
+        _check(lib().oba_plateau_init(ctypes.byref(self._s), window, rtol, min_steps),
+               "oba_plateau_init")
+
+    def observe(self, value) -> bool:
+        rc = lib().oba_plateau_observe(ctypes.byref(self._s), float(value))
+        if rc < 0:
+            _check(rc, "oba_plateau_observe")
+        return rc == 1
+
+    @property
+    def steps(self):
+        return self._s.steps
 
 
 def freeze_variance(L: Layout, v, denom, eta, bc2=1.0, stream=None):
@@ -327,10 +374,15 @@ class State:
         self.momentum()
         self.m_implicit = False
 
-    def warmup(self, lr, beta1, beta2, eta, bc1=1.0, bc2=1.0, g=None):
+    def warmup(self, lr, beta1, beta2, eta, bc1=1.0, bc2=1.0, g=None, vnorm=None):
+        """One warm-up step; with vnorm (float64 [1] CUDA tensor) also ||v||_2."""
         self._explicit_m()
-        adam_warmup_step(self.L, self.g if g is None else g, self.x, self.m, self.v, lr, beta1,
-                         beta2, eta, bc1, bc2)
+        g = self.g if g is None else g
+        if vnorm is None:
+            adam_warmup_step(self.L, g, self.x, self.m, self.v, lr, beta1, beta2, eta, bc1, bc2)
+        else:
+            adam_warmup_step_vnorm(self.L, g, self.x, self.m, self.v, lr, beta1, beta2, eta,
+                                   vnorm, bc1, bc2)
 
     def freeze(self, eta, bc2=1.0):
         """End of the warm-up: denom from v; errors (or, in the deferred

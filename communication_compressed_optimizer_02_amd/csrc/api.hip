@@ -247,15 +247,28 @@ size_t oba_workspace_bytes(oba_layout L) {
   return ((L->ws_worker + 255) / 256) * 256 + L->ws_server;
 }
 
-int oba_adam_warmup_step(oba_layout L, const void* g, int g_dtype, float* x, float* m, float* v,
-                         double lr, double beta1, double beta2, double eta, double bc1,
-                         double bc2, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int warmup(oba_layout L, const void* g, int g_dtype, float* x, float* m, float* v, double lr,
+           double beta1, double beta2, double eta, double bc1, double bc2, double* vnorm,
+           void* ws, size_t ws_bytes, hipStream_t stream) {
   OBA_TRY(check_layout(L));
   if (g_dtype != OBA_F32 && g_dtype != OBA_F16) return OBA_EINVAL;
   if (!is_finite(lr) || !beta_ok(beta1) || !beta_ok(beta2) || !is_finite(eta) || eta < 0.0 ||
       !is_finite(bc1) || bc1 <= 0.0 || !is_finite(bc2) || bc2 <= 0.0)
     return OBA_EINVAL;
-  if (L->geo.d == 0) return OBA_OK;
+  if (vnorm) OBA_TRY(check_buf(vnorm, 8));
+  if (L->geo.d == 0) {  // the norm of an empty vector is 0
+    if (!vnorm) return OBA_OK;
+    return launch("adam_warmup", stream,
+                  [&] { oba::launch_norm_finalize(nullptr, 0, vnorm, stream); });
+  }
+  if (vnorm) {
+    OBA_TRY(check_buf(ws, 8));
+    if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
+  }
   OBA_TRY(check_buf(g, 16));
   OBA_TRY(check_buf(x, 16));
   OBA_TRY(check_buf(m, 16));
@@ -263,9 +276,32 @@ int oba_adam_warmup_step(oba_layout L, const void* g, int g_dtype, float* x, flo
   oba::AdamCoef C{(float)lr, (float)beta1, (float)(1.0 - beta1), (float)beta2,
                   (float)(1.0 - beta2), (float)eta, (float)bc1, (float)bc2};
   const oba::Geo G = L->geo;
+  // the block partials fit the worker part of the workspace (its pieces
+  // outnumber the blocks of this grid)
+  double* part = static_cast<double*>(ws);
   return launch("adam_warmup", stream, [&] {
-    oba::launch_adam_warmup(G, g, g_dtype == OBA_F16, x, m, v, C, stream);
+    oba::launch_adam_warmup(G, g, g_dtype == OBA_F16, x, m, v, C, part, vnorm, stream);
   });
+}
+
+}  // namespace
+
+extern "C" {
+
+int oba_adam_warmup_step(oba_layout L, const void* g, int g_dtype, float* x, float* m, float* v,
+                         double lr, double beta1, double beta2, double eta, double bc1,
+                         double bc2, hipStream_t stream) {
+  return warmup(L, g, g_dtype, x, m, v, lr, beta1, beta2, eta, bc1, bc2, nullptr, nullptr, 0,
+                stream);
+}
+
+int oba_adam_warmup_step_vnorm(oba_layout L, const void* g, int g_dtype, float* x, float* m,
+                               float* v, double lr, double beta1, double beta2, double eta,
+                               double bc1, double bc2, double* vnorm, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  if (!vnorm) return OBA_EINVAL;
+  return warmup(L, g, g_dtype, x, m, v, lr, beta1, beta2, eta, bc1, bc2, vnorm, ws, ws_bytes,
+                stream);
 }
 
 int oba_freeze_variance(oba_layout L, const float* v, float* denom, double eta, double bc2,
@@ -457,6 +493,30 @@ int oba_server_momentum(oba_layout L, const uint64_t* sbits, const float* sscale
   const uint8_t* sbytes = reinterpret_cast<const uint8_t*>(sbits);
   return launch("server_momentum", stream,
                 [&] { oba::launch_server_momentum(G, sbytes, sscale, m, L->tau_w, stream); });
+}
+
+int oba_plateau_init(oba_plateau* p, int32_t window, double rtol, int32_t min_steps) {
+  if (!p || window < 1 || window > OBA_PLATEAU_MAX_WINDOW || !is_finite(rtol) || rtol < 0.0 ||
+      min_steps < 0)
+    return OBA_EINVAL;
+  std::memset(p, 0, sizeof(*p));
+  p->window = window;
+  p->min_steps = min_steps;
+  p->rtol = rtol;
+  return OBA_OK;
+}
+
+int oba_plateau_observe(oba_plateau* p, double value) {
+  if (!p || p->window < 1 || p->window > OBA_PLATEAU_MAX_WINDOW || !is_finite(value))
+    return OBA_EINVAL;
+  if (p->steps == INT32_MAX) return p->fired;
+  const int32_t t = ++p->steps;
+  double& slot = p->ring[t % p->window];  // holds h_{t-window} once t > window
+  if (!p->fired && t > p->window && t >= p->min_steps &&
+      std::fabs(value - slot) <= p->rtol * std::fabs(value))
+    p->fired = 1;
+  slot = value;
+  return p->fired;
 }
 
 int oba_timing_enable(int on, int32_t capacity) {

@@ -296,13 +296,17 @@ __device__ __forceinline__ float residual(float c, float s) { return (c < 0.0f) 
 }  // namespace
 
 // ===========================================================================
-// Warm-up Adam step on the mean gradient.
+// Warm-up Adam step on the mean gradient.  NORM: also the sum of squares of
+// the new v, one binary64 partial per block (part[blockIdx.x]).
 // ===========================================================================
-template <typename GT>
+template <typename GT, bool NORM>
 __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restrict__ g,
                                                         float* __restrict__ x,
                                                         float* __restrict__ m,
-                                                        float* __restrict__ v, AdamCoef C) {
+                                                        float* __restrict__ v, AdamCoef C,
+                                                        double* __restrict__ part) {
+  __shared__ double lds[kWaves];
+  double acc[1] = {0.0};
   const int64_t s_lo = dspan(G.S, G.nblk, blockIdx.x);
   const int64_t s_hi = dspan(G.S, G.nblk, blockIdx.x + 1);
   const float nf = (float)G.n;
@@ -343,6 +347,27 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
     store8(m, q, G.d, full, mv);
     store8(v, q, G.d, full, vv);
     store8(x, q, G.d, full, xv);
+    if (NORM) acc[0] += sumsq8(vv);  // coordinates past d read 0 and give v = 0
+  }
+  if (NORM) flush_rows<1>(acc, 1, part + blockIdx.x, 0, lds);
+}
+
+// sqrt of the sum of n binary64 partials, in a fixed order.  One block.
+constexpr int kNormBlock = 1024;
+
+__global__ __launch_bounds__(kNormBlock) void k_norm_finalize(const double* __restrict__ part,
+                                                              int32_t n,
+                                                              double* __restrict__ out) {
+  __shared__ double lds[kNormBlock / 64];
+  double t = 0.0;
+  for (int32_t q = threadIdx.x; q < n; q += kNormBlock) t += part[q];
+  t = wave_sum(t);
+  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = t;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double S = 0.0;
+    for (int w = 0; w < kNormBlock / 64; ++w) S += lds[w];  // fixed order
+    out[0] = __builtin_sqrt(S);
   }
 }
 
@@ -848,19 +873,31 @@ __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
 // ===========================================================================
 // launchers
 // ===========================================================================
+void launch_norm_finalize(const double* part, int32_t n, double* out, hipStream_t st);
+
 template <typename GT>
 static void launch_warmup(const Geo& G, const void* g, float* x, float* m, float* v,
-                          const AdamCoef& C, hipStream_t st) {
-  hipLaunchKernelGGL(k_adam_warmup<GT>, dim3(G.nblk), dim3(kBlock), 0, st, G,
-                     static_cast<const GT*>(g), x, m, v, C);
+                          const AdamCoef& C, double* part, double* vnorm, hipStream_t st) {
+  if (!vnorm) {
+    hipLaunchKernelGGL((k_adam_warmup<GT, false>), dim3(G.nblk), dim3(kBlock), 0, st, G,
+                       static_cast<const GT*>(g), x, m, v, C, nullptr);
+    return;
+  }
+  hipLaunchKernelGGL((k_adam_warmup<GT, true>), dim3(G.nblk), dim3(kBlock), 0, st, G,
+                     static_cast<const GT*>(g), x, m, v, C, part);
+  launch_norm_finalize(part, G.nblk, vnorm, st);
+}
+
+void launch_norm_finalize(const double* part, int32_t n, double* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_norm_finalize, dim3(1), dim3(kNormBlock), 0, st, part, n, out);
 }
 
 void launch_adam_warmup(const Geo& G, const void* g, bool f16, float* x, float* m, float* v,
-                        const AdamCoef& C, hipStream_t st) {
+                        const AdamCoef& C, double* part, double* vnorm, hipStream_t st) {
   if (f16)
-    launch_warmup<uint16_t>(G, g, x, m, v, C, st);
+    launch_warmup<uint16_t>(G, g, x, m, v, C, part, vnorm, st);
   else
-    launch_warmup<float>(G, g, x, m, v, C, st);
+    launch_warmup<float>(G, g, x, m, v, C, part, vnorm, st);
 }
 
 void launch_freeze(const Geo& G, const float* v, float* denom, float eta, float bc2,

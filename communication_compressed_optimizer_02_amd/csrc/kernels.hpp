@@ -48,8 +48,11 @@ struct AdamCoef {
   float lr, b1, omb1, b2, omb2, eta, bc1, bc2;
 };
 
+// out[0] = sqrt(part[0] + ... + part[n-1]) in a fixed order (0 for n = 0)
+void launch_norm_finalize(const double* part, int32_t n, double* out, hipStream_t st);
+// vnorm != nullptr: also ||v_new||_2 into vnorm[0] (part: nblk doubles)
 void launch_adam_warmup(const Geo& G, const void* g, bool f16, float* x, float* m, float* v,
-                        const AdamCoef& C, hipStream_t st);
+                        const AdamCoef& C, double* part, double* vnorm, hipStream_t st);
 void launch_freeze(const Geo& G, const float* v, float* denom, float eta, float bc2,
                    hipStream_t st);
 // Worker compression: read-only norm pass, then recompute c and store.

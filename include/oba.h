@@ -122,6 +122,39 @@ int oba_adam_warmup_step(oba_layout layout, const void* g, int g_dtype, float* x
                          float* v, double lr, double beta1, double beta2, double eta, double bc1,
                          double bc2, hipStream_t stream);
 
+/* ---- variance norm and the freeze trigger ---------------------------------
+ * [Tang] 3.3 and Figure 2 (the norm of the fused -- all-parameter -- variance
+ * vector levels off early in training, which motivates the freeze);
+ * [AIMech] definition (the warm-up runs until v stabilises) and limitations
+ * (v must be quasi-stationary by the end of the warm-up).
+ *
+ * The warm-up step of oba_adam_warmup_step that also writes vnorm[0] =
+ * ||v||_2 of the updated v over all d coordinates (binary64 sum of squares
+ * in a fixed order, then sqrt), computed in the same pass.  vnorm: one
+ * double of device memory (8-byte aligned); ws as for oba_compress (unused
+ * when d = 0, where vnorm[0] = 0). */
+int oba_adam_warmup_step_vnorm(oba_layout layout, const void* g, int g_dtype, float* x, float* m,
+                               float* v, double lr, double beta1, double beta2, double eta,
+                               double bc1, double bc2, double* vnorm, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+/* Plateau test on a scalar series, host only (no HIP call, no allocation).
+ * The pages show the plateau but give no rule; this one: the t-th observed
+ * value h_t (t = 1, 2, ...) passes when t > window, t >= min_steps and
+ * |h_t - h_{t-window}| <= rtol * |h_t|.  oba_plateau_observe returns 1 from
+ * the first step that passes onward (latched), 0 before, OBA_EINVAL for a
+ * null state or a non-finite value.  The caller owns the struct; init
+ * requires 1 <= window <= OBA_PLATEAU_MAX_WINDOW, rtol >= 0, min_steps >= 0.
+ * Observe ||v/bc2|| = vnorm/bc2 when the warm-up is bias corrected. */
+#define OBA_PLATEAU_MAX_WINDOW 1024
+typedef struct {
+  int32_t window, min_steps, steps, fired;
+  double rtol;
+  double ring[OBA_PLATEAU_MAX_WINDOW];
+} oba_plateau;
+int oba_plateau_init(oba_plateau* p, int32_t window, double rtol, int32_t min_steps);
+int oba_plateau_observe(oba_plateau* p, double value);
+
 /* ---- variance freeze ------------------------------------------------------
  * [AIMech] definition paragraph (V = diag(sqrt(v_Tw) + eps) is frozen);
  * [Tang] 3.3, 5.  denom[k] = sqrt(v[k]/bc2) + eta, once, at the end of the
@@ -240,7 +273,8 @@ int oba_deferred_errors(oba_layout layout, const float* c, const float* wscale, 
  * equals `kernel` ("compress_p1", "compress_p2", "finalize_scales",
  * "server_p1", "server_p2", "decompress_update", "adam_warmup",
  * "freeze_variance", "compress_deferred", "server_deferred",
- * "deferred_errors", "server_momentum").  oba_timing_reset drops all records. */
+ * "deferred_errors", "server_momentum"); "adam_warmup" includes the norm
+ * kernel of oba_adam_warmup_step_vnorm.  oba_timing_reset drops all records. */
 int oba_timing_enable(int on, int32_t capacity);
 int oba_timing_read(const char* kernel, double* total_ms, int64_t* launches);
 int oba_timing_reset(void);

@@ -46,6 +46,8 @@ def lib():
             "oracle_half_to_double": (D, [ctypes.c_uint16]),
             "oracle_adam_warmup_step": (None, [I64, I32, I64, P, I, P, P, P, D, D, D, D, D, D]),
             "oracle_freeze_variance": (None, [I64, P, P, D, D]),
+            "oracle_l2norm": (D, [I64, P]),
+            "oracle_plateau_first": (I64, [I64, P, I32, D, I32]),
             "oracle_sumsq": (D, [I64, P]),
             "oracle_scale": (F, [D, I64]),
             "oracle_pack_signs": (None, [I64, P, P, I64]),
@@ -113,6 +115,18 @@ def freeze_variance(v, eta, bc2=1.0):
     denom = np.empty_like(v)
     lib().oracle_freeze_variance(v.shape[0], _p(v), _p(denom), eta, bc2)
     return denom
+
+
+def l2norm(v):
+    """sqrt(sum v_k^2) in binary64 (the fused variance norm)."""
+    _chk(v, np.float32, "v")
+    return lib().oracle_l2norm(v.size, _p(v))
+
+
+def plateau_first(h, window, rtol, min_steps=0):
+    """First 1-based step at which the series h has levelled off, or 0."""
+    h = np.ascontiguousarray(np.asarray(h, dtype=np.float64))
+    return int(lib().oracle_plateau_first(h.size, _p(h), window, rtol, min_steps))
 
 
 def compensate(beta1, m, g_row, delta_row):

@@ -77,6 +77,33 @@ void oracle_adam_warmup_step(int64_t d, int32_t n, int64_t ld, const void* g, in
   }
 }
 
+/* Norm of the fused variance vector, the quantity whose levelling-off
+ * motivates the freeze ([Tang] 3.3, Figure 2): the plain definition
+ * sqrt(sum_k v_k^2), every square exact in binary64, summed in index order. */
+double oracle_l2norm(int64_t d, const float* v) {
+  double s = 0.0;
+  for (int64_t k = 0; k < d; ++k) {
+    const double x = (double)v[k];
+    s += x * x;
+  }
+  return sqrt(s);
+}
+
+/* When the warm-up may stop: the pages show the variance levelling off
+ * ([Tang] 3.3, Figure 2; [AIMech] definition: run Adam until v stabilises)
+ * but give no test.  Reading: at step t (1-based) the series h has levelled
+ * off when t > window, t >= min_steps and |h_t - h_{t-window}| <= rtol*|h_t|.
+ * Returns the first such t among h_1..h_len, or 0. */
+int64_t oracle_plateau_first(int64_t len, const double* h, int32_t window, double rtol,
+                             int32_t min_steps) {
+  for (int64_t t = 1; t <= len; ++t) {
+    if (t <= window || t < min_steps) continue;
+    const double now = h[t - 1], before = h[t - 1 - window];
+    if (fabs(now - before) <= rtol * fabs(now)) return t;
+  }
+  return 0;
+}
+
 /* Freeze: the variance stops changing and becomes the fixed preconditioner
  * V = diag(sqrt(v_Tw) + eta) ([AIMech] definition paragraph; [Tang] 3.3 and
  * 5).  denom = sqrt(v/bc2) + eta, stored once. */

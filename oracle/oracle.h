@@ -50,6 +50,9 @@ void oracle_adam_warmup_step(int64_t d, int32_t n, int64_t ld, const void* g, in
                              float* x, float* m, float* v, double lr, double beta1,
                              double beta2, double eta, double bc1, double bc2);
 void oracle_freeze_variance(int64_t d, const float* v, float* denom, double eta, double bc2);
+double oracle_l2norm(int64_t d, const float* v);
+int64_t oracle_plateau_first(int64_t len, const double* h, int32_t window, double rtol,
+                             int32_t min_steps);
 
 /* ---- the 1-bit error-compensated compressor, one segment at a time ------ */
 double oracle_sumsq(int64_t len, const float* c);

@@ -184,3 +184,42 @@ def test_planner_handles_the_tensor_list_and_random_tables(driver):
 def test_planner_rejects_bad_tables(driver):
     assert run_plan(driver, 100, 2, [0, 50, 50, 100], [0, 100])[0] == -3
     assert run_plan(driver, 100, 2, [0, 100], [0, 100], ld=100)[0] == -1
+
+
+def test_plateau_test_matches_the_oracle_rule():
+    """oba_plateau_* is host code: it runs here without a GPU."""
+    import oracle
+
+    rng = np.random.default_rng(9)
+    cases = [([3.0] * 40, 5, 0.0, 0), ([3.0] * 40, 5, 0.0, 17),
+             ([1.0 - 0.999 ** t for t in range(1, 4000)], 100, 0.01, 0),
+             ([1.0 - 0.99 ** t for t in range(1, 2000)], 1, 1e-4, 50)]
+    for _ in range(20):
+        h = np.cumsum(rng.exponential(1.0, 300) * np.exp(-np.arange(300) / rng.uniform(5, 80)))
+        cases.append((h.tolist(), int(rng.integers(1, 40)), float(rng.uniform(1e-4, 0.05)),
+                      int(rng.integers(0, 100))))
+    for h, w, rtol, mins in cases:
+        want = oracle.plateau_first(h, w, rtol, mins)
+        p = binding.Plateau(w, rtol, mins)
+        fired = [p.observe(x) for x in h]
+        first = fired.index(True) + 1 if any(fired) else 0
+        assert first == want
+        assert all(fired[first - 1:]) if first else not any(fired)  # latched
+        assert p.steps == len(h)
+
+
+def test_plateau_test_rejects_bad_arguments():
+    lib = binding.lib()
+    s = binding._PlateauState()
+    P = ctypes.byref
+    assert lib.oba_plateau_init(None, 3, 0.1, 0) == -1
+    assert lib.oba_plateau_init(P(s), 0, 0.1, 0) == -1
+    assert lib.oba_plateau_init(P(s), binding.PLATEAU_MAX_WINDOW + 1, 0.1, 0) == -1
+    assert lib.oba_plateau_init(P(s), 3, -0.1, 0) == -1
+    assert lib.oba_plateau_init(P(s), 3, float("nan"), 0) == -1
+    assert lib.oba_plateau_init(P(s), 3, 0.1, -1) == -1
+    assert lib.oba_plateau_init(P(s), binding.PLATEAU_MAX_WINDOW, 0.1, 0) == 0
+    assert lib.oba_plateau_observe(P(s), float("inf")) == -1
+    assert lib.oba_plateau_observe(None, 1.0) == -1
+    assert lib.oba_plateau_observe(P(s), 1.0) == 0
+    assert s.steps == 1

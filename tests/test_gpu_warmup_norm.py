@@ -1,0 +1,142 @@
+"""GPU tests of the warm-up step with the fused variance norm
+(oba_adam_warmup_step_vnorm) and of the freeze trigger built on it.
+
+The norm is a binary64 sum of exact squares in a fixed order; the oracle sums
+in index order, so the two agree to the rounding of a binary64 sum (bound
+used: 1e-12 relative).  The warm-up state written by the norm variant must be
+bitwise the state of the plain warm-up step."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_common import B1, B2, ETA, LR, assert_close, grads, padded, to_dev, to_host, torch
+from communication_compressed_optimizer_02_amd import binding as oba
+from communication_compressed_optimizer_02_amd import quadratic, synth
+
+pytestmark = pytest.mark.gpu
+NORM_RTOL = 1e-12
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("d,n,gdt,bc", [(4096, 2, "f32", False), (2049, 3, "f16", True),
+                                        (1, 1, "f32", False), (300_001, 5, "f32", True),
+                                        (9_000_017, 4, "f16", False)])
+def test_warmup_norm_matches_oracle_and_leaves_the_step_unchanged(d, n, gdt, bc):
+    say(f"[warmup vnorm] d={d} n={n} g={gdt} bias_correction={bc}")
+    rng = np.random.default_rng(d + n)
+    L = oba.Layout(d, n, synth.whole(d), synth.even_shards(d, n))
+    A, B = oba.State(L, gdt), oba.State(L, gdt)
+    x0 = rng.normal(0.0, 0.02, d).astype(np.float32)
+    for S in (A, B):
+        S.x.copy_(torch().from_numpy(x0))
+    x, m, v = x0.copy(), np.zeros(d, np.float32), np.zeros(d, np.float32)
+    vn = torch().zeros(1, dtype=torch().float64, device="cuda")
+    for t in range(1, 6):
+        bc1, bc2 = (1 - B1 ** t, 1 - B2 ** t) if bc else (1.0, 1.0)
+        g = grads(rng, n, d, gdt)
+        gd = to_dev(padded(g, L.ld))
+        A.warmup(LR, B1, B2, ETA, bc1, bc2, g=gd)
+        B.warmup(LR, B1, B2, ETA, bc1, bc2, g=gd, vnorm=vn)
+        oracle.adam_warmup_step(g, x, m, v, LR, B1, B2, ETA, bc1, bc2)
+        torch().cuda.synchronize()
+        for nm in ("x", "m", "v"):
+            assert torch().equal(getattr(A, nm), getattr(B, nm)), f"{nm} at step {t}"
+        assert_close(to_host(B.v), v, f"v at step {t}")
+        got = float(vn.item())
+        own = oracle.l2norm(to_host(B.v))  # the norm of the device's own v
+        assert abs(got - own) <= NORM_RTOL * own, (t, got, own)
+        ref = oracle.l2norm(v)  # and of the oracle's v (within the v tolerance)
+        assert abs(got - ref) <= 1e-5 * ref
+    L.close()
+
+
+def test_warmup_norm_of_an_empty_layout_is_zero():
+    L = oba.Layout(0, 2, [0], [0])
+    S = oba.State(L)
+    vn = torch().full((1,), 7.0, dtype=torch().float64, device="cuda")
+    S.warmup(LR, B1, B2, ETA, vnorm=vn)
+    torch().cuda.synchronize()
+    assert float(vn.item()) == 0.0
+    L.close()
+
+
+def test_warmup_norm_rejects_bad_arguments():
+    import ctypes
+
+    L = oba.Layout(100, 2, synth.whole(100), synth.even_shards(100, 2))
+    S = oba.State(L)
+    vn = torch().zeros(2, dtype=torch().float64, device="cuda")
+    P = ctypes.c_void_p
+    strm = P(torch().cuda.current_stream().cuda_stream)
+    lib = oba.lib()
+    args = [L.handle, P(S.g.data_ptr()), 0, P(S.x.data_ptr()), P(S.m.data_ptr()),
+            P(S.v.data_ptr()), LR, B1, B2, ETA, 1.0, 1.0]
+    assert lib.oba_adam_warmup_step_vnorm(*args, None, P(L.ws.data_ptr()), L.ws_bytes,
+                                          strm) == -1
+    assert lib.oba_adam_warmup_step_vnorm(*args, P(vn.data_ptr() + 4), P(L.ws.data_ptr()),
+                                          L.ws_bytes, strm) == -2
+    assert lib.oba_adam_warmup_step_vnorm(*args, P(vn.data_ptr()), P(L.ws.data_ptr()), 0,
+                                          strm) == -4
+    torch().cuda.synchronize()
+    L.close()
+
+
+def test_bert_large_warmup_norm_full_size():
+    """Full size, bench launch configuration: the norm of the device's v."""
+    w = synth.workload("bert_large")
+    say(f"[warmup vnorm full size] {w.name} d={w.d} n={w.n}")
+    L = oba.Layout(w.d, w.n, w.wseg, w.sseg)
+    S = oba.State(L, w.g_dtype)
+    gen = synth.device_generator(w.seed)
+    vn = torch().zeros(1, dtype=torch().float64, device="cuda")
+    for _ in range(2):
+        synth.device_grads(gen, w, S.g)
+        S.warmup(LR, B1, B2, ETA, vnorm=vn)
+    torch().cuda.synchronize()
+    got = float(vn.item())
+    own = oracle.l2norm(to_host(S.v))
+    assert abs(got - own) <= NORM_RTOL * own, (got, own)
+    L.close()
+
+
+def test_freeze_trigger_on_the_quadratic_matches_the_oracle_run():
+    """Bare warm-up on the noisy quadratic until the variance norm levels
+    off (its growth as 1 - b2^t slows below 2 % per 20 steps, near step 400):
+    the GPU run (fused norm + library plateau test) and the oracle run
+    (oracle warm-up, oracle norm, oracle rule) stop at the same step."""
+    d, n, T = 1 << 18, 4, 800
+    window, rtol = 20, 0.02
+    say(f"[freeze trigger] quadratic d={d} n={n} window={window} rtol={rtol}")
+    P = quadratic.Problem(d, n, seed=7)
+    a, xs = to_host(P.a), to_host(P.xstar)
+    L = oba.Layout(d, n, synth.whole(d), synth.even_shards(d, n))
+    S = oba.State(L)
+    vn = torch().zeros(1, dtype=torch().float64, device="cuda")
+    xi = torch().empty((n, d), device="cuda")
+    gen = P.noise_stream()
+    x, m, v = np.zeros(d, np.float32), np.zeros(d, np.float32), np.zeros(d, np.float32)
+    trig = oba.Plateau(window, rtol)
+    h_gpu, h_ora, fired_at = [], [], 0
+    for t in range(1, T + 1):
+        xi.normal_(0.0, 1.0, generator=gen)
+        P.grads(S.x, xi, S.g)
+        g_o = np.ascontiguousarray((a * (x - xs))[None, :] + np.float32(0.1) * to_host(xi),
+                                   dtype=np.float32)
+        S.warmup(LR, B1, B2, ETA, vnorm=vn)
+        oracle.adam_warmup_step(g_o, x, m, v, LR, B1, B2, ETA)
+        h_gpu.append(float(vn.item()))
+        h_ora.append(oracle.l2norm(v))
+        if trig.observe(h_gpu[-1]) and not fired_at:
+            fired_at = t
+            break
+    want = oracle.plateau_first(h_ora, window, rtol)
+    say(f"  GPU trigger at step {fired_at}, oracle rule at step {want}")
+    assert fired_at and fired_at == want
+    assert_close(to_host(S.v), v, "v at the trigger")
+    L.close()

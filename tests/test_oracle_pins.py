@@ -459,3 +459,79 @@ def test_tiny_workload_runs_and_tracks_adam_direction():
         _, wscale, _, sscale = oracle.step(st, G[t], w.wseg, w.sseg, B1, LR)
         assert np.all(np.isfinite(st["x"])) and np.all(wscale > 0) and np.all(sscale > 0)
     assert np.abs(st["x"] - x0).max() > 0
+
+
+# --------------------------------------------------------------------------
+# The fused variance norm and the plateau rule ([Tang] 3.3, Figure 2;
+# [AIMech] definition and limitations)
+# --------------------------------------------------------------------------
+
+def test_variance_norm_closed_forms():
+    # constant vector: ||c 1_d|| = c sqrt(d), exact for d = 4096, c = 3
+    assert oracle.l2norm(np.full(4096, 3.0, np.float32)) == 192.0
+    # Pythagorean pairs among zeros, and +-0 / subnormal-free inputs
+    v = np.zeros(1000, np.float32)
+    v[[7, 500]] = [3.0, 4.0]
+    assert oracle.l2norm(v) == 5.0
+    v[[7, 500, 999]] = [5.0, -12.0, 0.0]
+    assert oracle.l2norm(v) == 13.0
+    assert oracle.l2norm(np.zeros(0, np.float32)) == 0.0
+    # scaling by a power of two is exact
+    rng = np.random.default_rng(3)
+    w = rng.normal(0.0, 1.0, 5000).astype(np.float32)
+    assert oracle.l2norm(w * np.float32(2.0 ** -20)) == oracle.l2norm(w) * 2.0 ** -20
+
+
+def test_variance_norm_against_exact_sum():
+    """Within the binary64 rounding of an index-order sum of exact squares."""
+    from fractions import Fraction
+
+    rng = np.random.default_rng(4)
+    v = (rng.normal(0.0, 1e-3, 3000) ** 2).astype(np.float32)
+    exact = sum(Fraction(float(x)) ** 2 for x in v)
+    got = oracle.l2norm(v)
+    ref = math.sqrt(float(exact))
+    assert abs(got - ref) <= 3000 * 2.0 ** -53 * ref
+
+
+def test_bare_warmup_variance_norm_follows_its_closed_form():
+    """With the same gradient every step, the bare recurrence gives
+    v_t = (1 - b2^t) g^2 per coordinate, so ||v_t|| = (1 - b2^t) ||g^2||
+    (up to the binary32 rounding of v)."""
+    rng = np.random.default_rng(5)
+    d, n = 777, 2
+    g1 = rng.normal(0.0, 1e-2, d).astype(np.float32)
+    g = np.ascontiguousarray(np.stack([g1, g1]))
+    x, m, v = np.zeros(d, np.float32), np.zeros(d, np.float32), np.zeros(d, np.float32)
+    g2 = np.linalg.norm(g1.astype(np.float64) ** 2)
+    for t in range(1, 30):
+        oracle.adam_warmup_step(g, x, m, v, LR, B1, B2, ETA)
+        want = (1.0 - B2 ** t) * g2
+        assert abs(oracle.l2norm(v) - want) <= 2e-6 * want * t
+
+
+def expected_plateau(h, window, rtol, min_steps):
+    """The rule restated directly (test side)."""
+    for t in range(1, len(h) + 1):
+        if t > window and t >= min_steps and abs(h[t - 1] - h[t - 1 - window]) <= rtol * abs(h[t - 1]):
+            return t
+    return 0
+
+
+def test_plateau_rule_special_cases_and_closed_form():
+    # a constant series levels off as soon as the window allows
+    assert oracle.plateau_first([2.0] * 50, 10, 0.0, 0) == 11
+    assert oracle.plateau_first([2.0] * 50, 10, 0.0, 30) == 30
+    # a series that keeps rising by 1 % per step never passes at 0.5 %
+    assert oracle.plateau_first([1.01 ** t for t in range(300)], 1, 0.005, 0) == 0
+    assert oracle.plateau_first([], 3, 0.1, 0) == 0
+    # h_t = 1 - b^t (the bare v norm under a fixed gradient scale): the test
+    # b^(t-w) (1 - b^w) <= rtol (1 - b^t) first holds at t* with
+    # b^t* <= rtol / ((1 - b^w) b^-w + rtol), i.e. t* = ceil(log(...) / log b)
+    for b, w, rtol in [(0.999, 100, 0.01), (0.99, 10, 0.001), (0.999, 50, 0.05)]:
+        h = [1.0 - b ** t for t in range(1, 20001)]
+        bound = rtol / ((1.0 - b ** w) * b ** -w + rtol)
+        t_star = max(w + 1, math.ceil(math.log(bound) / math.log(b)))
+        got = oracle.plateau_first(h, w, rtol, 0)
+        assert abs(got - t_star) <= 1, (b, w, rtol, got, t_star)
+        assert got == expected_plateau(h, w, rtol, 0)
