@@ -1,9 +1,11 @@
 """GPU tests of the warm-up step with the fused variance norm
 (oba_adam_warmup_step_vnorm) and of the freeze trigger built on it.
 
-The norm is a binary64 sum of exact squares in a fixed order; the oracle sums
-in index order, so the two agree to the rounding of a binary64 sum (bound
-used: 1e-12 relative).  The warm-up state written by the norm variant must be
+The norm is a binary64 sum of exact, non-negative squares in a fixed order;
+the oracle sums in index order.  A sum of d non-negative terms in any order
+is within (d-1)*u of the exact sum (u = 2^-53), relative, and the square root
+halves that, so the two norms agree within d*u relative (4.5e-13 at d = 4096,
+3.7e-8 at 336M).  The warm-up state written by the norm variant must be
 bitwise the state of the plain warm-up step."""
 import sys
 
@@ -16,7 +18,10 @@ from communication_compressed_optimizer_02_amd import binding as oba
 from communication_compressed_optimizer_02_amd import quadratic, synth
 
 pytestmark = pytest.mark.gpu
-NORM_RTOL = 1e-12
+
+
+def norm_rtol(d):
+    return max(d, 1) * 2.0 ** -53
 
 
 def say(*a):
@@ -50,7 +55,7 @@ def test_warmup_norm_matches_oracle_and_leaves_the_step_unchanged(d, n, gdt, bc)
         assert_close(to_host(B.v), v, f"v at step {t}")
         got = float(vn.item())
         own = oracle.l2norm(to_host(B.v))  # the norm of the device's own v
-        assert abs(got - own) <= NORM_RTOL * own, (t, got, own)
+        assert abs(got - own) <= norm_rtol(d) * own, (t, got, own)
         ref = oracle.l2norm(v)  # and of the oracle's v (within the v tolerance)
         assert abs(got - ref) <= 1e-5 * ref
     L.close()
@@ -101,7 +106,8 @@ def test_bert_large_warmup_norm_full_size():
     torch().cuda.synchronize()
     got = float(vn.item())
     own = oracle.l2norm(to_host(S.v))
-    assert abs(got - own) <= NORM_RTOL * own, (got, own)
+    assert abs(got - own) <= norm_rtol(w.d) * own, (got, own)
+    say(f"  relative difference {abs(got - own) / own:.2e} (bound {norm_rtol(w.d):.1e})")
     L.close()
 
 
