@@ -297,9 +297,11 @@ __device__ __forceinline__ float residual(float c, float s) { return (c < 0.0f) 
 
 // ===========================================================================
 // Warm-up Adam step on the mean gradient.  NORM: also the sum of squares of
-// the new v, one binary64 partial per block (part[blockIdx.x]).
+// the new v, one binary64 partial per block (part[blockIdx.x]).  NB rows of g
+// are loaded together (NB = n for n <= 8; larger n loops over groups of 8),
+// after m, v and x, so that all of a span's loads are in flight at once.
 // ===========================================================================
-template <typename GT, bool NORM>
+template <typename GT, int NB, bool NORM>
 __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restrict__ g,
                                                         float* __restrict__ x,
                                                         float* __restrict__ m,
@@ -317,24 +319,24 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
     const Quads q = quads(lo);
     const bool full = lo + kSpan <= G.d;
     float sum[8], mv[8], vv[8], xv[8];
+    load8(m, q, G.d, full, mv);
+    load8(v, q, G.d, full, vv);
+    load8(x, q, G.d, full, xv);
 #pragma unroll
     for (int j = 0; j < 8; ++j) sum[j] = 0.0f;
-    for (int32_t i0 = 0; i0 < G.n; i0 += 4) {
-      // four rows loaded together (rows past n clamped, their terms skipped)
-      float gv[4][8];
+    for (int32_t i0 = 0; i0 < G.n; i0 += NB) {  // one pass when n <= NB
+      // rows past n are clamped to a valid row and their terms skipped
+      float gv[NB][8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < NB; ++u)
         load8(g + (int64_t)min(i0 + u, G.n - 1) * G.ld, q, G.d, full, gv[u]);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < NB; ++u)
         if (i0 + u < G.n) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) sum[j] = sum[j] + gv[u][j];
         }
     }
-    load8(m, q, G.d, full, mv);
-    load8(v, q, G.d, full, vv);
-    load8(x, q, G.d, full, xv);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float gb = pow2 ? sum[j] * inv_n : sum[j] / nf;  // identical for n = 2^k
@@ -875,16 +877,33 @@ __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
 // ===========================================================================
 void launch_norm_finalize(const double* part, int32_t n, double* out, hipStream_t st);
 
+template <typename GT, bool NORM>
+static void launch_warmup_nb(const Geo& G, const void* g, float* x, float* m, float* v,
+                             const AdamCoef& C, double* part, hipStream_t st) {
+#define OBA_WARMUP_LAUNCH(NB)                                                                \
+  hipLaunchKernelGGL((k_adam_warmup<GT, NB, NORM>), dim3(G.nblk), dim3(kBlock), 0, st, G,    \
+                     static_cast<const GT*>(g), x, m, v, C, part)
+  switch (G.n) {
+    case 1: OBA_WARMUP_LAUNCH(1); break;
+    case 2: OBA_WARMUP_LAUNCH(2); break;
+    case 3: OBA_WARMUP_LAUNCH(3); break;
+    case 4: OBA_WARMUP_LAUNCH(4); break;
+    case 5: OBA_WARMUP_LAUNCH(5); break;
+    case 6: OBA_WARMUP_LAUNCH(6); break;
+    case 7: OBA_WARMUP_LAUNCH(7); break;
+    default: OBA_WARMUP_LAUNCH(8); break;
+  }
+#undef OBA_WARMUP_LAUNCH
+}
+
 template <typename GT>
 static void launch_warmup(const Geo& G, const void* g, float* x, float* m, float* v,
                           const AdamCoef& C, double* part, double* vnorm, hipStream_t st) {
   if (!vnorm) {
-    hipLaunchKernelGGL((k_adam_warmup<GT, false>), dim3(G.nblk), dim3(kBlock), 0, st, G,
-                       static_cast<const GT*>(g), x, m, v, C, nullptr);
+    launch_warmup_nb<GT, false>(G, g, x, m, v, C, nullptr, st);
     return;
   }
-  hipLaunchKernelGGL((k_adam_warmup<GT, true>), dim3(G.nblk), dim3(kBlock), 0, st, G,
-                     static_cast<const GT*>(g), x, m, v, C, part);
+  launch_warmup_nb<GT, true>(G, g, x, m, v, C, part, st);
   launch_norm_finalize(part, G.nblk, vnorm, st);
 }
 
