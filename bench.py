@@ -47,6 +47,13 @@ def gbytes(w, schedule="deferred"):
             # server bits read, denom read, x read+written (m stays implicit)
             "decompress_update": 1 / 8 + 12,
         }
+    if schedule == "local":
+        return {
+            # g_i, m_i and the last c_i read; m_i, c_i and packed bits written
+            "compress_deferred_local": n * (gb + 16) + n / 8,
+            "server_deferred": n / 8 + 8 + 1 / 8,
+            "decompress_update": 1 / 8 + 12,
+        }
     reads = 4 + n * (gb + 4)  # m, g_i, delta_i
     return {
         # norm pass: m, g_i, delta_i read
@@ -273,7 +280,9 @@ def main():
         The deferred schedule's first step, which reads the warm-up's m
         instead of the server message, is never timed."""
         S.start_compression()
-        fn = S.step_deferred if schedule == "deferred" else S.step
+        if schedule == "local":
+            S.start_local_momentum()
+        fn = {"deferred": S.step_deferred, "explicit": S.step, "local": S.step_local}[schedule]
         log(f"[bench] {schedule}: {args.warmup} untimed steps, {args.steps} timed steps")
         if schedule == "deferred" and args.warmup == 0:
             fn(synth.BETA1, synth.LR, g=gsets[1])
@@ -303,6 +312,8 @@ def main():
 
     ms, alg, kernels = run("deferred")
     ms_x, alg_x, kernels_x = run("explicit")
+    ms_l, alg_l, kernels_l = run("local")
+    del S.m_local
     # dominant kernel: the largest share of the step's time
     dom = max(alg, key=lambda k: kernels[k]["avg_ms"])
     dom_ms = kernels[dom]["avg_ms"]
@@ -342,6 +353,11 @@ def main():
             "step_alg_bytes_per_param": round(sum(alg_x.values()), 3),
             "step_alg_GBps": round(sum(alg_x.values()) * w.d / (ms_x * 1e-3) / 1e9, 1),
             "kernels": kernels_x},
+        "local_momentum_schedule": {
+            "ms_per_step": round(ms_l, 4), "value": w.d / (ms_l * 1e-3),
+            "step_alg_bytes_per_param": round(sum(alg_l.values()), 3),
+            "step_alg_GBps": round(sum(alg_l.values()) * w.d / (ms_l * 1e-3) / 1e9, 1),
+            "kernels": kernels_l},
         "kernel_source_sha256": source_hash(),
     }
     del S, gsets

@@ -44,6 +44,7 @@ SIGNATURES = {
     "oba_decompress_update": (_I, [_P, _P, _P, _P, _P, _P, _D, _P]),
     "oba_server_momentum": (_I, [_P, _P, _P, _P, _P]),
     "oba_compress_deferred": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _D, _P, _SZ, _P]),
+    "oba_compress_deferred_local": (_I, [_P, _P, _I, _P, _P, _P, _P, _D, _P, _SZ, _P]),
     "oba_server_reduce_recompress_deferred": (_I, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "oba_deferred_errors": (_I, [_P, _P, _P, _P, _P, _P, _P, _P]),
     "oba_timing_enable": (_I, [_I, _I32]),
@@ -293,6 +294,20 @@ def compress_deferred(L: Layout, g, m, c, wbits, wscale, beta1, sbits_prev=None,
     _check(rc, "oba_compress_deferred")
 
 
+def compress_deferred_local(L: Layout, g, m_local, c, wbits, wscale, beta1, stream=None):
+    """Per-worker momentum: m_local [n][ld] and c [n][ld] in/out."""
+    import torch
+
+    f32 = (torch.float32,)
+    rc = lib().oba_compress_deferred_local(
+        L.handle, _ptr(g, "g", (torch.float32, torch.float16), (L.n, L.ld)), _gdtype(g),
+        _ptr(m_local, "m_local", f32, (L.n, L.ld)), _ptr(c, "c", f32, (L.n, L.ld)),
+        _ptr(wbits, "wbits", (torch.int64,), (L.n, L.W)),
+        _ptr(wscale, "wscale", f32, (L.n, L.n_wseg)), beta1,
+        ctypes.c_void_p(L.ws.data_ptr()), L.ws_bytes, _stream(stream))
+    _check(rc, "oba_compress_deferred_local")
+
+
 def server_reduce_recompress_deferred(L: Layout, wbits, wscale, a, sbits, sscale, stream=None):
     """a: last step's server vector in, this step's out; sscale: last step's
     server scales in, this step's out."""
@@ -407,6 +422,25 @@ class State:
         server_reduce_recompress(self.L, self.wbits, self.wscale, self.eps, self.sbits,
                                  self.sscale)
         decompress_update(self.L, self.sbits, self.sscale, self.denom, self.m, self.x, lr)
+
+    def start_local_momentum(self):
+        """Per-worker momentum from here on: every worker's m_i starts as the
+        shared m (call after the freeze)."""
+        import torch
+
+        self.m_local = self.momentum().unsqueeze(0).repeat(self.L.n, 1)
+        if self.L.ld != self.L.d:
+            self.m_local = torch.nn.functional.pad(self.m_local, (0, self.L.ld - self.L.d))
+        self.m_local = self.m_local.contiguous()
+
+    def step_local(self, beta1, lr, g=None):
+        """A compression step with per-worker momentum (deferred layout): the
+        broadcast m_hat moves x; each worker keeps its own m_i."""
+        compress_deferred_local(self.L, self.g if g is None else g, self.m_local, self.delta,
+                                self.wbits, self.wscale, beta1)
+        server_reduce_recompress_deferred(self.L, self.wbits, self.wscale, self.eps, self.sbits,
+                                          self.sscale)
+        decompress_update(self.L, self.sbits, self.sscale, self.denom, None, self.x, lr)
 
     def step_deferred(self, beta1, lr, g=None, implicit_m=True):
         """The same step in the deferred-residual layout: `delta` holds the

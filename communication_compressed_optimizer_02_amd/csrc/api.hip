@@ -412,6 +412,33 @@ int oba_compress_deferred(oba_layout L, const void* g, int g_dtype, const float*
                 [&] { oba::launch_finalize(part, G.n, L->sig_w, wscale, stream); });
 }
 
+int oba_compress_deferred_local(oba_layout L, const void* g, int g_dtype, float* m_local,
+                                float* c, uint64_t* wbits, float* wscale, double beta1, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  OBA_TRY(check_layout(L));
+  if (g_dtype != OBA_F32 && g_dtype != OBA_F16) return OBA_EINVAL;
+  if (!beta_ok(beta1)) return OBA_EINVAL;
+  if (L->geo.d == 0) return OBA_OK;
+  OBA_TRY(check_buf(g, 16));
+  OBA_TRY(check_buf(m_local, 16));
+  OBA_TRY(check_buf(c, 16));
+  OBA_TRY(check_buf(wbits, 8));
+  OBA_TRY(check_buf(wscale, 4));
+  OBA_TRY(check_buf(ws, 8));
+  if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
+  if ((const void*)m_local == (const void*)c) return OBA_EINVAL;
+  const oba::Geo G = L->geo_w;
+  double* part = static_cast<double*>(ws);
+  const float b1 = (float)beta1, omb1 = (float)(1.0 - beta1);
+  uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
+  OBA_TRY(launch("compress_deferred_local", stream, [&] {
+    oba::launch_compress_deferred_local(G, g, g_dtype == OBA_F16, m_local, c, wbytes, L->sig_w,
+                                        part, wscale, b1, omb1, stream);
+  }));
+  return launch("finalize_scales", stream,
+                [&] { oba::launch_finalize(part, G.n, L->sig_w, wscale, stream); });
+}
+
 int oba_server_reduce_recompress_deferred(oba_layout L, const uint64_t* wbits,
                                           const float* wscale, float* a, uint64_t* sbits,
                                           float* sscale, void* ws, size_t ws_bytes,

@@ -407,7 +407,10 @@ __global__ __launch_bounds__(kBlock) void k_freeze(Geo G, const float* __restric
 // kDeferredM: as kDeferred, but m is not read: after a compression step
 //         every worker's momentum is the server's m_hat = sbar*sign, so it is
 //         rebuilt from the last packed server bits and scales (1/8 byte
-//         instead of 4 bytes per coordinate).
+//         instead of 4 bytes per coordinate);
+// kDeferredLocal: as kDeferred with per-worker momentum: m is [n][ld], each
+//         worker's m_i = b1*m_i + (1-b1)*g_i is stored back and
+//         c = m_i + delta_i.
 // The scale needs the whole segment's norm before any residual can be
 // written, so the explicit layout needs c twice.  Recomputing it reads g, m,
 // delta twice but never writes c: on this HBM, writes cost more than reads,
@@ -417,7 +420,7 @@ __global__ __launch_bounds__(kBlock) void k_freeze(Geo G, const float* __restric
 // [i0, i0 + gridDim.y*NB); larger n takes one launch of full groups and one
 // for the remainder.  Grid: (nblk, groups).
 // ===========================================================================
-enum { kNorm = 1, kApply = 2, kDeferred = 3, kDeferredM = 4 };
+enum { kNorm = 1, kApply = 2, kDeferred = 3, kDeferredM = 4, kDeferredLocal = 5 };
 #ifndef OBA_WORKER_BATCH
 #define OBA_WORKER_BATCH 4
 #endif
@@ -432,7 +435,7 @@ constexpr int kWorkerBatch = OBA_WORKER_BATCH;
 
 template <typename GT, int NB, int MODE>
 __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t i0, const GT* __restrict__ g,
-                                                     const float* __restrict__ m,
+                                                     float* __restrict__ m,  // read; written by kDeferredLocal
                                                      float* __restrict__ delta,
                                                      uint8_t* __restrict__ wbytes, SegDev sig,
                                                      double* __restrict__ part,
@@ -488,6 +491,9 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
       while (pt < pt_end && pt_hi <= hi) {
         if (++pt < pt_end) pt_hi = ms.tau.phi[pt];
       }
+    } else if (MODE == kDeferredLocal) {  // per-worker rows, loaded with g below
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mv[j] = 0.0f;
     } else if (full) {
       load_full(m, q, mv);
     } else {
@@ -499,7 +505,8 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
     constexpr int NBB = NB < kWorkerBatch ? NB : kWorkerBatch;
 #pragma unroll
     for (int ib = 0; ib < NB; ib += NBB) {
-      float gv[NBB][8], c[NBB][8];
+      constexpr int NBL = MODE == kDeferredLocal ? NBB : 1;  // per-worker m rows
+      float gv[NBB][8], c[NBB][8], ml[NBL][8];
       // ib + u < NB is decided at compile time: a last batch may be partial
       if (full) {
 #pragma unroll
@@ -508,6 +515,7 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
           const int64_t row = (int64_t)(i0 + ib + u) * G.ld;
           load_full(g + row, q, gv[u]);
           load_full(delta + row, q, c[u]);
+          if (MODE == kDeferredLocal) load_full(m + row, q, ml[u]);
         }
       } else {
 #pragma unroll
@@ -516,6 +524,7 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
           const int64_t row = (int64_t)(i0 + ib + u) * G.ld;
           load_tail(g + row, q, G.d, gv[u]);
           load_tail(delta + row, q, G.d, c[u]);
+          if (MODE == kDeferredLocal) load_tail(m + row, q, G.d, ml[u]);
         }
       }
 #pragma unroll
@@ -535,7 +544,7 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
             for (int j = 0; j < 8; ++j) sv[j] = sc[jseg[j]];
           }
         }
-        if (MODE == kDeferred || MODE == kDeferredM) {  // c[u] holds c' of the last step
+        if (MODE >= kDeferred) {  // c[u] holds c' of the last step
 #pragma unroll
           for (int j = 0; j < 8; ++j) c[u][j] = residual(c[u][j], sv[j]);
           if (!full) {  // coordinates past d read as 0 and must stay 0 (no bit, no c^2)
@@ -544,10 +553,20 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
               if (coord(q, j) >= G.d) c[u][j] = 0.0f;
           }
         }
+        if (MODE == kDeferredLocal) {
+          // the same two products and two adds as compensate(), m_i kept
 #pragma unroll
-        for (int j = 0; j < 8; ++j) c[u][j] = compensate(b1, omb1, mv[j], gv[u][j], c[u][j]);
+          for (int j = 0; j < 8; ++j) {
+            ml[u][j] = b1 * ml[u][j] + omb1 * gv[u][j];
+            c[u][j] = ml[u][j] + c[u][j];
+          }
+          store8(m + row, q, G.d, full, ml[u]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) c[u][j] = compensate(b1, omb1, mv[j], gv[u][j], c[u][j]);
+        }
         if (MODE != kNorm) store_sign_bits(wbytes + (int64_t)(i0 + i) * rowbytes, q, sign_bits(c[u]), rowbytes);
-        if (MODE == kDeferred || MODE == kDeferredM) store8(delta + row, q, G.d, full, c[u]);
+        if (MODE >= kDeferred) store8(delta + row, q, G.d, full, c[u]);
         fs[i] = (MODE != kApply) ? sumsq8(c[u]) : 0.0;
         if (MODE == kApply) {
 #pragma unroll
@@ -574,7 +593,7 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
           const int64_t row = (int64_t)(i0 + i) * G.ld;
-          if (MODE == kDeferred || MODE == kDeferredM)
+          if (MODE >= kDeferred)
             acc[i] += sumsq_range(delta + row, q, cur, e);  // c was stored there
           else
             acc[i] += sumsq_range_c(m, g + row, delta + row, b1, omb1, q, cur, e);
@@ -930,8 +949,8 @@ static void launch_cmp(const Geo& G, int32_t i0, int groups, const void* g, cons
                        const float* wscale, float b1, float omb1, const MomSrc& ms,
                        hipStream_t st) {
   hipLaunchKernelGGL((k_compress<GT, NB, MODE>), dim3(G.nblk, groups), dim3(kBlock), 0, st, G,
-                     i0, static_cast<const GT*>(g), m, delta, wbytes, sig, part, wscale, b1,
-                     omb1, ms);
+                     i0, static_cast<const GT*>(g), const_cast<float*>(m), delta, wbytes, sig,
+                     part, wscale, b1, omb1, ms);
 }
 
 // Groups of GROUP workers per block, then one launch for the remainder.  A
@@ -953,7 +972,7 @@ template <typename GT, int MODE>
 static void launch_cmp_n(const Geo& G, const void* g, const float* m, float* delta,
                          uint8_t* wbytes, const SegDev& sig, double* part, const float* wscale,
                          float b1, float omb1, const MomSrc& ms, hipStream_t st) {
-  constexpr int GROUP = MODE == kDeferredM ? kImplicitNB : kMaxNB;
+  constexpr int GROUP = (MODE == kDeferredM || MODE == kDeferredLocal) ? kImplicitNB : kMaxNB;
   const int full = G.n / GROUP, rem = G.n % GROUP, i0 = full * GROUP;
 #define OBA_CMP(NB_, I0, GROUPS) \
   launch_cmp<GT, NB_, MODE>(G, I0, GROUPS, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms, st)
@@ -997,6 +1016,14 @@ void launch_compress_deferred(const Geo& G, const void* g, bool f16, const float
                              st);
   else
     launch_cmp_t<kDeferred>(G, g, f16, m, c, wbytes, sig, part, wscale_prev, b1, omb1, ms, st);
+}
+
+void launch_compress_deferred_local(const Geo& G, const void* g, bool f16, float* m_local,
+                                    float* c, uint8_t* wbytes, const SegDev& sig, double* part,
+                                    const float* wscale_prev, float b1, float omb1,
+                                    hipStream_t st) {
+  launch_cmp_t<kDeferredLocal>(G, g, f16, m_local, c, wbytes, sig, part, wscale_prev, b1, omb1,
+                               MomSrc{}, st);
 }
 
 void launch_compress_apply(const Geo& G, const void* g, bool f16, const float* m, float* delta,

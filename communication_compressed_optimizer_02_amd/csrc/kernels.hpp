@@ -59,6 +59,11 @@ void launch_freeze(const Geo& G, const float* v, float* denom, float eta, float 
 void launch_compress_norm(const Geo& G, const void* g, bool f16, const float* m,
                           const float* delta, const SegDev& sig, double* part, float b1,
                           float omb1, hipStream_t st);
+// per-worker momentum: m_local [n][ld] in/out
+void launch_compress_deferred_local(const Geo& G, const void* g, bool f16, float* m_local,
+                                    float* c, uint8_t* wbytes, const SegDev& sig, double* part,
+                                    const float* wscale_prev, float b1, float omb1,
+                                    hipStream_t st);
 void launch_compress_apply(const Geo& G, const void* g, bool f16, const float* m, float* delta,
                            uint8_t* wbytes, const SegDev& sig, const float* wscale, float b1,
                            float omb1, hipStream_t st);

@@ -63,13 +63,14 @@ class Problem:
 
 def run(d, n, steps, warmup, seed=4, every=10, lr=synth.LR, beta1=synth.BETA1,
         beta2=synth.BETA2, eta=synth.ETA, compressed=True, bias_correction=False, log=None,
-        auto_freeze=None, info=None):
+        auto_freeze=None, info=None, local_momentum=False):
     """Returns (losses {step: f}, optimizer ms per step, gradient ms per step).
     bias_correction: Kingma-Ba factors 1-b^t in the warm-up (and in the
     frozen variance); off = the bare recurrences.  auto_freeze = (window,
     rtol): the warm-up ends when the variance norm ||v/bc2|| levels off
     (library plateau test), at most at step `warmup`; info["freeze_step"]
-    receives the last warm-up step."""
+    receives the last warm-up step.  local_momentum: every worker keeps its
+    own momentum in the compression stage (the broadcast only moves x)."""
     import torch
 
     P = Problem(d, n, seed)
@@ -96,7 +97,11 @@ def run(d, n, steps, warmup, seed=4, every=10, lr=synth.LR, beta1=synth.BETA1,
                 stop = True
             if compressed and stop:
                 S.freeze(eta, bc2)
+                if local_momentum:
+                    S.start_local_momentum()
                 frozen_at = t
+        elif local_momentum:
+            S.step_local(beta1, lr)
         else:
             S.step_deferred(beta1, lr)
         e[2].record()
@@ -120,25 +125,29 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--seed", type=int, default=4)
+    ap.add_argument("--local-momentum", action="store_true",
+                    help="per-worker momentum in the compression stage")
     ap.add_argument("--auto-freeze", nargs=2, type=float, metavar=("WINDOW", "RTOL"),
                     help="end the warm-up when the variance norm levels off (at most at "
                          "--warmup), instead of at --warmup")
     args = ap.parse_args()
     auto = (int(args.auto_freeze[0]), args.auto_freeze[1]) if args.auto_freeze else None
+    local = args.local_momentum
 
     def log(msg):
         print(msg, flush=True)
 
     marks = [m for m in (args.warmup, 500, 1000, args.steps) if 0 < m <= args.steps]
     out = {"workload": "quadratic", "d": args.d, "n_workers": args.n, "steps": args.steps,
-           "warmup": args.warmup}
+           "warmup": args.warmup, "momentum": "per-worker" if args.local_momentum else "shared"}
     t0 = time.time()
     for name, bc in (("bare", False), ("bias_corrected", True)):
         log(f"[quadratic] {name} warm-up: 1-bit Adam, d={args.d} n={args.n} "
             f"steps={args.steps} warm-up={args.warmup} ({time.time() - t0:.0f} s)")
         info = {}
         f1, opt1, gr1 = run(args.d, args.n, args.steps, args.warmup, args.seed,
-                            bias_correction=bc, log=log, auto_freeze=auto, info=info)
+                            bias_correction=bc, log=log, auto_freeze=auto, info=info,
+                            local_momentum=local)
         log(f"[quadratic] {name} warm-up: Adam baseline ({time.time() - t0:.0f} s)")
         fa, opta, _ = run(args.d, args.n, args.steps, args.warmup, args.seed, compressed=False,
                           bias_correction=bc, log=log)

@@ -249,6 +249,19 @@ int oba_compress_deferred(oba_layout layout, const void* g, int g_dtype, const f
                           uint64_t* wbits, float* wscale, double beta1, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 
+/* Per-worker momentum (the other reading of [Tang] 4.3: every worker keeps
+ * its own momentum and the broadcast m_hat only moves x), in the deferred
+ * layout.  m_local: [n][ld] in/out, worker i's momentum (set every row to the
+ * warm-up's m at the freeze); c, wscale, g, wbits, ws as for
+ * oba_compress_deferred.  Per worker i and coordinate:
+ *   delta_i = c_i - s_i*sign(c_i);  m_i = b1*m_i + (1-b1)*g_i;
+ *   c_i = m_i + delta_i;  s_{i,sigma} = sqrt(sum c^2 / |sigma|);  bit = (c < 0).
+ * The step continues with oba_server_reduce_recompress_deferred and
+ * oba_decompress_update with m = NULL. */
+int oba_compress_deferred_local(oba_layout layout, const void* g, int g_dtype, float* m_local,
+                                float* c, uint64_t* wbits, float* wscale, double beta1, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
 /* a: [d] in (last a) / out (this a); sscale: [n_sseg] in (last) / out (this);
  * wbits, wscale: this step's worker messages; sbits, ws as for
  * oba_server_reduce_recompress.
@@ -273,7 +286,8 @@ int oba_deferred_errors(oba_layout layout, const float* c, const float* wscale, 
  * equals `kernel` ("compress_p1", "compress_p2", "finalize_scales",
  * "server_p1", "server_p2", "decompress_update", "adam_warmup",
  * "freeze_variance", "compress_deferred", "server_deferred",
- * "deferred_errors", "server_momentum"); "adam_warmup" includes the norm
+ * "deferred_errors", "server_momentum", "compress_deferred_local"); "adam_warmup"
+ * includes the norm
  * kernel of oba_adam_warmup_step_vnorm.  oba_timing_reset drops all records. */
 int oba_timing_enable(int on, int32_t capacity);
 int oba_timing_read(const char* kernel, double* total_ms, int64_t* launches);

@@ -55,6 +55,7 @@ def lib():
             "oracle_residual": (None, [I64, P, F, P]),
             "oracle_compensate": (None, [I64, D, P, P, I, I64, P, P]),
             "oracle_compress": (None, [I64, I32, I64, P, I32, P, I, P, P, P, P, D]),
+            "oracle_compress_local": (None, [I64, I32, I64, P, I32, P, I, P, P, P, P, D]),
             "oracle_server_average": (None, [I64, I64, I64, I32, P, I32, P, P, P, P]),
             "oracle_server_reduce_recompress": (None, [I64, I32, P, I32, P, I32, P, P, P, P, P]),
             "oracle_decompress_update": (None, [I64, I64, P, I32, P, P, P, P, P, D]),
@@ -177,6 +178,22 @@ def compress(g, m, delta, wseg, beta1):
     return wbits, wscale
 
 
+def compress_local(g, m_local, delta, wseg, beta1):
+    """Worker compression with per-worker momentum: m_local and delta [n][ld]
+    are updated in place.  Returns (wbits, wscale)."""
+    n, ld = g.shape
+    _chk(m_local, np.float32, "m_local")
+    _chk(delta, np.float32, "delta")
+    assert m_local.shape == (n, ld) and delta.shape == (n, ld)
+    d = int(wseg[-1])
+    wseg = _seg(wseg, d)
+    wbits = np.zeros((n, words(d)), np.uint64)
+    wscale = np.zeros((n, len(wseg) - 1), np.float32)
+    lib().oracle_compress_local(d, n, ld, _p(wseg), len(wseg) - 1, _p(g), _grad(g), _p(m_local),
+                                _p(delta), _p(wbits), _p(wscale), beta1)
+    return wbits, wscale
+
+
 def server_average(wbits, wscale, wseg, eps, k0=0, k1=None):
     """a[k] for k in [k0, k1) (other entries of the returned array are 0)."""
     n = wbits.shape[0]
@@ -223,9 +240,14 @@ def bit(bits, k):
 
 
 def step(state, g, wseg, sseg, beta1, lr):
-    """One compression step on a dict state {m, delta, eps, denom, x}.
-    Returns the messages (wbits, wscale, sbits, sscale)."""
-    wbits, wscale = compress(g, state["m"], state["delta"], wseg, beta1)
+    """One compression step on a dict state {m, delta, eps, denom, x}; with
+    "m_local" ([n][ld]) in the state, the per-worker-momentum variant (m_hat
+    then only moves x).  Returns the messages (wbits, wscale, sbits, sscale)."""
+    if "m_local" in state:
+        wbits, wscale = compress_local(g, state["m_local"], state["delta"], wseg, beta1)
+    else:
+        wbits, wscale = compress(g, state["m"], state["delta"], wseg, beta1)
     sbits, sscale = server_reduce_recompress(wbits, wscale, wseg, sseg, state["eps"])
-    decompress_update(sbits, sscale, sseg, state["denom"], state["m"], state["x"], lr)
+    m_hat = state["m"] if "m" in state else np.zeros_like(state["x"])
+    decompress_update(sbits, sscale, sseg, state["denom"], m_hat, state["x"], lr)
     return wbits, wscale, sbits, sscale

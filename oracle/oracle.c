@@ -190,6 +190,30 @@ void oracle_compress(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int3
   free(c);
 }
 
+/* Per-worker momentum: the other reading of [Tang] 4.3 (each worker keeps
+ * and updates its own momentum, the broadcast m_hat only moves x).  Worker i:
+ *   m_i = b1*m_i + (1-b1)*g_i      (kept by the worker)
+ *   c   = m_i + delta_i
+ * then the same compressor.  m_local, delta: [n][ld], updated in place. */
+void oracle_compress_local(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_wseg,
+                           const void* g, int g_is_f16, float* m_local, float* delta,
+                           uint64_t* wbits, float* wscale, double beta1_) {
+  const float beta1 = (float)beta1_;
+  const float omb1 = (float)(1.0 - beta1_);
+  int64_t W = (d + 63) / 64;
+  float* c = (float*)malloc((size_t)(d > 0 ? d : 1) * sizeof(float));
+  for (int32_t i = 0; i < n; ++i) {
+    float* mi = m_local + (int64_t)i * ld;
+    float* di = delta + (int64_t)i * ld;
+    for (int64_t k = 0; k < d; ++k) {
+      mi[k] = beta1 * mi[k] + omb1 * grad_at(g, g_is_f16, (int64_t)i * ld + k);
+      c[k] = mi[k] + di[k];
+    }
+    ec_onebit(d, wseg, n_wseg, c, wbits + (int64_t)i * W, wscale + (int64_t)i * n_wseg, di);
+  }
+  free(c);
+}
+
 /* Server side, per coordinate k in [k0, k1) ([Tang] 11: the server averages
  * the workers' messages, then compresses again; [AIMech] gather-broadcast
  * mechanism: server error memory):

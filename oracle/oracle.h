@@ -67,6 +67,9 @@ void oracle_compensate(int64_t len, double beta1, const float* m, const void* g,
 void oracle_compress(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_wseg,
                      const void* g, int g_is_f16, const float* m, float* delta, uint64_t* wbits,
                      float* wscale, double beta1);
+void oracle_compress_local(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_wseg,
+                           const void* g, int g_is_f16, float* m_local, float* delta,
+                           uint64_t* wbits, float* wscale, double beta1);
 void oracle_server_average(int64_t k0, int64_t k1, int64_t d, int32_t n, const int64_t* wseg,
                            int32_t n_wseg, const uint64_t* wbits, const float* wscale,
                            const float* eps, float* a);

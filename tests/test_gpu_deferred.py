@@ -213,3 +213,44 @@ def test_bert_large_deferred_step_equals_explicit_step_on_device():
     torch().cuda.synchronize()
     assert torch().equal(eps, E.eps), "eps"
     L.close()
+
+
+@pytest.mark.parametrize("d,n,gdt,tab", [(4096, 2, "f32", "shards"), (2049, 3, "f16", "cuts"),
+                                         (1_000_003, 8, "f16", "shards"),
+                                         (300_007, 5, "f32", "cuts")])
+def test_local_momentum_free_running_tracks_oracle(d, n, gdt, tab):
+    """Per-worker momentum (oba_compress_deferred_local): GPU and oracle run
+    freely from the same state for 6 steps."""
+    say(f"[local momentum] d={d} n={n} g={gdt} tables={tab}")
+    rng = np.random.default_rng(3 * d + n)
+    if tab == "shards":
+        wseg, sseg = synth.whole(d), synth.even_shards(d, n)
+    else:
+        wseg, sseg = cut_table(rng, d, 5), cut_table(rng, d, 4)
+    L = oba.Layout(d, n, wseg, sseg)
+    st0 = synth.host_state(rng, d, n)
+    S = oba.State(L, gdt)
+    S.m.copy_(torch().from_numpy(st0["m"]))
+    S.x.copy_(torch().from_numpy(st0["x"]))
+    denom = oracle.freeze_variance(st0["v"], ETA)
+    S.denom.copy_(torch().from_numpy(denom))
+    S.start_local_momentum()
+    st = dict(x=st0["x"].copy(), m_local=np.ascontiguousarray(np.stack([st0["m"]] * n)),
+              delta=np.zeros((n, d), np.float32), eps=np.zeros(d, np.float32), denom=denom)
+    delta = torch().zeros_like(S.delta)
+    eps = torch().zeros_like(S.eps)
+    for t in range(6):
+        g = grads(rng, n, d, gdt)
+        wb, ws, sb, ss = oracle.step(st, g, wseg, sseg, B1, LR)
+        S.step_local(B1, LR, g=to_dev(padded(g, L.ld)))
+        oba.deferred_errors(L, S.delta, S.wscale, S.eps, S.sscale, delta, eps)
+        torch().cuda.synchronize()
+        assert_words(to_host(S.wbits, np.uint64), wb, f"worker words, step {t}")
+        assert_words(to_host(S.sbits, np.uint64), sb, f"server words, step {t}")
+        assert_close(to_host(S.wscale), ws, f"worker scales, step {t}")
+        assert_close(to_host(S.sscale), ss, f"server scales, step {t}")
+        assert_close(to_host(S.m_local)[:, :d], st["m_local"], f"m_local, step {t}")
+        assert_close(to_host(delta)[:, :d], st["delta"], f"delta, step {t}")
+        assert_close(to_host(eps), st["eps"], f"eps, step {t}")
+        assert_close(to_host(S.x), st["x"], f"x, step {t}")
+    L.close()

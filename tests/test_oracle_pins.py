@@ -535,3 +535,48 @@ def test_plateau_rule_special_cases_and_closed_form():
         got = oracle.plateau_first(h, w, rtol, 0)
         assert abs(got - t_star) <= 1, (b, w, rtol, got, t_star)
         assert got == expected_plateau(h, w, rtol, 0)
+
+
+# --------------------------------------------------------------------------
+# Per-worker momentum (the other reading of [Tang] 4.3)
+# --------------------------------------------------------------------------
+
+def test_local_momentum_step_equals_the_shared_step_when_all_momenta_agree():
+    """If every worker's m_i equals the shared m, one per-worker step gives
+    the shared-momentum step's messages and errors bit for bit, and each m_i
+    becomes that worker's b1*m + (1-b1)*g_i."""
+    rng = np.random.default_rng(21)
+    d, n, ld = 1000, 3, 1000
+    wseg = np.array([0, 17, 500, 999, 1000], np.int64)
+    m = rng.normal(0, 1e-2, d).astype(np.float32)
+    g = rng.normal(0, 1.0, (n, ld)).astype(np.float32)
+    delta = rng.normal(0, 1e-3, (n, ld)).astype(np.float32)
+    d_a, d_b = delta.copy(), delta.copy()
+    ml = np.ascontiguousarray(np.stack([m] * n))
+    wa, sa = oracle.compress(g, m, d_a, wseg, B1)
+    wb, sb = oracle.compress_local(g, ml, d_b, wseg, B1)
+    assert np.array_equal(wa, wb) and np.array_equal(sa, sb) and np.array_equal(d_a, d_b)
+    want = (np.float32(B1) * m[None, :] + np.float32(1.0 - B1) * g).astype(np.float32)
+    assert np.array_equal(ml, want)
+
+
+def test_local_momentum_with_singleton_segments_is_momentum_sgd():
+    """Lossless compressor (one coordinate per segment, server included): the
+    server output is the mean of the workers' momenta, which obeys the
+    momentum recurrence of the mean gradient, so x follows momentum SGD with
+    per-coordinate step lr/denom (binary64 reference, binary32 tolerance)."""
+    rng = np.random.default_rng(22)
+    d, n, T = 64, 4, 12
+    seg = np.arange(d + 1, dtype=np.int64)
+    v = (rng.normal(0, 1e-2, d) ** 2).astype(np.float32)
+    denom = oracle.freeze_variance(v, ETA)
+    m0 = rng.normal(0, 1e-2, d).astype(np.float32)
+    st = dict(x=np.zeros(d, np.float32), m_local=np.ascontiguousarray(np.stack([m0] * n)),
+              delta=np.zeros((n, d), np.float32), eps=np.zeros(d, np.float32), denom=denom)
+    x64, m64 = np.zeros(d), m0.astype(np.float64)
+    for _ in range(T):
+        g = rng.normal(0, 1.0, (n, d)).astype(np.float32)
+        oracle.step(st, g, seg, seg, B1, LR)
+        m64 = B1 * m64 + (1 - B1) * g.astype(np.float64).mean(axis=0)
+        x64 = x64 - LR * m64 / denom.astype(np.float64)
+    assert np.allclose(st["x"], x64, rtol=1e-4, atol=1e-7)
