@@ -180,6 +180,65 @@ def cpu_baseline(w, torch, synth, d_sample):
                       f"at d={ws.d:,}, n={ws.n}, {ws.g_dtype} gradients: {dt:.2f} s on 1 thread"}
 
 
+def run_listed(w, S, g_flat, args, torch, oba, synth):
+    """The deferred step with x and every worker's gradient held as the
+    model's separate tensors (copies of the flat buffers), everything else
+    flat: W untimed and K timed steps from the freeze state."""
+    lengths = [int(k) for k in synth.gpt2_xl_tensor_sizes()]
+    L = S.L
+
+    def split(flat):
+        out, at = [], 0
+        for k in lengths:
+            out.append(flat[at:at + k].clone())
+            at += k
+        return out
+
+    S.start_compression()
+    TL = oba.TensorList(L, split(S.x), [split(g_flat[i, :w.d]) for i in range(w.n)])
+    log(f"[bench] tensor list ({len(lengths)} tensors): {args.warmup} untimed steps, "
+        f"{args.steps} timed steps")
+    state = {"implicit": False}
+
+    def step():
+        if state["implicit"]:
+            oba.compress_deferred_listed(L, TL, None, S.delta, S.wbits, S.wscale, synth.BETA1,
+                                         S.sbits, S.sscale)
+        else:
+            oba.compress_deferred_listed(L, TL, S.m, S.delta, S.wbits, S.wscale, synth.BETA1)
+        oba.server_reduce_recompress_deferred(L, S.wbits, S.wscale, S.eps, S.sbits, S.sscale)
+        oba.decompress_update_listed(L, TL, S.sbits, S.sscale, S.denom, None, synth.LR)
+        state["implicit"] = True
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    oba.timing_reset()
+    oba.timing_enable(True, 16 * max(1, args.steps))
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    oba.timing_enable(False, 1)
+    alg = gbytes(w, "deferred")
+    kernels = {}
+    for k in list(alg) + ["finalize_scales"]:
+        tot, cnt = oba.timing_read(k)
+        ent = {"avg_ms": round(tot / cnt, 4) if cnt else 0.0, "launches": cnt}
+        if k in alg and cnt:
+            ent["alg_GBps"] = round(alg[k] * w.d / (tot / cnt * 1e-3) / 1e9, 1)
+        kernels[k] = ent
+    oba.timing_reset()
+    TL.close()
+    del TL
+    S.m_implicit = False  # the listed run left S.m stale and sbits/sscale its own
+    torch.cuda.empty_cache()
+    return {"tensors": len(lengths), "ms_per_step": round(ms, 4), "value": w.d / (ms * 1e-3),
+            "step_alg_GBps": round(sum(alg.values()) * w.d / (ms * 1e-3) / 1e9, 1),
+            "kernels": kernels}
+
+
 def one_gpu_share(w, torch, oba, synth, steps, warmup):
     """The kernels one GPU of an n-GPU job would run per step, at their real
     shapes: its own worker's compression over all d coordinates, the server
@@ -259,6 +318,9 @@ def main():
     ap.add_argument("--workload", default="bert_large",
                     choices=["tiny", "bert_base", "bert_large", "gpt2_xl", "quadratic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tensor-list", action="store_true",
+                    help="also time the deferred step with x and the gradients as the model's "
+                         "separate tensors (gpt2_xl: its 388 tensors)")
     ap.add_argument("--cpu-sample", type=int, default=128_000_000)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -313,6 +375,11 @@ def main():
         return (t1 - t0) * 1e3 / args.steps, alg, kernels
 
     ms, alg, kernels = run("deferred")
+    listed = None
+    if args.tensor_list:
+        if w.name != "gpt2_xl":
+            raise SystemExit("--tensor-list needs the tensor-list workload (gpt2_xl)")
+        listed = run_listed(w, S, gsets[0], args, torch, oba, synth)
     ms_x, alg_x, kernels_x = run("explicit")
     ms_l, alg_l, kernels_l = run("local")
     del S.m_local
@@ -360,6 +427,7 @@ def main():
             "step_alg_bytes_per_param": round(sum(alg_l.values()), 3),
             "step_alg_GBps": round(sum(alg_l.values()) * w.d / (ms_l * 1e-3) / 1e9, 1),
             "kernels": kernels_l},
+        "tensor_list_schedule": listed,
         "kernel_source_sha256": source_hash(),
     }
     del S, gsets

@@ -47,6 +47,12 @@ SIGNATURES = {
     "oba_compress_deferred_local": (_I, [_P, _P, _I, _P, _P, _P, _P, _D, _P, _SZ, _P]),
     "oba_server_reduce_recompress_deferred": (_I, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "oba_deferred_errors": (_I, [_P, _P, _P, _P, _P, _P, _P, _P]),
+    "oba_tensors_create": (_I, [ctypes.POINTER(_P), _P, _I32, _P, _P, _P, _I]),
+    "oba_tensors_destroy": (None, [_P]),
+    "oba_adam_warmup_step_listed": (_I, [_P, _P, _P, _P, _D, _D, _D, _D, _D, _D, _P, _P, _SZ,
+                                         _P]),
+    "oba_compress_deferred_listed": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _D, _P, _SZ, _P]),
+    "oba_decompress_update_listed": (_I, [_P, _P, _P, _P, _P, _P, _D, _P]),
     "oba_timing_enable": (_I, [_I, _I32]),
     "oba_timing_read": (_I, [ctypes.c_char_p, ctypes.POINTER(_D), ctypes.POINTER(_I64)]),
     "oba_timing_reset": (_I, []),
@@ -336,6 +342,96 @@ def deferred_errors(L: Layout, c, wscale, a, sscale, delta=None, eps=None, strea
     sp = _ptr(sscale, "sscale", f32, (L.n_sseg,)) if eps is not None else P(None)
     _check(lib().oba_deferred_errors(L.handle, cp, wp, ap, sp, dp, ep, _stream(stream)),
            "oba_deferred_errors")
+
+
+class TensorList:
+    """Model tensors in their own allocations (oba_tensors): x as a list of T
+    float32 CUDA tensors, the gradients as n lists (one per worker) of T
+    tensors of the same lengths.  Keeps references to every tensor."""
+
+    def __init__(self, L: Layout, xs, gs):
+        import numpy as np
+        import torch
+
+        self.L = L
+        self.xs = list(xs)
+        self.gs = [list(row) for row in gs]
+        T = len(self.xs)
+        if len(self.gs) != L.n or any(len(row) != T for row in self.gs):
+            raise ValueError("gs must hold n rows of T tensors")
+        gdt = self.gs[0][0].dtype if T else torch.float32
+        self.g_dtype = OBA_F16 if gdt == torch.float16 else OBA_F32
+        lengths = np.array([t.numel() for t in self.xs], dtype=np.int64)
+        for t, x in enumerate(self.xs):
+            _ptr(x, f"x[{t}]", (torch.float32,))
+            for i in range(L.n):
+                g = self.gs[i][t]
+                _ptr(g, f"g[{i}][{t}]", (gdt,))
+                if g.numel() != x.numel():
+                    raise ValueError(f"g[{i}][{t}] length differs from x[{t}]")
+        self.lengths = lengths
+        xp = (ctypes.c_void_p * max(T, 1))(*[x.data_ptr() for x in self.xs])
+        gp = (ctypes.c_void_p * max(L.n * T, 1))(*[g.data_ptr() for row in self.gs for g in row])
+        h = ctypes.c_void_p()
+        _check(lib().oba_tensors_create(ctypes.byref(h), L.handle, T,
+                                        lengths.ctypes.data_as(ctypes.c_void_p), xp, gp,
+                                        self.g_dtype), "oba_tensors_create")
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            lib().oba_tensors_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def adam_warmup_step_listed(L: Layout, TLs: TensorList, m, v, lr, beta1, beta2, eta, bc1=1.0,
+                            bc2=1.0, vnorm=None, stream=None):
+    import torch
+
+    f32 = (torch.float32,)
+    vp = _ptr(vnorm, "vnorm", (torch.float64,), (1,)) if vnorm is not None else ctypes.c_void_p()
+    rc = lib().oba_adam_warmup_step_listed(
+        L.handle, TLs.handle, _ptr(m, "m", f32, (L.d,)), _ptr(v, "v", f32, (L.d,)), lr, beta1,
+        beta2, eta, bc1, bc2, vp, ctypes.c_void_p(L.ws.data_ptr()), L.ws_bytes, _stream(stream))
+    _check(rc, "oba_adam_warmup_step_listed")
+
+
+def compress_deferred_listed(L: Layout, TLs: TensorList, m, c, wbits, wscale, beta1,
+                             sbits_prev=None, sscale_prev=None, stream=None):
+    import torch
+
+    f32 = (torch.float32,)
+    P = ctypes.c_void_p
+    mp = _ptr(m, "m", f32, (L.d,)) if m is not None else P(None)
+    bp = (_ptr(sbits_prev, "sbits_prev", (torch.int64,), (L.W,)) if sbits_prev is not None
+          else P(None))
+    sp = (_ptr(sscale_prev, "sscale_prev", f32, (L.n_sseg,)) if sscale_prev is not None
+          else P(None))
+    rc = lib().oba_compress_deferred_listed(
+        L.handle, TLs.handle, mp, bp, sp, _ptr(c, "c", f32, (L.n, L.ld)),
+        _ptr(wbits, "wbits", (torch.int64,), (L.n, L.W)),
+        _ptr(wscale, "wscale", f32, (L.n, L.n_wseg)), beta1,
+        ctypes.c_void_p(L.ws.data_ptr()), L.ws_bytes, _stream(stream))
+    _check(rc, "oba_compress_deferred_listed")
+
+
+def decompress_update_listed(L: Layout, TLs: TensorList, sbits, sscale, denom, m, lr,
+                             stream=None):
+    import torch
+
+    f32 = (torch.float32,)
+    mp = _ptr(m, "m", f32, (L.d,)) if m is not None else ctypes.c_void_p(None)
+    rc = lib().oba_decompress_update_listed(
+        L.handle, TLs.handle, _ptr(sbits, "sbits", (torch.int64,), (L.W,)),
+        _ptr(sscale, "sscale", f32, (L.n_sseg,)), _ptr(denom, "denom", f32, (L.d,)), mp, lr,
+        _stream(stream))
+    _check(rc, "oba_decompress_update_listed")
 
 
 def timing_enable(on=True, capacity=4096):

@@ -11,6 +11,7 @@
 #include <mutex>
 #include <new>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "kernels.hpp"
@@ -28,6 +29,16 @@ struct oba_layout_s {
   oba::Geo geo_w{};     // worker grid
   oba::Geo geo{};       // server grid
   size_t ws_worker = 0, ws_server = 0;
+};
+
+struct oba_tensors_s {
+  int device = -1;
+  int g_dtype = OBA_F32;
+  int32_t T = 0;
+  int32_t n = 0;
+  void* dev = nullptr;  // one allocation holding every table below
+  oba::TList tl_w{};    // block table of the worker grid
+  oba::TList tl_s{};    // block table of the server grid
 };
 
 namespace {
@@ -521,6 +532,157 @@ int oba_server_momentum(oba_layout L, const uint64_t* sbits, const float* sscale
   const uint8_t* sbytes = reinterpret_cast<const uint8_t*>(sbits);
   return launch("server_momentum", stream,
                 [&] { oba::launch_server_momentum(G, sbytes, sscale, m, L->tau_w, stream); });
+}
+
+int oba_tensors_create(oba_tensors* out, oba_layout L, int32_t n_tensors,
+                       const int64_t* lengths, float* const* x_ptrs, const void* const* g_ptrs,
+                       int g_dtype) {
+  if (!out || !x_ptrs || !g_ptrs) return OBA_EINVAL;
+  OBA_TRY(check_layout(L));
+  if (g_dtype != OBA_F32 && g_dtype != OBA_F16) return OBA_EINVAL;
+  const oba::Plan& P = L->plan;
+  if (P.d == 0) return OBA_EINVAL;  // nothing to list
+  std::vector<int64_t> off;
+  int rc = oba::tensor_offsets(P, n_tensors, lengths, &off);
+  if (rc) return rc;
+  const int32_t T = n_tensors, n = P.n;
+  const uintptr_t galign = g_dtype == OBA_F32 ? 16 : 8;
+  for (int32_t t = 0; t < T; ++t) OBA_TRY(check_buf(x_ptrs[t], 16));
+  for (int64_t r = 0; r < (int64_t)n * T; ++r) OBA_TRY(check_buf(g_ptrs[r], galign));
+  std::vector<int32_t> bw, bs;
+  try {
+    oba::tensor_blocks(P, P.nblk_w, off, &bw);
+    oba::tensor_blocks(P, P.nblk, off, &bs);
+  } catch (...) {
+    return OBA_ENOMEM;
+  }
+  // layout of the allocation: off | g pointers | x pointers | bw | bs
+  const size_t b_off = off.size() * sizeof(int64_t);
+  const size_t b_g = (size_t)n * T * sizeof(void*);
+  const size_t b_x = (size_t)T * sizeof(float*);
+  const size_t b_bw = bw.size() * sizeof(int32_t), b_bs = bs.size() * sizeof(int32_t);
+  const size_t bytes = b_off + b_g + b_x + b_bw + b_bs;
+  oba_tensors_s* H = new (std::nothrow) oba_tensors_s();
+  if (!H) return OBA_ENOMEM;
+  H->device = L->device;
+  H->g_dtype = g_dtype;
+  H->T = T;
+  H->n = n;
+  hipError_t e = hipMalloc(&H->dev, bytes);
+  if (e != hipSuccess) {
+    delete H;
+    return OBA_ENOMEM;
+  }
+  char* base = static_cast<char*>(H->dev);
+  const std::pair<const void*, size_t> parts[] = {
+      {off.data(), b_off}, {g_ptrs, b_g}, {x_ptrs, b_x}, {bw.data(), b_bw}, {bs.data(), b_bs}};
+  size_t at = 0;
+  for (const auto& pr : parts) {
+    if (pr.second) e = hipMemcpy(base + at, pr.first, pr.second, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(H->dev);
+      delete H;
+      return hip_fail(e, "hipMemcpy (tensor tables)");
+    }
+    at += pr.second;
+  }
+  oba::TList tl{};
+  tl.off = reinterpret_cast<const int64_t*>(base);
+  tl.g = reinterpret_cast<const void* const*>(base + b_off);
+  tl.x = reinterpret_cast<float* const*>(base + b_off + b_g);
+  tl.T = T;
+  H->tl_w = tl;
+  H->tl_w.blk_first = reinterpret_cast<const int32_t*>(base + b_off + b_g + b_x);
+  H->tl_s = tl;
+  H->tl_s.blk_first = reinterpret_cast<const int32_t*>(base + b_off + b_g + b_x + b_bw);
+  *out = H;
+  return OBA_OK;
+}
+
+void oba_tensors_destroy(oba_tensors H) {
+  if (!H) return;
+  if (H->dev) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(H->dev);
+  }
+  delete H;
+}
+
+int oba_adam_warmup_step_listed(oba_layout L, oba_tensors H, float* m, float* v, double lr,
+                                double beta1, double beta2, double eta, double bc1, double bc2,
+                                double* vnorm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  OBA_TRY(check_layout(L));
+  if (!H || H->device != L->device || H->n != L->plan.n) return OBA_EINVAL;
+  if (!is_finite(lr) || !beta_ok(beta1) || !beta_ok(beta2) || !is_finite(eta) || eta < 0.0 ||
+      !is_finite(bc1) || bc1 <= 0.0 || !is_finite(bc2) || bc2 <= 0.0)
+    return OBA_EINVAL;
+  OBA_TRY(check_buf(m, 16));
+  OBA_TRY(check_buf(v, 16));
+  if (vnorm) {
+    OBA_TRY(check_buf(vnorm, 8));
+    OBA_TRY(check_buf(ws, 8));
+    if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
+  }
+  oba::AdamCoef C{(float)lr, (float)beta1, (float)(1.0 - beta1), (float)beta2,
+                  (float)(1.0 - beta2), (float)eta, (float)bc1, (float)bc2};
+  const oba::Geo G = L->geo;
+  double* part = static_cast<double*>(ws);
+  return launch("adam_warmup", stream, [&] {
+    oba::launch_adam_warmup_listed(G, H->tl_s, H->g_dtype == OBA_F16, m, v, C, part, vnorm,
+                                   stream);
+  });
+}
+
+int oba_compress_deferred_listed(oba_layout L, oba_tensors H, const float* m,
+                                 const uint64_t* sbits_prev, const float* sscale_prev, float* c,
+                                 uint64_t* wbits, float* wscale, double beta1, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  OBA_TRY(check_layout(L));
+  if (!H || H->device != L->device || H->n != L->plan.n) return OBA_EINVAL;
+  if (!beta_ok(beta1)) return OBA_EINVAL;
+  const bool implicit_m = !m;
+  if (implicit_m != (sbits_prev != nullptr) || implicit_m != (sscale_prev != nullptr))
+    return OBA_EINVAL;
+  if (implicit_m) {
+    OBA_TRY(check_buf(sbits_prev, 8));
+    OBA_TRY(check_buf(sscale_prev, 4));
+  } else {
+    OBA_TRY(check_buf(m, 16));
+  }
+  OBA_TRY(check_buf(c, 16));
+  OBA_TRY(check_buf(wbits, 8));
+  OBA_TRY(check_buf(wscale, 4));
+  OBA_TRY(check_buf(ws, 8));
+  if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
+  const oba::Geo G = L->geo_w;
+  double* part = static_cast<double*>(ws);
+  const float b1 = (float)beta1, omb1 = (float)(1.0 - beta1);
+  uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
+  const oba::MomSrc ms{reinterpret_cast<const uint8_t*>(sbits_prev), sscale_prev, L->tau_w};
+  OBA_TRY(launch("compress_deferred", stream, [&] {
+    oba::launch_compress_deferred_listed(G, H->tl_w, H->g_dtype == OBA_F16, m, c, wbytes,
+                                         L->sig_w, part, wscale, b1, omb1, ms, stream);
+  }));
+  return launch("finalize_scales", stream,
+                [&] { oba::launch_finalize(part, G.n, L->sig_w, wscale, stream); });
+}
+
+int oba_decompress_update_listed(oba_layout L, oba_tensors H, const uint64_t* sbits,
+                                 const float* sscale, const float* denom, float* m, double lr,
+                                 hipStream_t stream) {
+  OBA_TRY(check_layout(L));
+  if (!H || H->device != L->device || H->n != L->plan.n) return OBA_EINVAL;
+  if (!is_finite(lr)) return OBA_EINVAL;
+  OBA_TRY(check_buf(sbits, 8));
+  OBA_TRY(check_buf(sscale, 4));
+  OBA_TRY(check_buf(denom, 16));
+  if (m) OBA_TRY(check_buf(m, 16));
+  const oba::Geo G = L->geo_w;
+  const uint8_t* sbytes = reinterpret_cast<const uint8_t*>(sbits);
+  return launch("decompress_update", stream, [&] {
+    oba::launch_decompress_update_listed(G, H->tl_w, sbytes, sscale, denom, m, L->tau_w,
+                                         (float)lr, stream);
+  });
 }
 
 int oba_plateau_init(oba_plateau* p, int32_t window, double rtol, int32_t min_steps) {

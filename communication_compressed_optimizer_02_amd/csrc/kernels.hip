@@ -119,6 +119,74 @@ __device__ __forceinline__ void load8(const T* __restrict__ p, const Quads& q, i
     load_tail(p, q, d, v);
 }
 
+// ---- tensor lists: each quad's tensor and its offset inside it ------------
+struct LaneT {
+  int64_t relA, relB;  // quad offsets inside their tensors
+  int32_t tA, tB;      // tensors of the quads
+  bool okA, okB;       // quad inside [0, d)
+};
+
+// Tensor of coordinate k, walking forward from t (k >= off[t]; k < d).
+__device__ __forceinline__ int32_t tensor_walk(const int64_t* __restrict__ off, int32_t t,
+                                               int64_t k) {
+  while (off[t + 1] <= k) ++t;
+  return t;
+}
+
+// The lane's quads for a span starting in tensor t0 (quads past d: ok = false).
+__device__ __forceinline__ LaneT lane_tensors(const TList& tl, int32_t t0, const Quads& q,
+                                              int64_t d) {
+  LaneT lt;
+  lt.okA = q.kA < d;
+  lt.okB = q.kB < d;
+  lt.tA = lt.okA ? tensor_walk(tl.off, t0, q.kA) : t0;
+  lt.tB = lt.okB ? tensor_walk(tl.off, lt.tA, q.kB) : lt.tA;
+  lt.relA = q.kA - tl.off[lt.tA];
+  lt.relB = q.kB - tl.off[lt.tB];
+  return lt;
+}
+
+__device__ __forceinline__ void load_quad(const float* __restrict__ p, bool ok, float* v) {
+  if (ok) {
+    const f32x4 a = ldv(reinterpret_cast<const f32x4*>(p));
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  } else {
+    v[0] = v[1] = v[2] = v[3] = 0.0f;
+  }
+}
+
+__device__ __forceinline__ void load_quad(const uint16_t* __restrict__ p, bool ok, float* v) {
+  if (ok) {
+    const u32x2 a = ldv(reinterpret_cast<const u32x2*>(p));
+    v[0] = half_bits_to_float(a.x & 0xFFFFu);
+    v[1] = half_bits_to_float(a.x >> 16);
+    v[2] = half_bits_to_float(a.y & 0xFFFFu);
+    v[3] = half_bits_to_float(a.y >> 16);
+  } else {
+    v[0] = v[1] = v[2] = v[3] = 0.0f;
+  }
+}
+
+// Row `row` of a listed gradient (rows are workers) at the lane's quads.
+template <typename GT>
+__device__ __forceinline__ void load_listed(const TList& tl, int64_t row, const LaneT& lt,
+                                            float (&v)[8]) {
+  const GT* const* tab = reinterpret_cast<const GT* const*>(tl.g) + row * tl.T;
+  load_quad(tab[lt.tA] + lt.relA, lt.okA, v);
+  load_quad(tab[lt.tB] + lt.relB, lt.okB, v + 4);
+}
+
+__device__ __forceinline__ void load_listed_x(const TList& tl, const LaneT& lt, float (&v)[8]) {
+  load_quad(tl.x[lt.tA] + lt.relA, lt.okA, v);
+  load_quad(tl.x[lt.tB] + lt.relB, lt.okB, v + 4);
+}
+
+__device__ __forceinline__ void store_listed_x(const TList& tl, const LaneT& lt,
+                                               const float (&v)[8]) {
+  if (lt.okA) stv(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(tl.x[lt.tA] + lt.relA));
+  if (lt.okB) stv(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4*>(tl.x[lt.tB] + lt.relB));
+}
+
 __device__ __forceinline__ void store8(float* __restrict__ p, const Quads& q, int64_t d,
                                        bool full, const float (&v)[8]) {
   if (full) {
@@ -301,16 +369,18 @@ __device__ __forceinline__ float residual(float c, float s) { return (c < 0.0f) 
 // are loaded together (NB = n for n <= 8; larger n loops over groups of 8),
 // after m, v and x, so that all of a span's loads are in flight at once.
 // ===========================================================================
-template <typename GT, int NB, bool NORM>
+template <typename GT, int NB, bool NORM, bool TL>
 __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restrict__ g,
                                                         float* __restrict__ x,
                                                         float* __restrict__ m,
                                                         float* __restrict__ v, AdamCoef C,
-                                                        double* __restrict__ part) {
+                                                        double* __restrict__ part, TList tl) {
   __shared__ double lds[kWaves];
   double acc[1] = {0.0};
   const int64_t s_lo = dspan(G.S, G.nblk, blockIdx.x);
   const int64_t s_hi = dspan(G.S, G.nblk, blockIdx.x + 1);
+  int32_t tcur = 0;  // tensor cursor (tensor lists: x and g listed)
+  if constexpr (TL) tcur = tl.blk_first[blockIdx.x];
   const float nf = (float)G.n;
   const bool pow2 = (G.n & (G.n - 1)) == 0;
   const float inv_n = 1.0f / nf;
@@ -319,17 +389,29 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
     const Quads q = quads(lo);
     const bool full = lo + kSpan <= G.d;
     float sum[8], mv[8], vv[8], xv[8];
+    LaneT lt{};
+    if constexpr (TL) {
+      tcur = tensor_walk(tl.off, tcur, lo);
+      lt = lane_tensors(tl, tcur, q, G.d);
+    }
     load8(m, q, G.d, full, mv);
     load8(v, q, G.d, full, vv);
-    load8(x, q, G.d, full, xv);
+    if constexpr (TL)
+      load_listed_x(tl, lt, xv);
+    else
+      load8(x, q, G.d, full, xv);
 #pragma unroll
     for (int j = 0; j < 8; ++j) sum[j] = 0.0f;
     for (int32_t i0 = 0; i0 < G.n; i0 += NB) {  // one pass when n <= NB
       // rows past n are clamped to a valid row and their terms skipped
       float gv[NB][8];
 #pragma unroll
-      for (int u = 0; u < NB; ++u)
-        load8(g + (int64_t)min(i0 + u, G.n - 1) * G.ld, q, G.d, full, gv[u]);
+      for (int u = 0; u < NB; ++u) {
+        if constexpr (TL)
+          load_listed<GT>(tl, min(i0 + u, G.n - 1), lt, gv[u]);
+        else
+          load8(g + (int64_t)min(i0 + u, G.n - 1) * G.ld, q, G.d, full, gv[u]);
+      }
 #pragma unroll
       for (int u = 0; u < NB; ++u)
         if (i0 + u < G.n) {
@@ -348,7 +430,10 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
     }
     store8(m, q, G.d, full, mv);
     store8(v, q, G.d, full, vv);
-    store8(x, q, G.d, full, xv);
+    if constexpr (TL)
+      store_listed_x(tl, lt, xv);
+    else
+      store8(x, q, G.d, full, xv);
     if (NORM) acc[0] += sumsq8(vv);  // coordinates past d read 0 and give v = 0
   }
   if (NORM) flush_rows<1>(acc, 1, part + blockIdx.x, 0, lds);
@@ -433,14 +518,14 @@ constexpr int kWorkerBatch = OBA_WORKER_BATCH;
 #define OBA_CMP_ATTR
 #endif
 
-template <typename GT, int NB, int MODE>
+template <typename GT, int NB, int MODE, bool TL>
 __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t i0, const GT* __restrict__ g,
                                                      float* __restrict__ m,  // read; written by kDeferredLocal
                                                      float* __restrict__ delta,
                                                      uint8_t* __restrict__ wbytes, SegDev sig,
                                                      double* __restrict__ part,
                                                      const float* __restrict__ wscale, float b1,
-                                                     float omb1, MomSrc ms) {
+                                                     float omb1, MomSrc ms, TList tl) {
   __shared__ double lds[kWaves * NB];
   const int32_t b = blockIdx.x;
   i0 += blockIdx.y * NB;  // this block's workers: [i0, i0 + NB)
@@ -448,6 +533,9 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
   const int32_t p_end = sig.blk_first[b + 1];
   int32_t p = sig.blk_first[b];
   int64_t p_hi = sig.phi[p];
+  static_assert(!TL || MODE >= kDeferred, "tensor lists: deferred passes only");
+  int32_t tcur = 0;  // tensor cursor (tensor lists)
+  if constexpr (TL) tcur = tl.blk_first[b];
   // kDeferredM: cursor over the server segments (on this grid) for sbar
   int32_t pt = 0, pt_end = 0;
   int64_t pt_hi = 0;
@@ -469,6 +557,11 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
     const bool full = lo + kSpan <= G.d;
     int32_t jseg[8];
     if (MODE != kNorm && !uniform) lane_segs(sig.off, sig.pseg[p], q, G.d, jseg);
+    LaneT lt{};
+    if constexpr (TL) {
+      tcur = tensor_walk(tl.off, tcur, lo);
+      lt = lane_tensors(tl, tcur, q, G.d);
+    }
     // every load of the span first (all NB workers), then the arithmetic
     float mv[8];
     if (MODE == kDeferredM) {  // m = sbar*sign from the last server message
@@ -513,7 +606,10 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
         for (int u = 0; u < NBB; ++u) {
           if (ib + u >= NB) break;
           const int64_t row = (int64_t)(i0 + ib + u) * G.ld;
-          load_full(g + row, q, gv[u]);
+          if constexpr (TL)
+            load_listed<GT>(tl, i0 + ib + u, lt, gv[u]);
+          else
+            load_full(g + row, q, gv[u]);
           load_full(delta + row, q, c[u]);
           if (MODE == kDeferredLocal) load_full(m + row, q, ml[u]);
         }
@@ -522,7 +618,10 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
         for (int u = 0; u < NBB; ++u) {
           if (ib + u >= NB) break;
           const int64_t row = (int64_t)(i0 + ib + u) * G.ld;
-          load_tail(g + row, q, G.d, gv[u]);
+          if constexpr (TL)
+            load_listed<GT>(tl, i0 + ib + u, lt, gv[u]);
+          else
+            load_tail(g + row, q, G.d, gv[u]);
           load_tail(delta + row, q, G.d, c[u]);
           if (MODE == kDeferredLocal) load_tail(m + row, q, G.d, ml[u]);
         }
@@ -843,15 +942,17 @@ __global__ __launch_bounds__(kBlock) OBA_SRV_ATTR void k_server_p1(Geo G, const 
 // Decompress + precondition + update: m_hat = sbar*sign; m = m_hat (when
 // WRITE_M); x = x - (lr*m_hat)/denom (when UPDATE_X).  Grid: the worker grid.
 // ===========================================================================
-template <bool WRITE_M, bool UPDATE_X>
+template <bool WRITE_M, bool UPDATE_X, bool TL>
 __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
                                                               const uint8_t* __restrict__ sbytes,
                                                               const float* __restrict__ sscale,
                                                               const float* __restrict__ denom,
                                                               float* __restrict__ m,
                                                               float* __restrict__ x, SegDev tau,
-                                                              float lr) {
+                                                              float lr, TList tl) {
   const int32_t b = blockIdx.x;
+  int32_t tcur = 0;  // tensor cursor (tensor lists: x listed)
+  if constexpr (TL) tcur = tl.blk_first[b];
   const int64_t s_lo = dspan(G.S, G.nblk, b), s_hi = dspan(G.S, G.nblk, b + 1);
   const int32_t p_end = tau.blk_first[b + 1];
   int32_t p = tau.blk_first[b];
@@ -864,9 +965,17 @@ __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
     float sv[8], dv[8], xv[8], mh[8];
     const uint32_t bits = full ? load_sign_bits<true, OBA_PAIRS_UPD>(sbytes, q, G.d)
                                : load_sign_bits<false, OBA_PAIRS_UPD>(sbytes, q, G.d);
+    LaneT lt{};
+    if constexpr (TL) {
+      tcur = tensor_walk(tl.off, tcur, lo);
+      lt = lane_tensors(tl, tcur, q, G.d);
+    }
     if (UPDATE_X) {
       load8(denom, q, G.d, full, dv);
-      load8(x, q, G.d, full, xv);
+      if constexpr (TL)
+        load_listed_x(tl, lt, xv);
+      else
+        load8(x, q, G.d, full, xv);
     }
     if (hi <= p_hi) {
       const float s_ = sscale[tau.pseg[p]];
@@ -884,7 +993,12 @@ __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
       if (UPDATE_X) xv[j] = xv[j] - (lr * mh[j]) / dv[j];
     }
     if (WRITE_M) store8(m, q, G.d, full, mh);
-    if (UPDATE_X) store8(x, q, G.d, full, xv);
+    if (UPDATE_X) {
+      if constexpr (TL)
+        store_listed_x(tl, lt, xv);
+      else
+        store8(x, q, G.d, full, xv);
+    }
     while (p < p_end && p_hi <= hi) {
       if (++p < p_end) p_hi = tau.phi[p];
     }
@@ -896,12 +1010,12 @@ __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
 // ===========================================================================
 void launch_norm_finalize(const double* part, int32_t n, double* out, hipStream_t st);
 
-template <typename GT, bool NORM>
+template <typename GT, bool NORM, bool TL>
 static void launch_warmup_nb(const Geo& G, const void* g, float* x, float* m, float* v,
-                             const AdamCoef& C, double* part, hipStream_t st) {
-#define OBA_WARMUP_LAUNCH(NB)                                                                \
-  hipLaunchKernelGGL((k_adam_warmup<GT, NB, NORM>), dim3(G.nblk), dim3(kBlock), 0, st, G,    \
-                     static_cast<const GT*>(g), x, m, v, C, part)
+                             const AdamCoef& C, double* part, const TList& tl, hipStream_t st) {
+#define OBA_WARMUP_LAUNCH(NB)                                                                 \
+  hipLaunchKernelGGL((k_adam_warmup<GT, NB, NORM, TL>), dim3(G.nblk), dim3(kBlock), 0, st, G, \
+                     static_cast<const GT*>(g), x, m, v, C, part, tl)
   switch (G.n) {
     case 1: OBA_WARMUP_LAUNCH(1); break;
     case 2: OBA_WARMUP_LAUNCH(2); break;
@@ -915,14 +1029,15 @@ static void launch_warmup_nb(const Geo& G, const void* g, float* x, float* m, fl
 #undef OBA_WARMUP_LAUNCH
 }
 
-template <typename GT>
+template <typename GT, bool TL>
 static void launch_warmup(const Geo& G, const void* g, float* x, float* m, float* v,
-                          const AdamCoef& C, double* part, double* vnorm, hipStream_t st) {
+                          const AdamCoef& C, double* part, double* vnorm, const TList& tl,
+                          hipStream_t st) {
   if (!vnorm) {
-    launch_warmup_nb<GT, false>(G, g, x, m, v, C, nullptr, st);
+    launch_warmup_nb<GT, false, TL>(G, g, x, m, v, C, nullptr, tl, st);
     return;
   }
-  launch_warmup_nb<GT, true>(G, g, x, m, v, C, part, st);
+  launch_warmup_nb<GT, true, TL>(G, g, x, m, v, C, part, tl, st);
   launch_norm_finalize(part, G.nblk, vnorm, st);
 }
 
@@ -933,9 +1048,17 @@ void launch_norm_finalize(const double* part, int32_t n, double* out, hipStream_
 void launch_adam_warmup(const Geo& G, const void* g, bool f16, float* x, float* m, float* v,
                         const AdamCoef& C, double* part, double* vnorm, hipStream_t st) {
   if (f16)
-    launch_warmup<uint16_t>(G, g, x, m, v, C, part, vnorm, st);
+    launch_warmup<uint16_t, false>(G, g, x, m, v, C, part, vnorm, TList{}, st);
   else
-    launch_warmup<float>(G, g, x, m, v, C, part, vnorm, st);
+    launch_warmup<float, false>(G, g, x, m, v, C, part, vnorm, TList{}, st);
+}
+
+void launch_adam_warmup_listed(const Geo& G, const TList& tl, bool f16, float* m, float* v,
+                               const AdamCoef& C, double* part, double* vnorm, hipStream_t st) {
+  if (f16)
+    launch_warmup<uint16_t, true>(G, nullptr, nullptr, m, v, C, part, vnorm, tl, st);
+  else
+    launch_warmup<float, true>(G, nullptr, nullptr, m, v, C, part, vnorm, tl, st);
 }
 
 void launch_freeze(const Geo& G, const float* v, float* denom, float eta, float bc2,
@@ -943,14 +1066,14 @@ void launch_freeze(const Geo& G, const float* v, float* denom, float eta, float 
   hipLaunchKernelGGL(k_freeze, dim3(G.nblk), dim3(kBlock), 0, st, G, v, denom, eta, bc2);
 }
 
-template <typename GT, int NB, int MODE>
+template <typename GT, int NB, int MODE, bool TL>
 static void launch_cmp(const Geo& G, int32_t i0, int groups, const void* g, const float* m,
                        float* delta, uint8_t* wbytes, const SegDev& sig, double* part,
                        const float* wscale, float b1, float omb1, const MomSrc& ms,
-                       hipStream_t st) {
-  hipLaunchKernelGGL((k_compress<GT, NB, MODE>), dim3(G.nblk, groups), dim3(kBlock), 0, st, G,
-                     i0, static_cast<const GT*>(g), const_cast<float*>(m), delta, wbytes, sig,
-                     part, wscale, b1, omb1, ms);
+                       const TList& tl, hipStream_t st) {
+  hipLaunchKernelGGL((k_compress<GT, NB, MODE, TL>), dim3(G.nblk, groups), dim3(kBlock), 0, st,
+                     G, i0, static_cast<const GT*>(g), const_cast<float*>(m), delta, wbytes, sig,
+                     part, wscale, b1, omb1, ms, tl);
 }
 
 // Groups of GROUP workers per block, then one launch for the remainder.  A
@@ -968,14 +1091,16 @@ constexpr int kImplicitNB = OBA_IMPLICIT_NB;
 static_assert(kMaxNB >= 1 && kMaxNB <= 8 && kImplicitNB >= 1 && kImplicitNB <= 8,
               "worker groups hold 1 to 8 workers");
 
-template <typename GT, int MODE>
+template <typename GT, int MODE, bool TL>
 static void launch_cmp_n(const Geo& G, const void* g, const float* m, float* delta,
                          uint8_t* wbytes, const SegDev& sig, double* part, const float* wscale,
-                         float b1, float omb1, const MomSrc& ms, hipStream_t st) {
+                         float b1, float omb1, const MomSrc& ms, const TList& tl,
+                         hipStream_t st) {
   constexpr int GROUP = (MODE == kDeferredM || MODE == kDeferredLocal) ? kImplicitNB : kMaxNB;
   const int full = G.n / GROUP, rem = G.n % GROUP, i0 = full * GROUP;
 #define OBA_CMP(NB_, I0, GROUPS) \
-  launch_cmp<GT, NB_, MODE>(G, I0, GROUPS, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms, st)
+  launch_cmp<GT, NB_, MODE, TL>(G, I0, GROUPS, g, m, delta, wbytes, sig, part, wscale, b1, omb1, \
+                                ms, tl, st)
   if (full) OBA_CMP(GROUP, 0, full);
   switch (rem) {
     case 1: OBA_CMP(1, i0, 1); break;
@@ -990,14 +1115,17 @@ static void launch_cmp_n(const Geo& G, const void* g, const float* m, float* del
 #undef OBA_CMP
 }
 
-template <int MODE>
+template <int MODE, bool TL = false>
 static void launch_cmp_t(const Geo& G, const void* g, bool f16, const float* m, float* delta,
                          uint8_t* wbytes, const SegDev& sig, double* part, const float* wscale,
-                         float b1, float omb1, const MomSrc& ms, hipStream_t st) {
+                         float b1, float omb1, const MomSrc& ms, hipStream_t st,
+                         const TList& tl = TList{}) {
   if (f16)
-    launch_cmp_n<uint16_t, MODE>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms, st);
+    launch_cmp_n<uint16_t, MODE, TL>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms, tl,
+                                     st);
   else
-    launch_cmp_n<float, MODE>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms, st);
+    launch_cmp_n<float, MODE, TL>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms, tl,
+                                  st);
 }
 
 void launch_compress_norm(const Geo& G, const void* g, bool f16, const float* m,
@@ -1016,6 +1144,18 @@ void launch_compress_deferred(const Geo& G, const void* g, bool f16, const float
                              st);
   else
     launch_cmp_t<kDeferred>(G, g, f16, m, c, wbytes, sig, part, wscale_prev, b1, omb1, ms, st);
+}
+
+void launch_compress_deferred_listed(const Geo& G, const TList& tl, bool f16, const float* m,
+                                     float* c, uint8_t* wbytes, const SegDev& sig, double* part,
+                                     const float* wscale_prev, float b1, float omb1,
+                                     const MomSrc& ms, hipStream_t st) {
+  if (ms.sbytes)
+    launch_cmp_t<kDeferredM, true>(G, nullptr, f16, nullptr, c, wbytes, sig, part, wscale_prev,
+                                   b1, omb1, ms, st, tl);
+  else
+    launch_cmp_t<kDeferred, true>(G, nullptr, f16, m, c, wbytes, sig, part, wscale_prev, b1,
+                                  omb1, ms, st, tl);
 }
 
 void launch_compress_deferred_local(const Geo& G, const void* g, bool f16, float* m_local,
@@ -1088,17 +1228,28 @@ void launch_decompress_update(const Geo& G, const uint8_t* sbytes, const float* 
                               const float* denom, float* m, float* x, const SegDev& tau, float lr,
                               hipStream_t st) {
   if (m)
-    hipLaunchKernelGGL((k_decompress_update<true, true>), dim3(G.nblk), dim3(kBlock), 0, st, G,
-                       sbytes, sscale, denom, m, x, tau, lr);
+    hipLaunchKernelGGL((k_decompress_update<true, true, false>), dim3(G.nblk), dim3(kBlock), 0,
+                       st, G, sbytes, sscale, denom, m, x, tau, lr, TList{});
   else
-    hipLaunchKernelGGL((k_decompress_update<false, true>), dim3(G.nblk), dim3(kBlock), 0, st, G,
-                       sbytes, sscale, denom, m, x, tau, lr);
+    hipLaunchKernelGGL((k_decompress_update<false, true, false>), dim3(G.nblk), dim3(kBlock), 0,
+                       st, G, sbytes, sscale, denom, m, x, tau, lr, TList{});
+}
+
+void launch_decompress_update_listed(const Geo& G, const TList& tl, const uint8_t* sbytes,
+                                     const float* sscale, const float* denom, float* m,
+                                     const SegDev& tau, float lr, hipStream_t st) {
+  if (m)
+    hipLaunchKernelGGL((k_decompress_update<true, true, true>), dim3(G.nblk), dim3(kBlock), 0,
+                       st, G, sbytes, sscale, denom, m, nullptr, tau, lr, tl);
+  else
+    hipLaunchKernelGGL((k_decompress_update<false, true, true>), dim3(G.nblk), dim3(kBlock), 0,
+                       st, G, sbytes, sscale, denom, m, nullptr, tau, lr, tl);
 }
 
 void launch_server_momentum(const Geo& G, const uint8_t* sbytes, const float* sscale, float* m,
                             const SegDev& tau, hipStream_t st) {
-  hipLaunchKernelGGL((k_decompress_update<true, false>), dim3(G.nblk), dim3(kBlock), 0, st, G,
-                     sbytes, sscale, nullptr, m, nullptr, tau, 0.0f);
+  hipLaunchKernelGGL((k_decompress_update<true, false, false>), dim3(G.nblk), dim3(kBlock), 0, st,
+                     G, sbytes, sscale, nullptr, m, nullptr, tau, 0.0f, TList{});
 }
 
 }  // namespace oba

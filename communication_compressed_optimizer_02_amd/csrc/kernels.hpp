@@ -35,6 +35,18 @@ inline size_t partial_bytes(const SegDev& T, int32_t rows) {
   return al((size_t)T.n_pieces * rows * 8) + al((size_t)T.n_items * rows * 8);
 }
 
+// Model tensors given as a list (x and the gradient rows live in separate
+// allocations).  Tensor t covers flat coordinates [off[t], off[t+1]); every
+// length is a multiple of 4, so a lane's 4-coordinate quads never straddle
+// two tensors.
+struct TList {
+  const int64_t* off;        // [T+1]
+  const int32_t* blk_first;  // [nblk] tensor holding each block's first coordinate
+  const void* const* g;      // [n][T] gradient tensors (g dtype)
+  float* const* x;           // [T] parameter tensors
+  int32_t T;
+};
+
 // Momentum source of the deferred worker pass: null sbytes = read m;
 // otherwise m = sbar*sign from the last packed server bits and scales, with
 // the server segments cut on the worker pass's grid.
@@ -59,6 +71,17 @@ void launch_freeze(const Geo& G, const float* v, float* denom, float eta, float 
 void launch_compress_norm(const Geo& G, const void* g, bool f16, const float* m,
                           const float* delta, const SegDev& sig, double* part, float b1,
                           float omb1, hipStream_t st);
+// Tensor lists (x and g rows listed; everything else flat).  The listed
+// worker pass supports the deferred modes (m read, or implicit with ms).
+void launch_adam_warmup_listed(const Geo& G, const TList& tl, bool f16, float* m, float* v,
+                               const AdamCoef& C, double* part, double* vnorm, hipStream_t st);
+void launch_compress_deferred_listed(const Geo& G, const TList& tl, bool f16, const float* m,
+                                     float* c, uint8_t* wbytes, const SegDev& sig, double* part,
+                                     const float* wscale_prev, float b1, float omb1,
+                                     const MomSrc& ms, hipStream_t st);
+void launch_decompress_update_listed(const Geo& G, const TList& tl, const uint8_t* sbytes,
+                                     const float* sscale, const float* denom, float* m,
+                                     const SegDev& tau, float lr, hipStream_t st);
 // per-worker momentum: m_local [n][ld] in/out
 void launch_compress_deferred_local(const Geo& G, const void* g, bool f16, float* m_local,
                                     float* c, uint8_t* wbytes, const SegDev& sig, double* part,

@@ -105,4 +105,30 @@ int make_plan(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_w
   return kOk;
 }
 
+int tensor_offsets(const Plan& P, int32_t T, const int64_t* lengths, std::vector<int64_t>* off) {
+  if (!lengths || T < 1 || T > INT32_MAX - 1) return kEInval;
+  try {
+    off->assign((size_t)T + 1, 0);
+  } catch (...) {
+    return kENoMem;
+  }
+  for (int32_t t = 0; t < T; ++t) {
+    const int64_t len = lengths[t];
+    if (len <= 0 || len % 4 != 0 || len > P.d - (*off)[t]) return kEInval;
+    (*off)[t + 1] = (*off)[t] + len;
+  }
+  return (*off)[T] == P.d ? kOk : kEInval;
+}
+
+void tensor_blocks(const Plan& P, int32_t nblk, const std::vector<int64_t>& off,
+                   std::vector<int32_t>* first) {
+  first->assign((size_t)nblk, 0);
+  int32_t t = 0;
+  for (int32_t b = 0; b < nblk; ++b) {
+    const int64_t k = span_begin(P.S, nblk, b) * kSpan;
+    while (off[t + 1] <= k) ++t;
+    (*first)[b] = t;
+  }
+}
+
 }  // namespace oba

@@ -78,4 +78,11 @@ inline int64_t span_begin(int64_t S, int32_t nblk, int32_t b) {
   return (int64_t)b * S / nblk;
 }
 
+// Tensor lists: checks lengths (each a positive multiple of 4, summing to d)
+// and fills off [T+1] and, for a grid of nblk blocks, the tensor holding
+// each block's first coordinate.
+int tensor_offsets(const Plan& P, int32_t T, const int64_t* lengths, std::vector<int64_t>* off);
+void tensor_blocks(const Plan& P, int32_t nblk, const std::vector<int64_t>& off,
+                   std::vector<int32_t>* first);
+
 }  // namespace oba

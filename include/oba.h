@@ -278,6 +278,45 @@ int oba_server_reduce_recompress_deferred(oba_layout layout, const uint64_t* wbi
 int oba_deferred_errors(oba_layout layout, const float* c, const float* wscale, const float* a,
                         const float* sscale, float* delta, float* eps, hipStream_t stream);
 
+/* ---- tensor lists ----------------------------------------------------------
+ * The parameters x and the n workers' gradients may live in T separate
+ * tensors instead of flat buffers ([AIMech] definition: x and g are the
+ * model's parameters and gradients; [Tang] 11: the implementation works per
+ * tensor chunk).  Tensor t covers the flat coordinates [o_t, o_t + len_t),
+ * o_0 = 0, o_{t+1} = o_t + len_t, and the lengths sum to the layout's d.
+ * Every length must be a positive multiple of 4.  Segment tables, messages,
+ * scales and all other state (m, v, denom, c, a) keep the flat coordinates.
+ *
+ * x_ptrs: host array [T] of device pointers to binary32 tensors (16-byte
+ * aligned); g_ptrs: host array [n][T] of device pointers, row i = worker i
+ * (16-byte aligned for OBA_F32, 8 for OBA_F16).  The tables are copied to
+ * the device at creation: the tensors must stay allocated (and at the same
+ * addresses) while the handle is used.  *out is set only on success. */
+typedef struct oba_tensors_s* oba_tensors;
+int oba_tensors_create(oba_tensors* out, oba_layout layout, int32_t n_tensors,
+                       const int64_t* lengths, float* const* x_ptrs, const void* const* g_ptrs,
+                       int g_dtype);
+/* Frees the device tables (synchronises the device first). */
+void oba_tensors_destroy(oba_tensors tensors);
+
+/* oba_adam_warmup_step (vnorm == NULL) or oba_adam_warmup_step_vnorm on the
+ * listed x and g; m, v: [d] flat. */
+int oba_adam_warmup_step_listed(oba_layout layout, oba_tensors tensors, float* m, float* v,
+                                double lr, double beta1, double beta2, double eta, double bc1,
+                                double bc2, double* vnorm, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/* oba_compress_deferred on the listed gradients (same momentum sources). */
+int oba_compress_deferred_listed(oba_layout layout, oba_tensors tensors, const float* m,
+                                 const uint64_t* sbits_prev, const float* sscale_prev, float* c,
+                                 uint64_t* wbits, float* wscale, double beta1, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/* oba_decompress_update on the listed x (m may be NULL as there). */
+int oba_decompress_update_listed(oba_layout layout, oba_tensors tensors, const uint64_t* sbits,
+                                 const float* sscale, const float* denom, float* m, double lr,
+                                 hipStream_t stream);
+
 /* ---- kernel timing (measurement aid) ---------------------------------------
  * While enabled, every kernel the library launches is bracketed by two HIP
  * events on the launch stream (up to `capacity` launches are kept).
@@ -286,7 +325,8 @@ int oba_deferred_errors(oba_layout layout, const float* c, const float* wscale, 
  * equals `kernel` ("compress_p1", "compress_p2", "finalize_scales",
  * "server_p1", "server_p2", "decompress_update", "adam_warmup",
  * "freeze_variance", "compress_deferred", "server_deferred",
- * "deferred_errors", "server_momentum", "compress_deferred_local"); "adam_warmup"
+ * "deferred_errors", "server_momentum", "compress_deferred_local"; the listed
+ * entry points record under the names of their flat forms); "adam_warmup"
  * includes the norm
  * kernel of oba_adam_warmup_step_vnorm.  oba_timing_reset drops all records. */
 int oba_timing_enable(int on, int32_t capacity);

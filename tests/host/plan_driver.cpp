@@ -5,7 +5,9 @@
 // server segments on the server grid and the server segments on the worker
 // grid: "T <n_pieces> <n_seg>", one
 // "P lo hi seg" line per piece, "B" + blk_first, "S" + seg_first, "I" +
-// item_q, "J" + seg_item (the last two empty for one-stage sums).  Built by the test suite with the host compiler and
+// item_q, "J" + seg_item (the last two empty for one-stage sums).  With a
+// tensor list appended ("nt l_0 .. l_{nt-1}"): "TO <status>", then for the
+// worker grid and the server grid "TB" + the first tensor of each block.  Built by the test suite with the host compiler and
 // sanitizers; it calls nothing of HIP.
 #include <cstdio>
 #include <cstdlib>
@@ -48,5 +50,23 @@ int main(int argc, char** argv) {
   dump(P.wp_s, nw);
   dump(P.sp, ns);
   dump(P.sp_w, ns);
+  // optional tensor list: nt l_0 .. l_{nt-1}
+  if (a < argc) {
+    const int nt = (int)next();
+    std::vector<int64_t> len(nt > 0 ? nt : 1);
+    for (int t = 0; t < nt; ++t) len[t] = next();
+    std::vector<int64_t> off;
+    const int trc = oba::tensor_offsets(P, nt, len.data(), &off);
+    std::printf("TO %d\n", trc);
+    if (trc == 0) {
+      for (int32_t nb : {P.nblk_w, P.nblk}) {
+        std::vector<int32_t> first;
+        oba::tensor_blocks(P, nb, off, &first);
+        std::printf("TB");
+        for (int v : first) std::printf(" %d", v);
+        std::printf("\n");
+      }
+    }
+  }
   return 0;
 }

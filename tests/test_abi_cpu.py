@@ -223,3 +223,41 @@ def test_plateau_test_rejects_bad_arguments():
     assert lib.oba_plateau_observe(None, 1.0) == -1
     assert lib.oba_plateau_observe(P(s), 1.0) == 0
     assert s.steps == 1
+
+
+def run_tensors(exe, d, n, lengths):
+    args = [exe, str(d), str(n), str(binding.default_ld(d)), "1", "0", str(d), "1", "0", str(d),
+            str(len(lengths)), *map(str, lengths)]
+    out = subprocess.run(args, check=True, capture_output=True, text=True).stdout.split("\n")
+    i = next(k for k, line in enumerate(out) if line.startswith("TO "))
+    rc = int(out[i].split()[1])
+    if rc:
+        return rc, None, None
+    _, dd, W, S, nblk, nblk_w = out[1].split()
+    firsts = [list(map(int, out[i + 1 + k].split()[1:])) for k in range(2)]
+    return 0, (int(S), int(nblk_w), int(nblk)), firsts
+
+
+def test_tensor_list_block_tables(driver):
+    rng = np.random.default_rng(17)
+    cases = [[4], [8, 4, 2048, 2052], [1600] * 7 + [4800, 12, 100_000]]
+    for _ in range(6):
+        cases.append([4 * int(x) for x in rng.integers(1, 3000, size=rng.integers(1, 60))])
+    for lengths in cases:
+        d = sum(lengths)
+        rc, (S, nblk_w, nblk), firsts = run_tensors(driver, d, 3, lengths)
+        assert rc == 0
+        off = np.concatenate([[0], np.cumsum(lengths)])
+        for nb, first in zip((nblk_w, nblk), firsts):
+            assert len(first) == nb
+            for b, t in enumerate(first):
+                k = (b * S // nb) * SPAN
+                assert off[t] <= k < off[t + 1]
+
+
+def test_tensor_list_rejects_bad_lengths(driver):
+    assert run_tensors(driver, 12, 2, [4, 6, 2])[0] == -1   # not a multiple of 4
+    assert run_tensors(driver, 12, 2, [4, 4])[0] == -1      # does not reach d
+    assert run_tensors(driver, 12, 2, [4, 0, 8])[0] == -1   # empty tensor
+    assert run_tensors(driver, 12, 2, [8, 8])[0] == -1      # past d
+    assert run_tensors(driver, 12, 2, [12])[0] == 0

@@ -1,0 +1,141 @@
+"""GPU tests of the tensor-list boundary (oba_tensors_*, *_listed): the
+parameters and the workers' gradients live in separate tensors; every other
+buffer stays flat.  The listed kernels perform the flat kernels' arithmetic
+on other addresses, so from the same inputs they must give bitwise the flat
+path's results."""
+import sys
+
+import numpy as np
+import pytest
+
+from gpu_common import B1, B2, ETA, LR, cut_table, torch
+from communication_compressed_optimizer_02_amd import binding as oba
+from communication_compressed_optimizer_02_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def split(flat, lengths):
+    """Separate allocations holding the pieces of a flat tensor."""
+    out, at = [], 0
+    for n in lengths:
+        out.append(flat[at:at + n].clone())
+        at += n
+    return out
+
+
+def same(a, b, what):
+    assert torch().equal(a.view(torch().int32) if a.dtype == torch().float32 else a,
+                         b.view(torch().int32) if b.dtype == torch().float32 else b), what
+
+
+def run_pair(L, lengths, gdt, steps, seed, sseg_cut=False):
+    t = torch()
+    d, n = L.d, L.n
+    gen = synth.device_generator(seed)
+    F = oba.State(L, gdt)  # flat path
+    F.x.normal_(0.0, 0.02, generator=gen)
+    xs = split(F.x, lengths)
+    gs = [[t.empty(k, dtype=F.g.dtype, device="cuda") for k in lengths] for _ in range(n)]
+    TL = oba.TensorList(L, xs, gs)
+    M = {nm: t.zeros_like(getattr(F, nm)) for nm in ("m", "v", "denom", "delta", "eps",
+                                                      "wbits", "wscale", "sbits", "sscale")}
+    vf = t.zeros(1, dtype=t.float64, device="cuda")
+    vl = t.zeros(1, dtype=t.float64, device="cuda")
+
+    def fill_grads():
+        F.g[:, :d].normal_(0.0, 1.0, generator=gen)
+        for i in range(n):
+            at = 0
+            for k, g in zip(lengths, gs[i]):
+                g.copy_(F.g[i, at:at + k])
+                at += k
+
+    def gathered_x():
+        return t.cat(xs)
+
+    for step in range(3):  # warm-up, with the variance norm
+        fill_grads()
+        F.warmup(LR, B1, B2, ETA, g=F.g, vnorm=vf)
+        oba.adam_warmup_step_listed(L, TL, M["m"], M["v"], LR, B1, B2, ETA, vnorm=vl)
+        t.cuda.synchronize()
+        same(F.m, M["m"], f"m, warm-up {step}")
+        same(F.v, M["v"], f"v, warm-up {step}")
+        same(F.x, gathered_x(), f"x, warm-up {step}")
+        assert float(vf.item()) == float(vl.item())
+    F.freeze(ETA)
+    oba.freeze_variance(L, M["v"], M["denom"], ETA)
+    m_implicit = False
+    for step in range(steps):
+        fill_grads()
+        F.step_deferred(B1, LR)
+        if m_implicit:
+            oba.compress_deferred_listed(L, TL, None, M["delta"], M["wbits"], M["wscale"], B1,
+                                         M["sbits"], M["sscale"])
+        else:
+            oba.compress_deferred_listed(L, TL, M["m"], M["delta"], M["wbits"], M["wscale"], B1)
+        oba.server_reduce_recompress_deferred(L, M["wbits"], M["wscale"], M["eps"], M["sbits"],
+                                              M["sscale"])
+        oba.decompress_update_listed(L, TL, M["sbits"], M["sscale"], M["denom"], None, LR)
+        m_implicit = True
+        t.cuda.synchronize()
+        for nm in ("wbits", "wscale", "sbits", "sscale", "eps"):
+            same(getattr(F, nm), M[nm], f"{nm}, step {step}")
+        same(F.delta[:, :d], M["delta"][:, :d], f"c, step {step}")
+        same(F.x, gathered_x(), f"x, step {step}")
+    TL.close()
+
+
+@pytest.mark.parametrize("lengths,n,gdt", [
+    ([4], 2, "f32"),
+    ([8, 4, 2048, 2052, 1600, 12], 3, "f16"),
+    ([1600] * 7 + [4800, 12, 100_000, 4], 8, "f32"),
+    ("random", 5, "f16"),
+])
+def test_listed_path_is_bitwise_the_flat_path(lengths, n, gdt):
+    rng = np.random.default_rng(23)
+    if lengths == "random":
+        lengths = [4 * int(k) for k in rng.integers(1, 40_000, size=57)]
+    d = sum(lengths)
+    say(f"[tensor list] T={len(lengths)} d={d} n={n} g={gdt}")
+    L = oba.Layout(d, n, synth.whole(d), cut_table(rng, d, 3))
+    run_pair(L, lengths, gdt, steps=4, seed=d)
+    L.close()
+
+
+def test_listed_path_rejects_bad_tensors():
+    t = torch()
+    L = oba.Layout(16, 2, synth.whole(16), synth.even_shards(16, 2))
+    x = [t.zeros(8, device="cuda"), t.zeros(8, device="cuda")]
+    g = [[t.zeros(8, device="cuda"), t.zeros(8, device="cuda")] for _ in range(2)]
+    with pytest.raises(ValueError):
+        oba.TensorList(L, x, g[:1])  # one row short
+    with pytest.raises(oba.ObaError):
+        oba.TensorList(L, [x[0]], [[g[0][0]], [g[1][0]]])  # lengths do not reach d
+    odd = t.zeros(9, device="cuda")[1:]  # 4-byte aligned only
+    with pytest.raises(oba.ObaError):
+        oba.TensorList(L, [odd, x[1]], g)
+    TL = oba.TensorList(L, x, g)
+    L2 = oba.Layout(16, 3, synth.whole(16), synth.even_shards(16, 3))
+    m = t.zeros(16, device="cuda")
+    with pytest.raises(oba.ObaError):  # handle made for another worker count
+        oba.adam_warmup_step_listed(L2, TL, m, m.clone(), LR, B1, B2, ETA)
+    TL.close()
+    L.close()
+    L2.close()
+
+
+def test_gpt2_xl_tensor_list_full_size():
+    """The 388-tensor list at full size (the workload the boundary is for)."""
+    w = synth.workload("gpt2_xl")
+    lengths = [int(k) for k in synth.gpt2_xl_tensor_sizes()]
+    assert sum(lengths) == w.d
+    say(f"[tensor list full size] {w.name} T={len(lengths)} d={w.d} n={w.n}")
+    L = oba.Layout(w.d, w.n, w.wseg, w.sseg)
+    run_pair(L, lengths, w.g_dtype, steps=2, seed=w.seed)
+    L.close()
