@@ -556,11 +556,25 @@ int oba_tensors_create(oba_tensors* out, oba_layout L, int32_t n_tensors,
   } catch (...) {
     return OBA_ENOMEM;
   }
-  // layout of the allocation: off | g pointers | x pointers | bw | bs
+  std::vector<oba::TBlk> tw, ts;
+  try {
+    for (auto* pr : {&bw, &bs}) {
+      auto& dst = pr == &bw ? tw : ts;
+      dst.resize(pr->size());
+      for (size_t b = 0; b < pr->size(); ++b) {
+        const int32_t t = (*pr)[b];
+        dst[b] = oba::TBlk{off[t], off[t + 1], t, 0};
+      }
+    }
+  } catch (...) {
+    return OBA_ENOMEM;
+  }
+  // layout of the allocation: block tables (worker, server grid) | off | g
+  // pointers | x pointers
+  const size_t b_bw = tw.size() * sizeof(oba::TBlk), b_bs = ts.size() * sizeof(oba::TBlk);
   const size_t b_off = off.size() * sizeof(int64_t);
   const size_t b_g = (size_t)n * T * sizeof(void*);
   const size_t b_x = (size_t)T * sizeof(float*);
-  const size_t b_bw = bw.size() * sizeof(int32_t), b_bs = bs.size() * sizeof(int32_t);
   const size_t bytes = b_off + b_g + b_x + b_bw + b_bs;
   oba_tensors_s* H = new (std::nothrow) oba_tensors_s();
   if (!H) return OBA_ENOMEM;
@@ -575,7 +589,7 @@ int oba_tensors_create(oba_tensors* out, oba_layout L, int32_t n_tensors,
   }
   char* base = static_cast<char*>(H->dev);
   const std::pair<const void*, size_t> parts[] = {
-      {off.data(), b_off}, {g_ptrs, b_g}, {x_ptrs, b_x}, {bw.data(), b_bw}, {bs.data(), b_bs}};
+      {tw.data(), b_bw}, {ts.data(), b_bs}, {off.data(), b_off}, {g_ptrs, b_g}, {x_ptrs, b_x}};
   size_t at = 0;
   for (const auto& pr : parts) {
     if (pr.second) e = hipMemcpy(base + at, pr.first, pr.second, hipMemcpyHostToDevice);
@@ -587,14 +601,14 @@ int oba_tensors_create(oba_tensors* out, oba_layout L, int32_t n_tensors,
     at += pr.second;
   }
   oba::TList tl{};
-  tl.off = reinterpret_cast<const int64_t*>(base);
-  tl.g = reinterpret_cast<const void* const*>(base + b_off);
-  tl.x = reinterpret_cast<float* const*>(base + b_off + b_g);
+  tl.off = reinterpret_cast<const int64_t*>(base + b_bw + b_bs);
+  tl.g = reinterpret_cast<const void* const*>(base + b_bw + b_bs + b_off);
+  tl.x = reinterpret_cast<float* const*>(base + b_bw + b_bs + b_off + b_g);
   tl.T = T;
   H->tl_w = tl;
-  H->tl_w.blk_first = reinterpret_cast<const int32_t*>(base + b_off + b_g + b_x);
+  H->tl_w.blk = reinterpret_cast<const oba::TBlk*>(base);
   H->tl_s = tl;
-  H->tl_s.blk_first = reinterpret_cast<const int32_t*>(base + b_off + b_g + b_x + b_bw);
+  H->tl_s.blk = reinterpret_cast<const oba::TBlk*>(base + b_bw);
   *out = H;
   return OBA_OK;
 }

@@ -123,6 +123,7 @@ __device__ __forceinline__ void load8(const T* __restrict__ p, const Quads& q, i
 struct LaneT {
   int64_t relA, relB;  // quad offsets inside their tensors
   int32_t tA, tB;      // tensors of the quads
+  int32_t tu;          // the span's tensor if the whole span lies in one, else -1
   bool okA, okB;       // quad inside [0, d)
 };
 
@@ -133,21 +134,56 @@ __device__ __forceinline__ int32_t tensor_walk(const int64_t* __restrict__ off, 
   return t;
 }
 
-// The lane's quads for a span starting in tensor t0 (quads past d: ok = false).
-__device__ __forceinline__ LaneT lane_tensors(const TList& tl, int32_t t0, const Quads& q,
-                                              int64_t d) {
+// Block-uniform cursor: the tensor holding the current span's first
+// coordinate and its range, started from the per-block table (one load) and
+// advanced span by span.
+struct TCur {
+  int64_t lo, hi;
+  int32_t t;
+};
+
+__device__ __forceinline__ TCur tcur_start(const TList& tl, int32_t b) {
+  const TBlk e = tl.blk[b];
+  return {e.lo, e.hi, e.t};
+}
+
+__device__ __forceinline__ void tcur_advance(const TList& tl, TCur& c, int64_t lo) {
+  while (c.hi <= lo) {
+    ++c.t;
+    c.lo = c.hi;
+    c.hi = tl.off[c.t + 1];
+  }
+}
+
+// The lane's quads for the span [lo, hi) whose first coordinate lies in the
+// cursor's tensor (quads past d: ok = false).  A span inside one tensor (the
+// common case) needs no lookup and keeps the tensor index block-uniform, so
+// its pointers are scalar loads.
+__device__ __forceinline__ LaneT lane_tensors(const TList& tl, const TCur& c, const Quads& q,
+                                              int64_t hi, int64_t d) {
   LaneT lt;
   lt.okA = q.kA < d;
   lt.okB = q.kB < d;
-  lt.tA = lt.okA ? tensor_walk(tl.off, t0, q.kA) : t0;
-  lt.tB = lt.okB ? tensor_walk(tl.off, lt.tA, q.kB) : lt.tA;
-  lt.relA = q.kA - tl.off[lt.tA];
-  lt.relB = q.kB - tl.off[lt.tB];
+  if (c.hi >= hi) {
+    lt.tu = c.t;
+    lt.tA = lt.tB = c.t;
+    lt.relA = q.kA - c.lo;
+    lt.relB = q.kB - c.lo;
+  } else {
+    lt.tu = -1;
+    lt.tA = lt.okA ? tensor_walk(tl.off, c.t, q.kA) : c.t;
+    lt.tB = lt.okB ? tensor_walk(tl.off, lt.tA, q.kB) : lt.tA;
+    lt.relA = q.kA - tl.off[lt.tA];
+    lt.relB = q.kB - tl.off[lt.tB];
+  }
   return lt;
 }
 
+// One quad; CHECK: zeros when !ok (the tail span), else an unconditional load
+// (a branch around each load would serialise the span's loads).
+template <bool CHECK>
 __device__ __forceinline__ void load_quad(const float* __restrict__ p, bool ok, float* v) {
-  if (ok) {
+  if (!CHECK || ok) {
     const f32x4 a = ldv(reinterpret_cast<const f32x4*>(p));
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
   } else {
@@ -155,8 +191,9 @@ __device__ __forceinline__ void load_quad(const float* __restrict__ p, bool ok, 
   }
 }
 
+template <bool CHECK>
 __device__ __forceinline__ void load_quad(const uint16_t* __restrict__ p, bool ok, float* v) {
-  if (ok) {
+  if (!CHECK || ok) {
     const u32x2 a = ldv(reinterpret_cast<const u32x2*>(p));
     v[0] = half_bits_to_float(a.x & 0xFFFFu);
     v[1] = half_bits_to_float(a.x >> 16);
@@ -168,23 +205,57 @@ __device__ __forceinline__ void load_quad(const uint16_t* __restrict__ p, bool o
 }
 
 // Row `row` of a listed gradient (rows are workers) at the lane's quads.
+template <bool CHECK, typename GT>
+__device__ __forceinline__ void load_listed_q(const TList& tl, int64_t row, const LaneT& lt,
+                                              float (&v)[8]) {
+  const GT* const* tab = reinterpret_cast<const GT* const*>(tl.g) + row * tl.T;
+  if (lt.tu >= 0) {  // block-uniform: one pointer for the whole span
+    const GT* p = tab[lt.tu];
+    load_quad<CHECK>(p + lt.relA, lt.okA, v);
+    load_quad<CHECK>(p + lt.relB, lt.okB, v + 4);
+  } else {
+    load_quad<CHECK>(tab[lt.tA] + lt.relA, lt.okA, v);
+    load_quad<CHECK>(tab[lt.tB] + lt.relB, lt.okB, v + 4);
+  }
+}
+
 template <typename GT>
 __device__ __forceinline__ void load_listed(const TList& tl, int64_t row, const LaneT& lt,
-                                            float (&v)[8]) {
-  const GT* const* tab = reinterpret_cast<const GT* const*>(tl.g) + row * tl.T;
-  load_quad(tab[lt.tA] + lt.relA, lt.okA, v);
-  load_quad(tab[lt.tB] + lt.relB, lt.okB, v + 4);
+                                            bool full, float (&v)[8]) {
+  if (full)
+    load_listed_q<false, GT>(tl, row, lt, v);
+  else
+    load_listed_q<true, GT>(tl, row, lt, v);
 }
 
-__device__ __forceinline__ void load_listed_x(const TList& tl, const LaneT& lt, float (&v)[8]) {
-  load_quad(tl.x[lt.tA] + lt.relA, lt.okA, v);
-  load_quad(tl.x[lt.tB] + lt.relB, lt.okB, v + 4);
+template <bool CHECK>
+__device__ __forceinline__ void load_listed_x_q(const TList& tl, const LaneT& lt, float (&v)[8]) {
+  if (lt.tu >= 0) {
+    const float* p = tl.x[lt.tu];
+    load_quad<CHECK>(p + lt.relA, lt.okA, v);
+    load_quad<CHECK>(p + lt.relB, lt.okB, v + 4);
+  } else {
+    load_quad<CHECK>(tl.x[lt.tA] + lt.relA, lt.okA, v);
+    load_quad<CHECK>(tl.x[lt.tB] + lt.relB, lt.okB, v + 4);
+  }
 }
 
-__device__ __forceinline__ void store_listed_x(const TList& tl, const LaneT& lt,
+__device__ __forceinline__ void load_listed_x(const TList& tl, const LaneT& lt, bool full,
+                                              float (&v)[8]) {
+  if (full)
+    load_listed_x_q<false>(tl, lt, v);
+  else
+    load_listed_x_q<true>(tl, lt, v);
+}
+
+__device__ __forceinline__ void store_listed_x(const TList& tl, const LaneT& lt, bool full,
                                                const float (&v)[8]) {
-  if (lt.okA) stv(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(tl.x[lt.tA] + lt.relA));
-  if (lt.okB) stv(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4*>(tl.x[lt.tB] + lt.relB));
+  float* pA = lt.tu >= 0 ? tl.x[lt.tu] : tl.x[lt.tA];
+  float* pB = lt.tu >= 0 ? pA : tl.x[lt.tB];
+  if (full || lt.okA)
+    stv(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(pA + lt.relA));
+  if (full || lt.okB)
+    stv(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4*>(pB + lt.relB));
 }
 
 __device__ __forceinline__ void store8(float* __restrict__ p, const Quads& q, int64_t d,
@@ -379,8 +450,8 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
   double acc[1] = {0.0};
   const int64_t s_lo = dspan(G.S, G.nblk, blockIdx.x);
   const int64_t s_hi = dspan(G.S, G.nblk, blockIdx.x + 1);
-  int32_t tcur = 0;  // tensor cursor (tensor lists: x and g listed)
-  if constexpr (TL) tcur = tl.blk_first[blockIdx.x];
+  TCur tcur{};  // tensor cursor (tensor lists: x and g listed)
+  if constexpr (TL) tcur = tcur_start(tl, blockIdx.x);
   const float nf = (float)G.n;
   const bool pow2 = (G.n & (G.n - 1)) == 0;
   const float inv_n = 1.0f / nf;
@@ -391,13 +462,13 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
     float sum[8], mv[8], vv[8], xv[8];
     LaneT lt{};
     if constexpr (TL) {
-      tcur = tensor_walk(tl.off, tcur, lo);
-      lt = lane_tensors(tl, tcur, q, G.d);
+      tcur_advance(tl, tcur, lo);
+      lt = lane_tensors(tl, tcur, q, min(lo + kSpan, G.d), G.d);
     }
     load8(m, q, G.d, full, mv);
     load8(v, q, G.d, full, vv);
     if constexpr (TL)
-      load_listed_x(tl, lt, xv);
+      load_listed_x(tl, lt, full, xv);
     else
       load8(x, q, G.d, full, xv);
 #pragma unroll
@@ -408,7 +479,7 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         if constexpr (TL)
-          load_listed<GT>(tl, min(i0 + u, G.n - 1), lt, gv[u]);
+          load_listed<GT>(tl, min(i0 + u, G.n - 1), lt, full, gv[u]);
         else
           load8(g + (int64_t)min(i0 + u, G.n - 1) * G.ld, q, G.d, full, gv[u]);
       }
@@ -431,7 +502,7 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
     store8(m, q, G.d, full, mv);
     store8(v, q, G.d, full, vv);
     if constexpr (TL)
-      store_listed_x(tl, lt, xv);
+      store_listed_x(tl, lt, full, xv);
     else
       store8(x, q, G.d, full, xv);
     if (NORM) acc[0] += sumsq8(vv);  // coordinates past d read 0 and give v = 0
@@ -534,8 +605,8 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
   int32_t p = sig.blk_first[b];
   int64_t p_hi = sig.phi[p];
   static_assert(!TL || MODE >= kDeferred, "tensor lists: deferred passes only");
-  int32_t tcur = 0;  // tensor cursor (tensor lists)
-  if constexpr (TL) tcur = tl.blk_first[b];
+  TCur tcur{};  // tensor cursor (tensor lists)
+  if constexpr (TL) tcur = tcur_start(tl, b);
   // kDeferredM: cursor over the server segments (on this grid) for sbar
   int32_t pt = 0, pt_end = 0;
   int64_t pt_hi = 0;
@@ -559,8 +630,8 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
     if (MODE != kNorm && !uniform) lane_segs(sig.off, sig.pseg[p], q, G.d, jseg);
     LaneT lt{};
     if constexpr (TL) {
-      tcur = tensor_walk(tl.off, tcur, lo);
-      lt = lane_tensors(tl, tcur, q, G.d);
+      tcur_advance(tl, tcur, lo);
+      lt = lane_tensors(tl, tcur, q, min(lo + kSpan, G.d), G.d);
     }
     // every load of the span first (all NB workers), then the arithmetic
     float mv[8];
@@ -607,7 +678,7 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
           if (ib + u >= NB) break;
           const int64_t row = (int64_t)(i0 + ib + u) * G.ld;
           if constexpr (TL)
-            load_listed<GT>(tl, i0 + ib + u, lt, gv[u]);
+            load_listed<GT>(tl, i0 + ib + u, lt, full, gv[u]);
           else
             load_full(g + row, q, gv[u]);
           load_full(delta + row, q, c[u]);
@@ -619,7 +690,7 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
           if (ib + u >= NB) break;
           const int64_t row = (int64_t)(i0 + ib + u) * G.ld;
           if constexpr (TL)
-            load_listed<GT>(tl, i0 + ib + u, lt, gv[u]);
+            load_listed<GT>(tl, i0 + ib + u, lt, full, gv[u]);
           else
             load_tail(g + row, q, G.d, gv[u]);
           load_tail(delta + row, q, G.d, c[u]);
@@ -951,8 +1022,8 @@ __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
                                                               float* __restrict__ x, SegDev tau,
                                                               float lr, TList tl) {
   const int32_t b = blockIdx.x;
-  int32_t tcur = 0;  // tensor cursor (tensor lists: x listed)
-  if constexpr (TL) tcur = tl.blk_first[b];
+  TCur tcur{};  // tensor cursor (tensor lists: x listed)
+  if constexpr (TL) tcur = tcur_start(tl, b);
   const int64_t s_lo = dspan(G.S, G.nblk, b), s_hi = dspan(G.S, G.nblk, b + 1);
   const int32_t p_end = tau.blk_first[b + 1];
   int32_t p = tau.blk_first[b];
@@ -967,13 +1038,13 @@ __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
                                : load_sign_bits<false, OBA_PAIRS_UPD>(sbytes, q, G.d);
     LaneT lt{};
     if constexpr (TL) {
-      tcur = tensor_walk(tl.off, tcur, lo);
-      lt = lane_tensors(tl, tcur, q, G.d);
+      tcur_advance(tl, tcur, lo);
+      lt = lane_tensors(tl, tcur, q, min(lo + kSpan, G.d), G.d);
     }
     if (UPDATE_X) {
       load8(denom, q, G.d, full, dv);
       if constexpr (TL)
-        load_listed_x(tl, lt, xv);
+        load_listed_x(tl, lt, full, xv);
       else
         load8(x, q, G.d, full, xv);
     }
@@ -995,7 +1066,7 @@ __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
     if (WRITE_M) store8(m, q, G.d, full, mh);
     if (UPDATE_X) {
       if constexpr (TL)
-        store_listed_x(tl, lt, xv);
+        store_listed_x(tl, lt, full, xv);
       else
         store8(x, q, G.d, full, xv);
     }

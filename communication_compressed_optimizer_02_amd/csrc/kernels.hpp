@@ -39,11 +39,16 @@ inline size_t partial_bytes(const SegDev& T, int32_t rows) {
 // allocations).  Tensor t covers flat coordinates [off[t], off[t+1]); every
 // length is a multiple of 4, so a lane's 4-coordinate quads never straddle
 // two tensors.
+struct TBlk {      // the tensor holding a block's first coordinate
+  int64_t lo, hi;  // its flat range [off[t], off[t+1])
+  int32_t t, pad;
+};
+
 struct TList {
-  const int64_t* off;        // [T+1]
-  const int32_t* blk_first;  // [nblk] tensor holding each block's first coordinate
-  const void* const* g;      // [n][T] gradient tensors (g dtype)
-  float* const* x;           // [T] parameter tensors
+  const int64_t* off;    // [T+1]
+  const TBlk* blk;       // [nblk] per block of the grid in use
+  const void* const* g;  // [n][T] gradient tensors (g dtype)
+  float* const* x;       // [T] parameter tensors
   int32_t T;
 };
 
