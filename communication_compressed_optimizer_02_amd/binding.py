@@ -6,7 +6,7 @@ the stream (``torch.cuda.current_stream()``).  There is no fallback: if the
 library is missing or a call fails, an exception is raised.
 
 Buffers (all CUDA tensors on the layout's device, C-contiguous):
-  g      [n][ld]  float32 or float16     delta  [n][ld]  float32
+  g      [n][ld]  float32, float16 or bfloat16   delta [n][ld] float32
          (ld = row stride, a multiple of 8 >= d; default d rounded up to 8)
   x, m, v, denom, eps  [d] float32
   wbits  [n][W]  int64 (packed 64-bit words)   sbits [W] int64
@@ -20,7 +20,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboba.so")
 
-OBA_F32, OBA_F16 = 0, 1
+OBA_F32, OBA_F16, OBA_BF16 = 0, 1, 2
 _lib = None
 
 # name -> (restype, argtypes); mirrors include/oba.h
@@ -162,7 +162,13 @@ class Layout:
 def _gdtype(g):
     import torch
 
-    return OBA_F16 if g.dtype == torch.float16 else OBA_F32
+    return {torch.float16: OBA_F16, torch.bfloat16: OBA_BF16}.get(g.dtype, OBA_F32)
+
+
+def _gtypes():
+    import torch
+
+    return (torch.float32, torch.float16, torch.bfloat16)
 
 
 def adam_warmup_step(L: Layout, g, x, m, v, lr, beta1, beta2, eta, bc1=1.0, bc2=1.0, stream=None):
@@ -170,7 +176,7 @@ def adam_warmup_step(L: Layout, g, x, m, v, lr, beta1, beta2, eta, bc1=1.0, bc2=
 
     f32 = (torch.float32,)
     rc = lib().oba_adam_warmup_step(
-        L.handle, _ptr(g, "g", (torch.float32, torch.float16), (L.n, L.ld)), _gdtype(g),
+        L.handle, _ptr(g, "g", _gtypes(), (L.n, L.ld)), _gdtype(g),
         _ptr(x, "x", f32, (L.d,)), _ptr(m, "m", f32, (L.d,)), _ptr(v, "v", f32, (L.d,)),
         lr, beta1, beta2, eta, bc1, bc2, _stream(stream))
     _check(rc, "oba_adam_warmup_step")
@@ -184,7 +190,7 @@ def adam_warmup_step_vnorm(L: Layout, g, x, m, v, lr, beta1, beta2, eta, vnorm, 
 
     f32 = (torch.float32,)
     rc = lib().oba_adam_warmup_step_vnorm(
-        L.handle, _ptr(g, "g", (torch.float32, torch.float16), (L.n, L.ld)), _gdtype(g),
+        L.handle, _ptr(g, "g", _gtypes(), (L.n, L.ld)), _gdtype(g),
         _ptr(x, "x", f32, (L.d,)), _ptr(m, "m", f32, (L.d,)), _ptr(v, "v", f32, (L.d,)),
         lr, beta1, beta2, eta, bc1, bc2, _ptr(vnorm, "vnorm", (torch.float64,), (1,)),
         ctypes.c_void_p(L.ws.data_ptr()), L.ws_bytes, _stream(stream))
@@ -233,7 +239,7 @@ def compress(L: Layout, g, m, delta, wbits, wscale, beta1, stream=None):
 
     f32 = (torch.float32,)
     rc = lib().oba_compress(
-        L.handle, _ptr(g, "g", (torch.float32, torch.float16), (L.n, L.ld)), _gdtype(g),
+        L.handle, _ptr(g, "g", _gtypes(), (L.n, L.ld)), _gdtype(g),
         _ptr(m, "m", f32, (L.d,)), _ptr(delta, "delta", f32, (L.n, L.ld)),
         _ptr(wbits, "wbits", (torch.int64,), (L.n, L.W)),
         _ptr(wscale, "wscale", f32, (L.n, L.n_wseg)), beta1,
@@ -292,7 +298,7 @@ def compress_deferred(L: Layout, g, m, c, wbits, wscale, beta1, sbits_prev=None,
     sp = (_ptr(sscale_prev, "sscale_prev", f32, (L.n_sseg,)) if sscale_prev is not None
           else P(None))
     rc = lib().oba_compress_deferred(
-        L.handle, _ptr(g, "g", (torch.float32, torch.float16), (L.n, L.ld)), _gdtype(g),
+        L.handle, _ptr(g, "g", _gtypes(), (L.n, L.ld)), _gdtype(g),
         mp, bp, sp, _ptr(c, "c", f32, (L.n, L.ld)),
         _ptr(wbits, "wbits", (torch.int64,), (L.n, L.W)),
         _ptr(wscale, "wscale", f32, (L.n, L.n_wseg)), beta1,
@@ -306,7 +312,7 @@ def compress_deferred_local(L: Layout, g, m_local, c, wbits, wscale, beta1, stre
 
     f32 = (torch.float32,)
     rc = lib().oba_compress_deferred_local(
-        L.handle, _ptr(g, "g", (torch.float32, torch.float16), (L.n, L.ld)), _gdtype(g),
+        L.handle, _ptr(g, "g", _gtypes(), (L.n, L.ld)), _gdtype(g),
         _ptr(m_local, "m_local", f32, (L.n, L.ld)), _ptr(c, "c", f32, (L.n, L.ld)),
         _ptr(wbits, "wbits", (torch.int64,), (L.n, L.W)),
         _ptr(wscale, "wscale", f32, (L.n, L.n_wseg)), beta1,
@@ -360,7 +366,7 @@ class TensorList:
         if len(self.gs) != L.n or any(len(row) != T for row in self.gs):
             raise ValueError("gs must hold n rows of T tensors")
         gdt = self.gs[0][0].dtype if T else torch.float32
-        self.g_dtype = OBA_F16 if gdt == torch.float16 else OBA_F32
+        self.g_dtype = _gdtype(self.gs[0][0]) if T else OBA_F32
         lengths = np.array([t.numel() for t in self.xs], dtype=np.int64)
         for t, x in enumerate(self.xs):
             _ptr(x, f"x[{t}]", (torch.float32,))
@@ -459,7 +465,8 @@ class State:
         dev = "cuda"
         f = torch.float32
         self.L = L
-        self.g = torch.zeros((L.n, L.ld), dtype=torch.float16 if g_dtype == "f16" else f, device=dev)
+        gt = {"f16": torch.float16, "bf16": torch.bfloat16}.get(g_dtype, f)
+        self.g = torch.zeros((L.n, L.ld), dtype=gt, device=dev)
         self.x = torch.zeros(L.d, dtype=f, device=dev)
         self.m = torch.zeros(L.d, dtype=f, device=dev)
         self.v = torch.zeros(L.d, dtype=f, device=dev)

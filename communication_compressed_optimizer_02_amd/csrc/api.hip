@@ -120,6 +120,7 @@ int check_buf(const void* p, uintptr_t align) {
 }
 
 bool is_finite(double x) { return std::isfinite(x); }
+bool gdtype_ok(int t) { return t == OBA_F32 || t == OBA_F16 || t == OBA_BF16; }
 bool beta_ok(double b) { return is_finite(b) && b >= 0.0 && b < 1.0; }
 
 #define OBA_TRY(expr)          \
@@ -266,7 +267,7 @@ int warmup(oba_layout L, const void* g, int g_dtype, float* x, float* m, float* 
            double beta1, double beta2, double eta, double bc1, double bc2, double* vnorm,
            void* ws, size_t ws_bytes, hipStream_t stream) {
   OBA_TRY(check_layout(L));
-  if (g_dtype != OBA_F32 && g_dtype != OBA_F16) return OBA_EINVAL;
+  if (!gdtype_ok(g_dtype)) return OBA_EINVAL;
   if (!is_finite(lr) || !beta_ok(beta1) || !beta_ok(beta2) || !is_finite(eta) || eta < 0.0 ||
       !is_finite(bc1) || bc1 <= 0.0 || !is_finite(bc2) || bc2 <= 0.0)
     return OBA_EINVAL;
@@ -292,7 +293,7 @@ int warmup(oba_layout L, const void* g, int g_dtype, float* x, float* m, float* 
   // outnumber the blocks of this grid)
   double* part = static_cast<double*>(ws);
   return launch("adam_warmup", stream, [&] {
-    oba::launch_adam_warmup(G, g, g_dtype == OBA_F16, x, m, v, C, part, vnorm, stream);
+    oba::launch_adam_warmup(G, g, g_dtype, x, m, v, C, part, vnorm, stream);
   });
 }
 
@@ -333,7 +334,7 @@ int oba_compress(oba_layout L, const void* g, int g_dtype, const float* m, float
                  uint64_t* wbits, float* wscale, double beta1, void* ws, size_t ws_bytes,
                  hipStream_t stream) {
   OBA_TRY(check_layout(L));
-  if (g_dtype != OBA_F32 && g_dtype != OBA_F16) return OBA_EINVAL;
+  if (!gdtype_ok(g_dtype)) return OBA_EINVAL;
   if (!beta_ok(beta1)) return OBA_EINVAL;
   if (L->geo.d == 0) return OBA_OK;
   OBA_TRY(check_buf(g, 16));
@@ -350,13 +351,13 @@ int oba_compress(oba_layout L, const void* g, int g_dtype, const float* m, float
   // the read-only norm pass runs on the server grid (a few spans per block:
   // its per-block reduction would dominate at one span per block)
   OBA_TRY(launch("compress_p1", stream, [&] {
-    oba::launch_compress_norm(L->geo, g, g_dtype == OBA_F16, m, delta, L->sig, part, b1, omb1,
+    oba::launch_compress_norm(L->geo, g, g_dtype, m, delta, L->sig, part, b1, omb1,
                               stream);
   }));
   OBA_TRY(launch("finalize_scales", stream,
                  [&] { oba::launch_finalize(part, G.n, L->sig, wscale, stream); }));
   return launch("compress_p2", stream, [&] {
-    oba::launch_compress_apply(G, g, g_dtype == OBA_F16, m, delta, wbytes, L->sig_w, wscale, b1,
+    oba::launch_compress_apply(G, g, g_dtype, m, delta, wbytes, L->sig_w, wscale, b1,
                                omb1, stream);
   });
 }
@@ -392,7 +393,7 @@ int oba_compress_deferred(oba_layout L, const void* g, int g_dtype, const float*
                           uint64_t* wbits, float* wscale, double beta1, void* ws, size_t ws_bytes,
                           hipStream_t stream) {
   OBA_TRY(check_layout(L));
-  if (g_dtype != OBA_F32 && g_dtype != OBA_F16) return OBA_EINVAL;
+  if (!gdtype_ok(g_dtype)) return OBA_EINVAL;
   if (!beta_ok(beta1)) return OBA_EINVAL;
   const bool implicit_m = !m;
   if (implicit_m != (sbits_prev != nullptr) || implicit_m != (sscale_prev != nullptr))
@@ -416,7 +417,7 @@ int oba_compress_deferred(oba_layout L, const void* g, int g_dtype, const float*
   uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
   const oba::MomSrc ms{reinterpret_cast<const uint8_t*>(sbits_prev), sscale_prev, L->tau_w};
   OBA_TRY(launch("compress_deferred", stream, [&] {
-    oba::launch_compress_deferred(G, g, g_dtype == OBA_F16, m, c, wbytes, L->sig_w, part, wscale,
+    oba::launch_compress_deferred(G, g, g_dtype, m, c, wbytes, L->sig_w, part, wscale,
                                   b1, omb1, ms, stream);
   }));
   return launch("finalize_scales", stream,
@@ -427,7 +428,7 @@ int oba_compress_deferred_local(oba_layout L, const void* g, int g_dtype, float*
                                 float* c, uint64_t* wbits, float* wscale, double beta1, void* ws,
                                 size_t ws_bytes, hipStream_t stream) {
   OBA_TRY(check_layout(L));
-  if (g_dtype != OBA_F32 && g_dtype != OBA_F16) return OBA_EINVAL;
+  if (!gdtype_ok(g_dtype)) return OBA_EINVAL;
   if (!beta_ok(beta1)) return OBA_EINVAL;
   if (L->geo.d == 0) return OBA_OK;
   OBA_TRY(check_buf(g, 16));
@@ -443,7 +444,7 @@ int oba_compress_deferred_local(oba_layout L, const void* g, int g_dtype, float*
   const float b1 = (float)beta1, omb1 = (float)(1.0 - beta1);
   uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
   OBA_TRY(launch("compress_deferred_local", stream, [&] {
-    oba::launch_compress_deferred_local(G, g, g_dtype == OBA_F16, m_local, c, wbytes, L->sig_w,
+    oba::launch_compress_deferred_local(G, g, g_dtype, m_local, c, wbytes, L->sig_w,
                                         part, wscale, b1, omb1, stream);
   }));
   return launch("finalize_scales", stream,
@@ -539,14 +540,14 @@ int oba_tensors_create(oba_tensors* out, oba_layout L, int32_t n_tensors,
                        int g_dtype) {
   if (!out || !x_ptrs || !g_ptrs) return OBA_EINVAL;
   OBA_TRY(check_layout(L));
-  if (g_dtype != OBA_F32 && g_dtype != OBA_F16) return OBA_EINVAL;
+  if (!gdtype_ok(g_dtype)) return OBA_EINVAL;
   const oba::Plan& P = L->plan;
   if (P.d == 0) return OBA_EINVAL;  // nothing to list
   std::vector<int64_t> off;
   int rc = oba::tensor_offsets(P, n_tensors, lengths, &off);
   if (rc) return rc;
   const int32_t T = n_tensors, n = P.n;
-  const uintptr_t galign = g_dtype == OBA_F32 ? 16 : 8;
+  const uintptr_t galign = g_dtype == OBA_F32 ? 16 : 8;  // a quad: 16 or 8 bytes
   for (int32_t t = 0; t < T; ++t) OBA_TRY(check_buf(x_ptrs[t], 16));
   for (int64_t r = 0; r < (int64_t)n * T; ++r) OBA_TRY(check_buf(g_ptrs[r], galign));
   std::vector<int32_t> bw, bs;
@@ -642,7 +643,7 @@ int oba_adam_warmup_step_listed(oba_layout L, oba_tensors H, float* m, float* v,
   const oba::Geo G = L->geo;
   double* part = static_cast<double*>(ws);
   return launch("adam_warmup", stream, [&] {
-    oba::launch_adam_warmup_listed(G, H->tl_s, H->g_dtype == OBA_F16, m, v, C, part, vnorm,
+    oba::launch_adam_warmup_listed(G, H->tl_s, H->g_dtype, m, v, C, part, vnorm,
                                    stream);
   });
 }
@@ -674,7 +675,7 @@ int oba_compress_deferred_listed(oba_layout L, oba_tensors H, const float* m,
   uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
   const oba::MomSrc ms{reinterpret_cast<const uint8_t*>(sbits_prev), sscale_prev, L->tau_w};
   OBA_TRY(launch("compress_deferred", stream, [&] {
-    oba::launch_compress_deferred_listed(G, H->tl_w, H->g_dtype == OBA_F16, m, c, wbytes,
+    oba::launch_compress_deferred_listed(G, H->tl_w, H->g_dtype, m, c, wbytes,
                                          L->sig_w, part, wscale, b1, omb1, ms, stream);
   }));
   return launch("finalize_scales", stream,

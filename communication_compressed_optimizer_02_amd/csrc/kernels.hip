@@ -73,9 +73,21 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
 }
 
+// bfloat16 storage: the upper half of a binary32, so decoding is exact
+struct bf16_bits {
+  uint16_t b;
+};
+
+__device__ __forceinline__ float bf16_to_float(uint32_t h) {
+  return __builtin_bit_cast(float, h << 16);
+}
+
 __device__ __forceinline__ float elem(const float* p, int64_t k) { return p[k]; }
 __device__ __forceinline__ float elem(const uint16_t* p, int64_t k) {
   return half_bits_to_float(p[k]);
+}
+__device__ __forceinline__ float elem(const bf16_bits* p, int64_t k) {
+  return bf16_to_float(p[k].b);
 }
 
 __device__ __forceinline__ void load_full(const float* __restrict__ p, const Quads& q,
@@ -98,6 +110,20 @@ __device__ __forceinline__ void load_full(const uint16_t* __restrict__ p, const 
   v[5] = half_bits_to_float(b.x >> 16);
   v[6] = half_bits_to_float(b.y & 0xFFFFu);
   v[7] = half_bits_to_float(b.y >> 16);
+}
+
+__device__ __forceinline__ void load_full(const bf16_bits* __restrict__ p, const Quads& q,
+                                          float (&v)[8]) {
+  const u32x2 a = ldv(reinterpret_cast<const u32x2*>(p + q.kA));
+  const u32x2 b = ldv(reinterpret_cast<const u32x2*>(p + q.kB));
+  v[0] = bf16_to_float(a.x & 0xFFFFu);
+  v[1] = bf16_to_float(a.x >> 16);
+  v[2] = bf16_to_float(a.y & 0xFFFFu);
+  v[3] = bf16_to_float(a.y >> 16);
+  v[4] = bf16_to_float(b.x & 0xFFFFu);
+  v[5] = bf16_to_float(b.x >> 16);
+  v[6] = bf16_to_float(b.y & 0xFFFFu);
+  v[7] = bf16_to_float(b.y >> 16);
 }
 
 template <typename T>
@@ -199,6 +225,19 @@ __device__ __forceinline__ void load_quad(const uint16_t* __restrict__ p, bool o
     v[1] = half_bits_to_float(a.x >> 16);
     v[2] = half_bits_to_float(a.y & 0xFFFFu);
     v[3] = half_bits_to_float(a.y >> 16);
+  } else {
+    v[0] = v[1] = v[2] = v[3] = 0.0f;
+  }
+}
+
+template <bool CHECK>
+__device__ __forceinline__ void load_quad(const bf16_bits* __restrict__ p, bool ok, float* v) {
+  if (!CHECK || ok) {
+    const u32x2 a = ldv(reinterpret_cast<const u32x2*>(p));
+    v[0] = bf16_to_float(a.x & 0xFFFFu);
+    v[1] = bf16_to_float(a.x >> 16);
+    v[2] = bf16_to_float(a.y & 0xFFFFu);
+    v[3] = bf16_to_float(a.y >> 16);
   } else {
     v[0] = v[1] = v[2] = v[3] = 0.0f;
   }
@@ -1116,18 +1155,22 @@ void launch_norm_finalize(const double* part, int32_t n, double* out, hipStream_
   hipLaunchKernelGGL(k_norm_finalize, dim3(1), dim3(kNormBlock), 0, st, part, n, out);
 }
 
-void launch_adam_warmup(const Geo& G, const void* g, bool f16, float* x, float* m, float* v,
+void launch_adam_warmup(const Geo& G, const void* g, int gdt, float* x, float* m, float* v,
                         const AdamCoef& C, double* part, double* vnorm, hipStream_t st) {
-  if (f16)
+  if (gdt == kGradF16)
     launch_warmup<uint16_t, false>(G, g, x, m, v, C, part, vnorm, TList{}, st);
+  else if (gdt == kGradBF16)
+    launch_warmup<bf16_bits, false>(G, g, x, m, v, C, part, vnorm, TList{}, st);
   else
     launch_warmup<float, false>(G, g, x, m, v, C, part, vnorm, TList{}, st);
 }
 
-void launch_adam_warmup_listed(const Geo& G, const TList& tl, bool f16, float* m, float* v,
+void launch_adam_warmup_listed(const Geo& G, const TList& tl, int gdt, float* m, float* v,
                                const AdamCoef& C, double* part, double* vnorm, hipStream_t st) {
-  if (f16)
+  if (gdt == kGradF16)
     launch_warmup<uint16_t, true>(G, nullptr, nullptr, m, v, C, part, vnorm, tl, st);
+  else if (gdt == kGradBF16)
+    launch_warmup<bf16_bits, true>(G, nullptr, nullptr, m, v, C, part, vnorm, tl, st);
   else
     launch_warmup<float, true>(G, nullptr, nullptr, m, v, C, part, vnorm, tl, st);
 }
@@ -1187,60 +1230,63 @@ static void launch_cmp_n(const Geo& G, const void* g, const float* m, float* del
 }
 
 template <int MODE, bool TL = false>
-static void launch_cmp_t(const Geo& G, const void* g, bool f16, const float* m, float* delta,
+static void launch_cmp_t(const Geo& G, const void* g, int gdt, const float* m, float* delta,
                          uint8_t* wbytes, const SegDev& sig, double* part, const float* wscale,
                          float b1, float omb1, const MomSrc& ms, hipStream_t st,
                          const TList& tl = TList{}) {
-  if (f16)
+  if (gdt == kGradF16)
     launch_cmp_n<uint16_t, MODE, TL>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms, tl,
                                      st);
+  else if (gdt == kGradBF16)
+    launch_cmp_n<bf16_bits, MODE, TL>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms,
+                                      tl, st);
   else
     launch_cmp_n<float, MODE, TL>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms, tl,
                                   st);
 }
 
-void launch_compress_norm(const Geo& G, const void* g, bool f16, const float* m,
+void launch_compress_norm(const Geo& G, const void* g, int gdt, const float* m,
                           const float* delta, const SegDev& sig, double* part, float b1,
                           float omb1, hipStream_t st) {
-  launch_cmp_t<kNorm>(G, g, f16, m, const_cast<float*>(delta), nullptr, sig, part, nullptr, b1,
+  launch_cmp_t<kNorm>(G, g, gdt, m, const_cast<float*>(delta), nullptr, sig, part, nullptr, b1,
                       omb1, MomSrc{}, st);
 }
 
-void launch_compress_deferred(const Geo& G, const void* g, bool f16, const float* m, float* c,
+void launch_compress_deferred(const Geo& G, const void* g, int gdt, const float* m, float* c,
                               uint8_t* wbytes, const SegDev& sig, double* part,
                               const float* wscale_prev, float b1, float omb1, const MomSrc& ms,
                               hipStream_t st) {
   if (ms.sbytes)
-    launch_cmp_t<kDeferredM>(G, g, f16, nullptr, c, wbytes, sig, part, wscale_prev, b1, omb1, ms,
+    launch_cmp_t<kDeferredM>(G, g, gdt, nullptr, c, wbytes, sig, part, wscale_prev, b1, omb1, ms,
                              st);
   else
-    launch_cmp_t<kDeferred>(G, g, f16, m, c, wbytes, sig, part, wscale_prev, b1, omb1, ms, st);
+    launch_cmp_t<kDeferred>(G, g, gdt, m, c, wbytes, sig, part, wscale_prev, b1, omb1, ms, st);
 }
 
-void launch_compress_deferred_listed(const Geo& G, const TList& tl, bool f16, const float* m,
+void launch_compress_deferred_listed(const Geo& G, const TList& tl, int gdt, const float* m,
                                      float* c, uint8_t* wbytes, const SegDev& sig, double* part,
                                      const float* wscale_prev, float b1, float omb1,
                                      const MomSrc& ms, hipStream_t st) {
   if (ms.sbytes)
-    launch_cmp_t<kDeferredM, true>(G, nullptr, f16, nullptr, c, wbytes, sig, part, wscale_prev,
+    launch_cmp_t<kDeferredM, true>(G, nullptr, gdt, nullptr, c, wbytes, sig, part, wscale_prev,
                                    b1, omb1, ms, st, tl);
   else
-    launch_cmp_t<kDeferred, true>(G, nullptr, f16, m, c, wbytes, sig, part, wscale_prev, b1,
+    launch_cmp_t<kDeferred, true>(G, nullptr, gdt, m, c, wbytes, sig, part, wscale_prev, b1,
                                   omb1, ms, st, tl);
 }
 
-void launch_compress_deferred_local(const Geo& G, const void* g, bool f16, float* m_local,
+void launch_compress_deferred_local(const Geo& G, const void* g, int gdt, float* m_local,
                                     float* c, uint8_t* wbytes, const SegDev& sig, double* part,
                                     const float* wscale_prev, float b1, float omb1,
                                     hipStream_t st) {
-  launch_cmp_t<kDeferredLocal>(G, g, f16, m_local, c, wbytes, sig, part, wscale_prev, b1, omb1,
+  launch_cmp_t<kDeferredLocal>(G, g, gdt, m_local, c, wbytes, sig, part, wscale_prev, b1, omb1,
                                MomSrc{}, st);
 }
 
-void launch_compress_apply(const Geo& G, const void* g, bool f16, const float* m, float* delta,
+void launch_compress_apply(const Geo& G, const void* g, int gdt, const float* m, float* delta,
                            uint8_t* wbytes, const SegDev& sig, const float* wscale, float b1,
                            float omb1, hipStream_t st) {
-  launch_cmp_t<kApply>(G, g, f16, m, delta, wbytes, sig, nullptr, wscale, b1, omb1, MomSrc{}, st);
+  launch_cmp_t<kApply>(G, g, gdt, m, delta, wbytes, sig, nullptr, wscale, b1, omb1, MomSrc{}, st);
 }
 
 void launch_finalize(double* part, int32_t rows, const SegDev& T, float* scale,

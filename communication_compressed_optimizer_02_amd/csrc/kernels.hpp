@@ -39,6 +39,9 @@ inline size_t partial_bytes(const SegDev& T, int32_t rows) {
 // allocations).  Tensor t covers flat coordinates [off[t], off[t+1]); every
 // length is a multiple of 4, so a lane's 4-coordinate quads never straddle
 // two tensors.
+// gradient element types (the ABI's OBA_F32, OBA_F16, OBA_BF16)
+constexpr int kGradF32 = 0, kGradF16 = 1, kGradBF16 = 2;
+
 struct TBlk {      // the tensor holding a block's first coordinate
   int64_t lo, hi;  // its flat range [off[t], off[t+1])
   int32_t t, pad;
@@ -68,19 +71,19 @@ struct AdamCoef {
 // out[0] = sqrt(part[0] + ... + part[n-1]) in a fixed order (0 for n = 0)
 void launch_norm_finalize(const double* part, int32_t n, double* out, hipStream_t st);
 // vnorm != nullptr: also ||v_new||_2 into vnorm[0] (part: nblk doubles)
-void launch_adam_warmup(const Geo& G, const void* g, bool f16, float* x, float* m, float* v,
+void launch_adam_warmup(const Geo& G, const void* g, int gdt, float* x, float* m, float* v,
                         const AdamCoef& C, double* part, double* vnorm, hipStream_t st);
 void launch_freeze(const Geo& G, const float* v, float* denom, float eta, float bc2,
                    hipStream_t st);
 // Worker compression: read-only norm pass, then recompute c and store.
-void launch_compress_norm(const Geo& G, const void* g, bool f16, const float* m,
+void launch_compress_norm(const Geo& G, const void* g, int gdt, const float* m,
                           const float* delta, const SegDev& sig, double* part, float b1,
                           float omb1, hipStream_t st);
 // Tensor lists (x and g rows listed; everything else flat).  The listed
 // worker pass supports the deferred modes (m read, or implicit with ms).
-void launch_adam_warmup_listed(const Geo& G, const TList& tl, bool f16, float* m, float* v,
+void launch_adam_warmup_listed(const Geo& G, const TList& tl, int gdt, float* m, float* v,
                                const AdamCoef& C, double* part, double* vnorm, hipStream_t st);
-void launch_compress_deferred_listed(const Geo& G, const TList& tl, bool f16, const float* m,
+void launch_compress_deferred_listed(const Geo& G, const TList& tl, int gdt, const float* m,
                                      float* c, uint8_t* wbytes, const SegDev& sig, double* part,
                                      const float* wscale_prev, float b1, float omb1,
                                      const MomSrc& ms, hipStream_t st);
@@ -88,11 +91,11 @@ void launch_decompress_update_listed(const Geo& G, const TList& tl, const uint8_
                                      const float* sscale, const float* denom, float* m,
                                      const SegDev& tau, float lr, hipStream_t st);
 // per-worker momentum: m_local [n][ld] in/out
-void launch_compress_deferred_local(const Geo& G, const void* g, bool f16, float* m_local,
+void launch_compress_deferred_local(const Geo& G, const void* g, int gdt, float* m_local,
                                     float* c, uint8_t* wbytes, const SegDev& sig, double* part,
                                     const float* wscale_prev, float b1, float omb1,
                                     hipStream_t st);
-void launch_compress_apply(const Geo& G, const void* g, bool f16, const float* m, float* delta,
+void launch_compress_apply(const Geo& G, const void* g, int gdt, const float* m, float* delta,
                            uint8_t* wbytes, const SegDev& sig, const float* wscale, float b1,
                            float omb1, hipStream_t st);
 void launch_finalize(double* part, int32_t rows, const SegDev& T, float* scale,
@@ -101,7 +104,7 @@ void launch_residual(const Geo& G, const float* src, int64_t src_ld, float* dst,
                      int32_t rows, const float* scale, const SegDev& T, hipStream_t st);
 // Deferred-residual state: rows hold the last step's c (worker) / a (server)
 // and the scale buffers its scales; see kernels.hip.
-void launch_compress_deferred(const Geo& G, const void* g, bool f16, const float* m, float* c,
+void launch_compress_deferred(const Geo& G, const void* g, int gdt, const float* m, float* c,
                               uint8_t* wbytes, const SegDev& sig, double* part,
                               const float* wscale_prev, float b1, float omb1, const MomSrc& ms,
                               hipStream_t st);

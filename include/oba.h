@@ -74,7 +74,9 @@ enum {
   OBA_ENOMEM = -6      /* host or device allocation of the layout failed */
 };
 
-enum { OBA_F32 = 0, OBA_F16 = 1 }; /* gradient dtype: binary32 or binary16 */
+/* gradient dtype: binary32, binary16, or bfloat16 (the upper half of a
+ * binary32; decoded exactly).  All state and arithmetic stay binary32. */
+enum { OBA_F32 = 0, OBA_F16 = 1, OBA_BF16 = 2 };
 
 typedef struct oba_layout_s* oba_layout;
 
@@ -289,7 +291,7 @@ int oba_deferred_errors(oba_layout layout, const float* c, const float* wscale, 
  *
  * x_ptrs: host array [T] of device pointers to binary32 tensors (16-byte
  * aligned); g_ptrs: host array [n][T] of device pointers, row i = worker i
- * (16-byte aligned for OBA_F32, 8 for OBA_F16).  The tables are copied to
+ * (16-byte aligned for OBA_F32, 8 for OBA_F16 and OBA_BF16).  The tables are copied to
  * the device at creation: the tensors must stay allocated (and at the same
  * addresses) while the handle is used.  *out is set only on success. */
 typedef struct oba_tensors_s* oba_tensors;

@@ -44,6 +44,7 @@ def lib():
         I = ctypes.c_int
         sig = {
             "oracle_half_to_double": (D, [ctypes.c_uint16]),
+            "oracle_bfloat16_to_double": (D, [ctypes.c_uint16]),
             "oracle_adam_warmup_step": (None, [I64, I32, I64, P, I, P, P, P, D, D, D, D, D, D]),
             "oracle_freeze_variance": (None, [I64, P, P, D, D]),
             "oracle_l2norm": (D, [I64, P]),
@@ -78,12 +79,24 @@ def _chk(a, dtype, name):
         raise TypeError(f"{name}: expected C-contiguous numpy {np.dtype(dtype).name}")
 
 
+class BF16(np.ndarray):
+    """bfloat16 gradients: a uint16 array of bfloat16 bit patterns
+    (``oracle.bf16(bits)``); numpy has no bfloat16 type."""
+
+
+def bf16(bits: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(bits, dtype=np.uint16)
+    return a.view(BF16)
+
+
 def _grad(g):
+    if isinstance(g, BF16):
+        return 2
     if g.dtype == np.float16:
         return 1
     if g.dtype == np.float32:
         return 0
-    raise TypeError("gradients must be float32 or float16")
+    raise TypeError("gradients must be float32, float16 or oracle.bf16(bits)")
 
 
 def words(d: int) -> int:
@@ -95,6 +108,10 @@ def _seg(seg, d):
     if seg.ndim != 1 or len(seg) < 2 or seg[0] != 0 or seg[-1] != d or np.any(np.diff(seg) <= 0):
         raise ValueError("segment table must rise strictly from 0 to d")
     return seg
+
+
+def bfloat16_to_float(h: int) -> float:
+    return lib().oracle_bfloat16_to_double(h)
 
 
 def half_to_float(h: int) -> float:

@@ -40,8 +40,27 @@ double oracle_half_to_double(uint16_t h) {
   return sign ? -v : v;
 }
 
-static float grad_at(const void* g, int g_is_f16, int64_t idx) {
-  if (g_is_f16) return (float)oracle_half_to_double(((const uint16_t*)g)[idx]);
+/* bfloat16 decoded from its definition: sign, 8-bit biased exponent (bias
+ * 127), 7-bit fraction; exponent 0 is subnormal (f * 2^-133).  Every
+ * bfloat16 value is exactly representable in binary32. */
+double oracle_bfloat16_to_double(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 7) & 255;
+  int f = h & 127;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -133);
+  else if (e == 255)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp((double)(128 + f), e - 134);
+  return sign ? -v : v;
+}
+
+/* g_kind: 0 binary32, 1 binary16, 2 bfloat16 */
+static float grad_at(const void* g, int g_kind, int64_t idx) {
+  if (g_kind == 1) return (float)oracle_half_to_double(((const uint16_t*)g)[idx]);
+  if (g_kind == 2) return (float)oracle_bfloat16_to_double(((const uint16_t*)g)[idx]);
   return ((const float*)g)[idx];
 }
 
@@ -58,7 +77,7 @@ static float grad_at(const void* g, int g_is_f16, int64_t idx) {
  * The binary32 coefficients are the binary64 hyperparameters rounded once;
  * (1-b1) and (1-b2) are formed in binary64 before that rounding.
  * ------------------------------------------------------------------------- */
-void oracle_adam_warmup_step(int64_t d, int32_t n, int64_t ld, const void* g, int g_is_f16,
+void oracle_adam_warmup_step(int64_t d, int32_t n, int64_t ld, const void* g, int g_kind,
                              float* x, float* m, float* v, double lr_, double beta1_,
                              double beta2_, double eta_, double bc1_, double bc2_) {
   const float lr = (float)lr_, beta1 = (float)beta1_, beta2 = (float)beta2_;
@@ -67,7 +86,7 @@ void oracle_adam_warmup_step(int64_t d, int32_t n, int64_t ld, const void* g, in
   const float omb2 = (float)(1.0 - beta2_);
   for (int64_t k = 0; k < d; ++k) {
     float sum = 0.0f;
-    for (int32_t i = 0; i < n; ++i) sum = sum + grad_at(g, g_is_f16, (int64_t)i * ld + k);
+    for (int32_t i = 0; i < n; ++i) sum = sum + grad_at(g, g_kind, (int64_t)i * ld + k);
     float gbar = sum / (float)n;
     float mk = beta1 * m[k] + omb1 * gbar;
     float vk = beta2 * v[k] + omb2 * (gbar * gbar);
@@ -167,24 +186,24 @@ static void ec_onebit(int64_t d, const int64_t* seg, int32_t n_seg, const float*
  * paragraph for the momentum recurrence):
  *   c = (b1*m + (1-b1)*g) + delta      two products, then two adds
  * with b1 and (1-b1) rounded to binary32 from binary64 as in the warm-up. */
-void oracle_compensate(int64_t len, double beta1_, const float* m, const void* g, int g_is_f16,
+void oracle_compensate(int64_t len, double beta1_, const float* m, const void* g, int g_kind,
                        int64_t g_off, const float* delta, float* c) {
   const float beta1 = (float)beta1_;
   const float omb1 = (float)(1.0 - beta1_);
   for (int64_t k = 0; k < len; ++k) {
-    float p = beta1 * m[k] + omb1 * grad_at(g, g_is_f16, g_off + k);
+    float p = beta1 * m[k] + omb1 * grad_at(g, g_kind, g_off + k);
     c[k] = p + delta[k];
   }
 }
 
 void oracle_compress(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_wseg,
-                     const void* g, int g_is_f16, const float* m, float* delta, uint64_t* wbits,
+                     const void* g, int g_kind, const float* m, float* delta, uint64_t* wbits,
                      float* wscale, double beta1) {
   int64_t W = (d + 63) / 64;
   float* c = (float*)malloc((size_t)(d > 0 ? d : 1) * sizeof(float));
   for (int32_t i = 0; i < n; ++i) {
     float* di = delta + (int64_t)i * ld;
-    oracle_compensate(d, beta1, m, g, g_is_f16, (int64_t)i * ld, di, c);
+    oracle_compensate(d, beta1, m, g, g_kind, (int64_t)i * ld, di, c);
     ec_onebit(d, wseg, n_wseg, c, wbits + (int64_t)i * W, wscale + (int64_t)i * n_wseg, di);
   }
   free(c);
@@ -196,7 +215,7 @@ void oracle_compress(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int3
  *   c   = m_i + delta_i
  * then the same compressor.  m_local, delta: [n][ld], updated in place. */
 void oracle_compress_local(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_wseg,
-                           const void* g, int g_is_f16, float* m_local, float* delta,
+                           const void* g, int g_kind, float* m_local, float* delta,
                            uint64_t* wbits, float* wscale, double beta1_) {
   const float beta1 = (float)beta1_;
   const float omb1 = (float)(1.0 - beta1_);
@@ -206,7 +225,7 @@ void oracle_compress_local(int64_t d, int32_t n, int64_t ld, const int64_t* wseg
     float* mi = m_local + (int64_t)i * ld;
     float* di = delta + (int64_t)i * ld;
     for (int64_t k = 0; k < d; ++k) {
-      mi[k] = beta1 * mi[k] + omb1 * grad_at(g, g_is_f16, (int64_t)i * ld + k);
+      mi[k] = beta1 * mi[k] + omb1 * grad_at(g, g_kind, (int64_t)i * ld + k);
       c[k] = mi[k] + di[k];
     }
     ec_onebit(d, wseg, n_wseg, c, wbits + (int64_t)i * W, wscale + (int64_t)i * n_wseg, di);

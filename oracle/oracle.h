@@ -42,11 +42,13 @@
 extern "C" {
 #endif
 
-/* ---- gradient element access: binary32, or binary16 decoded exactly ---- */
+/* ---- gradient element access: binary32, or binary16 / bfloat16 decoded
+ * exactly; g_kind 0, 1, 2 respectively ----------------------------------- */
 double oracle_half_to_double(uint16_t h);
+double oracle_bfloat16_to_double(uint16_t h);
 
 /* ---- warm-up and freeze -------------------------------------------------- */
-void oracle_adam_warmup_step(int64_t d, int32_t n, int64_t ld, const void* g, int g_is_f16,
+void oracle_adam_warmup_step(int64_t d, int32_t n, int64_t ld, const void* g, int g_kind,
                              float* x, float* m, float* v, double lr, double beta1,
                              double beta2, double eta, double bc1, double bc2);
 void oracle_freeze_variance(int64_t d, const float* v, float* denom, double eta, double bc2);
@@ -62,13 +64,13 @@ int oracle_bit(const uint64_t* bits, int64_t k);
 void oracle_residual(int64_t len, const float* c, float s, float* err);
 
 /* ---- the step, composed ------------------------------------------------- */
-void oracle_compensate(int64_t len, double beta1, const float* m, const void* g, int g_is_f16,
+void oracle_compensate(int64_t len, double beta1, const float* m, const void* g, int g_kind,
                        int64_t g_off, const float* delta, float* c);
 void oracle_compress(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_wseg,
-                     const void* g, int g_is_f16, const float* m, float* delta, uint64_t* wbits,
+                     const void* g, int g_kind, const float* m, float* delta, uint64_t* wbits,
                      float* wscale, double beta1);
 void oracle_compress_local(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_wseg,
-                           const void* g, int g_is_f16, float* m_local, float* delta,
+                           const void* g, int g_kind, float* m_local, float* delta,
                            uint64_t* wbits, float* wscale, double beta1);
 void oracle_server_average(int64_t k0, int64_t k1, int64_t d, int32_t n, const int64_t* wseg,
                            int32_t n_wseg, const uint64_t* wbits, const float* wscale,

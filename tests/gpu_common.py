@@ -17,8 +17,17 @@ def torch():
     return t
 
 
+def is_bf16(a) -> bool:
+    import oracle
+
+    return isinstance(a, oracle.BF16)
+
+
 def to_dev(a: np.ndarray):
     t = torch()
+    if is_bf16(a):  # bfloat16 bit patterns
+        return t.from_numpy(np.ascontiguousarray(a).view(np.int16).copy()).view(
+            t.bfloat16).cuda()
     if a.dtype == np.uint64:
         return t.from_numpy(a.view(np.int64).copy()).cuda()
     return t.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -36,7 +45,7 @@ def padded(a: np.ndarray, ld: int) -> np.ndarray:
     n, d = a.shape
     out = np.full((n, ld), 7.0, dtype=a.dtype)
     out[:, :d] = a
-    return out
+    return out.view(type(a)) if is_bf16(a) else out
 
 
 def assert_close(gpu, ora, what, atol=ATOL, rtol=RTOL):
@@ -59,6 +68,17 @@ def assert_words(gpu, ora, what):
 
 def grads(rng, n, d, dtype, special=True):
     """Gradients with exact zeros, -0.0 and (for fp16) subnormals mixed in."""
+    if dtype == "bf16":  # round-to-nearest-even to bfloat16 (torch), bits for both sides
+        import oracle
+
+        g32 = (1e-3 * synth.student_t3(rng, (n, d))).astype(np.float32)
+        if special and d > 4:
+            z = rng.choice(d, size=max(1, d // 100), replace=False)
+            g32[:, z] = 0.0
+            g32[:, z[: len(z) // 2]] = -0.0
+            g32[0, rng.integers(0, d)] = 1e-40  # a bfloat16 subnormal
+        bits = torch().from_numpy(g32).to(torch().bfloat16).view(torch().int16).numpy()
+        return oracle.bf16(bits.view(np.uint16))
     if dtype == "f16":
         g = (1e-3 * synth.student_t3(rng, (n, d))).astype(np.float16)
         if special and d > 4:

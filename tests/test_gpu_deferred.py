@@ -46,6 +46,7 @@ def same(a, b, what):
 
 @pytest.mark.parametrize("d,n,gdt,tab", [(4096, 2, "f32", "shards"), (2049, 3, "f16", "cuts"),
                                          (300, 2, "f32", "singletons"),
+                                         (20_011, 5, "bf16", "cuts"),
                                          (3_000_017, 8, "f16", "shards"),
                                          (1_000_003, 11, "f32", "cuts")])
 def test_deferred_layout_is_bitwise_the_explicit_step(d, n, gdt, tab):

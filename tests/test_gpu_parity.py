@@ -45,6 +45,7 @@ CASES = [
     (63, 2, "f32", "singletons"),
     (64, 1, "f32", "whole_shards"),
     (65, 2, "f16", "random_cuts"),
+    (129, 3, "bf16", "random_cuts"),
     (2049, 5, "f32", "random_cuts"),
     (4096, 2, "f32", "whole_shards"),
     (4096 + 37, 3, "f32", "many_small"),
@@ -53,6 +54,7 @@ CASES = [
     (131_072 + 5, 8, "f16", "whole_shards"),
     (5_000_003, 3, "f16", "whole_shards"),
     (4_200_007, 4, "f32", "random_cuts"),
+    (1_000_037, 8, "bf16", "whole_shards"),
 ]
 
 
@@ -125,7 +127,8 @@ def test_compress_server_update_match_oracle(case):
 @pytest.mark.parametrize("d,n,gdt,bc", [(1, 1, "f32", False), (4096, 2, "f32", False),
                                         (4096 + 37, 3, "f16", True),
                                         (1_000_003, 8, "f16", False),
-                                        (100_001, 5, "f32", True)])
+                                        (100_001, 5, "f32", True),
+                                        (70_001, 4, "bf16", True)])
 def test_warmup_and_freeze_match_oracle(d, n, gdt, bc):
     say(f"[warmup] d={d} n={n} g={gdt} bias_correction={bc}")
     rng = np.random.default_rng(d + n)

@@ -380,6 +380,44 @@ def test_fp16_gradients_match_their_fp32_image():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and np.array_equal(d1, d2)
 
 
+def test_bfloat16_decode_matches_torch_for_every_pattern():
+    import torch
+
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(pats.view(np.int16).copy()).view(torch.bfloat16).to(
+        torch.float64).numpy()
+    got = np.array([oracle.bfloat16_to_float(int(p)) for p in pats])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert math.copysign(1.0, oracle.bfloat16_to_float(0x8000)) == -1.0
+    assert oracle.bfloat16_to_float(0x0001) == 2.0 ** -133
+
+
+def test_bf16_gradients_match_their_fp32_image():
+    import torch
+
+    rng = np.random.default_rng(9)
+    d, n = 300, 3
+    g32 = (1e-3 * synth.student_t3(rng, (n, d))).astype(np.float32)
+    g32[:, ::7] = 0.0
+    g32[0, 0] = 1e-40  # subnormal in bfloat16
+    tb = torch.from_numpy(g32).to(torch.bfloat16)
+    bits = oracle.bf16(tb.view(torch.int16).numpy().view(np.uint16))
+    image = np.ascontiguousarray(tb.to(torch.float32).numpy())
+    m = rng.normal(0, 1e-3, d).astype(np.float32)
+    d1 = rng.normal(0, 1e-4, (n, d)).astype(np.float32)
+    d2 = d1.copy()
+    a = oracle.compress(bits, m, d1, [0, d], B1)
+    b = oracle.compress(image, m, d2, [0, d], B1)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and np.array_equal(d1, d2)
+    x1, m1, v1 = np.zeros(d, np.float32), m.copy(), np.zeros(d, np.float32)
+    x2, m2, v2 = x1.copy(), m.copy(), v1.copy()
+    oracle.adam_warmup_step(bits, x1, m1, v1, LR, B1, B2, ETA)
+    oracle.adam_warmup_step(image, x2, m2, v2, LR, B1, B2, ETA)
+    assert np.array_equal(x1, x2) and np.array_equal(m1, m2) and np.array_equal(v1, v2)
+
+
 # --------------------------------------------------------------------------
 # bit layout round trips (every pattern up to d = 12, across segments)
 # --------------------------------------------------------------------------
