@@ -55,6 +55,7 @@ CASES = [
     (5_000_003, 3, "f16", "whole_shards"),
     (4_200_007, 4, "f32", "random_cuts"),
     (1_000_037, 8, "bf16", "whole_shards"),
+    (1_000, 4096, "f16", "random_cuts"),  # the most workers a layout takes
 ]
 
 
