@@ -284,3 +284,17 @@ def test_abi_example_compiles_and_links(tmp_path):
                     f"-L{os.path.join(ROOT, 'oracle')}", "-loba", "-loracle"],
                    check=True, capture_output=True)
     assert os.path.exists(out) and hasattr(entry, "build_abi_example")
+
+
+def test_oracle_under_sanitizers(tmp_path):
+    """Every oracle function, built with address and undefined-behaviour
+    sanitizers, on awkward small inputs (no report, finite results)."""
+    exe = str(tmp_path / "oracle_driver")
+    ora = os.path.join(ROOT, "oracle")
+    subprocess.run(["gcc", "-O1", "-g", "-std=c11", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all", "-ffp-contract=off", f"-I{ora}",
+                    os.path.join(ROOT, "tests", "host", "oracle_driver.c"),
+                    os.path.join(ora, "oracle.c"), "-o", exe, "-lm"], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.startswith("checksum ")
