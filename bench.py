@@ -79,14 +79,22 @@ def method_bytes(w):
     return w.n * (gb + 8.25) + 20.25
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank lines (a comment edit does not
+    change a kernel)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def source_hash():
-    """Hash of the kernel sources and of the code that picks their launch
-    grids (everything under csrc/)."""
+    """Hash of the code of the kernels and of the code that picks their
+    launch grids (everything under csrc/), comments excluded."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".hip", ".hpp", ".cpp")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+                h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -12,9 +12,9 @@
 // odd lane byte u of the B half, so every packed byte has one writer.
 // Sums of squares are binary64 per lane (the square of a binary32 value is
 // exact there), reduced across the wave by a butterfly and across the waves
-// through LDS into one partial per (piece, row); a second tiny kernel sums a
-// segment's partials in piece order.  No atomics: results are bitwise
-// reproducible.
+// through LDS into one partial per (piece, row); small kernels then sum a
+// segment's partials in a fixed order (in two stages when a segment has many
+// pieces).  No atomics: results are bitwise reproducible.
 //
 // Method passages are cited in include/oba.h beside each entry point.
 #include <hip/hip_runtime.h>
