@@ -23,14 +23,14 @@ constexpr int kWaves = kBlock / 64;         // wave64s per block
 constexpr int kVec = 8;                     // consecutive coordinates per lane
 constexpr int64_t kSpan = kBlock * kVec;    // coordinates per block pass
 #ifndef OBA_MAX_BLOCKS
-#define OBA_MAX_BLOCKS 65536
+#define OBA_MAX_BLOCKS 262144
 #endif
 #ifndef OBA_MAX_BLOCKS_WORKER
 #define OBA_MAX_BLOCKS_WORKER 2097152
 #endif
 // Streaming grids: the worker-side kernels and the update run best with one
 // span per block (up to 2^21 blocks, 4.3e9 coordinates), the server pass (n
-// packed rows per span) with at least four spans per block.
+// packed rows per span) with four spans per block (up to 2^18 blocks).
 #ifndef OBA_SERVER_SPANS
 #define OBA_SERVER_SPANS 4
 #endif

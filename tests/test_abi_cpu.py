@@ -15,7 +15,7 @@ from communication_compressed_optimizer_02_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "oba.h")
 CSRC = os.path.join(ROOT, "communication_compressed_optimizer_02_amd", "csrc")
-SPAN, MAXB, MAXB_W, SRV_SPANS = 2048, 65536, 1 << 21, 4
+SPAN, MAXB, MAXB_W, SRV_SPANS = 2048, 262144, 1 << 21, 4
 
 
 def declared_symbols():
