@@ -22,11 +22,13 @@ struct oba_layout_s {
   oba::Plan plan;
   int device = -1;
   void* dev_tables = nullptr;
-  oba::SegDev sig_w{};  // worker segments, worker grid (compress kernels)
+  oba::SegDev sig_c{};  // worker segments, compress grid
   oba::SegDev sig{};    // worker segments, server grid
   oba::SegDev tau{};    // server segments, server grid
-  oba::SegDev tau_w{};  // server segments, worker grid (implicit momentum, update)
-  oba::Geo geo_w{};     // worker grid
+  oba::SegDev tau_w{};  // server segments, update grid
+  oba::SegDev tau_c{};  // server segments, compress grid (implicit momentum)
+  oba::Geo geo_w{};     // update grid (one span per block)
+  oba::Geo geo_c{};     // compress grid
   oba::Geo geo{};       // server grid
   size_t ws_worker = 0, ws_server = 0;
 };
@@ -37,7 +39,8 @@ struct oba_tensors_s {
   int32_t T = 0;
   int32_t n = 0;
   void* dev = nullptr;  // one allocation holding every table below
-  oba::TList tl_w{};    // block table of the worker grid
+  oba::TList tl_c{};    // block table of the compress grid
+  oba::TList tl_w{};    // block table of the update grid
   oba::TList tl_s{};    // block table of the server grid
 };
 
@@ -189,12 +192,13 @@ int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const i
     o32[4] = h32.size();
     h32.insert(h32.end(), pc.seg_item.begin(), pc.seg_item.end());
   };
-  size_t w64[2], w32[5], v64[2], v32[5], s64[2], s32[5], t64[2], t32[5];
+  size_t w64[2], w32[5], v64[2], v32[5], s64[2], s32[5], t64[2], t32[5], c64[2], c32[5];
   try {
     put(P.wp, P.wseg, w64, w32);
     put(P.wp_s, P.wseg, v64, v32);
     put(P.sp, P.sseg, s64, s32);
     put(P.sp_w, P.sseg, t64, t32);
+    put(P.sp_c, P.sseg, c64, c32);
   } catch (...) {
     delete L;
     return OBA_ENOMEM;
@@ -233,13 +237,15 @@ int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const i
     s.n_items = pc.item_q.empty() ? 0 : (int32_t)pc.item_q.size() - 1;
     return s;
   };
-  L->sig_w = view(P.wp, w64, w32, (int32_t)P.wseg.size() - 1);
+  L->sig_c = view(P.wp, w64, w32, (int32_t)P.wseg.size() - 1);
   L->sig = view(P.wp_s, v64, v32, (int32_t)P.wseg.size() - 1);
   L->tau = view(P.sp, s64, s32, (int32_t)P.sseg.size() - 1);
   L->tau_w = view(P.sp_w, t64, t32, (int32_t)P.sseg.size() - 1);
+  L->tau_c = view(P.sp_c, c64, c32, (int32_t)P.sseg.size() - 1);
   L->geo_w = oba::Geo{P.d, P.ld, P.W, P.S, P.n, P.nblk_w};
+  L->geo_c = oba::Geo{P.d, P.ld, P.W, P.S, P.n, P.nblk_c};
   L->geo = oba::Geo{P.d, P.ld, P.W, P.S, P.n, P.nblk};
-  L->ws_worker = std::max(oba::partial_bytes(L->sig_w, P.n), oba::partial_bytes(L->sig, P.n));
+  L->ws_worker = std::max(oba::partial_bytes(L->sig_c, P.n), oba::partial_bytes(L->sig, P.n));
   L->ws_server = oba::partial_bytes(L->tau, 1);
   *out = L;
   return OBA_OK;
@@ -344,7 +350,7 @@ int oba_compress(oba_layout L, const void* g, int g_dtype, const float* m, float
   OBA_TRY(check_buf(wscale, 4));
   OBA_TRY(check_buf(ws, 8));
   if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
-  const oba::Geo G = L->geo_w;
+  const oba::Geo G = L->geo_c;
   double* part = static_cast<double*>(ws);
   const float b1 = (float)beta1, omb1 = (float)(1.0 - beta1);
   uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
@@ -357,7 +363,7 @@ int oba_compress(oba_layout L, const void* g, int g_dtype, const float* m, float
   OBA_TRY(launch("finalize_scales", stream,
                  [&] { oba::launch_finalize(part, G.n, L->sig, wscale, stream); }));
   return launch("compress_p2", stream, [&] {
-    oba::launch_compress_apply(G, g, g_dtype, m, delta, wbytes, L->sig_w, wscale, b1,
+    oba::launch_compress_apply(G, g, g_dtype, m, delta, wbytes, L->sig_c, wscale, b1,
                                omb1, stream);
   });
 }
@@ -411,17 +417,17 @@ int oba_compress_deferred(oba_layout L, const void* g, int g_dtype, const float*
   OBA_TRY(check_buf(wscale, 4));
   OBA_TRY(check_buf(ws, 8));
   if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
-  const oba::Geo G = L->geo_w;
+  const oba::Geo G = L->geo_c;
   double* part = static_cast<double*>(ws);
   const float b1 = (float)beta1, omb1 = (float)(1.0 - beta1);
   uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
-  const oba::MomSrc ms{reinterpret_cast<const uint8_t*>(sbits_prev), sscale_prev, L->tau_w};
+  const oba::MomSrc ms{reinterpret_cast<const uint8_t*>(sbits_prev), sscale_prev, L->tau_c};
   OBA_TRY(launch("compress_deferred", stream, [&] {
-    oba::launch_compress_deferred(G, g, g_dtype, m, c, wbytes, L->sig_w, part, wscale,
+    oba::launch_compress_deferred(G, g, g_dtype, m, c, wbytes, L->sig_c, part, wscale,
                                   b1, omb1, ms, stream);
   }));
   return launch("finalize_scales", stream,
-                [&] { oba::launch_finalize(part, G.n, L->sig_w, wscale, stream); });
+                [&] { oba::launch_finalize(part, G.n, L->sig_c, wscale, stream); });
 }
 
 int oba_compress_deferred_local(oba_layout L, const void* g, int g_dtype, float* m_local,
@@ -439,16 +445,16 @@ int oba_compress_deferred_local(oba_layout L, const void* g, int g_dtype, float*
   OBA_TRY(check_buf(ws, 8));
   if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
   if ((const void*)m_local == (const void*)c) return OBA_EINVAL;
-  const oba::Geo G = L->geo_w;
+  const oba::Geo G = L->geo_c;
   double* part = static_cast<double*>(ws);
   const float b1 = (float)beta1, omb1 = (float)(1.0 - beta1);
   uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
   OBA_TRY(launch("compress_deferred_local", stream, [&] {
-    oba::launch_compress_deferred_local(G, g, g_dtype, m_local, c, wbytes, L->sig_w,
+    oba::launch_compress_deferred_local(G, g, g_dtype, m_local, c, wbytes, L->sig_c,
                                         part, wscale, b1, omb1, stream);
   }));
   return launch("finalize_scales", stream,
-                [&] { oba::launch_finalize(part, G.n, L->sig_w, wscale, stream); });
+                [&] { oba::launch_finalize(part, G.n, L->sig_c, wscale, stream); });
 }
 
 int oba_server_reduce_recompress_deferred(oba_layout L, const uint64_t* wbits,
@@ -550,29 +556,27 @@ int oba_tensors_create(oba_tensors* out, oba_layout L, int32_t n_tensors,
   const uintptr_t galign = g_dtype == OBA_F32 ? 16 : 8;  // a quad: 16 or 8 bytes
   for (int32_t t = 0; t < T; ++t) OBA_TRY(check_buf(x_ptrs[t], 16));
   for (int64_t r = 0; r < (int64_t)n * T; ++r) OBA_TRY(check_buf(g_ptrs[r], galign));
-  std::vector<int32_t> bw, bs;
+  // per-block tensor tables of the compress, update and server grids
+  std::vector<oba::TBlk> tc, tw, ts;
   try {
-    oba::tensor_blocks(P, P.nblk_w, off, &bw);
-    oba::tensor_blocks(P, P.nblk, off, &bs);
-  } catch (...) {
-    return OBA_ENOMEM;
-  }
-  std::vector<oba::TBlk> tw, ts;
-  try {
-    for (auto* pr : {&bw, &bs}) {
-      auto& dst = pr == &bw ? tw : ts;
-      dst.resize(pr->size());
-      for (size_t b = 0; b < pr->size(); ++b) {
-        const int32_t t = (*pr)[b];
-        dst[b] = oba::TBlk{off[t], off[t + 1], t, 0};
+    std::vector<int32_t> first;
+    for (auto pr : {std::make_pair(P.nblk_c, &tc), std::make_pair(P.nblk_w, &tw),
+                    std::make_pair(P.nblk, &ts)}) {
+      oba::tensor_blocks(P, pr.first, off, &first);
+      pr.second->resize(first.size());
+      for (size_t b = 0; b < first.size(); ++b) {
+        const int32_t t = first[b];
+        (*pr.second)[b] = oba::TBlk{off[t], off[t + 1], t, 0};
       }
     }
   } catch (...) {
     return OBA_ENOMEM;
   }
-  // layout of the allocation: block tables (worker, server grid) | off | g
-  // pointers | x pointers
-  const size_t b_bw = tw.size() * sizeof(oba::TBlk), b_bs = ts.size() * sizeof(oba::TBlk);
+  // layout of the allocation: block tables (compress, update, server grid) |
+  // off | g pointers | x pointers
+  const size_t b_bc = tc.size() * sizeof(oba::TBlk);
+  const size_t b_bw = b_bc + tw.size() * sizeof(oba::TBlk);  // tables up to tw
+  const size_t b_bs = ts.size() * sizeof(oba::TBlk);
   const size_t b_off = off.size() * sizeof(int64_t);
   const size_t b_g = (size_t)n * T * sizeof(void*);
   const size_t b_x = (size_t)T * sizeof(float*);
@@ -590,7 +594,8 @@ int oba_tensors_create(oba_tensors* out, oba_layout L, int32_t n_tensors,
   }
   char* base = static_cast<char*>(H->dev);
   const std::pair<const void*, size_t> parts[] = {
-      {tw.data(), b_bw}, {ts.data(), b_bs}, {off.data(), b_off}, {g_ptrs, b_g}, {x_ptrs, b_x}};
+      {tc.data(), b_bc}, {tw.data(), b_bw - b_bc}, {ts.data(), b_bs}, {off.data(), b_off},
+      {g_ptrs, b_g}, {x_ptrs, b_x}};
   size_t at = 0;
   for (const auto& pr : parts) {
     if (pr.second) e = hipMemcpy(base + at, pr.first, pr.second, hipMemcpyHostToDevice);
@@ -606,8 +611,10 @@ int oba_tensors_create(oba_tensors* out, oba_layout L, int32_t n_tensors,
   tl.g = reinterpret_cast<const void* const*>(base + b_bw + b_bs + b_off);
   tl.x = reinterpret_cast<float* const*>(base + b_bw + b_bs + b_off + b_g);
   tl.T = T;
+  H->tl_c = tl;
+  H->tl_c.blk = reinterpret_cast<const oba::TBlk*>(base);
   H->tl_w = tl;
-  H->tl_w.blk = reinterpret_cast<const oba::TBlk*>(base);
+  H->tl_w.blk = reinterpret_cast<const oba::TBlk*>(base + b_bc);
   H->tl_s = tl;
   H->tl_s.blk = reinterpret_cast<const oba::TBlk*>(base + b_bw);
   *out = H;
@@ -669,17 +676,17 @@ int oba_compress_deferred_listed(oba_layout L, oba_tensors H, const float* m,
   OBA_TRY(check_buf(wscale, 4));
   OBA_TRY(check_buf(ws, 8));
   if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
-  const oba::Geo G = L->geo_w;
+  const oba::Geo G = L->geo_c;
   double* part = static_cast<double*>(ws);
   const float b1 = (float)beta1, omb1 = (float)(1.0 - beta1);
   uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
-  const oba::MomSrc ms{reinterpret_cast<const uint8_t*>(sbits_prev), sscale_prev, L->tau_w};
+  const oba::MomSrc ms{reinterpret_cast<const uint8_t*>(sbits_prev), sscale_prev, L->tau_c};
   OBA_TRY(launch("compress_deferred", stream, [&] {
-    oba::launch_compress_deferred_listed(G, H->tl_w, H->g_dtype, m, c, wbytes,
-                                         L->sig_w, part, wscale, b1, omb1, ms, stream);
+    oba::launch_compress_deferred_listed(G, H->tl_c, H->g_dtype, m, c, wbytes,
+                                         L->sig_c, part, wscale, b1, omb1, ms, stream);
   }));
   return launch("finalize_scales", stream,
-                [&] { oba::launch_finalize(part, G.n, L->sig_w, wscale, stream); });
+                [&] { oba::launch_finalize(part, G.n, L->sig_c, wscale, stream); });
 }
 
 int oba_decompress_update_listed(oba_layout L, oba_tensors H, const uint64_t* sbits,

@@ -37,6 +37,10 @@ constexpr int64_t kSpan = kBlock * kVec;    // coordinates per block pass
 constexpr int kMaxBlocks = OBA_MAX_BLOCKS;
 constexpr int kServerSpans = OBA_SERVER_SPANS;  // least spans per block of the server grid
 constexpr int kMaxBlocksWorker = OBA_MAX_BLOCKS_WORKER;
+// Spans per block of the compress grid: one when a block holds four workers
+// or more; with fewer workers per block a block does too little work per
+// span, and 4/n spans per block measured 16 % faster for one worker.
+inline int32_t compress_spans(int32_t n) { return n >= 4 ? 1 : 4 / n; }
 constexpr int32_t kMaxWorkers = 4096;
 
 // A segment cut into more than kSplitAbove pieces has its partials summed in
@@ -59,12 +63,14 @@ struct Plan {
   int64_t d = 0, ld = 0, W = 0, S = 0;
   int32_t n = 0;
   int32_t nblk = 0;    // grid of the server, residual, warm-up, freeze, norm kernels
-  int32_t nblk_w = 0;  // grid of the worker-side compress kernels and the update
+  int32_t nblk_w = 0;  // grid of the update (one span per block)
+  int32_t nblk_c = 0;  // grid of the worker-side compress kernels
   std::vector<int64_t> wseg, sseg;  // offsets, n_seg+1 each
-  Pieces wp;    // worker segments cut on the worker grid (compress kernels)
+  Pieces wp;    // worker segments cut on the compress grid
   Pieces wp_s;  // worker segments cut on the server grid (scale lookups there)
   Pieces sp;    // server segments cut on the server grid
-  Pieces sp_w;  // server segments cut on the worker grid (update, implicit momentum)
+  Pieces sp_w;  // server segments cut on the update grid
+  Pieces sp_c;  // server segments cut on the compress grid (implicit momentum)
 };
 
 // Status codes mirror the C ABI (0 ok, negative error).

@@ -1,13 +1,13 @@
 // plan_driver.cpp -- test driver for the host-only piece planner.
 // Usage: plan_driver d n ld n_wseg o_0 .. o_nw n_sseg o_0 .. o_ns
-// Prints "rc <status>", then "G d W S nblk nblk_w", then for the worker
-// segments on the worker grid, the worker segments on the server grid, the
-// server segments on the server grid and the server segments on the worker
-// grid: "T <n_pieces> <n_seg>", one
+// Prints "rc <status>", then "G d W S nblk nblk_w nblk_c", then for the
+// worker segments on the compress grid, the worker segments on the server
+// grid, the server segments on the server grid, on the update grid and on the
+// compress grid: "T <n_pieces> <n_seg>", one
 // "P lo hi seg" line per piece, "B" + blk_first, "S" + seg_first, "I" +
 // item_q, "J" + seg_item (the last two empty for one-stage sums).  With a
 // tensor list appended ("nt l_0 .. l_{nt-1}"): "TO <status>", then for the
-// worker grid and the server grid "TB" + the first tensor of each block.  Built by the test suite with the host compiler and
+// update, server and compress grids "TB" + the first tensor of each block.  Built by the test suite with the host compiler and
 // sanitizers; it calls nothing of HIP.
 #include <cstdio>
 #include <cstdlib>
@@ -44,12 +44,13 @@ int main(int argc, char** argv) {
   int rc = oba::make_plan(d, (int32_t)n, ld, w.data(), nw, s.data(), ns, &P);
   std::printf("rc %d\n", rc);
   if (rc) return 0;
-  std::printf("G %lld %lld %lld %d %d\n", (long long)P.d, (long long)P.W, (long long)P.S,
-              P.nblk, P.nblk_w);
+  std::printf("G %lld %lld %lld %d %d %d\n", (long long)P.d, (long long)P.W, (long long)P.S,
+              P.nblk, P.nblk_w, P.nblk_c);
   dump(P.wp, nw);
   dump(P.wp_s, nw);
   dump(P.sp, ns);
   dump(P.sp_w, ns);
+  dump(P.sp_c, ns);
   // optional tensor list: nt l_0 .. l_{nt-1}
   if (a < argc) {
     const int nt = (int)next();
@@ -59,7 +60,7 @@ int main(int argc, char** argv) {
     const int trc = oba::tensor_offsets(P, nt, len.data(), &off);
     std::printf("TO %d\n", trc);
     if (trc == 0) {
-      for (int32_t nb : {P.nblk_w, P.nblk}) {
+      for (int32_t nb : {P.nblk_w, P.nblk, P.nblk_c}) {
         std::vector<int32_t> first;
         oba::tensor_blocks(P, nb, off, &first);
         std::printf("TB");

@@ -80,10 +80,11 @@ def run_plan(exe, d, n, wseg, sseg, ld=None):
     rc = int(out[0].split()[1])
     if rc:
         return rc, None
-    _, dd, W, S, nblk, nblk_w = out[1].split()
-    res = dict(d=int(dd), W=int(W), S=int(S), nblk=int(nblk), nblk_w=int(nblk_w), tabs=[])
+    _, dd, W, S, nblk, nblk_w, nblk_c = out[1].split()
+    res = dict(d=int(dd), W=int(W), S=int(S), nblk=int(nblk), nblk_w=int(nblk_w),
+               nblk_c=int(nblk_c), tabs=[])
     i = 2
-    for _ in range(4):
+    for _ in range(5):
         _, npc, nseg = out[i].split()
         i += 1
         pcs = [tuple(map(int, out[i + k].split()[1:])) for k in range(int(npc))]
@@ -115,12 +116,12 @@ def check_items(segf, items, seg_item):
 
 def check_pieces(res, offs):
     """offs: (worker table, server table); tables: worker segments on the
-    worker grid, worker segments on the server grid, server segments on the
-    server grid, server segments on the worker grid."""
+    compress grid, worker segments on the server grid, server segments on the
+    server grid, on the update grid and on the compress grid."""
     d, S = res["d"], res["S"]
-    grids = (res["nblk_w"], res["nblk"], res["nblk"], res["nblk_w"])
+    grids = (res["nblk_c"], res["nblk"], res["nblk"], res["nblk_w"], res["nblk_c"])
     for (pcs, blk, segf, items, seg_item), off, nblk in zip(
-            res["tabs"], (offs[0], offs[0], offs[1], offs[1]), grids):
+            res["tabs"], (offs[0], offs[0], offs[1], offs[1], offs[1]), grids):
         check_items(segf, items, seg_item)
         assert len(blk) == nblk + 1 and blk[0] == 0 and blk[-1] == len(pcs)
         # pieces tile [0, d) in order
@@ -159,6 +160,8 @@ def test_planner_pieces_under_sanitizers(driver, d, n, wseg, sseg):
     assert res["W"] == (d + 63) // 64 and res["S"] == -(-d // SPAN)
     assert res["nblk"] == min(-(-res["S"] // SRV_SPANS), MAXB)
     assert res["nblk_w"] == min(res["S"], MAXB_W)
+    spc = 1 if n >= 4 else 4 // n
+    assert res["nblk_c"] == min(-(-res["S"] // spc), MAXB_W)
     check_pieces(res, [wseg, sseg])
 
 
@@ -233,9 +236,9 @@ def run_tensors(exe, d, n, lengths):
     rc = int(out[i].split()[1])
     if rc:
         return rc, None, None
-    _, dd, W, S, nblk, nblk_w = out[1].split()
-    firsts = [list(map(int, out[i + 1 + k].split()[1:])) for k in range(2)]
-    return 0, (int(S), int(nblk_w), int(nblk)), firsts
+    _, dd, W, S, nblk, nblk_w, nblk_c = out[1].split()
+    firsts = [list(map(int, out[i + 1 + k].split()[1:])) for k in range(3)]
+    return 0, (int(S), int(nblk_w), int(nblk), int(nblk_c)), firsts
 
 
 def test_tensor_list_block_tables(driver):
@@ -245,10 +248,11 @@ def test_tensor_list_block_tables(driver):
         cases.append([4 * int(x) for x in rng.integers(1, 3000, size=rng.integers(1, 60))])
     for lengths in cases:
         d = sum(lengths)
-        rc, (S, nblk_w, nblk), firsts = run_tensors(driver, d, 3, lengths)
+        n = 1 + len(lengths) % 4  # 1..4 workers: compress grids of 4, 2, 1 spans per block
+        rc, (S, nblk_w, nblk, nblk_c), firsts = run_tensors(driver, d, n, lengths)
         assert rc == 0
         off = np.concatenate([[0], np.cumsum(lengths)])
-        for nb, first in zip((nblk_w, nblk), firsts):
+        for nb, first in zip((nblk_w, nblk, nblk_c), firsts):
             assert len(first) == nb
             for b, t in enumerate(first):
                 k = (b * S // nb) * SPAN
