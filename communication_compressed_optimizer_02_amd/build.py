@@ -31,6 +31,8 @@ HIP_FLAGS = [
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+# one translation unit per pass, plus the C ABI
+HIP_SOURCES = ("warmup.hip", "compress.hip", "scales.hip", "server.hip", "update.hip", "api.hip")
 
 
 def hipcc() -> str:
@@ -54,7 +56,7 @@ def build(verbose: bool = False) -> str:
     o = os.path.join(obj_dir, "layout.o")
     run(["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "layout.cpp"), "-o", o])
     objs.append(o)
-    for src in ("kernels.hip", "api.hip"):
+    for src in HIP_SOURCES:
         o = os.path.join(obj_dir, src.replace(".hip", ".o"))
         run([hipcc(), *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", o])
         objs.append(o)

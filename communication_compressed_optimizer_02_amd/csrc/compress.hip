@@ -1,0 +1,351 @@
+// compress.hip -- the worker pass: momentum, error feedback, 1-bit compression (gfx950).
+// Method passages are cited in include/oba.h beside each entry point.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "device.hpp"
+
+namespace oba {
+
+// ===========================================================================
+// Worker side, for NB workers at once (m is read once per coordinate):
+//   c = (b1*m + (1-b1)*g_i) + delta_i
+// kNorm:  only reduce sum c^2 per (piece, worker) -- reads only;
+// kApply: recompute c bit for bit, store the sign bits and
+//         delta_i = c - s*sign(c) with the finished scales;
+// kDeferred: the state row holds the previous step's c (not delta) and the
+//         scale buffer its scales s'; the residual of the last step is formed
+//         where it is consumed, delta_i = c' - s'*sign(c'), then
+//         c = (b1*m + (1-b1)*g_i) + delta_i is stored over c' with its sign
+//         bits and its sum c^2 is reduced -- one pass instead of two;
+// kDeferredM: as kDeferred, but m is not read: after a compression step
+//         every worker's momentum is the server's m_hat = sbar*sign, so it is
+//         rebuilt from the last packed server bits and scales (1/8 byte
+//         instead of 4 bytes per coordinate);
+// kDeferredLocal: as kDeferred with per-worker momentum: m is [n][ld], each
+//         worker's m_i = b1*m_i + (1-b1)*g_i is stored back and
+//         c = m_i + delta_i.
+// The scale needs the whole segment's norm before any residual can be
+// written, so the explicit layout needs c twice.  Recomputing it reads g, m,
+// delta twice but never writes c: on this HBM, writes cost more than reads,
+// and storing c in a first pass to re-read it was measured 15 % slower per
+// step.
+// NB is the exact number of workers of a block: a launch covers workers
+// [i0, i0 + gridDim.y*NB); larger n takes one launch of full groups and one
+// for the remainder.  Grid: (nblk, groups).
+// ===========================================================================
+enum { kNorm = 1, kApply = 2, kDeferred = 3, kDeferredM = 4, kDeferredLocal = 5 };
+#ifndef OBA_WORKER_BATCH
+#define OBA_WORKER_BATCH 4
+#endif
+constexpr int kWorkerBatch = OBA_WORKER_BATCH;
+
+// Optional occupancy target of the worker pass (waves per SIMD), a tuning knob.
+#ifdef OBA_CMP_WAVES
+#define OBA_CMP_ATTR __attribute__((amdgpu_waves_per_eu(OBA_CMP_WAVES, OBA_CMP_WAVES)))
+#else
+#define OBA_CMP_ATTR
+#endif
+
+template <typename GT, int NB, int MODE, bool TL>
+__global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t i0, const GT* __restrict__ g,
+                                                     float* __restrict__ m,  // read; written by kDeferredLocal
+                                                     float* __restrict__ delta,
+                                                     uint8_t* __restrict__ wbytes, SegDev sig,
+                                                     double* __restrict__ part,
+                                                     const float* __restrict__ wscale, float b1,
+                                                     float omb1, MomSrc ms, TList tl) {
+  __shared__ double lds[kWaves * NB];
+  const int32_t b = blockIdx.x;
+  i0 += blockIdx.y * NB;  // this block's workers: [i0, i0 + NB)
+  const int64_t s_lo = dspan(G.S, G.nblk, b), s_hi = dspan(G.S, G.nblk, b + 1);
+  const int32_t p_end = sig.blk_first[b + 1];
+  int32_t p = sig.blk_first[b];
+  int64_t p_hi = sig.phi[p];
+  static_assert(!TL || MODE >= kDeferred, "tensor lists: deferred passes only");
+  TCur tcur{};  // tensor cursor (tensor lists)
+  if constexpr (TL) tcur = tcur_start(tl, b);
+  // kDeferredM: cursor over the server segments (on this grid) for sbar
+  int32_t pt = 0, pt_end = 0;
+  int64_t pt_hi = 0;
+  if (MODE == kDeferredM) {
+    pt = ms.tau.blk_first[b];
+    pt_end = ms.tau.blk_first[b + 1];
+    pt_hi = ms.tau.phi[pt];
+  }
+  const int64_t rowbytes = G.W * 8;
+  double acc[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) acc[i] = 0.0;
+
+  for (int64_t s = s_lo; s < s_hi; ++s) {
+    const int64_t lo = s * kSpan;
+    const int64_t hi = min(lo + kSpan, G.d);
+    const Quads q = quads(lo);
+    const bool uniform = hi <= p_hi;  // span inside the current piece
+    const bool full = lo + kSpan <= G.d;
+    int32_t jseg[8];
+    if (MODE != kNorm && !uniform) lane_segs(sig.off, sig.pseg[p], q, G.d, jseg);
+    LaneT lt{};
+    if constexpr (TL) {
+      tcur_advance(tl, tcur, lo);
+      lt = lane_tensors(tl, tcur, q, min(lo + kSpan, G.d), G.d);
+    }
+    // every load of the span first (all NB workers), then the arithmetic
+    float mv[8];
+    if (MODE == kDeferredM) {  // m = sbar*sign from the last server message
+      const uint32_t bits = full ? load_sign_bits<true, OBA_PAIRS_CMP>(ms.sbytes, q, G.d)
+                                 : load_sign_bits<false, OBA_PAIRS_CMP>(ms.sbytes, q, G.d);
+      float sb[8];
+      if (hi <= pt_hi) {
+        const float s_ = ms.sscale[ms.tau.pseg[pt]];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sb[j] = s_;
+      } else {
+        int32_t jt[8];
+        lane_segs(ms.tau.off, ms.tau.pseg[pt], q, G.d, jt);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sb[j] = ms.sscale[jt[j]];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        mv[j] = (!full && coord(q, j) >= G.d) ? 0.0f : (((bits >> j) & 1u) ? -sb[j] : sb[j]);
+      while (pt < pt_end && pt_hi <= hi) {
+        if (++pt < pt_end) pt_hi = ms.tau.phi[pt];
+      }
+    } else if (MODE == kDeferredLocal) {  // per-worker rows, loaded with g below
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mv[j] = 0.0f;
+    } else if (full) {
+      load_full(m, q, mv);
+    } else {
+      load_tail(m, q, G.d, mv);
+    }
+    double fs[NB];
+    // workers in batches of NBB: all loads of a batch, then its arithmetic
+    // and stores (NBB < NB trades loads in flight per wave for occupancy)
+    constexpr int NBB = NB < kWorkerBatch ? NB : kWorkerBatch;
+#pragma unroll
+    for (int ib = 0; ib < NB; ib += NBB) {
+      constexpr int NBL = MODE == kDeferredLocal ? NBB : 1;  // per-worker m rows
+      float gv[NBB][8], c[NBB][8], ml[NBL][8];
+      // ib + u < NB is decided at compile time: a last batch may be partial
+      if (full) {
+#pragma unroll
+        for (int u = 0; u < NBB; ++u) {
+          if (ib + u >= NB) break;
+          const int64_t row = (int64_t)(i0 + ib + u) * G.ld;
+          if constexpr (TL)
+            load_listed<GT>(tl, i0 + ib + u, lt, full, gv[u]);
+          else
+            load_full(g + row, q, gv[u]);
+          load_full(delta + row, q, c[u]);
+          if (MODE == kDeferredLocal) load_full(m + row, q, ml[u]);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < NBB; ++u) {
+          if (ib + u >= NB) break;
+          const int64_t row = (int64_t)(i0 + ib + u) * G.ld;
+          if constexpr (TL)
+            load_listed<GT>(tl, i0 + ib + u, lt, full, gv[u]);
+          else
+            load_tail(g + row, q, G.d, gv[u]);
+          load_tail(delta + row, q, G.d, c[u]);
+          if (MODE == kDeferredLocal) load_tail(m + row, q, G.d, ml[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NBB; ++u) {
+        const int i = ib + u;
+        if (i >= NB) break;
+        const int64_t row = (int64_t)(i0 + i) * G.ld;
+        const float* sc = wscale + (int64_t)(i0 + i) * sig.n_seg;
+        float sv[8];
+        if (MODE != kNorm) {
+          if (uniform) {
+            const float s_ = sc[sig.pseg[p]];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sv[j] = s_;
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sv[j] = sc[jseg[j]];
+          }
+        }
+        if (MODE >= kDeferred) {  // c[u] holds c' of the last step
+#pragma unroll
+          for (int j = 0; j < 8; ++j) c[u][j] = residual(c[u][j], sv[j]);
+          if (!full) {  // coordinates past d read as 0 and must stay 0 (no bit, no c^2)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (coord(q, j) >= G.d) c[u][j] = 0.0f;
+          }
+        }
+        if (MODE == kDeferredLocal) {
+          // the same two products and two adds as compensate(), m_i kept
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            ml[u][j] = b1 * ml[u][j] + omb1 * gv[u][j];
+            c[u][j] = ml[u][j] + c[u][j];
+          }
+          store8(m + row, q, G.d, full, ml[u]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) c[u][j] = compensate(b1, omb1, mv[j], gv[u][j], c[u][j]);
+        }
+        if (MODE != kNorm) store_sign_bits(wbytes + (int64_t)(i0 + i) * rowbytes, q, sign_bits(c[u]), rowbytes);
+        if (MODE >= kDeferred) store8(delta + row, q, G.d, full, c[u]);
+        fs[i] = (MODE != kApply) ? sumsq8(c[u]) : 0.0;
+        if (MODE == kApply) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) c[u][j] = residual(c[u][j], sv[j]);
+          store8(delta + row, q, G.d, full, c[u]);
+        }
+      }
+    }
+    if (MODE == kApply) {
+      while (p < p_end && p_hi <= hi) {
+        if (++p < p_end) p_hi = sig.phi[p];
+      }
+    } else if (uniform) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) acc[i] += fs[i];
+      if (hi == p_hi) {
+        flush_rows<NB>(acc, NB, part + (int64_t)i0 * sig.n_pieces + p, sig.n_pieces, lds);
+        if (++p < p_end) p_hi = sig.phi[p];
+      }
+    } else {  // span crosses piece boundaries: sum this lane's c piece by piece
+      int64_t cur = lo;
+      while (cur < hi) {
+        const int64_t e = min(p_hi, hi);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const int64_t row = (int64_t)(i0 + i) * G.ld;
+          if (MODE >= kDeferred)
+            acc[i] += sumsq_range(delta + row, q, cur, e);  // c was stored there
+          else
+            acc[i] += sumsq_range_c(m, g + row, delta + row, b1, omb1, q, cur, e);
+        }
+        if (p_hi <= hi) {
+          flush_rows<NB>(acc, NB, part + (int64_t)i0 * sig.n_pieces + p, sig.n_pieces, lds);
+          if (++p < p_end) p_hi = sig.phi[p];
+        }
+        cur = e;
+      }
+    }
+  }
+}
+
+// ---- launchers ----------------------------------------------------------------
+
+template <typename GT, int NB, int MODE, bool TL>
+static void launch_cmp(const Geo& G, int32_t i0, int groups, const void* g, const float* m,
+                       float* delta, uint8_t* wbytes, const SegDev& sig, double* part,
+                       const float* wscale, float b1, float omb1, const MomSrc& ms,
+                       const TList& tl, hipStream_t st) {
+  hipLaunchKernelGGL((k_compress<GT, NB, MODE, TL>), dim3(G.nblk, groups), dim3(kBlock), 0, st,
+                     G, i0, static_cast<const GT*>(g), const_cast<float*>(m), delta, wbytes, sig,
+                     part, wscale, b1, omb1, ms, tl);
+}
+
+// Groups of GROUP workers per block, then one launch for the remainder.  A
+// pass that reads m shares it across the block's workers (4 bytes per
+// coordinate per group); the implicit momentum costs 1/8 byte per group, so
+// that pass can take smaller groups (fewer registers, more blocks).
+#ifndef OBA_MAX_NB
+#define OBA_MAX_NB 8
+#endif
+#ifndef OBA_IMPLICIT_NB
+#define OBA_IMPLICIT_NB 4
+#endif
+constexpr int kMaxNB = OBA_MAX_NB;
+constexpr int kImplicitNB = OBA_IMPLICIT_NB;
+static_assert(kMaxNB >= 1 && kMaxNB <= 8 && kImplicitNB >= 1 && kImplicitNB <= 8,
+              "worker groups hold 1 to 8 workers");
+
+template <typename GT, int MODE, bool TL>
+static void launch_cmp_n(const Geo& G, const void* g, const float* m, float* delta,
+                         uint8_t* wbytes, const SegDev& sig, double* part, const float* wscale,
+                         float b1, float omb1, const MomSrc& ms, const TList& tl,
+                         hipStream_t st) {
+  constexpr int GROUP = (MODE == kDeferredM || MODE == kDeferredLocal) ? kImplicitNB : kMaxNB;
+  const int full = G.n / GROUP, rem = G.n % GROUP, i0 = full * GROUP;
+#define OBA_CMP(NB_, I0, GROUPS) \
+  launch_cmp<GT, NB_, MODE, TL>(G, I0, GROUPS, g, m, delta, wbytes, sig, part, wscale, b1, omb1, \
+                                ms, tl, st)
+  if (full) OBA_CMP(GROUP, 0, full);
+  switch (rem) {
+    case 1: OBA_CMP(1, i0, 1); break;
+    case 2: OBA_CMP(2, i0, 1); break;
+    case 3: OBA_CMP(3, i0, 1); break;
+    case 4: OBA_CMP(4, i0, 1); break;
+    case 5: OBA_CMP(5, i0, 1); break;
+    case 6: OBA_CMP(6, i0, 1); break;
+    case 7: OBA_CMP(7, i0, 1); break;
+    default: break;
+  }
+#undef OBA_CMP
+}
+
+template <int MODE, bool TL = false>
+static void launch_cmp_t(const Geo& G, const void* g, int gdt, const float* m, float* delta,
+                         uint8_t* wbytes, const SegDev& sig, double* part, const float* wscale,
+                         float b1, float omb1, const MomSrc& ms, hipStream_t st,
+                         const TList& tl = TList{}) {
+  if (gdt == kGradF16)
+    launch_cmp_n<uint16_t, MODE, TL>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms, tl,
+                                     st);
+  else if (gdt == kGradBF16)
+    launch_cmp_n<bf16_bits, MODE, TL>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms,
+                                      tl, st);
+  else
+    launch_cmp_n<float, MODE, TL>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms, tl,
+                                  st);
+}
+
+void launch_compress_norm(const Geo& G, const void* g, int gdt, const float* m,
+                          const float* delta, const SegDev& sig, double* part, float b1,
+                          float omb1, hipStream_t st) {
+  launch_cmp_t<kNorm>(G, g, gdt, m, const_cast<float*>(delta), nullptr, sig, part, nullptr, b1,
+                      omb1, MomSrc{}, st);
+}
+
+void launch_compress_deferred(const Geo& G, const void* g, int gdt, const float* m, float* c,
+                              uint8_t* wbytes, const SegDev& sig, double* part,
+                              const float* wscale_prev, float b1, float omb1, const MomSrc& ms,
+                              hipStream_t st) {
+  if (ms.sbytes)
+    launch_cmp_t<kDeferredM>(G, g, gdt, nullptr, c, wbytes, sig, part, wscale_prev, b1, omb1, ms,
+                             st);
+  else
+    launch_cmp_t<kDeferred>(G, g, gdt, m, c, wbytes, sig, part, wscale_prev, b1, omb1, ms, st);
+}
+
+void launch_compress_deferred_listed(const Geo& G, const TList& tl, int gdt, const float* m,
+                                     float* c, uint8_t* wbytes, const SegDev& sig, double* part,
+                                     const float* wscale_prev, float b1, float omb1,
+                                     const MomSrc& ms, hipStream_t st) {
+  if (ms.sbytes)
+    launch_cmp_t<kDeferredM, true>(G, nullptr, gdt, nullptr, c, wbytes, sig, part, wscale_prev,
+                                   b1, omb1, ms, st, tl);
+  else
+    launch_cmp_t<kDeferred, true>(G, nullptr, gdt, m, c, wbytes, sig, part, wscale_prev, b1,
+                                  omb1, ms, st, tl);
+}
+
+void launch_compress_deferred_local(const Geo& G, const void* g, int gdt, float* m_local,
+                                    float* c, uint8_t* wbytes, const SegDev& sig, double* part,
+                                    const float* wscale_prev, float b1, float omb1,
+                                    hipStream_t st) {
+  launch_cmp_t<kDeferredLocal>(G, g, gdt, m_local, c, wbytes, sig, part, wscale_prev, b1, omb1,
+                               MomSrc{}, st);
+}
+
+void launch_compress_apply(const Geo& G, const void* g, int gdt, const float* m, float* delta,
+                           uint8_t* wbytes, const SegDev& sig, const float* wscale, float b1,
+                           float omb1, hipStream_t st) {
+  launch_cmp_t<kApply>(G, g, gdt, m, delta, wbytes, sig, nullptr, wscale, b1, omb1, MomSrc{}, st);
+}
+
+}  // namespace oba

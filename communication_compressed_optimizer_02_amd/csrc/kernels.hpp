@@ -103,7 +103,7 @@ void launch_finalize(double* part, int32_t rows, const SegDev& T, float* scale,
 void launch_residual(const Geo& G, const float* src, int64_t src_ld, float* dst, int64_t dst_ld,
                      int32_t rows, const float* scale, const SegDev& T, hipStream_t st);
 // Deferred-residual state: rows hold the last step's c (worker) / a (server)
-// and the scale buffers its scales; see kernels.hip.
+// and the scale buffers its scales; see compress.hip.
 void launch_compress_deferred(const Geo& G, const void* g, int gdt, const float* m, float* c,
                               uint8_t* wbytes, const SegDev& sig, double* part,
                               const float* wscale_prev, float b1, float omb1, const MomSrc& ms,

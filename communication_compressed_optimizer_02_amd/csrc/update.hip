@@ -1,0 +1,108 @@
+// update.hip -- decompress, precondition and update; the momentum accessor (gfx950).
+// Method passages are cited in include/oba.h beside each entry point.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "device.hpp"
+
+namespace oba {
+
+// ===========================================================================
+// Decompress + precondition + update: m_hat = sbar*sign; m = m_hat (when
+// WRITE_M); x = x - (lr*m_hat)/denom (when UPDATE_X).  Grid: the worker grid.
+// ===========================================================================
+template <bool WRITE_M, bool UPDATE_X, bool TL>
+__global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
+                                                              const uint8_t* __restrict__ sbytes,
+                                                              const float* __restrict__ sscale,
+                                                              const float* __restrict__ denom,
+                                                              float* __restrict__ m,
+                                                              float* __restrict__ x, SegDev tau,
+                                                              float lr, TList tl) {
+  const int32_t b = blockIdx.x;
+  TCur tcur{};  // tensor cursor (tensor lists: x listed)
+  if constexpr (TL) tcur = tcur_start(tl, b);
+  const int64_t s_lo = dspan(G.S, G.nblk, b), s_hi = dspan(G.S, G.nblk, b + 1);
+  const int32_t p_end = tau.blk_first[b + 1];
+  int32_t p = tau.blk_first[b];
+  int64_t p_hi = tau.phi[p];
+  for (int64_t s = s_lo; s < s_hi; ++s) {
+    const int64_t lo = s * kSpan;
+    const int64_t hi = min(lo + kSpan, G.d);
+    const Quads q = quads(lo);
+    const bool full = lo + kSpan <= G.d;
+    float sv[8], dv[8], xv[8], mh[8];
+    const uint32_t bits = full ? load_sign_bits<true, OBA_PAIRS_UPD>(sbytes, q, G.d)
+                               : load_sign_bits<false, OBA_PAIRS_UPD>(sbytes, q, G.d);
+    LaneT lt{};
+    if constexpr (TL) {
+      tcur_advance(tl, tcur, lo);
+      lt = lane_tensors(tl, tcur, q, min(lo + kSpan, G.d), G.d);
+    }
+    if (UPDATE_X) {
+      load8(denom, q, G.d, full, dv);
+      if constexpr (TL)
+        load_listed_x(tl, lt, full, xv);
+      else
+        load8(x, q, G.d, full, xv);
+    }
+    if (hi <= p_hi) {
+      const float s_ = sscale[tau.pseg[p]];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sv[j] = s_;
+    } else {
+      int32_t js[8];
+      lane_segs(tau.off, tau.pseg[p], q, G.d, js);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sv[j] = sscale[js[j]];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      mh[j] = ((bits >> j) & 1u) ? -sv[j] : sv[j];
+      if (UPDATE_X) xv[j] = xv[j] - (lr * mh[j]) / dv[j];
+    }
+    if (WRITE_M) store8(m, q, G.d, full, mh);
+    if (UPDATE_X) {
+      if constexpr (TL)
+        store_listed_x(tl, lt, full, xv);
+      else
+        store8(x, q, G.d, full, xv);
+    }
+    while (p < p_end && p_hi <= hi) {
+      if (++p < p_end) p_hi = tau.phi[p];
+    }
+  }
+}
+
+// ---- launchers ----------------------------------------------------------------
+
+void launch_decompress_update(const Geo& G, const uint8_t* sbytes, const float* sscale,
+                              const float* denom, float* m, float* x, const SegDev& tau, float lr,
+                              hipStream_t st) {
+  if (m)
+    hipLaunchKernelGGL((k_decompress_update<true, true, false>), dim3(G.nblk), dim3(kBlock), 0,
+                       st, G, sbytes, sscale, denom, m, x, tau, lr, TList{});
+  else
+    hipLaunchKernelGGL((k_decompress_update<false, true, false>), dim3(G.nblk), dim3(kBlock), 0,
+                       st, G, sbytes, sscale, denom, m, x, tau, lr, TList{});
+}
+
+void launch_decompress_update_listed(const Geo& G, const TList& tl, const uint8_t* sbytes,
+                                     const float* sscale, const float* denom, float* m,
+                                     const SegDev& tau, float lr, hipStream_t st) {
+  if (m)
+    hipLaunchKernelGGL((k_decompress_update<true, true, true>), dim3(G.nblk), dim3(kBlock), 0,
+                       st, G, sbytes, sscale, denom, m, nullptr, tau, lr, tl);
+  else
+    hipLaunchKernelGGL((k_decompress_update<false, true, true>), dim3(G.nblk), dim3(kBlock), 0,
+                       st, G, sbytes, sscale, denom, m, nullptr, tau, lr, tl);
+}
+
+void launch_server_momentum(const Geo& G, const uint8_t* sbytes, const float* sscale, float* m,
+                            const SegDev& tau, hipStream_t st) {
+  hipLaunchKernelGGL((k_decompress_update<true, false, false>), dim3(G.nblk), dim3(kBlock), 0, st,
+                     G, sbytes, sscale, nullptr, m, nullptr, tau, 0.0f, TList{});
+}
+
+}  // namespace oba
