@@ -10,7 +10,7 @@ from .binding import (OBA_BF16, OBA_F16, OBA_F32, Layout, ObaError, Plateau, Sta
                       adam_warmup_step_vnorm, compress, compress_deferred_local,
                       compress_deferred, decompress_update, deferred_errors, freeze_variance,
                       server_momentum, server_reduce_recompress,
-                      server_reduce_recompress_deferred, timing_enable, timing_read, timing_reset, validate)
+                      server_reduce_recompress_deferred, step_small, timing_enable, timing_read, timing_reset, validate)
 
 __all__ = [
     "OBA_BF16", "OBA_F16", "OBA_F32", "Layout", "ObaError", "Plateau", "State", "TensorList",
@@ -19,6 +19,6 @@ __all__ = [
     "adam_warmup_step_vnorm", "compress", "compress_deferred_local",
     "compress_deferred", "decompress_update", "deferred_errors", "freeze_variance",
     "server_momentum", "server_reduce_recompress", "server_reduce_recompress_deferred",
-    "timing_enable",
+    "step_small", "timing_enable",
     "timing_read", "timing_reset", "validate",
 ]

@@ -53,6 +53,7 @@ SIGNATURES = {
                                          _P]),
     "oba_compress_deferred_listed": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _D, _P, _SZ, _P]),
     "oba_decompress_update_listed": (_I, [_P, _P, _P, _P, _P, _P, _D, _P]),
+    "oba_step_small": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _D, _D, _P]),
     "oba_timing_enable": (_I, [_I, _I32]),
     "oba_timing_read": (_I, [ctypes.c_char_p, ctypes.POINTER(_D), ctypes.POINTER(_I64)]),
     "oba_timing_reset": (_I, []),
@@ -440,6 +441,26 @@ def decompress_update_listed(L: Layout, TLs: TensorList, sbits, sscale, denom, m
     _check(rc, "oba_decompress_update_listed")
 
 
+def step_small(L: Layout, g, m, c, wbits, wscale, a, sbits, sscale, denom, m_out, x, beta1, lr,
+               stream=None):
+    """The whole deferred step in one launch (small layouts).  m=None: the
+    implicit momentum in (sbits, sscale); m_out=None: m not stored."""
+    import torch
+
+    f32 = (torch.float32,)
+    P = ctypes.c_void_p
+    rc = lib().oba_step_small(
+        L.handle, _ptr(g, "g", _gtypes(), (L.n, L.ld)), _gdtype(g),
+        _ptr(m, "m", f32, (L.d,)) if m is not None else P(None),
+        _ptr(c, "c", f32, (L.n, L.ld)), _ptr(wbits, "wbits", (torch.int64,), (L.n, L.W)),
+        _ptr(wscale, "wscale", f32, (L.n, L.n_wseg)), _ptr(a, "a", f32, (L.d,)),
+        _ptr(sbits, "sbits", (torch.int64,), (L.W,)), _ptr(sscale, "sscale", f32, (L.n_sseg,)),
+        _ptr(denom, "denom", f32, (L.d,)),
+        _ptr(m_out, "m_out", f32, (L.d,)) if m_out is not None else P(None),
+        _ptr(x, "x", f32, (L.d,)), beta1, lr, _stream(stream))
+    _check(rc, "oba_step_small")
+
+
 def timing_enable(on=True, capacity=4096):
     _check(lib().oba_timing_enable(1 if on else 0, capacity), "oba_timing_enable")
 
@@ -544,6 +565,13 @@ class State:
         server_reduce_recompress_deferred(self.L, self.wbits, self.wscale, self.eps, self.sbits,
                                           self.sscale)
         decompress_update(self.L, self.sbits, self.sscale, self.denom, None, self.x, lr)
+
+    def step_small(self, beta1, lr, g=None, implicit_m=True):
+        """step_deferred in one launch (layouts of at most 65536 coordinates)."""
+        step_small(self.L, self.g if g is None else g, None if self.m_implicit else self.m,
+                   self.delta, self.wbits, self.wscale, self.eps, self.sbits, self.sscale,
+                   self.denom, None if implicit_m else self.m, self.x, beta1, lr)
+        self.m_implicit = implicit_m
 
     def step_deferred(self, beta1, lr, g=None, implicit_m=True):
         """The same step in the deferred-residual layout: `delta` holds the

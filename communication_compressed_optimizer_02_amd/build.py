@@ -32,7 +32,8 @@ HIP_FLAGS = [
 ]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 # one translation unit per pass, plus the C ABI
-HIP_SOURCES = ("warmup.hip", "compress.hip", "scales.hip", "server.hip", "update.hip", "api.hip")
+HIP_SOURCES = ("warmup.hip", "compress.hip", "scales.hip", "server.hip", "update.hip",
+               "small.hip", "api.hip")
 
 
 def hipcc() -> str:

@@ -731,6 +731,55 @@ int oba_plateau_observe(oba_plateau* p, double value) {
   return p->fired;
 }
 
+int oba_step_small(oba_layout L, const void* g, int g_dtype, const float* m, float* c,
+                   uint64_t* wbits, float* wscale, float* a, uint64_t* sbits, float* sscale,
+                   const float* denom, float* m_out, float* x, double beta1, double lr,
+                   hipStream_t stream) {
+  OBA_TRY(check_layout(L));
+  if (!gdtype_ok(g_dtype) || !beta_ok(beta1) || !is_finite(lr)) return OBA_EINVAL;
+  const oba::Plan& P = L->plan;
+  if (P.d > oba::kSmallMaxD || P.n > oba::kSmallMaxN ||
+      (int64_t)P.wseg.size() - 1 > oba::kSmallMaxSeg ||
+      (int64_t)P.sseg.size() - 1 > oba::kSmallMaxSeg)
+    return OBA_EINVAL;
+  if (P.d == 0) return OBA_OK;
+  OBA_TRY(check_buf(g, 16));
+  if (m) OBA_TRY(check_buf(m, 16));
+  OBA_TRY(check_buf(c, 16));
+  OBA_TRY(check_buf(wbits, 8));
+  OBA_TRY(check_buf(wscale, 4));
+  OBA_TRY(check_buf(a, 16));
+  OBA_TRY(check_buf(sbits, 8));
+  OBA_TRY(check_buf(sscale, 4));
+  OBA_TRY(check_buf(denom, 16));
+  if (m_out) OBA_TRY(check_buf(m_out, 16));
+  OBA_TRY(check_buf(x, 16));
+  oba::SmallArgs A{};
+  A.d = P.d;
+  A.ld = P.ld;
+  A.W = P.W;
+  A.n = P.n;
+  A.n_wseg = (int32_t)P.wseg.size() - 1;
+  A.n_sseg = (int32_t)P.sseg.size() - 1;
+  A.wseg = L->sig.off;
+  A.sseg = L->tau.off;
+  A.g = g;
+  A.m_in = m;
+  A.c = c;
+  A.wbits = wbits;
+  A.wscale = wscale;
+  A.a = a;
+  A.sbits = sbits;
+  A.sscale = sscale;
+  A.denom = denom;
+  A.m_out = m_out;
+  A.x = x;
+  A.b1 = (float)beta1;
+  A.omb1 = (float)(1.0 - beta1);
+  A.lr = (float)lr;
+  return launch("step_small", stream, [&] { oba::launch_step_small(A, g_dtype, stream); });
+}
+
 int oba_timing_enable(int on, int32_t capacity) {
   std::lock_guard<std::mutex> lk(g_tmu);
   if (on) {

@@ -55,6 +55,31 @@ struct TList {
   int32_t T;
 };
 
+// The whole deferred step in one block (small layouts, latency bound).
+constexpr int kSmallBlock = 1024;
+constexpr int64_t kSmallMaxD = 65536;
+constexpr int32_t kSmallMaxN = 64;
+constexpr int32_t kSmallMaxSeg = 64;
+struct SmallArgs {
+  int64_t d, ld, W;
+  int32_t n, n_wseg, n_sseg;
+  const int64_t* wseg;  // device segment offsets
+  const int64_t* sseg;
+  const void* g;
+  const float* m_in;    // null: m = sscale * sign(sbits) (implicit momentum)
+  float* c;
+  uint64_t* wbits;
+  float* wscale;
+  float* a;
+  uint64_t* sbits;
+  float* sscale;
+  const float* denom;
+  float* m_out;         // null: m not stored
+  float* x;
+  float b1, omb1, lr;
+};
+void launch_step_small(const SmallArgs& A, int gdt, hipStream_t st);
+
 // Momentum source of the deferred worker pass: null sbytes = read m;
 // otherwise m = sbar*sign from the last packed server bits and scales, with
 // the server segments cut on the worker pass's grid.

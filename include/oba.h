@@ -319,6 +319,22 @@ int oba_decompress_update_listed(oba_layout layout, oba_tensors tensors, const u
                                  const float* sscale, const float* denom, float* m, double lr,
                                  hipStream_t stream);
 
+/* ---- the whole deferred step in one launch (small layouts) ------------------
+ * For layouts whose step is bound by launch latency rather than HBM
+ * (d <= 65536, n <= 64, at most 64 worker and 64 server segments; OBA_EINVAL
+ * otherwise): oba_compress_deferred, oba_server_reduce_recompress_deferred and
+ * oba_decompress_update in one launch of one thread block, with the same
+ * arguments and per-coordinate arithmetic.  m: the momentum ([d]), or NULL
+ * for the implicit momentum held in (sbits, sscale); c, wscale, a, sbits,
+ * sscale: the deferred state, last step's in and this step's out; m_out: [d]
+ * or NULL (m not stored); x updated in place.  No workspace.  The norms are
+ * summed in another fixed order than the streaming kernels', so scales may
+ * differ from theirs in the last bit (results are still reproducible). */
+int oba_step_small(oba_layout layout, const void* g, int g_dtype, const float* m, float* c,
+                   uint64_t* wbits, float* wscale, float* a, uint64_t* sbits, float* sscale,
+                   const float* denom, float* m_out, float* x, double beta1, double lr,
+                   hipStream_t stream);
+
 /* ---- kernel timing (measurement aid) ---------------------------------------
  * While enabled, every kernel the library launches is bracketed by two HIP
  * events on the launch stream (up to `capacity` launches are kept).
@@ -327,10 +343,10 @@ int oba_decompress_update_listed(oba_layout layout, oba_tensors tensors, const u
  * equals `kernel` ("compress_p1", "compress_p2", "finalize_scales",
  * "server_p1", "server_p2", "decompress_update", "adam_warmup",
  * "freeze_variance", "compress_deferred", "server_deferred",
- * "deferred_errors", "server_momentum", "compress_deferred_local"; the listed
- * entry points record under the names of their flat forms); "adam_warmup"
- * includes the norm
- * kernel of oba_adam_warmup_step_vnorm.  oba_timing_reset drops all records. */
+ * "deferred_errors", "server_momentum", "compress_deferred_local",
+ * "step_small"; the listed entry points record under the names of their flat
+ * forms; "adam_warmup" includes the norm kernel of
+ * oba_adam_warmup_step_vnorm).  oba_timing_reset drops all records. */
 int oba_timing_enable(int on, int32_t capacity);
 int oba_timing_read(const char* kernel, double* total_ms, int64_t* launches);
 int oba_timing_reset(void);
