@@ -214,6 +214,54 @@ def run_graph(S, gsets, args, torch, synth):
     return round(ms, 4)
 
 
+def run_small(w, S, gsets, args, torch, oba, synth):
+    """The deferred step as one launch of one block (oba_step_small), for
+    layouts within its limits: W untimed and K timed eager steps from the
+    freeze state, then the same step replayed from HIP graphs."""
+    L = S.L
+    if L.d > 65536 or L.n > 64 or L.n_wseg > 64 or L.n_sseg > 64:
+        return None
+    S.start_compression()
+    log(f"[bench] one-block step: {args.warmup} untimed steps, {args.steps} timed steps")
+    S.step_small(synth.BETA1, synth.LR, g=gsets[1])  # the step that reads the warm-up m
+    for i in range(args.warmup):
+        S.step_small(synth.BETA1, synth.LR, g=gsets[i % 2])
+    torch.cuda.synchronize()
+    oba.timing_reset()
+    oba.timing_enable(True, 16 * max(1, args.steps))
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        S.step_small(synth.BETA1, synth.LR, g=gsets[i % 2])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    oba.timing_enable(False, 1)
+    tot, cnt = oba.timing_read("step_small")
+    oba.timing_reset()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    with torch.cuda.stream(side):
+        for g in gsets:
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=side):
+                S.step_small(synth.BETA1, synth.LR, g=g)
+            graphs.append(gr)
+    torch.cuda.current_stream().wait_stream(side)
+    for i in range(max(1, args.warmup)):
+        graphs[i % 2].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % 2].replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    del graphs
+    return {"ms_per_step": round(ms, 4), "value": w.d / (ms * 1e-3),
+            "kernel_avg_ms": round(tot / cnt, 4) if cnt else None,
+            "graph_replay_ms_per_step": round(graph_ms, 4),
+            "graph_replay_value": w.d / (graph_ms * 1e-3)}
+
+
 def run_listed(w, S, g_flat, args, torch, oba, synth):
     """The deferred step with x and every worker's gradient held as the
     model's separate tensors (copies of the flat buffers), everything else
@@ -411,6 +459,7 @@ def main():
     ms, alg, kernels = run("deferred")
     log("[bench] deferred step replayed from HIP graphs")
     graph_ms = run_graph(S, gsets, args, torch, synth)
+    small = run_small(w, S, gsets, args, torch, oba, synth)
     listed = None
     if args.tensor_list:
         if w.name != "gpt2_xl":
@@ -466,6 +515,7 @@ def main():
             "step_alg_GBps": round(sum(alg_l.values()) * w.d / (ms_l * 1e-3) / 1e9, 1),
             "kernels": kernels_l},
         "tensor_list_schedule": listed,
+        "one_block_step": small,
         "kernel_source_sha256": source_hash(),
     }
     del S, gsets
