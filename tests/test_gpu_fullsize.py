@@ -1,25 +1,34 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py
-times (same layout, grid and kernels), teacher-forced per call.
+times (same layout, grids and kernels).
 
-The state comes from bench.py's own preparation (warm-up steps on the GPU,
-freeze, pre-generated gradient sets).  For each checked coordinate range --
-all of d for the flat workloads, whole chunks for the tensor list -- the
-inputs of each call are copied to the host, the oracle recomputes the call's
-outputs from them, and every output in the range is compared: packed words
-bit-exact, binary32 values within 1e-6 absolute + 1e-5 relative.
+Every run starts from a state that only the seeded generators drew (no library
+call precedes the first step) and then runs freely, on the GPU and in the
+oracle, from the same inputs: the oracle never sees a value the GPU computed.
+
+Comparison (the method's tolerance): scales and binary32 values within 1e-6
+absolute + 1e-5 relative; packed words bit-exact, except at a coordinate whose
+encoded value is within 1e-6 of its scale (|c| < 1e-6 s for a worker,
+|a| < 1e-6 s_bar for the server).  There the two sides may take different
+signs when one scale rounds to the neighbouring binary32 (the scales are
+binary64 sums in different orders), and the values computed from that sign
+at that coordinate -- the worker's residual, the server average and its sign
+and residual, m and x -- differ by about twice a scale, so they are left out
+of the value comparison.  Each test prints how many coordinates that was.
 """
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
 
-import bench
 import oracle
-from gpu_common import B1, LR, assert_close, assert_words, torch
+from gpu_common import B1, LR, assert_close, torch
 from communication_compressed_optimizer_02_amd import binding as oba
 from communication_compressed_optimizer_02_amd import synth
 
 pytestmark = pytest.mark.gpu
+
+NEAR_ZERO = 1e-6
 
 
 def say(*a):
@@ -33,7 +42,7 @@ def h(t):
 
 def local_table(seg, lo, hi):
     """Segments of `seg` inside [lo, hi) (which must be a union of them),
-    shifted to start at 0, and their indices."""
+    shifted to start at 0, and the index range of those segments."""
     seg = np.asarray(seg, dtype=np.int64)
     j0 = int(np.searchsorted(seg, lo))
     j1 = int(np.searchsorted(seg, hi))
@@ -41,81 +50,245 @@ def local_table(seg, lo, hi):
     return seg[j0:j1 + 1] - lo, j0, j1
 
 
-def check_ranges(w, L, S, g, ranges):
+def flipped(gw, ow):
+    """Coordinates (bit positions) where two packed rows differ."""
+    gw, ow = np.asarray(gw).view(np.uint64), np.asarray(ow).view(np.uint64)
+    out = []
+    for j in np.nonzero(gw != ow)[0]:
+        x = int(gw[j]) ^ int(ow[j])
+        while x:
+            out.append(int(j) * 64 + ((x & -x).bit_length() - 1))
+            x &= x - 1
+    return np.array(out, dtype=np.int64)
+
+
+def seg_index(seg, ks):
+    return np.searchsorted(seg, ks, side="right") - 1
+
+
+def close_except(gpu, ora, skip, what):
+    """assert_close over the coordinates not in `skip`; bitwise-equal arrays
+    (the common case) pass without the elementwise tolerance pass."""
+    if skip.size:
+        keep = np.ones(ora.shape[0], bool)
+        keep[skip] = False
+        gpu, ora = gpu[keep], ora[keep]
+    if gpu.dtype == ora.dtype == np.float32 and np.array_equal(gpu.view(np.uint32),
+                                                               ora.view(np.uint32)):
+        return
+    assert_close(gpu, ora, what)
+
+
+class Range:
+    """One coordinate range [lo, hi) (a union of worker and of server
+    segments, lo a multiple of 64) followed on both sides."""
+
+    def __init__(self, w, lo, hi):
+        assert lo % 64 == 0 and (hi % 64 == 0 or hi == w.d)
+        self.lo, self.hi = lo, hi
+        self.wl, self.j0, self.j1 = local_table(w.wseg, lo, hi)
+        self.sl, self.t0, self.t1 = local_table(w.sseg, lo, hi)
+        self.w0, self.w1 = lo // 64, (hi + 63) // 64
+        # coordinates whose state has diverged at an allowed sign difference
+        # of an earlier step: their later values follow different inputs
+        self.carry = np.zeros(hi - lo, bool)
+
+    def oracle_step(self, st, g):
+        """One oracle step on the range (st updated in place); returns its
+        messages and the values it encoded (c per worker, a)."""
+        n = g.shape[0]
+
+        def worker(i):  # workers are independent: one oracle call each, in threads
+            c_i = oracle.compensate(B1, st["m"], g[i], st["delta"][i])
+            wb_i, ws_i = oracle.compress(g[i:i + 1], st["m"], st["delta"][i:i + 1], self.wl, B1)
+            return c_i, wb_i[0], ws_i[0]
+
+        with ThreadPoolExecutor(min(n, 8)) as ex:
+            res = list(ex.map(worker, range(n)))
+        c = np.stack([r[0] for r in res])
+        wb = np.stack([r[1] for r in res])
+        ws = np.stack([r[2] for r in res])
+        del res
+        a = oracle.server_average(wb, ws, self.wl, st["eps"])
+        sb, ss = oracle.server_reduce_recompress(wb, ws, self.wl, self.sl, st["eps"])
+        oracle.decompress_update(sb, ss, self.sl, st["denom"], st["m"], st["x"], LR)
+        return dict(wbits=wb, wscale=ws, sbits=sb, sscale=ss, c=c, a=a)
+
+    def compare(self, name, gpu, ora, st):
+        """gpu: device tensors of the step's outputs over all of d (delta
+        [n][ld] and eps materialised as errors); ora, st: the oracle's step
+        outputs and state after it."""
+        lo, hi = self.lo, self.hi
+        n = ora["wbits"].shape[0]
+        assert_close(h(gpu["wscale"][:, self.j0:self.j1]), ora["wscale"], "worker scales")
+        assert_close(h(gpu["sscale"][self.t0:self.t1]), ora["sscale"], "server scales")
+        carried = self.carry
+        exempt = carried.copy()
+        flips = 0
+        for i in range(n):
+            ks = flipped(h(gpu["wbits"][i, self.w0:self.w1]), ora["wbits"][i])
+            if ks.size:
+                s = ora["wscale"][i][seg_index(self.wl, ks)].astype(np.float64)
+                cv = np.abs(ora["c"][i][ks].astype(np.float64))
+                bad = ks[~((cv < NEAR_ZERO * s) | carried[ks])]
+                assert bad.size == 0, (f"worker {i}: sign differs at {bad[:4] + lo} where "
+                                       f"|c| >= {NEAR_ZERO} s")
+                exempt[ks] = True
+                flips += ks.size
+            skip_i = np.union1d(np.nonzero(carried)[0], ks)
+            close_except(h(gpu["delta"][i, lo:hi]), st["delta"][i], skip_i,
+                         f"worker {i} error delta")
+        ks = flipped(h(gpu["sbits"][self.w0:self.w1]), ora["sbits"])
+        if ks.size:
+            s = ora["sscale"][seg_index(self.sl, ks)].astype(np.float64)
+            near = np.abs(ora["a"][ks].astype(np.float64)) < NEAR_ZERO * s
+            bad = ks[~(near | exempt[ks])]
+            assert bad.size == 0, (f"server sign differs at {bad[:4] + lo} where |a| >= "
+                                   f"{NEAR_ZERO} s_bar and every worker sign agrees")
+            exempt[ks] = True
+        skip = np.nonzero(exempt)[0]
+        close_except(h(gpu["eps"][lo:hi]), st["eps"], skip, "server error eps")
+        close_except(h(gpu["m"][lo:hi]), st["m"], skip, "momentum m")
+        close_except(h(gpu["x"][lo:hi]), st["x"], skip, "parameters x")
+        self.carry = exempt
+        say(f"  [{name}] [{lo}, {hi}) matches: {flips} worker and {ks.size} server signs "
+            f"differ at near-zero values, {skip.size} coordinates exempt")
+
+
+def seeded_deferred_state(S, gen):
+    """A mid-run deferred state (last c, a and scales, m explicit, x, denom)
+    drawn on the device."""
+    S.delta.normal_(0.0, 1e-3, generator=gen)
+    S.eps.normal_(0.0, 1e-3, generator=gen)
+    S.wscale.uniform_(5e-4, 1.5e-3, generator=gen)
+    S.sscale.uniform_(5e-4, 1.5e-3, generator=gen)
+    S.x.normal_(0.0, 0.02, generator=gen)
+    S.m.normal_(0.0, 1e-3, generator=gen)
+    S.denom.uniform_(1e-3, 2e-3, generator=gen)
+    S.m_implicit = False
+
+
+def oracle_state(w, S, rg):
+    """The oracle's explicit state over range rg for the drawn deferred state
+    in S: delta and eps are the oracle's residuals of the drawn c and a."""
+    lo, hi = rg.lo, rg.hi
+    c = h(S.delta[:, lo:hi])
+    ws = h(S.wscale[:, rg.j0:rg.j1])
+    delta = np.empty_like(c)
+
+    def worker(i):
+        for j in range(len(rg.wl) - 1):
+            a_, b_ = int(rg.wl[j]), int(rg.wl[j + 1])
+            delta[i, a_:b_] = oracle.residual(np.ascontiguousarray(c[i, a_:b_]), float(ws[i, j]))
+
+    with ThreadPoolExecutor(min(w.n, 8)) as ex:
+        list(ex.map(worker, range(w.n)))
+    del c
+    a = h(S.eps[lo:hi])
+    ss = h(S.sscale[rg.t0:rg.t1])
+    eps = np.empty_like(a)
+    for j in range(len(rg.sl) - 1):
+        a_, b_ = int(rg.sl[j]), int(rg.sl[j + 1])
+        eps[a_:b_] = oracle.residual(np.ascontiguousarray(a[a_:b_]), float(ss[j]))
+    return dict(x=h(S.x[lo:hi]), m=h(S.m[lo:hi]), denom=h(S.denom[lo:hi]), delta=delta, eps=eps)
+
+
+def deferred_outputs(L, S, delta, eps):
+    oba.deferred_errors(L, S.delta, S.wscale, S.eps, S.sscale, delta, eps)
+    torch().cuda.synchronize()
+    return dict(wbits=S.wbits, wscale=S.wscale, sbits=S.sbits, sscale=S.sscale, delta=delta,
+                eps=eps, m=S.momentum(), x=S.x)
+
+
+def run_deferred(name, ranges_of, start="mid-run"):
+    """Two deferred steps (the first reads m, the second rebuilds it from the
+    first step's server message) from a seeded state, compared after each.
+    start="freeze": c, a and the scales zero, as right after the freeze."""
+    t = torch()
+    w = synth.workload(name)
     d, n = w.d, w.n
-    # ---- inputs of the step, per range, on the host (before any call) ----
-    before = []
-    for lo, hi in ranges:
-        assert lo % 64 == 0 and (hi % 64 == 0 or hi == d)
-        before.append(dict(g=h(g[:, lo:hi]), m=h(S.m[lo:hi]), delta=h(S.delta[:, lo:hi]),
-                           eps=h(S.eps[lo:hi]), x=h(S.x[lo:hi]), denom=h(S.denom[lo:hi])))
-    say(f"  [{w.name}] inputs copied; running compress, server, update on the GPU")
-    spans = []
-    for lo, hi in ranges:
-        _, j0, j1 = local_table(w.wseg, lo, hi)
-        _, t0, t1 = local_table(w.sseg, lo, hi)
-        spans.append((lo // 64, (hi + 63) // 64, j0, j1, t0, t1))
-    out = [dict() for _ in ranges]
-    oba.compress(L, g, S.m, S.delta, S.wbits, S.wscale, B1)
-    torch().cuda.synchronize()
-    for o, (lo, hi), (w0, w1, j0, j1, t0, t1) in zip(out, ranges, spans):
-        o.update(wbits=h(S.wbits[:, w0:w1]).view(np.uint64), wscale=h(S.wscale[:, j0:j1]),
-                 delta=h(S.delta[:, lo:hi]))
-    oba.server_reduce_recompress(L, S.wbits, S.wscale, S.eps, S.sbits, S.sscale)
-    torch().cuda.synchronize()
-    for o, (lo, hi), (w0, w1, j0, j1, t0, t1) in zip(out, ranges, spans):
-        o.update(sbits=h(S.sbits[w0:w1]).view(np.uint64), sscale=h(S.sscale[t0:t1]),
-                 eps=h(S.eps[lo:hi]))
-    oba.decompress_update(L, S.sbits, S.sscale, S.denom, S.m, S.x, LR)
-    torch().cuda.synchronize()
-    for o, (lo, hi) in zip(out, ranges):
-        o.update(m=h(S.m[lo:hi]), x=h(S.x[lo:hi]))
-    for (lo, hi), inp, o in zip(ranges, before, out):
-        wl, _, _ = local_table(w.wseg, lo, hi)
-        sl, _, _ = local_table(w.sseg, lo, hi)
-        say(f"  [{w.name}] range [{lo}, {hi}): {len(wl) - 1} worker and {len(sl) - 1} server "
-            f"segments")
-        # worker compression (oracle updates its delta copy in place)
-        d_ora = inp["delta"].copy()
-        wb_o, ws_o = oracle.compress(inp["g"], inp["m"], d_ora, wl, B1)
-        assert_words(o["wbits"], wb_o, "worker sign words")
-        assert_close(o["wscale"], ws_o, "worker scales")
-        assert_close(o["delta"], d_ora, "worker errors delta")
-        del d_ora
-        say(f"  [{w.name}]   worker side matches")
-        # server, fed the GPU's own messages (the inputs the GPU call had)
-        e_ora = inp["eps"].copy()
-        sb_o, ss_o = oracle.server_reduce_recompress(o["wbits"], o["wscale"], wl, sl, e_ora)
-        assert_words(o["sbits"], sb_o, "server sign words")
-        assert_close(o["sscale"], ss_o, "server scales")
-        assert_close(o["eps"], e_ora, "server error eps")
-        say(f"  [{w.name}]   server side matches")
-        # update, fed the GPU's server message
-        m_o, x_o = inp["m"].copy(), inp["x"].copy()
-        oracle.decompress_update(o["sbits"], o["sscale"], sl, inp["denom"], m_o, x_o, LR)
-        assert_close(o["m"], m_o, "momentum m")
-        assert_close(o["x"], x_o, "parameters x")
-        say(f"  [{w.name}]   update matches")
+    say(f"[full-size deferred] {name}: d={d} n={n} g={w.g_dtype}, seeded {start} state")
+    L = oba.Layout(d, n, w.wseg, w.sseg)
+    S = oba.State(L, w.g_dtype)
+    gen = synth.device_generator(w.seed + 500)
+    if start == "freeze":
+        zero_idx = synth.device_zero_mask(gen, d) if name == "bert_large" else None
+        S.x.normal_(0.0, 0.02, generator=gen)
+        S.m.normal_(0.0, 1e-3, generator=gen)
+        S.denom.uniform_(1e-3, 2e-3, generator=gen)
+        S.start_compression()
+    else:
+        seeded_deferred_state(S, gen)
+        zero_idx = synth.device_zero_mask(gen, d) if name == "bert_large" else None
+    gs = [S.g, t.empty_like(S.g)]
+    for g in gs:
+        synth.device_grads(gen, w, g, zero_idx)
+    del zero_idx
+    t.cuda.synchronize()
+    ranges = [Range(w, lo, hi) for lo, hi in ranges_of(w)]
+    states = [oracle_state(w, S, rg) for rg in ranges]
+    delta, eps = t.empty_like(S.delta), t.empty_like(S.eps)
+    for step, g in enumerate(gs):
+        S.step_deferred(B1, LR, g=g)
+        gpu = deferred_outputs(L, S, delta, eps)
+        for rg, st in zip(ranges, states):
+            say(f"  [{name}] step {step + 1}, range [{rg.lo}, {rg.hi}): oracle step")
+            ora = rg.oracle_step(st, h(g[:, rg.lo:rg.hi]))
+            rg.compare(name, gpu, ora, st)
+            del ora
+    del gs, gpu, delta, eps, S
+    L.close()
+    t.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,start", [("bert_base", "mid-run"), ("bert_large", "freeze")])
+def test_deferred_full_size_free_run_matches_oracle(name, start):
+    run_deferred(name, lambda w: [(0, w.d)], start)
+
+
+def test_deferred_gpt2_chunks_free_run_matches_oracle():
+    """The tensor-list workload (392 chunks, one worker and one server scale
+    each): the GPU steps all of d, the oracle follows chosen chunks (chunks
+    are independent: every segment lies inside one)."""
+    def pick(w):
+        t = w.wseg
+        js = [0, 4, 5, 6, 100, 250, len(t) - 3, len(t) - 2]  # wte head and tail, wpe, layers, ln_f
+        return [(int(t[j]), int(t[j + 1])) for j in js]
+    run_deferred("gpt2_xl", pick)
 
 
 @pytest.mark.parametrize("name", ["bert_base", "bert_large"])
-def test_flat_workload_full_size_step_matches_oracle(name):
+def test_explicit_full_size_step_matches_oracle(name):
+    """One step of the explicit-state kernels (norm pass, apply pass, server
+    and residual passes, update writing m) from a seeded explicit state."""
+    t = torch()
     w = synth.workload(name)
-    say(f"[full-size] {name}: d={w.d} n={w.n} g={w.g_dtype}; preparing state as bench.py does")
-    L, S, gsets = bench.make_state(w, torch(), oba, synth)
-    check_ranges(w, L, S, gsets[0], [(0, w.d)])
-    del S, gsets
+    d, n = w.d, w.n
+    say(f"[full-size explicit] {name}: d={d} n={n} g={w.g_dtype}, seeded state")
+    L = oba.Layout(d, n, w.wseg, w.sseg)
+    S = oba.State(L, w.g_dtype)
+    gen = synth.device_generator(w.seed + 600)
+    S.delta.normal_(0.0, 1e-4, generator=gen)
+    S.eps.normal_(0.0, 1e-4, generator=gen)
+    S.x.normal_(0.0, 0.02, generator=gen)
+    S.m.normal_(0.0, 1e-3, generator=gen)
+    S.denom.uniform_(1e-3, 2e-3, generator=gen)
+    S.m_implicit = False
+    zero_idx = synth.device_zero_mask(gen, d) if name == "bert_large" else None
+    synth.device_grads(gen, w, S.g, zero_idx)
+    del zero_idx
+    t.cuda.synchronize()
+    rg = Range(w, 0, d)
+    st = dict(x=h(S.x), m=h(S.m), denom=h(S.denom), delta=h(S.delta[:, :d]), eps=h(S.eps))
+    g = h(S.g[:, :d])
+    S.step(B1, LR)
+    t.cuda.synchronize()
+    say(f"  [{name}] oracle step")
+    ora = rg.oracle_step(st, g)
+    del g
+    gpu = dict(wbits=S.wbits, wscale=S.wscale, sbits=S.sbits, sscale=S.sscale, delta=S.delta,
+               eps=S.eps, m=S.m, x=S.x)
+    rg.compare(name, gpu, ora, st)
+    del ora, st, gpu, S
     L.close()
-    torch().cuda.empty_cache()
-
-
-def test_tensor_list_full_size_chunks_match_oracle():
-    w = synth.workload("gpt2_xl")
-    say(f"[full-size] gpt2_xl: d={w.d} n={w.n}, {len(w.wseg) - 1} chunks; preparing state")
-    L, S, gsets = bench.make_state(w, torch(), oba, synth)
-    t = w.wseg
-    pick = [0, 4, 5, 6, 100, 250, len(t) - 3, len(t) - 2]  # wte head and tail, wpe, layers, ln_f
-    check_ranges(w, L, S, gsets[0], [(int(t[j]), int(t[j + 1])) for j in pick])
-    del S, gsets
-    L.close()
-    torch().cuda.empty_cache()
+    t.cuda.empty_cache()
