@@ -86,10 +86,14 @@ __global__ __launch_bounds__(kBlock) OBA_SRV_ATTR void k_server_p1(Geo G, const 
   const int32_t ps_end = sig.blk_first[b + 1], pt_end = tau.blk_first[b + 1];
   int32_t ps = sig.blk_first[b], pt = tau.blk_first[b];
   int64_t ps_hi = sig.phi[ps], pt_hi = tau.phi[pt];
+  // segments of the current pieces, read when a cursor moves (not per span,
+  // so that no wait for them sits between a span's loads)
+  int32_t js_cur = sig.pseg[ps], jt_cur = tau.pseg[pt];
   const int64_t rowbytes = G.W * 8;
   const float nf = (float)G.n;
   const bool pow2 = (G.n & (G.n - 1)) == 0;
   const float inv_n = 1.0f / nf;
+  const bool stager = OBA_SRV_LDS != 0 && (int)threadIdx.x < NB * 32;
   double acc[1] = {0.0};
   for (int64_t s = s_lo; s < s_hi; ++s) {
     const int64_t lo = s * kSpan;
@@ -97,15 +101,19 @@ __global__ __launch_bounds__(kBlock) OBA_SRV_ATTR void k_server_p1(Geo G, const 
     const Quads q = quads(lo);
     float a[8];
     if (hi <= ps_hi && hi <= pt_hi && lo + kSpan <= G.d) {
-      // fast path: full span, one worker and one server segment; loads first
-      const int32_t js0 = sig.pseg[ps];
+      // fast path: full span, one worker and one server segment.  The first
+      // group's packed rows are requested before a', so one wait covers both.
+      const int32_t js0 = js_cur;
+      uint2 rowv = make_uint2(0u, 0u);
+      if constexpr (OBA_SRV_LDS != 0) {
+        if (stager) {
+          const int64_t r = min((int)(threadIdx.x >> 5), G.n - 1);
+          rowv = *reinterpret_cast<const uint2*>(wbytes + r * rowbytes + (lo >> 3) +
+                                                 8 * (threadIdx.x & 31));
+        }
+      }
       float t[8];
       load_full(eps, q, a);
-      if (DEFERRED) {
-        const float sp = sscale_prev[tau.pseg[pt]];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) a[j] = residual(a[j], sp);
-      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) t[j] = 0.0f;
       for (int32_t i0 = 0; i0 < G.n; i0 += NB) {  // one pass when n <= NB
@@ -113,13 +121,13 @@ __global__ __launch_bounds__(kBlock) OBA_SRV_ATTR void k_server_p1(Geo G, const 
         uint32_t bits[NB];
         float sw[NB];
         if constexpr (OBA_SRV_LDS != 0) {
-          __syncthreads();  // the previous span's reads of rows_lds are done
-          if ((int)threadIdx.x < NB * 32) {
-            const int u = threadIdx.x >> 5, c = threadIdx.x & 31;
-            const int64_t r = min(i0 + u, G.n - 1);
-            rows_lds[threadIdx.x] =
-                *reinterpret_cast<const uint2*>(wbytes + r * rowbytes + (lo >> 3) + 8 * c);
+          if (i0 > 0 && stager) {
+            const int64_t r = min(i0 + (int)(threadIdx.x >> 5), G.n - 1);
+            rowv = *reinterpret_cast<const uint2*>(wbytes + r * rowbytes + (lo >> 3) +
+                                                   8 * (threadIdx.x & 31));
           }
+          __syncthreads();  // the previous reads of rows_lds are done
+          if (stager) rows_lds[threadIdx.x] = rowv;
           __syncthreads();
           const uint8_t* lb = reinterpret_cast<const uint8_t*>(rows_lds);
           const uint32_t sh = (threadIdx.x & 1) ? 4u : 0u;
@@ -146,6 +154,11 @@ __global__ __launch_bounds__(kBlock) OBA_SRV_ATTR void k_server_p1(Geo G, const 
           }
         }
       }
+      if (DEFERRED) {
+        const float sp = sscale_prev[jt_cur];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] = residual(a[j], sp);
+      }
       if (pow2) {  // t * (1/n) is t / n exactly when n is a power of two
 #pragma unroll
         for (int j = 0; j < 8; ++j) a[j] = t[j] * inv_n + a[j];
@@ -157,8 +170,8 @@ __global__ __launch_bounds__(kBlock) OBA_SRV_ATTR void k_server_p1(Geo G, const 
     } else {
       // general path (a segment boundary in the span, or the tail): one
       // coordinate at a time, same operations in the same order
-      int32_t js = sig.pseg[ps];
-      int32_t jt = tau.pseg[pt];
+      int32_t js = js_cur;
+      int32_t jt = jt_cur;
 #pragma unroll 1
       for (int j = 0; j < 8; ++j) {
         const int64_t k = coord(q, j);
@@ -186,14 +199,20 @@ __global__ __launch_bounds__(kBlock) OBA_SRV_ATTR void k_server_p1(Geo G, const 
     const double fs = sumsq8(a);  // coordinates past d hold 0
     // advance the worker-segment cursor to the piece holding hi
     while (ps < ps_end && ps_hi <= hi) {
-      if (++ps < ps_end) ps_hi = sig.phi[ps];
+      if (++ps < ps_end) {
+        ps_hi = sig.phi[ps];
+        js_cur = sig.pseg[ps];
+      }
     }
     // server-segment reduction
     if (hi <= pt_hi) {
       acc[0] += fs;
       if (hi == pt_hi) {
         flush_rows<1>(acc, 1, part + pt, 0, lds);
-        if (++pt < pt_end) pt_hi = tau.phi[pt];
+        if (++pt < pt_end) {
+          pt_hi = tau.phi[pt];
+          jt_cur = tau.pseg[pt];
+        }
       }
     } else {
       int64_t cur = lo;
@@ -202,7 +221,10 @@ __global__ __launch_bounds__(kBlock) OBA_SRV_ATTR void k_server_p1(Geo G, const 
         acc[0] += sumsq_range(eps, q, cur, e);
         if (pt_hi <= hi) {
           flush_rows<1>(acc, 1, part + pt, 0, lds);
-          if (++pt < pt_end) pt_hi = tau.phi[pt];
+          if (++pt < pt_end) {
+            pt_hi = tau.phi[pt];
+            jt_cur = tau.pseg[pt];
+          }
         }
         cur = e;
       }
