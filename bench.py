@@ -98,15 +98,16 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload, kernel):
-    """HBM bytes per launch measured by rocprofv3 counters, if the committed
-    summary was taken on the current kernel source."""
+def traffic_from_profiles(workload, kernel, field="hbm_bytes_per_launch"):
+    """HBM bytes measured by rocprofv3 counters (per launch of the dominant
+    kernel, or with field="step_hbm_bytes" per headline step), if the
+    committed summary was taken on the current kernel source."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
-    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    val = re.search(field + r":\s*([0-9.eE+]+)", text)
     if not src or not val or src.group(1) != source_hash():
         return None
     return float(val.group(1))
@@ -475,6 +476,7 @@ def main():
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = traffic_from_profiles(w.name, dom)
     step_alg = sum(alg.values()) * w.d
+    step_hbm = traffic_from_profiles(w.name, dom, "step_hbm_bytes")  # counters, per step
     out = {
         "metric": METRIC,
         "value": w.d / (ms * 1e-3),
@@ -494,6 +496,7 @@ def main():
                    "schedule": "deferred-residual state (c, a kept; residuals formed on use; "
                                "momentum rebuilt from the server message)"},
         "step_alg_GBps": round(step_alg / (ms * 1e-3) / 1e9, 1),
+        "step_hbm_GBps": (round(step_hbm / (ms * 1e-3) / 1e9, 1) if step_hbm else None),
         "step_alg_bytes_per_param": round(sum(alg.values()), 3),
         "method_bytes_per_param": round(method_bytes(w), 3),
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
