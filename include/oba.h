@@ -95,10 +95,10 @@ int oba_layout_validate(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, i
                         const int64_t* sseg, int32_t n_sseg);
 
 /* Validates as above, then builds the handle: small device copies of the
- * segment tables and of the per-block piece lists the kernels walk (four
+ * segment tables and of the per-block piece lists the kernels walk (five
  * tables, each about 16 bytes per thread block of its grid plus 20 bytes per
- * segment; the grids have at most 131072 and 65536 blocks, so about 6 MB at
- * 336M parameters).  Allocates on the current device; the handle must be used on that
+ * segment; the worker and update grids have at most 2^21 blocks and the
+ * server grid 2^18, so about 9 MB at 336M parameters).  Allocates on the current device; the handle must be used on that
  * device only.  *out is set only on success. */
 int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const int64_t* wseg,
                       int32_t n_wseg, const int64_t* sseg, int32_t n_sseg);
