@@ -153,6 +153,8 @@ def check_pieces(res, offs):
     (336_000_000, 8, [0, 336_000_000], [j * 336_000_000 // 8 for j in range(9)]),
     (5_000_003, 5, [0, 5_000_003], [j * 5_000_003 // 5 for j in range(6)]),
     (300, 2, list(range(301)), [0, 150, 300]),
+    # past 2^31 coordinates (64-bit offsets everywhere), a ragged tail
+    (2**31 + 2**20 + 37, 2, [0, 2**31 + 2**20 + 37], [0, 2**30 + 64, 2**31 + 2**20 + 37]),
 ])
 def test_planner_pieces_under_sanitizers(driver, d, n, wseg, sseg):
     rc, res = run_plan(driver, d, n, wseg, sseg)

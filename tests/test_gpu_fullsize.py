@@ -292,3 +292,55 @@ def test_explicit_full_size_step_matches_oracle(name):
     del ora, st, gpu, S
     L.close()
     t.cuda.empty_cache()
+
+
+def test_deferred_step_past_2_31_coordinates():
+    """The largest case: one deferred step at d = 2^31 + 2^20 + 37 (n = 2,
+    binary16 gradients), so every coordinate, word and byte offset past the
+    middle is beyond the 32-bit range.  The step starts from a drawn mid-run
+    state whose momentum is implicit (a drawn server message), so it runs the
+    bench's worker kernel.  The GPU steps all of d; segments are cut so that
+    the oracle can follow two of them whole: the first, and one that
+    straddles 2^31 and ends in the ragged tail."""
+    t = torch()
+    d, n = 2**31 + 2**20 + 37, 2
+    lo_tail = 2**31 - 2**20
+    wseg = np.array([0, 2**20, lo_tail, d], np.int64)
+    sseg = np.array([0, 2**20, 2**30 + 64, lo_tail, d], np.int64)
+    w = synth.Workload("past_int32", d, n, "f16", 7, 0, wseg, sseg, 1e-3)
+    say(f"[past 2^31] d={d} n={n} g=f16")
+    L = oba.Layout(d, n, wseg, sseg)
+    S = oba.State(L, "f16")
+    gen = synth.device_generator(w.seed + 700)
+    seeded_deferred_state(S, gen)
+    halves = [t.randint(0, 2**32, S.sbits.shape, dtype=t.int64, device="cuda", generator=gen)
+              for _ in range(2)]
+    S.sbits.copy_((halves[0] << 32) | halves[1])  # every 64-bit pattern, top bit included
+    del halves
+    tail = d % 64
+    if tail:
+        S.sbits[-1:].bitwise_and_((1 << tail) - 1)  # no bits past d
+    S.m_implicit = True
+    synth.device_grads(gen, w, S.g)
+    t.cuda.synchronize()
+    ranges = [Range(w, 0, 2**20), Range(w, lo_tail, d)]
+    states, grads_h = [], []
+    for rg in ranges:
+        st = oracle_state(w, S, rg)
+        st["m"] = np.zeros(rg.hi - rg.lo, np.float32)  # the message decoded by the oracle
+        oracle.decompress_update(h(S.sbits[rg.w0:rg.w1]).view(np.uint64),
+                                 h(S.sscale[rg.t0:rg.t1]), rg.sl,
+                                 np.ones(rg.hi - rg.lo, np.float32), st["m"],
+                                 np.zeros(rg.hi - rg.lo, np.float32), 0.0)
+        states.append(st)
+        grads_h.append(h(S.g[:, rg.lo:rg.hi]))
+    S.step_deferred(B1, LR)
+    delta, eps = t.empty_like(S.delta), t.empty_like(S.eps)
+    gpu = deferred_outputs(L, S, delta, eps)
+    for rg, st, g in zip(ranges, states, grads_h):
+        say(f"  [past 2^31] range [{rg.lo}, {rg.hi}): oracle step")
+        ora = rg.oracle_step(st, g)
+        rg.compare("past 2^31", gpu, ora, st)
+    del gpu, delta, eps, S
+    L.close()
+    t.cuda.empty_cache()
