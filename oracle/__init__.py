@@ -27,8 +27,11 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast
 
 
 def build(force: bool = False) -> str:
-    """Compile liboracle.so with gcc (seconds)."""
-    if force or not os.path.exists(_LIB_PATH):
+    """Compile liboracle.so with gcc (seconds), also when a source is newer."""
+    stale = not os.path.exists(_LIB_PATH) or any(
+        os.path.getmtime(os.path.join(_HERE, f)) > os.path.getmtime(_LIB_PATH)
+        for f in ("oracle.c", "oracle.h"))
+    if force or stale:
         tmp = _LIB_PATH + ".tmp"
         subprocess.run(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
         os.replace(tmp, _LIB_PATH)
@@ -60,6 +63,11 @@ def lib():
             "oracle_server_average": (None, [I64, I64, I64, I32, P, I32, P, P, P, P]),
             "oracle_server_reduce_recompress": (None, [I64, I32, P, I32, P, I32, P, P, P, P, P]),
             "oracle_decompress_update": (None, [I64, I64, P, I32, P, P, P, P, P, D]),
+            "oracle_float_to_half": (ctypes.c_uint16, [F]),
+            "oracle_float_to_bfloat16": (ctypes.c_uint16, [F]),
+            "oracle_round16": (None, [I64, P, P, I]),
+            "oracle_compress_deferred16": (None, [I64, I32, I64, P, I32, P, I, P, P, I, P, P, P,
+                                                  D]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -192,6 +200,52 @@ def compress(g, m, delta, wseg, beta1):
     wscale = np.zeros((n, len(wseg) - 1), np.float32)
     lib().oracle_compress(d, n, ld, _p(wseg), len(wseg) - 1, _p(g), _grad(g), _p(m), _p(delta),
                           _p(wbits), _p(wscale), beta1)
+    return wbits, wscale
+
+
+KIND16 = {"f16": 1, "bf16": 2}
+
+
+def round16(x, kind):
+    """binary32 array -> uint16 bit patterns of the nearest binary16 ("f16")
+    or bfloat16 ("bf16") values, ties to even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().oracle_round16(x.size, _p(x), _p(out), KIND16[kind])
+    return out
+
+
+_DECODE16 = {}
+
+
+def decode16(bits, kind):
+    """uint16 bit patterns of binary16 / bfloat16 values -> binary32 (exact),
+    through a table of the oracle's decoders over all 65 536 patterns."""
+    if kind not in _DECODE16:
+        f = half_to_float if kind == "f16" else bfloat16_to_float
+        _DECODE16[kind] = np.array([f(h) for h in range(65536)], dtype=np.float64).astype(
+            np.float32)
+    return _DECODE16[kind][np.asarray(bits, dtype=np.uint16)]
+
+
+def compress_deferred16(g, m, c16, kind, wscale_prev, wseg, beta1):
+    """Worker compression with each worker's compensated momentum held in a
+    16-bit format: c16 [n][ld] uint16 (the last compressed vectors) is
+    updated in place, wscale_prev [n][n_wseg] holds their scales.  Returns
+    (wbits [n][W] uint64, wscale [n][n_wseg] float32)."""
+    n, ld = g.shape
+    d = m.shape[0]
+    _chk(m, np.float32, "m")
+    _chk(c16, np.uint16, "c16")
+    _chk(wscale_prev, np.float32, "wscale_prev")
+    assert c16.shape == (n, ld)
+    wseg = _seg(wseg, d)
+    assert wscale_prev.shape == (n, len(wseg) - 1)
+    wbits = np.zeros((n, words(d)), np.uint64)
+    wscale = np.zeros((n, len(wseg) - 1), np.float32)
+    lib().oracle_compress_deferred16(d, n, ld, _p(wseg), len(wseg) - 1, _p(g), _grad(g), _p(m),
+                                     _p(c16), KIND16[kind], _p(wscale_prev), _p(wbits),
+                                     _p(wscale), beta1)
     return wbits, wscale
 
 

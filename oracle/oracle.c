@@ -57,6 +57,56 @@ double oracle_bfloat16_to_double(uint16_t h) {
   return sign ? -v : v;
 }
 
+/* Round x to the nearest value of a binary floating-point format with p
+ * significand bits (the leading bit included), smallest normal exponent
+ * emin and largest finite value maxv; a tie goes to the even significand
+ * (IEEE 754 roundTiesToEven).  Below 2^emin the grid is the subnormal one,
+ * 2^(emin - p + 1).  A result above maxv becomes an infinity of x's sign;
+ * zeros keep their sign.  The result is a double that the format holds
+ * exactly. */
+static double round_to_format(double x, int p, int emin, double maxv) {
+  if (isnan(x) || isinf(x) || x == 0.0) return x;
+  int e;
+  frexp(fabs(x), &e); /* |x| = f * 2^e with 1/2 <= f < 1: x's exponent is e - 1 */
+  int ex = e - 1 < emin ? emin : e - 1;
+  const double ulp = ldexp(1.0, ex - (p - 1));
+  const double r = nearbyint(x / ulp) * ulp; /* x / ulp is exact: a power-of-two scaling */
+  return fabs(r) > maxv ? copysign(INFINITY, x) : r;
+}
+
+/* The bit pattern of v, a value of a 16-bit binary format (fraction bits fb,
+ * exponent bias bias, all-ones exponent for inf and NaN), from its parts. */
+static uint16_t format_bits(double v, int fb, int bias) {
+  const uint16_t sign = signbit(v) ? 0x8000u : 0u;
+  const int emax_field = (1 << (15 - fb)) - 1;
+  if (isnan(v)) return (uint16_t)(sign | (emax_field << fb) | (1u << (fb - 1)));
+  if (isinf(v)) return (uint16_t)(sign | (emax_field << fb));
+  const double a = fabs(v);
+  if (a < ldexp(1.0, 1 - bias)) /* zero or subnormal: a = f * 2^(1 - bias - fb) */
+    return (uint16_t)(sign | (uint16_t)ldexp(a, bias - 1 + fb));
+  int e;
+  const double f = frexp(a, &e); /* a = (2f) * 2^(e-1), 1 <= 2f < 2 */
+  const uint16_t frac = (uint16_t)ldexp(2.0 * f - 1.0, fb);
+  return (uint16_t)(sign | (uint16_t)((e - 1 + bias) << fb) | frac);
+}
+
+/* binary32 -> binary16 (p = 11, emin = -14, max 65504), nearest, ties even */
+uint16_t oracle_float_to_half(float x) {
+  return format_bits(round_to_format((double)x, 11, -14, 65504.0), 10, 15);
+}
+
+/* binary32 -> bfloat16 (p = 8, emin = -126, max (2 - 2^-7) 2^127), nearest,
+ * ties even */
+uint16_t oracle_float_to_bfloat16(float x) {
+  return format_bits(round_to_format((double)x, 8, -126, ldexp(255.0, 120)), 7, 127);
+}
+
+/* kind 1: binary16, kind 2: bfloat16 */
+void oracle_round16(int64_t len, const float* x, uint16_t* out, int kind) {
+  for (int64_t k = 0; k < len; ++k)
+    out[k] = kind == 1 ? oracle_float_to_half(x[k]) : oracle_float_to_bfloat16(x[k]);
+}
+
 /* g_kind: 0 binary32, 1 binary16, 2 bfloat16 */
 static float grad_at(const void* g, int g_kind, int64_t idx) {
   if (g_kind == 1) return (float)oracle_half_to_double(((const uint16_t*)g)[idx]);
@@ -207,6 +257,49 @@ void oracle_compress(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int3
     ec_onebit(d, wseg, n_wseg, c, wbits + (int64_t)i * W, wscale + (int64_t)i * n_wseg, di);
   }
   free(c);
+}
+
+/* The worker pass with each worker's compensated momentum held in a 16-bit
+ * format, c_kind 1 (binary16) or 2 (bfloat16): the deferred layout of the
+ * state, where c16 [n][ld] holds each worker's last compressed vector and
+ * wscale_prev its scales.  Worker i, coordinate k:
+ *   c'    = c16 decoded;  delta = c' - s'*sign(c')   (s' the scale of k's segment)
+ *   c     = (b1*m + (1-b1)*g) + delta                 (binary32, as above)
+ *   c~    = c rounded to the 16-bit format, nearest, ties to even
+ * then c~ is the vector compressed ([Tang] 4.3; [CwP] scale) and stored as
+ * the new c16.  The rounding c - c~ is this variant's own loss and is not
+ * fed back; the residual the next step feeds back is exact for what was
+ * sent.  wbits, wscale as for oracle_compress. */
+void oracle_compress_deferred16(int64_t d, int32_t n, int64_t ld, const int64_t* wseg,
+                                int32_t n_wseg, const void* g, int g_kind, const float* m,
+                                uint16_t* c16, int c_kind, const float* wscale_prev,
+                                uint64_t* wbits, float* wscale, double beta1) {
+  int64_t W = (d + 63) / 64;
+  size_t bytes = (size_t)(d > 0 ? d : 1) * sizeof(float);
+  float* cp = (float*)malloc(bytes);
+  float* delta = (float*)malloc(bytes);
+  float* c = (float*)malloc(bytes);
+  float* unused = (float*)malloc(bytes);
+  for (int32_t i = 0; i < n; ++i) {
+    uint16_t* row = c16 + (int64_t)i * ld;
+    for (int64_t k = 0; k < d; ++k)
+      cp[k] = (float)(c_kind == 1 ? oracle_half_to_double(row[k])
+                                  : oracle_bfloat16_to_double(row[k]));
+    for (int32_t j = 0; j < n_wseg; ++j)
+      oracle_residual(wseg[j + 1] - wseg[j], cp + wseg[j],
+                      wscale_prev[(int64_t)i * n_wseg + j], delta + wseg[j]);
+    oracle_compensate(d, beta1, m, g, g_kind, (int64_t)i * ld, delta, c);
+    for (int64_t k = 0; k < d; ++k) {
+      row[k] = c_kind == 1 ? oracle_float_to_half(c[k]) : oracle_float_to_bfloat16(c[k]);
+      c[k] = (float)(c_kind == 1 ? oracle_half_to_double(row[k])
+                                 : oracle_bfloat16_to_double(row[k]));
+    }
+    ec_onebit(d, wseg, n_wseg, c, wbits + (int64_t)i * W, wscale + (int64_t)i * n_wseg, unused);
+  }
+  free(cp);
+  free(delta);
+  free(c);
+  free(unused);
 }
 
 /* Per-worker momentum: the other reading of [Tang] 4.3 (each worker keeps

@@ -47,6 +47,12 @@ extern "C" {
 double oracle_half_to_double(uint16_t h);
 double oracle_bfloat16_to_double(uint16_t h);
 
+/* ---- binary32 rounded to a 16-bit format (nearest, ties to even), from
+ * the formats' definitions; kind 1 binary16, 2 bfloat16 ------------------- */
+uint16_t oracle_float_to_half(float x);
+uint16_t oracle_float_to_bfloat16(float x);
+void oracle_round16(int64_t len, const float* x, uint16_t* out, int kind);
+
 /* ---- warm-up and freeze -------------------------------------------------- */
 void oracle_adam_warmup_step(int64_t d, int32_t n, int64_t ld, const void* g, int g_kind,
                              float* x, float* m, float* v, double lr, double beta1,
@@ -69,6 +75,10 @@ void oracle_compensate(int64_t len, double beta1, const float* m, const void* g,
 void oracle_compress(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_wseg,
                      const void* g, int g_kind, const float* m, float* delta, uint64_t* wbits,
                      float* wscale, double beta1);
+void oracle_compress_deferred16(int64_t d, int32_t n, int64_t ld, const int64_t* wseg,
+                                int32_t n_wseg, const void* g, int g_kind, const float* m,
+                                uint16_t* c16, int c_kind, const float* wscale_prev,
+                                uint64_t* wbits, float* wscale, double beta1);
 void oracle_compress_local(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_wseg,
                            const void* g, int g_kind, float* m_local, float* delta,
                            uint64_t* wbits, float* wscale, double beta1);

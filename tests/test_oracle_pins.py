@@ -618,3 +618,125 @@ def test_local_momentum_with_singleton_segments_is_momentum_sgd():
         m64 = B1 * m64 + (1 - B1) * g.astype(np.float64).mean(axis=0)
         x64 = x64 - LR * m64 / denom.astype(np.float64)
     assert np.allclose(st["x"], x64, rtol=1e-4, atol=1e-7)
+
+
+# ---- the 16-bit worker state (binary16 / bfloat16 error-feedback storage) ----
+
+def _probe_floats(kind, rng):
+    """binary32 values that probe rounding to a 16-bit format: random bit
+    patterns (all exponents), the midpoints between neighbouring 16-bit
+    values (ties) and one binary32 step either side of them, the overflow
+    threshold and the subnormal range."""
+    raw = rng.integers(0, 2**32, size=400_000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    raw = raw[~np.isnan(raw)]
+    h = rng.integers(0, 2**16, size=100_000).astype(np.uint16)
+    if kind == "f16":
+        lo = h.view(np.float16).astype(np.float64)
+        hi = (h + np.uint16(1)).view(np.float16).astype(np.float64)
+        big = [65504.0, 65519.0, 65519.996, 65520.0, 65536.0, 1e6]
+        small = [2.0**-24, 2.0**-25, 3 * 2.0**-25, 2.0**-26, 2.0**-14, 2.0**-14 - 2.0**-25]
+    else:
+        import torch
+
+        def dec(b):
+            return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).float().numpy()
+        lo = dec(h).astype(np.float64)
+        hi = dec(h + np.uint16(1)).astype(np.float64)
+        big = [3.3895314e38, 3.3961775e38, 3.4e38, float(np.finfo(np.float32).max)]
+        small = [2.0**-133, 2.0**-134, 3 * 2.0**-134, 2.0**-126, 2.0**-149]
+    ok = np.isfinite(lo) & np.isfinite(hi) & (np.sign(lo) == np.sign(hi))
+    mid = ((lo[ok] + hi[ok]) / 2).astype(np.float32)  # exact: one more bit than the format
+    up = np.nextafter(mid, np.float32(np.inf))
+    down = np.nextafter(mid, np.float32(-np.inf))
+    spec = np.array(big + small + [0.0, np.inf], np.float32)
+    return np.concatenate([raw, mid, up, down, spec, -spec])
+
+
+def test_round16_binary16_matches_numpy():
+    rng = np.random.default_rng(16)
+    x = _probe_floats("f16", rng)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    got = oracle.round16(x, "f16")
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, f"{bad.size} differ, e.g. {x[bad[:3]]}: {got[bad[:3]]} vs {ref[bad[:3]]}"
+    nan = oracle.round16(np.array([np.nan], np.float32), "f16")[0]
+    assert (nan & 0x7C00) == 0x7C00 and (nan & 0x3FF) != 0
+
+
+def test_round16_bfloat16_matches_torch():
+    import torch
+
+    rng = np.random.default_rng(17)
+    x = _probe_floats("bf16", rng)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.round16(x, "bf16")
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, f"{bad.size} differ, e.g. {x[bad[:3]]}: {got[bad[:3]]} vs {ref[bad[:3]]}"
+    nan = oracle.round16(np.array([np.nan], np.float32), "bf16")[0]
+    assert (nan & 0x7F80) == 0x7F80 and (nan & 0x7F) != 0
+
+
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+def test_round16_round_trips_every_finite_pattern(kind):
+    h = np.arange(65536, dtype=np.uint16)
+    v = oracle.decode16(h, kind)
+    fin = np.isfinite(v)
+    assert np.array_equal(oracle.round16(v[fin], kind), h[fin])
+
+
+def _decode_ref(bits, kind):
+    """16-bit patterns decoded by numpy (binary16) or torch (bfloat16)."""
+    if kind == "f16":
+        return bits.view(np.float16).astype(np.float32)
+    import torch
+
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+
+
+def _encode_ref(x, kind):
+    if kind == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    import torch
+
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("kind,gdt", [("f16", "f32"), ("bf16", "f16"), ("bf16", "f32")])
+def test_compress_deferred16_follows_its_definition(kind, gdt):
+    """Two chained steps of the 16-bit worker state against the definition
+    recomputed with numpy binary32 arithmetic and numpy / torch conversions:
+    residual of the decoded state, compensation, rounding, then the signs and
+    the L2 scale of the rounded vector."""
+    rng = np.random.default_rng(1600 + len(kind) + len(gdt))
+    d, n = 1_003, 3
+    wseg = np.array([0, 1, 64, 500, 777, d], np.int64)
+    nw = len(wseg) - 1
+    m = rng.normal(0, 1e-3, d).astype(np.float32)
+    c16 = _encode_ref(rng.normal(0, 1e-3, (n, d)).astype(np.float32), kind)
+    c16[:, :5] = 0  # +0 in the state
+    ws = rng.uniform(5e-4, 1.5e-3, (n, nw)).astype(np.float32)
+    b1, omb1 = np.float32(synth.BETA1), np.float32(1.0 - synth.BETA1)
+    for step in range(2):
+        g = rng.normal(0, 1e-3, (n, d)).astype(np.float32 if gdt == "f32" else np.float16)
+        g[:, 7] = 0
+        # definition, by numpy / torch
+        seg_of = np.searchsorted(wseg, np.arange(d), side="right") - 1
+        cp = _decode_ref(c16, kind)
+        sg = np.where(cp < 0, np.float32(-1), np.float32(1))
+        delta = cp - ws[:, seg_of] * sg
+        c = (b1 * m + omb1 * g.astype(np.float32)) + delta
+        ct_bits = _encode_ref(c, kind)
+        ct = _decode_ref(ct_bits, kind)
+        bits_ref = np.zeros((n, oracle.words(d) * 64), np.uint8)
+        bits_ref[:, :d] = ct < 0
+        wb_ref = np.packbits(bits_ref, axis=1, bitorder="little").view(np.uint64)
+        sc_ref = np.stack([[np.sqrt(np.sum(ct[i, wseg[j]:wseg[j + 1]].astype(np.float64) ** 2)
+                                    / (wseg[j + 1] - wseg[j])) for j in range(nw)]
+                           for i in range(n)])
+        # oracle
+        wb, wsc = oracle.compress_deferred16(g, m, c16, kind, ws, wseg, synth.BETA1)
+        assert np.array_equal(c16, ct_bits), f"stored state, step {step}"
+        assert np.array_equal(wb, wb_ref), f"sign words, step {step}"
+        assert np.allclose(wsc, sc_ref, rtol=2e-7, atol=0), f"scales, step {step}"
+        ws = wsc
