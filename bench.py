@@ -47,6 +47,14 @@ def gbytes(w, schedule="deferred"):
             # server bits read, denom read, x read+written (m stays implicit)
             "decompress_update": 1 / 8 + 12,
         }
+    if schedule == "state16":
+        return {
+            # as the deferred pass, with each worker's c read and written as
+            # 16-bit values
+            "compress_deferred16": 1 / 8 + n * (gb + 2) + 2 * n + n / 8,
+            "server_deferred": n / 8 + 8 + 1 / 8,
+            "decompress_update": 1 / 8 + 12,
+        }
     if schedule == "local":
         return {
             # g_i, m_i and the last c_i read; m_i, c_i and packed bits written
@@ -429,9 +437,12 @@ def main():
         S.start_compression()
         if schedule == "local":
             S.start_local_momentum()
-        fn = {"deferred": S.step_deferred, "explicit": S.step, "local": S.step_local}[schedule]
+        if schedule == "state16":
+            S.start_state16("bf16")
+        fn = {"deferred": S.step_deferred, "explicit": S.step, "local": S.step_local,
+              "state16": S.step_deferred16}[schedule]
         log(f"[bench] {schedule}: {args.warmup} untimed steps, {args.steps} timed steps")
-        if schedule == "deferred" and args.warmup == 0:
+        if schedule in ("deferred", "state16") and args.warmup == 0:
             fn(synth.BETA1, synth.LR, g=gsets[1])
         for i in range(args.warmup):
             fn(synth.BETA1, synth.LR, g=gsets[i % 2])
@@ -469,6 +480,7 @@ def main():
     ms_x, alg_x, kernels_x = run("explicit")
     ms_l, alg_l, kernels_l = run("local")
     del S.m_local
+    ms_h, alg_h, kernels_h = run("state16")  # last: it frees the binary32 rows
     # dominant kernel: the largest share of the step's time
     dom = max(alg, key=lambda k: kernels[k]["avg_ms"])
     dom_ms = kernels[dom]["avg_ms"]
@@ -517,6 +529,12 @@ def main():
             "step_alg_bytes_per_param": round(sum(alg_l.values()), 3),
             "step_alg_GBps": round(sum(alg_l.values()) * w.d / (ms_l * 1e-3) / 1e9, 1),
             "kernels": kernels_l},
+        "state16_schedule": {
+            "state": "each worker's compensated momentum c held in bfloat16",
+            "ms_per_step": round(ms_h, 4), "value": w.d / (ms_h * 1e-3),
+            "step_alg_bytes_per_param": round(sum(alg_h.values()), 3),
+            "step_alg_GBps": round(sum(alg_h.values()) * w.d / (ms_h * 1e-3) / 1e9, 1),
+            "kernels": kernels_h},
         "tensor_list_schedule": listed,
         "one_block_step": small,
         "kernel_source_sha256": source_hash(),

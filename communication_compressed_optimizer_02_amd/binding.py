@@ -44,6 +44,8 @@ SIGNATURES = {
     "oba_decompress_update": (_I, [_P, _P, _P, _P, _P, _P, _D, _P]),
     "oba_server_momentum": (_I, [_P, _P, _P, _P, _P]),
     "oba_compress_deferred": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _D, _P, _SZ, _P]),
+    "oba_compress_deferred16": (_I, [_P, _P, _I, _P, _P, _P, _P, _I, _P, _P, _D, _P, _SZ,
+                                     _P]),
     "oba_compress_deferred_local": (_I, [_P, _P, _I, _P, _P, _P, _P, _D, _P, _SZ, _P]),
     "oba_server_reduce_recompress_deferred": (_I, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "oba_deferred_errors": (_I, [_P, _P, _P, _P, _P, _P, _P, _P]),
@@ -307,6 +309,30 @@ def compress_deferred(L: Layout, g, m, c, wbits, wscale, beta1, sbits_prev=None,
     _check(rc, "oba_compress_deferred")
 
 
+def compress_deferred16(L: Layout, g, m, c16, wbits, wscale, beta1, sbits_prev=None,
+                        sscale_prev=None, stream=None):
+    """As compress_deferred with a 16-bit state: c16 [n][ld] torch.float16
+    (binary16) or torch.bfloat16, in (last c) / out (this c, rounded to the
+    format before it is compressed)."""
+    import torch
+
+    f32 = (torch.float32,)
+    P = ctypes.c_void_p
+    mp = _ptr(m, "m", f32, (L.d,)) if m is not None else P(None)
+    bp = (_ptr(sbits_prev, "sbits_prev", (torch.int64,), (L.W,)) if sbits_prev is not None
+          else P(None))
+    sp = (_ptr(sscale_prev, "sscale_prev", f32, (L.n_sseg,)) if sscale_prev is not None
+          else P(None))
+    cp = _ptr(c16, "c16", (torch.float16, torch.bfloat16), (L.n, L.ld))
+    rc = lib().oba_compress_deferred16(
+        L.handle, _ptr(g, "g", _gtypes(), (L.n, L.ld)), _gdtype(g),
+        mp, bp, sp, cp, _gdtype(c16),
+        _ptr(wbits, "wbits", (torch.int64,), (L.n, L.W)),
+        _ptr(wscale, "wscale", f32, (L.n, L.n_wseg)), beta1,
+        ctypes.c_void_p(L.ws.data_ptr()), L.ws_bytes, _stream(stream))
+    _check(rc, "oba_compress_deferred16")
+
+
 def compress_deferred_local(L: Layout, g, m_local, c, wbits, wscale, beta1, stream=None):
     """Per-worker momentum: m_local [n][ld] and c [n][ld] in/out."""
     import torch
@@ -533,7 +559,10 @@ class State:
         """State of the first compression step: m explicit, errors (or the
         stored c, a) and scales zero."""
         self._explicit_m()
-        self.delta.zero_()
+        if self.delta is not None:
+            self.delta.zero_()
+        if getattr(self, "c16", None) is not None:
+            self.c16.zero_()
         self.eps.zero_()
         self.wscale.zero_()
         self.sscale.zero_()
@@ -572,6 +601,31 @@ class State:
                    self.delta, self.wbits, self.wscale, self.eps, self.sbits, self.sscale,
                    self.denom, None if implicit_m else self.m, self.x, beta1, lr)
         self.m_implicit = implicit_m
+
+    def start_state16(self, kind="bf16"):
+        """Hold the workers' compensated vectors in a 16-bit format ("f16"
+        binary16 or "bf16" bfloat16) for step_deferred16: c16 [n][ld] zero,
+        scales zero, m explicit (the warm-up's); frees the binary32 rows."""
+        import torch
+
+        dt = {"f16": torch.float16, "bf16": torch.bfloat16}[kind]
+        self.delta = None
+        self.c16 = torch.zeros((self.L.n, self.L.ld), dtype=dt, device="cuda")
+        self.start_compression()
+
+    def step_deferred16(self, beta1, lr, g=None):
+        """The deferred step with the 16-bit worker state c16 (see
+        oba_compress_deferred16); the momentum stays implicit."""
+        g = self.g if g is None else g
+        if self.m_implicit:
+            compress_deferred16(self.L, g, None, self.c16, self.wbits, self.wscale, beta1,
+                                self.sbits, self.sscale)
+        else:
+            compress_deferred16(self.L, g, self.m, self.c16, self.wbits, self.wscale, beta1)
+        server_reduce_recompress_deferred(self.L, self.wbits, self.wscale, self.eps, self.sbits,
+                                          self.sscale)
+        decompress_update(self.L, self.sbits, self.sscale, self.denom, None, self.x, lr)
+        self.m_implicit = True
 
     def step_deferred(self, beta1, lr, g=None, implicit_m=True):
         """The same step in the deferred-residual layout: `delta` holds the

@@ -18,6 +18,10 @@
 #include "layout.hpp"
 #include "oba.h"
 
+#ifndef OBA_S16_GRID
+#define OBA_S16_GRID 0
+#endif
+
 struct oba_layout_s {
   oba::Plan plan;
   int device = -1;
@@ -242,9 +246,13 @@ int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const i
   L->tau = view(P.sp, s64, s32, (int32_t)P.sseg.size() - 1);
   L->tau_w = view(P.sp_w, t64, t32, (int32_t)P.sseg.size() - 1);
   L->tau_c = view(P.sp_c, c64, c32, (int32_t)P.sseg.size() - 1);
-  L->geo_w = oba::Geo{P.d, P.ld, P.W, P.S, P.n, P.nblk_w};
-  L->geo_c = oba::Geo{P.d, P.ld, P.W, P.S, P.n, P.nblk_c};
-  L->geo = oba::Geo{P.d, P.ld, P.W, P.S, P.n, P.nblk};
+  auto geo = [&](int32_t nblk) {  // an empty layout has no blocks
+    return oba::Geo{P.d, P.ld, P.W, P.S, P.n, nblk, nblk ? P.S / nblk : 0,
+                    nblk ? (int32_t)(P.S % nblk) : 0};
+  };
+  L->geo_w = geo(P.nblk_w);
+  L->geo_c = geo(P.nblk_c);
+  L->geo = geo(P.nblk);
   L->ws_worker = std::max(oba::partial_bytes(L->sig_c, P.n), oba::partial_bytes(L->sig, P.n));
   L->ws_server = oba::partial_bytes(L->tau, 1);
   *out = L;
@@ -428,6 +436,48 @@ int oba_compress_deferred(oba_layout L, const void* g, int g_dtype, const float*
   }));
   return launch("finalize_scales", stream,
                 [&] { oba::launch_finalize(part, G.n, L->sig_c, wscale, stream); });
+}
+
+int oba_compress_deferred16(oba_layout L, const void* g, int g_dtype, const float* m,
+                            const uint64_t* sbits_prev, const float* sscale_prev, void* c,
+                            int c_dtype, uint64_t* wbits, float* wscale, double beta1, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  OBA_TRY(check_layout(L));
+  if (!gdtype_ok(g_dtype)) return OBA_EINVAL;
+  if (c_dtype != OBA_F16 && c_dtype != OBA_BF16) return OBA_EINVAL;
+  if (!beta_ok(beta1)) return OBA_EINVAL;
+  const bool implicit_m = !m;
+  if (implicit_m != (sbits_prev != nullptr) || implicit_m != (sscale_prev != nullptr))
+    return OBA_EINVAL;
+  if (L->geo.d == 0) return OBA_OK;
+  OBA_TRY(check_buf(g, 16));
+  if (implicit_m) {
+    OBA_TRY(check_buf(sbits_prev, 8));
+    OBA_TRY(check_buf(sscale_prev, 4));
+  } else {
+    OBA_TRY(check_buf(m, 16));
+  }
+  OBA_TRY(check_buf(c, 8));
+  OBA_TRY(check_buf(wbits, 8));
+  OBA_TRY(check_buf(wscale, 4));
+  OBA_TRY(check_buf(ws, 8));
+  if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
+  // grid: the compress grid, or (OBA_S16_GRID = 1) the server grid's
+  // blocks of several spans, whose tables also cover this pass
+  const bool sg = OBA_S16_GRID != 0;
+  const oba::Geo G = sg ? L->geo : L->geo_c;
+  const oba::SegDev& sig = sg ? L->sig : L->sig_c;
+  double* part = static_cast<double*>(ws);
+  const float b1 = (float)beta1, omb1 = (float)(1.0 - beta1);
+  uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
+  const oba::MomSrc ms{reinterpret_cast<const uint8_t*>(sbits_prev), sscale_prev,
+                       sg ? L->tau : L->tau_c};
+  OBA_TRY(launch("compress_deferred16", stream, [&] {
+    oba::launch_compress_deferred16(G, g, g_dtype, m, c, c_dtype, wbytes, sig, part, wscale, b1,
+                                    omb1, ms, stream);
+  }));
+  return launch("finalize_scales", stream,
+                [&] { oba::launch_finalize(part, G.n, sig, wscale, stream); });
 }
 
 int oba_compress_deferred_local(oba_layout L, const void* g, int g_dtype, float* m_local,

@@ -26,6 +26,12 @@ namespace oba {
 // kDeferredLocal: as kDeferred with per-worker momentum: m is [n][ld], each
 //         worker's m_i = b1*m_i + (1-b1)*g_i is stored back and
 //         c = m_i + delta_i.
+// CT is the type of the state rows (delta, or c in the deferred modes):
+// binary32, or -- kDeferred and kDeferredM only -- a 16-bit format (uint16_t
+// binary16, bf16_bits bfloat16).  With a 16-bit row, c is rounded to the
+// format (nearest, ties to even) before its bits, its sum of squares and its
+// store, so the vector compressed is the one the next step reads back, and
+// the residual fed back is exact for what was sent.
 // The scale needs the whole segment's norm before any residual can be
 // written, so the explicit layout needs c twice.  Recomputing it reads g, m,
 // delta twice but never writes c: on this HBM, writes cost more than reads,
@@ -41,29 +47,45 @@ enum { kNorm = 1, kApply = 2, kDeferred = 3, kDeferredM = 4, kDeferredLocal = 5 
 #endif
 constexpr int kWorkerBatch = OBA_WORKER_BATCH;
 
-// Optional occupancy target of the worker pass (waves per SIMD), a tuning knob.
+// Workers loaded together by the pass with 16-bit state rows (a span of such
+// rows holds less data per worker, so it can take more workers per load batch
+// or fewer registers), a tuning knob.
+#ifndef OBA_WORKER_BATCH16
+#define OBA_WORKER_BATCH16 4
+#endif
+constexpr int kWorkerBatch16 = OBA_WORKER_BATCH16;
+
+// Optional occupancy targets (waves per SIMD) of the worker pass and of its
+// 16-bit-state instances, tuning knobs.
 #ifdef OBA_CMP_WAVES
 #define OBA_CMP_ATTR __attribute__((amdgpu_waves_per_eu(OBA_CMP_WAVES, OBA_CMP_WAVES)))
 #else
 #define OBA_CMP_ATTR
 #endif
+#ifdef OBA_CMP16_WAVES
+#define OBA_CMP16_ATTR __attribute__((amdgpu_waves_per_eu(OBA_CMP16_WAVES, OBA_CMP16_WAVES)))
+#else
+#define OBA_CMP16_ATTR
+#endif
 
-template <typename GT, int NB, int MODE, bool TL>
-__global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t i0, const GT* __restrict__ g,
-                                                     float* __restrict__ m,  // read; written by kDeferredLocal
-                                                     float* __restrict__ delta,
-                                                     uint8_t* __restrict__ wbytes, SegDev sig,
-                                                     double* __restrict__ part,
-                                                     const float* __restrict__ wscale, float b1,
-                                                     float omb1, MomSrc ms, TList tl) {
+template <typename GT, typename CT, int NB, int MODE, bool TL>
+__device__ __forceinline__ void compress_body(Geo G, int32_t i0, const GT* __restrict__ g,
+                                              float* __restrict__ m,  // read; written by kDeferredLocal
+                                              CT* __restrict__ delta,
+                                              uint8_t* __restrict__ wbytes, SegDev sig,
+                                              double* __restrict__ part,
+                                              const float* __restrict__ wscale, float b1,
+                                              float omb1, MomSrc ms, TList tl) {
   __shared__ double lds[kWaves * NB];
   const int32_t b = blockIdx.x;
   i0 += blockIdx.y * NB;  // this block's workers: [i0, i0 + NB)
-  const int64_t s_lo = dspan(G.S, G.nblk, b), s_hi = dspan(G.S, G.nblk, b + 1);
+  const int64_t s_lo = dspan(G, b), s_hi = dspan(G, b + 1);
   const int32_t p_end = sig.blk_first[b + 1];
   int32_t p = sig.blk_first[b];
   int64_t p_hi = sig.phi[p];
   static_assert(!TL || MODE >= kDeferred, "tensor lists: deferred passes only");
+  static_assert(__is_same(CT, float) || MODE == kDeferred || MODE == kDeferredM,
+                "16-bit state rows: the deferred passes with the shared momentum only");
   TCur tcur{};  // tensor cursor (tensor lists)
   if constexpr (TL) tcur = tcur_start(tl, b);
   // kDeferredM: cursor over the server segments (on this grid) for sbar
@@ -125,11 +147,13 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
     double fs[NB];
     // workers in batches of NBB: all loads of a batch, then its arithmetic
     // and stores (NBB < NB trades loads in flight per wave for occupancy)
-    constexpr int NBB = NB < kWorkerBatch ? NB : kWorkerBatch;
+    constexpr int kBatch = __is_same(CT, float) ? kWorkerBatch : kWorkerBatch16;
+    constexpr int NBB = NB < kBatch ? NB : kBatch;
 #pragma unroll
     for (int ib = 0; ib < NB; ib += NBB) {
       constexpr int NBL = MODE == kDeferredLocal ? NBB : 1;  // per-worker m rows
       float gv[NBB][8], c[NBB][8], ml[NBL][8];
+      uint32_t h16[NBB][4];  // a 16-bit state row's patterns
       // ib + u < NB is decided at compile time: a last batch may be partial
       if (full) {
 #pragma unroll
@@ -193,14 +217,15 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j) c[u][j] = compensate(b1, omb1, mv[j], gv[u][j], c[u][j]);
+          round_to_row<CT>(c[u], h16[u]);  // a 16-bit state: c as the row holds it
         }
         if (MODE != kNorm) store_sign_bits(wbytes + (int64_t)(i0 + i) * rowbytes, q, sign_bits(c[u]), rowbytes);
-        if (MODE >= kDeferred) store8(delta + row, q, G.d, full, c[u]);
+        if (MODE >= kDeferred) store_row(delta + row, q, G.d, full, c[u], h16[u]);
         fs[i] = (MODE != kApply) ? sumsq8(c[u]) : 0.0;
         if (MODE == kApply) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) c[u][j] = residual(c[u][j], sv[j]);
-          store8(delta + row, q, G.d, full, c[u]);
+          store_row(delta + row, q, G.d, full, c[u], h16[u]);
         }
       }
     }
@@ -222,7 +247,7 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
           const int64_t row = (int64_t)(i0 + i) * G.ld;
-          if (MODE >= kDeferred)
+          if constexpr (MODE >= kDeferred)
             acc[i] += sumsq_range(delta + row, q, cur, e);  // c was stored there
           else
             acc[i] += sumsq_range_c(m, g + row, delta + row, b1, omb1, q, cur, e);
@@ -237,16 +262,40 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(Geo G, int32_t
   }
 }
 
+template <typename GT, typename CT, int NB, int MODE, bool TL>
+__global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(
+    Geo G, int32_t i0, const GT* __restrict__ g, float* __restrict__ m, CT* __restrict__ delta,
+    uint8_t* __restrict__ wbytes, SegDev sig, double* __restrict__ part,
+    const float* __restrict__ wscale, float b1, float omb1, MomSrc ms, TList tl) {
+  compress_body<GT, CT, NB, MODE, TL>(G, i0, g, m, delta, wbytes, sig, part, wscale, b1, omb1,
+                                      ms, tl);
+}
+
+// the 16-bit-state instances (their own occupancy knob)
+template <typename GT, typename CT, int NB, int MODE, bool TL>
+__global__ __launch_bounds__(kBlock) OBA_CMP16_ATTR void k_compress16(
+    Geo G, int32_t i0, const GT* __restrict__ g, float* __restrict__ m, CT* __restrict__ delta,
+    uint8_t* __restrict__ wbytes, SegDev sig, double* __restrict__ part,
+    const float* __restrict__ wscale, float b1, float omb1, MomSrc ms, TList tl) {
+  compress_body<GT, CT, NB, MODE, TL>(G, i0, g, m, delta, wbytes, sig, part, wscale, b1, omb1,
+                                      ms, tl);
+}
+
 // ---- launchers ----------------------------------------------------------------
 
-template <typename GT, int NB, int MODE, bool TL>
+template <typename GT, typename CT, int NB, int MODE, bool TL>
 static void launch_cmp(const Geo& G, int32_t i0, int groups, const void* g, const float* m,
-                       float* delta, uint8_t* wbytes, const SegDev& sig, double* part,
+                       void* delta, uint8_t* wbytes, const SegDev& sig, double* part,
                        const float* wscale, float b1, float omb1, const MomSrc& ms,
                        const TList& tl, hipStream_t st) {
-  hipLaunchKernelGGL((k_compress<GT, NB, MODE, TL>), dim3(G.nblk, groups), dim3(kBlock), 0, st,
-                     G, i0, static_cast<const GT*>(g), const_cast<float*>(m), delta, wbytes, sig,
-                     part, wscale, b1, omb1, ms, tl);
+  if constexpr (__is_same(CT, float))
+    hipLaunchKernelGGL((k_compress<GT, CT, NB, MODE, TL>), dim3(G.nblk, groups), dim3(kBlock), 0,
+                       st, G, i0, static_cast<const GT*>(g), const_cast<float*>(m),
+                       static_cast<CT*>(delta), wbytes, sig, part, wscale, b1, omb1, ms, tl);
+  else
+    hipLaunchKernelGGL((k_compress16<GT, CT, NB, MODE, TL>), dim3(G.nblk, groups), dim3(kBlock),
+                       0, st, G, i0, static_cast<const GT*>(g), const_cast<float*>(m),
+                       static_cast<CT*>(delta), wbytes, sig, part, wscale, b1, omb1, ms, tl);
 }
 
 // Groups of GROUP workers per block, then one launch for the remainder.  A
@@ -264,15 +313,15 @@ constexpr int kImplicitNB = OBA_IMPLICIT_NB;
 static_assert(kMaxNB >= 1 && kMaxNB <= 8 && kImplicitNB >= 1 && kImplicitNB <= 8,
               "worker groups hold 1 to 8 workers");
 
-template <typename GT, int MODE, bool TL>
-static void launch_cmp_n(const Geo& G, const void* g, const float* m, float* delta,
+template <typename GT, typename CT, int MODE, bool TL>
+static void launch_cmp_n(const Geo& G, const void* g, const float* m, void* delta,
                          uint8_t* wbytes, const SegDev& sig, double* part, const float* wscale,
                          float b1, float omb1, const MomSrc& ms, const TList& tl,
                          hipStream_t st) {
   constexpr int GROUP = (MODE == kDeferredM || MODE == kDeferredLocal) ? kImplicitNB : kMaxNB;
   const int full = G.n / GROUP, rem = G.n % GROUP, i0 = full * GROUP;
 #define OBA_CMP(NB_, I0, GROUPS) \
-  launch_cmp<GT, NB_, MODE, TL>(G, I0, GROUPS, g, m, delta, wbytes, sig, part, wscale, b1, omb1, \
+  launch_cmp<GT, CT, NB_, MODE, TL>(G, I0, GROUPS, g, m, delta, wbytes, sig, part, wscale, b1, omb1, \
                                 ms, tl, st)
   if (full) OBA_CMP(GROUP, 0, full);
   switch (rem) {
@@ -288,20 +337,20 @@ static void launch_cmp_n(const Geo& G, const void* g, const float* m, float* del
 #undef OBA_CMP
 }
 
-template <int MODE, bool TL = false>
-static void launch_cmp_t(const Geo& G, const void* g, int gdt, const float* m, float* delta,
+template <int MODE, bool TL = false, typename CT = float>
+static void launch_cmp_t(const Geo& G, const void* g, int gdt, const float* m, void* delta,
                          uint8_t* wbytes, const SegDev& sig, double* part, const float* wscale,
                          float b1, float omb1, const MomSrc& ms, hipStream_t st,
                          const TList& tl = TList{}) {
   if (gdt == kGradF16)
-    launch_cmp_n<uint16_t, MODE, TL>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms, tl,
-                                     st);
+    launch_cmp_n<uint16_t, CT, MODE, TL>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms,
+                                         tl, st);
   else if (gdt == kGradBF16)
-    launch_cmp_n<bf16_bits, MODE, TL>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms,
-                                      tl, st);
+    launch_cmp_n<bf16_bits, CT, MODE, TL>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1,
+                                          ms, tl, st);
   else
-    launch_cmp_n<float, MODE, TL>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms, tl,
-                                  st);
+    launch_cmp_n<float, CT, MODE, TL>(G, g, m, delta, wbytes, sig, part, wscale, b1, omb1, ms,
+                                      tl, st);
 }
 
 void launch_compress_norm(const Geo& G, const void* g, int gdt, const float* m,
@@ -320,6 +369,28 @@ void launch_compress_deferred(const Geo& G, const void* g, int gdt, const float*
                              st);
   else
     launch_cmp_t<kDeferred>(G, g, gdt, m, c, wbytes, sig, part, wscale_prev, b1, omb1, ms, st);
+}
+
+void launch_compress_deferred16(const Geo& G, const void* g, int gdt, const float* m, void* c,
+                                int cdt, uint8_t* wbytes, const SegDev& sig, double* part,
+                                const float* wscale_prev, float b1, float omb1, const MomSrc& ms,
+                                hipStream_t st) {
+  const TList none{};
+  if (cdt == kGradBF16) {
+    if (ms.sbytes)
+      launch_cmp_t<kDeferredM, false, bf16_bits>(G, g, gdt, nullptr, c, wbytes, sig, part,
+                                                 wscale_prev, b1, omb1, ms, st, none);
+    else
+      launch_cmp_t<kDeferred, false, bf16_bits>(G, g, gdt, m, c, wbytes, sig, part, wscale_prev,
+                                                b1, omb1, ms, st, none);
+  } else {
+    if (ms.sbytes)
+      launch_cmp_t<kDeferredM, false, uint16_t>(G, g, gdt, nullptr, c, wbytes, sig, part,
+                                                wscale_prev, b1, omb1, ms, st, none);
+    else
+      launch_cmp_t<kDeferred, false, uint16_t>(G, g, gdt, m, c, wbytes, sig, part, wscale_prev,
+                                               b1, omb1, ms, st, none);
+  }
 }
 
 void launch_compress_deferred_listed(const Geo& G, const TList& tl, int gdt, const float* m,

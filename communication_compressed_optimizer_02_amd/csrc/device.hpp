@@ -314,6 +314,71 @@ __device__ __forceinline__ void store8(float* __restrict__ p, const Quads& q, in
   }
 }
 
+// ---- 16-bit state rows (binary16 as uint16_t, bfloat16 as bf16_bits) --------
+// A lane's 8 values are rounded in pairs with gfx950's packed conversions
+// (v_cvt_pk_f16_f32, v_cvt_pk_bf16_f32): nearest, ties to even, subnormals
+// kept, overflow to an infinity.  h[i] holds values 2i (low half) and 2i+1.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack2(const uint16_t*, float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+__device__ __forceinline__ uint32_t pack2(const bf16_bits*, float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ float lo16(const uint16_t*, uint32_t h) {
+  return half_bits_to_float(h & 0xFFFFu);
+}
+__device__ __forceinline__ float hi16(const uint16_t*, uint32_t h) {
+  return half_bits_to_float(h >> 16);
+}
+__device__ __forceinline__ float lo16(const bf16_bits*, uint32_t h) {
+  return __builtin_bit_cast(float, h << 16);
+}
+__device__ __forceinline__ float hi16(const bf16_bits*, uint32_t h) {
+  return __builtin_bit_cast(float, h & 0xFFFF0000u);
+}
+
+// The values a row of type T holds for v: v itself for binary32; else v
+// rounded to the 16-bit format, whose bit patterns go to h for the store.
+template <typename T>
+__device__ __forceinline__ void round_to_row(float (&v)[8], uint32_t (&h)[4]) {
+  if constexpr (!__is_same(T, float)) {
+    const T* tag = nullptr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[i] = pack2(tag, v[2 * i], v[2 * i + 1]);
+      v[2 * i] = lo16(tag, h[i]);
+      v[2 * i + 1] = hi16(tag, h[i]);
+    }
+  }
+}
+
+// Store a row's values: binary32 from v; a 16-bit row from the patterns h
+// that round_to_row made.
+__device__ __forceinline__ void store_row(float* __restrict__ p, const Quads& q, int64_t d,
+                                          bool full, const float (&v)[8], const uint32_t (&)[4]) {
+  store8(p, q, d, full, v);
+}
+
+template <typename T16>
+__device__ __forceinline__ void store_row(T16* __restrict__ p, const Quads& q, int64_t d,
+                                          bool full, const float (&)[8], const uint32_t (&h)[4]) {
+  if (full) {
+    stv(u32x2{h[0], h[1]}, reinterpret_cast<u32x2*>(p + q.kA));
+    stv(u32x2{h[2], h[3]}, reinterpret_cast<u32x2*>(p + q.kB));
+  } else {
+    uint16_t* e = reinterpret_cast<uint16_t*>(p);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t k = coord(q, j);
+      if (k < d) e[k] = (uint16_t)(h[j >> 1] >> (16 * (j & 1)));
+    }
+  }
+}
+
 // c = (b1*m + (1-b1)*g) + delta: two products, then two adds (no contraction)
 __device__ __forceinline__ float compensate(float b1, float omb1, float m, float g, float dl) {
   const float p = b1 * m + omb1 * g;
@@ -414,9 +479,10 @@ __device__ __forceinline__ void flush_rows(double (&acc)[NB], int nw, double* __
   __syncthreads();
 }
 
-// First span of block b (same split as the host planner's span_begin).
-__device__ __forceinline__ int64_t dspan(int64_t S, int32_t nblk, int32_t b) {
-  return (int64_t)b * S / nblk;
+// First span of block b (same split as the host planner's span_begin): a
+// multiply and a min, no 64-bit division in the prologue of short blocks.
+__device__ __forceinline__ int64_t dspan(const Geo& G, int32_t b) {
+  return (int64_t)b * G.q + min(b, G.r);
 }
 
 // Segment of coordinate k, walking forward from segment j0 (k >= off[j0]).
@@ -440,14 +506,15 @@ __device__ __forceinline__ void lane_segs(const int64_t* __restrict__ off, int32
 }
 
 // Sum of squares of row[k] for the lane's coordinates k in [a, e).
-__device__ __forceinline__ double sumsq_range(const float* row, const Quads& q, int64_t a,
+template <typename T>
+__device__ __forceinline__ double sumsq_range(const T* row, const Quads& q, int64_t a,
                                               int64_t e) {
   double s = 0.0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int64_t k = coord(q, j);
     if (k >= a && k < e) {
-      const double x = (double)row[k];
+      const double x = (double)elem(row, k);
       s = __builtin_fma(x, x, s);
     }
   }

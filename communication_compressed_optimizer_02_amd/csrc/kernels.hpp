@@ -12,6 +12,8 @@ namespace oba {
 struct Geo {
   int64_t d, ld, W, S;
   int32_t n, nblk;
+  int64_t q;  // S / nblk: spans per block (the first r blocks take one more)
+  int32_t r;  // S % nblk
 };
 
 // Device view of one segmentation (see layout.hpp for pieces).
@@ -133,6 +135,12 @@ void launch_compress_deferred(const Geo& G, const void* g, int gdt, const float*
                               uint8_t* wbytes, const SegDev& sig, double* part,
                               const float* wscale_prev, float b1, float omb1, const MomSrc& ms,
                               hipStream_t st);
+// The same pass with 16-bit state rows c (cdt: kGradF16 binary16, kGradBF16
+// bfloat16): c is rounded to the format before it is compressed and stored.
+void launch_compress_deferred16(const Geo& G, const void* g, int gdt, const float* m, void* c,
+                                int cdt, uint8_t* wbytes, const SegDev& sig, double* part,
+                                const float* wscale_prev, float b1, float omb1, const MomSrc& ms,
+                                hipStream_t st);
 void launch_server_deferred(const Geo& G, const uint8_t* wbytes, const float* wscale, float* a,
                             uint8_t* sbytes, const SegDev& sig, const SegDev& tau, double* part,
                             const float* sscale_prev, hipStream_t st);

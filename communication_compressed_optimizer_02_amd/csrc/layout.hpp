@@ -1,8 +1,9 @@
 // layout.hpp -- host-only planning of the streaming grid and segment pieces.
 //
 // The streaming kernels cut [0, d) into spans of kSpan coordinates (one span
-// = one pass of a 256-thread block, 8 consecutive coordinates per lane) and
-// give block b the contiguous span range [b*S/nblk, (b+1)*S/nblk).  A segment
+// = one pass of a 256-thread block, 8 coordinates per lane) and give each
+// block a contiguous range of spans: floor(S/nblk) each, one more for the
+// first S mod nblk blocks (span_begin).  A segment
 // table is then cut at block boundaries into "pieces": each piece lies in one
 // block and one segment, so a block can reduce its part of a segment's sum of
 // squares into one binary64 partial per piece without atomics, and a segment's
@@ -80,8 +81,11 @@ int validate(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_ws
 int make_plan(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_wseg,
               const int64_t* sseg, int32_t n_sseg, Plan* out);
 
+// First span of block b: every block takes S / nblk spans and the first
+// S % nblk blocks one more.
 inline int64_t span_begin(int64_t S, int32_t nblk, int32_t b) {
-  return (int64_t)b * S / nblk;
+  const int64_t q = S / nblk, r = S % nblk;
+  return (int64_t)b * q + std::min<int64_t>(b, r);
 }
 
 // Tensor lists: checks lengths (each a positive multiple of 4, summing to d)

@@ -20,7 +20,7 @@ __global__ __launch_bounds__(kBlock) void k_residual(Geo G, const float* src, in
   const float* srow = src + (int64_t)blockIdx.y * src_ld;
   float* drow = dst + (int64_t)blockIdx.y * dst_ld;
   const float* sc = scale + (int64_t)blockIdx.y * T.n_seg;
-  const int64_t s_lo = dspan(G.S, G.nblk, b), s_hi = dspan(G.S, G.nblk, b + 1);
+  const int64_t s_lo = dspan(G, b), s_hi = dspan(G, b + 1);
   const int32_t p_end = T.blk_first[b + 1];
   int32_t p = T.blk_first[b];
   int64_t p_hi = T.phi[p];
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kBlock) OBA_SRV_ATTR void k_server_p1(Geo G, const 
   // (measured 6 % faster than a byte load per lane and row plus a swap)
   __shared__ uint2 rows_lds[OBA_SRV_LDS ? NB * 32 : 1];
   const int32_t b = blockIdx.x;
-  const int64_t s_lo = dspan(G.S, G.nblk, b), s_hi = dspan(G.S, G.nblk, b + 1);
+  const int64_t s_lo = dspan(G, b), s_hi = dspan(G, b + 1);
   const int32_t ps_end = sig.blk_first[b + 1], pt_end = tau.blk_first[b + 1];
   int32_t ps = sig.blk_first[b], pt = tau.blk_first[b];
   int64_t ps_hi = sig.phi[ps], pt_hi = tau.phi[pt];

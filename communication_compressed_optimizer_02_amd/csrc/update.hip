@@ -23,7 +23,7 @@ __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
   const int32_t b = blockIdx.x;
   TCur tcur{};  // tensor cursor (tensor lists: x listed)
   if constexpr (TL) tcur = tcur_start(tl, b);
-  const int64_t s_lo = dspan(G.S, G.nblk, b), s_hi = dspan(G.S, G.nblk, b + 1);
+  const int64_t s_lo = dspan(G, b), s_hi = dspan(G, b + 1);
   const int32_t p_end = tau.blk_first[b + 1];
   int32_t p = tau.blk_first[b];
   int64_t p_hi = tau.phi[p];

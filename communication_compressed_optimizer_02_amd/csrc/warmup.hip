@@ -22,8 +22,8 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
                                                         double* __restrict__ part, TList tl) {
   __shared__ double lds[kWaves];
   double acc[1] = {0.0};
-  const int64_t s_lo = dspan(G.S, G.nblk, blockIdx.x);
-  const int64_t s_hi = dspan(G.S, G.nblk, blockIdx.x + 1);
+  const int64_t s_lo = dspan(G, (int32_t)blockIdx.x);
+  const int64_t s_hi = dspan(G, (int32_t)blockIdx.x + 1);
   TCur tcur{};  // tensor cursor (tensor lists: x and g listed)
   if constexpr (TL) tcur = tcur_start(tl, blockIdx.x);
   const float nf = (float)G.n;
@@ -109,8 +109,8 @@ __global__ __launch_bounds__(kNormBlock) void k_norm_finalize(const double* __re
 __global__ __launch_bounds__(kBlock) void k_freeze(Geo G, const float* __restrict__ v,
                                                    float* __restrict__ denom, float eta,
                                                    float bc2) {
-  const int64_t s_lo = dspan(G.S, G.nblk, blockIdx.x);
-  const int64_t s_hi = dspan(G.S, G.nblk, blockIdx.x + 1);
+  const int64_t s_lo = dspan(G, (int32_t)blockIdx.x);
+  const int64_t s_hi = dspan(G, (int32_t)blockIdx.x + 1);
   for (int64_t s = s_lo; s < s_hi; ++s) {
     const int64_t lo = s * kSpan;
     const Quads q = quads(lo);

@@ -264,6 +264,31 @@ int oba_compress_deferred_local(oba_layout layout, const void* g, int g_dtype, f
                                 float* c, uint64_t* wbits, float* wscale, double beta1, void* ws,
                                 size_t ws_bytes, hipStream_t stream);
 
+/* The worker pass of the deferred layout with each worker's compensated
+ * vector held in a 16-bit format (c_dtype OBA_F16 binary16 or OBA_BF16
+ * bfloat16): half the bytes of the largest state and of its two streams per
+ * step ([AIMech] limitations: the error buffers are the method's memory
+ * cost; [Tang] 4.3 and [CwP] fix the compressor, which is unchanged).
+ * c: [n][ld] 16-bit elements, 8-byte aligned, in (last c, exactly as stored)
+ * / out; every other argument as for oba_compress_deferred.  Per worker i
+ * and coordinate, in binary32:
+ *   c'  = c_i decoded (exact);  delta_i = c' - s_i*sign(c');
+ *   c   = (b1*m + (1-b1)*g_i) + delta_i;
+ *   c~  = c rounded to the format (nearest, ties to even; overflow gives an
+ *         infinity, as the format's conversion does);
+ * then c~ is compressed (scale sqrt(sum c~^2 / |sigma|), bit = (c~ < 0), so a
+ * c that rounds to -0 encodes +1) and stored as the new c_i.  The residual
+ * the next step feeds back is exact for the message sent; the rounding c - c~
+ * is this variant's own loss and is not fed back.  The step continues with
+ * oba_server_reduce_recompress_deferred and oba_decompress_update, unchanged.
+ * Start of the compression stage: zero c (all-zero bits) and wscale.
+ * OBA_EINVAL for another c_dtype; otherwise the errors of
+ * oba_compress_deferred. */
+int oba_compress_deferred16(oba_layout layout, const void* g, int g_dtype, const float* m,
+                            const uint64_t* sbits_prev, const float* sscale_prev, void* c,
+                            int c_dtype, uint64_t* wbits, float* wscale, double beta1, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
 /* a: [d] in (last a) / out (this a); sscale: [n_sseg] in (last) / out (this);
  * wbits, wscale: this step's worker messages; sbits, ws as for
  * oba_server_reduce_recompress.

@@ -132,9 +132,10 @@ def check_pieces(res, offs):
             pos = hi
         assert pos == d
         # each block's pieces cover exactly its span range
+        q, r = divmod(S, nblk)  # floor(S/nblk) spans per block, one more for the first r
         for b in range(nblk):
-            r0 = (b * S // nblk) * SPAN
-            r1 = min(((b + 1) * S // nblk) * SPAN, d)
+            r0 = (b * q + min(b, r)) * SPAN
+            r1 = min(((b + 1) * q + min(b + 1, r)) * SPAN, d)
             mine = pcs[blk[b]:blk[b + 1]]
             assert mine and mine[0][0] == r0 and mine[-1][1] == r1
         # each segment's pieces are consecutive, first index recorded
@@ -256,8 +257,9 @@ def test_tensor_list_block_tables(driver):
         off = np.concatenate([[0], np.cumsum(lengths)])
         for nb, first in zip((nblk_w, nblk, nblk_c), firsts):
             assert len(first) == nb
+            q, r = divmod(S, nb)
             for b, t in enumerate(first):
-                k = (b * S // nb) * SPAN
+                k = (b * q + min(b, r)) * SPAN
                 assert off[t] <= k < off[t + 1]
 
 

@@ -1,0 +1,246 @@
+"""GPU tests of the worker pass with a 16-bit compensated-momentum state
+(oba_compress_deferred16): each worker's c is rounded to binary16 or
+bfloat16 (nearest, ties to even) before it is compressed and stored.
+
+Single calls from the same state must match the oracle bit for bit in the
+stored 16-bit c and the packed words (both sides compute c in the same
+binary32 order and round it by the format's definition), with scales within
+the binary32 tolerance.  Free runs track the oracle through the whole step
+(server pass and update unchanged)."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_common import (B1, ETA, LR, assert_close, assert_words, cut_table, grads, padded,
+                        to_dev, to_host, torch)
+from communication_compressed_optimizer_02_amd import binding as oba
+from communication_compressed_optimizer_02_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+ULP_REL = {"f16": 2.0 ** -10, "bf16": 2.0 ** -7}  # one unit in the last place, relative
+SENTINEL = {"f16": 0x5555, "bf16": 0x3F99}  # padding columns the kernel must not touch
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev16(bits, kind):
+    t = torch()
+    dt = t.float16 if kind == "f16" else t.bfloat16
+    return t.from_numpy(np.ascontiguousarray(bits).view(np.int16).copy()).view(dt).cuda()
+
+
+def host16(x):
+    return x.detach().cpu().view(torch().int16).numpy().view(np.uint16)
+
+
+def tables(rng, d, n, tab):
+    if tab == "shards":
+        return synth.whole(d), synth.even_shards(d, n)
+    if tab == "singletons":
+        s = np.arange(d + 1, dtype=np.int64)
+        return s, s
+    return cut_table(rng, d, 6), cut_table(rng, d, 4)
+
+
+def implicit_m(rng, d, sseg):
+    """A random last server message (bits, scales) and the momentum it
+    carries, m = sbar*sign, from the oracle's update."""
+    W = oracle.words(d)
+    sbits = rng.integers(0, 2 ** 63, size=W, dtype=np.int64).astype(np.uint64)
+    sbits ^= rng.integers(0, 2, size=W).astype(np.uint64) << np.uint64(63)
+    if d % 64:
+        sbits[-1] &= np.uint64((1 << (d % 64)) - 1)
+    sscale = rng.uniform(1e-4, 2e-3, len(sseg) - 1).astype(np.float32)
+    m = np.zeros(d, np.float32)
+    x = np.zeros(d, np.float32)
+    oracle.decompress_update(sbits, sscale, sseg, np.ones(d, np.float32), m, x, 0.0)
+    return sbits, sscale, m
+
+
+@pytest.mark.parametrize("d,n,gdt,kind,tab,imp", [
+    (4096, 2, "f32", "bf16", "shards", False),
+    (2049, 3, "f16", "f16", "cuts", True),
+    (300, 2, "f32", "f16", "singletons", False),
+    (20_011, 5, "bf16", "bf16", "cuts", True),
+    (1_000_003, 8, "f16", "bf16", "shards", True),
+    (300_007, 11, "f32", "f16", "cuts", False),
+    (1, 1, "f32", "bf16", "shards", False),
+])
+def test_one_call_matches_oracle_bitwise(d, n, gdt, kind, tab, imp):
+    say(f"[state16 one call] d={d} n={n} g={gdt} c={kind} tables={tab} implicit_m={imp}")
+    rng = np.random.default_rng(11 * d + n)
+    wseg, sseg = tables(rng, d, n, tab)
+    L = oba.Layout(d, n, wseg, sseg)
+    st = synth.host_state(rng, d, n)
+    g = padded(grads(rng, n, d, gdt), L.ld)
+    # last c: compensated-momentum-sized values, rounded to the format
+    c_prev = np.full((n, L.ld), SENTINEL[kind], np.uint16)
+    c_prev[:, :d] = oracle.round16(rng.normal(0.0, 1e-3, (n, d)), kind)
+    wsp = rng.uniform(1e-4, 2e-3, (n, len(wseg) - 1)).astype(np.float32)
+    if imp:
+        sbits, sscale, m = implicit_m(rng, d, sseg)
+    else:
+        m = st["m"]
+    c_ora = c_prev.copy()
+    wb, ws = oracle.compress_deferred16(g, m, c_ora, kind, wsp, wseg, B1)
+
+    c_dev = dev16(c_prev, kind)
+    wbits = torch().zeros((n, L.W), dtype=torch().int64, device="cuda")
+    wscale = torch().from_numpy(wsp.copy()).cuda()
+    if imp:
+        oba.compress_deferred16(L, to_dev(g), None, c_dev, wbits, wscale, B1,
+                                to_dev(sbits), to_dev(sscale))
+    else:
+        oba.compress_deferred16(L, to_dev(g), to_dev(m), c_dev, wbits, wscale, B1)
+    torch().cuda.synchronize()
+    got = host16(c_dev)
+    bad = np.argwhere(got[:, :d] != c_ora[:, :d])
+    assert len(bad) == 0, f"c16: {len(bad)} elements differ, first at {bad[:4]}"
+    assert (got[:, d:] == SENTINEL[kind]).all(), "padding columns were written"
+    assert_words(to_host(wbits, np.uint64), wb, "worker words")
+    assert_close(to_host(wscale), ws, "worker scales")
+    L.close()
+
+
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+def test_rounding_edges(kind):
+    """With beta1 = 0, binary32 gradients, a zero last c and zero scales, the
+    compensated vector is the gradient itself, so the rounding sees chosen
+    values: ties, the largest finite values and overflow, subnormals,
+    negative values that round to -0 (which encode +1).  Every coordinate is
+    its own worker segment, so each scale is |c~| exactly."""
+    say(f"[state16 rounding edges] c={kind}")
+    if kind == "f16":
+        vals = [1 + 2 ** -11, 1 + 3 * 2 ** -11, -(1 + 2 ** -11), 65504.0, 65519.0, 65520.0,
+                -65520.0, 2 ** -25, 3 * 2 ** -25, -(2 ** -26), 2 ** -24, 6.0e-5, 2 ** -14,
+                2 ** -14 - 2 ** -25, 1e5, -1e-30, 0.0, -0.0, 1.0e-3, -7.77e-4]
+    else:
+        vals = [1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 3.3895314e38, 3.4028235e38,
+                -3.4028235e38, 1e-40, -1e-40, 2 ** -133, 3 * 2 ** -134, -(2 ** -135),
+                1.17549435e-38, 0.0, -0.0, 1.0e-3, -7.77e-4, 1.0 + 2 ** -9 + 2 ** -20]
+    rng = np.random.default_rng(5)
+    vals += list(rng.normal(0.0, 1.0, 64 - len(vals)) * np.exp(rng.uniform(-20, 20, 64 - len(vals))))
+    d, n = len(vals), 1
+    seg = np.arange(d + 1, dtype=np.int64)
+    L = oba.Layout(d, n, seg, seg)
+    g = padded(np.array([vals], np.float32), L.ld)
+    c_ora = np.zeros((n, L.ld), np.uint16)
+    wsp = np.zeros((n, d), np.float32)
+    m = np.zeros(d, np.float32)
+    wb, ws = oracle.compress_deferred16(g, m, c_ora, kind, wsp, seg, 0.0)
+    c_dev = dev16(np.zeros((n, L.ld), np.uint16), kind)
+    wbits = torch().zeros((n, L.W), dtype=torch().int64, device="cuda")
+    wscale = torch().zeros((n, d), dtype=torch().float32, device="cuda")
+    oba.compress_deferred16(L, to_dev(g), to_dev(m), c_dev, wbits, wscale, 0.0)
+    torch().cuda.synchronize()
+    got = host16(c_dev)[:, :d]
+    bad = np.nonzero(got[0] != c_ora[0, :d])[0]
+    assert len(bad) == 0, [(vals[k], hex(got[0, k]), hex(c_ora[0, k])) for k in bad[:6]]
+    # c = (0*m + 1*g) + 0 is g itself, except that -0.0 becomes +0.0 in the
+    # first add; the oracle's rounding is pinned to numpy and torch
+    ref = oracle.round16(np.array(vals, np.float32) + np.float32(0.0), kind)
+    assert np.array_equal(ref, c_ora[0, :d])
+    assert_words(to_host(wbits, np.uint64), wb, "worker words")
+    assert np.array_equal(to_host(wscale), ws), "scales (|c~| per coordinate)"
+    L.close()
+
+
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+def test_tiny_free_run_tracks_oracle(kind):
+    """The tiny workload from the same start: 10 warm-up steps, the freeze,
+    then 10 steps with the 16-bit state on both sides (server pass and update
+    unchanged, momentum implicit after the first step)."""
+    w = synth.workload("tiny")
+    say(f"[state16 free run] tiny d={w.d} n={w.n} c={kind}")
+    x0, G = synth.tiny_inputs(w.seed, w.d, w.n)
+    L = oba.Layout(w.d, w.n, w.wseg, w.sseg)
+    S = oba.State(L)
+    S.x.copy_(torch().from_numpy(x0))
+    x, m, v = x0.copy(), np.zeros(w.d, np.float32), np.zeros(w.d, np.float32)
+    for t in range(10):
+        oracle.adam_warmup_step(G[t], x, m, v, LR, B1, synth.BETA2, ETA)
+        S.warmup(LR, B1, synth.BETA2, ETA, g=to_dev(G[t]))
+    S.freeze(ETA)
+    S.start_state16(kind)
+    run_free(L, S, kind, G[10:20], w.wseg, w.sseg,
+             dict(x=x, m=m, eps=np.zeros(w.d, np.float32), denom=oracle.freeze_variance(v, ETA)))
+    L.close()
+
+
+@pytest.mark.parametrize("d,n,gdt,kind,tab", [(1_000_003, 8, "f16", "bf16", "shards"),
+                                              (300_007, 5, "f32", "f16", "cuts")])
+def test_free_run_tracks_oracle(d, n, gdt, kind, tab):
+    say(f"[state16 free run] d={d} n={n} g={gdt} c={kind} tables={tab}")
+    rng = np.random.default_rng(d + 3 * n)
+    wseg, sseg = tables(rng, d, n, tab)
+    L = oba.Layout(d, n, wseg, sseg)
+    st = synth.host_state(rng, d, n)
+    S = oba.State(L, gdt)
+    denom = oracle.freeze_variance(st["v"], ETA)
+    for nm, a in (("m", st["m"]), ("x", st["x"]), ("denom", denom)):
+        getattr(S, nm).copy_(torch().from_numpy(a))
+    S.start_state16(kind)
+    G = [grads(rng, n, d, gdt) for _ in range(5)]
+    run_free(L, S, kind, G, wseg, sseg,
+             dict(x=st["x"].copy(), m=st["m"].copy(), eps=np.zeros(d, np.float32), denom=denom))
+    L.close()
+
+
+def run_free(L, S, kind, G, wseg, sseg, st):
+    d, n = L.d, L.n
+    c16 = np.zeros((n, L.ld), np.uint16)
+    wsp = np.zeros((n, len(wseg) - 1), np.float32)
+    eps = torch().zeros_like(S.eps)
+    for t, g in enumerate(G):
+        gp = padded(g, L.ld)
+        wb, ws = oracle.compress_deferred16(gp, st["m"], c16, kind, wsp, wseg, B1)
+        wsp = ws
+        sb, ss = oracle.server_reduce_recompress(wb, ws, wseg, sseg, st["eps"])
+        oracle.decompress_update(sb, ss, sseg, st["denom"], st["m"], st["x"], LR)
+        S.step_deferred16(B1, LR, g=to_dev(gp))
+        oba.deferred_errors(L, None, None, S.eps, S.sscale, None, eps)
+        torch().cuda.synchronize()
+        assert_words(to_host(S.wbits, np.uint64), wb, f"worker words, step {t}")
+        assert_words(to_host(S.sbits, np.uint64), sb, f"server words, step {t}")
+        assert_close(to_host(S.wscale), ws, f"worker scales, step {t}")
+        assert_close(to_host(S.sscale), ss, f"server scales, step {t}")
+        got = host16(S.c16)[:, :d]
+        ref = c16[:, :d]
+        same = float(np.mean(got == ref))
+        assert same > 0.999, f"c16, step {t}: only {same:.5f} of the elements bit-identical"
+        assert_close(oracle.decode16(got, kind), oracle.decode16(ref, kind), f"c16, step {t}",
+                     rtol=ULP_REL[kind])
+        assert_close(to_host(eps), st["eps"], f"eps, step {t}")
+        assert_close(to_host(S.momentum()), st["m"], f"m, step {t}")
+        assert_close(to_host(S.x), st["x"], f"x, step {t}")
+        S.m_implicit = True  # momentum() wrote m out; the next step still rebuilds it
+
+
+def test_state16_rejects_bad_arguments():
+    import ctypes
+
+    L = oba.Layout(100, 2, synth.whole(100), synth.even_shards(100, 2))
+    S = oba.State(L)
+    S.start_state16("f16")
+    P = ctypes.c_void_p
+    strm = P(torch().cuda.current_stream().cuda_stream)
+    lib = oba.lib()
+
+    def call(cdt, c=None, m=P(S.m.data_ptr())):
+        c = P(S.c16.data_ptr()) if c is None else c
+        return lib.oba_compress_deferred16(L.handle, P(S.g.data_ptr()), 0, m, None, None, c, cdt,
+                                           P(S.wbits.data_ptr()), P(S.wscale.data_ptr()), B1,
+                                           P(L.ws.data_ptr()), L.ws_bytes, strm)
+    assert call(0) == -1  # binary32 is not a 16-bit format
+    assert call(3) == -1
+    assert call(1, c=P(S.c16.data_ptr() + 2)) == -2  # 8-byte alignment
+    assert call(1, m=None) == -1  # no momentum source
+    assert call(1) == 0 and call(2) == 0
+    torch().cuda.synchronize()
+    L.close()
