@@ -41,7 +41,12 @@ constexpr int kMaxBlocksWorker = OBA_MAX_BLOCKS_WORKER;
 // Spans per block of the compress grid: one when a block holds four workers
 // or more; with fewer workers per block a block does too little work per
 // span, and 4/n spans per block measured 16 % faster for one worker.
-inline int32_t compress_spans(int32_t n) { return n >= 4 ? 1 : 4 / n; }
+// Spans per block of the compress grid for four or more workers, a tuning
+// knob (fewer workers take 4/n, so a block still has about four workers' spans).
+#ifndef OBA_CMP_SPANS
+#define OBA_CMP_SPANS 1
+#endif
+inline int32_t compress_spans(int32_t n) { return n >= 4 ? OBA_CMP_SPANS : 4 / n; }
 constexpr int32_t kMaxWorkers = 4096;
 
 // A segment cut into more than kSplitAbove pieces has its partials summed in
