@@ -244,3 +244,104 @@ def test_state16_rejects_bad_arguments():
     assert call(1) == 0 and call(2) == 0
     torch().cuda.synchronize()
     L.close()
+
+
+def test_bert_large_state16_full_size_free_run():
+    """bert_large in bench.py's launch configuration of the 16-bit state
+    (bfloat16 c on the server grid): from a drawn freeze state (x, m, denom
+    drawn on the device; c and the scales zero), two steps on the GPU and in
+    the oracle, the first reading m and the second rebuilding it from the
+    server message.  Packed words must match bit for bit except where the
+    encoded value is within 1e-6 of its scale (R17 of the tolerance); the
+    stored c~ within one unit in its last place (bit-identical almost
+    everywhere); scales, eps, m and x within the binary32 tolerance, outside
+    the coordinates such a sign difference reaches."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    t = torch()
+    w = synth.workload("bert_large")
+    d, n, kind = w.d, w.n, "bf16"
+    say(f"[state16 full size] bert_large d={d} n={n} c={kind}")
+    L = oba.Layout(d, n, w.wseg, w.sseg)
+    S = oba.State(L, w.g_dtype)
+    gen = synth.device_generator(w.seed + 800)
+    zero_idx = synth.device_zero_mask(gen, d)
+    S.x.normal_(0.0, 0.02, generator=gen)
+    S.m.normal_(0.0, 1e-3, generator=gen)
+    S.denom.uniform_(1e-3, 2e-3, generator=gen)
+    S.start_state16(kind)
+    gs = [S.g, t.empty_like(S.g)]
+    for g in gs:
+        synth.device_grads(gen, w, g, zero_idx)
+    del zero_idx
+    t.cuda.synchronize()
+
+    def hcopy(x):
+        return np.ascontiguousarray(x.detach().cpu().numpy())
+
+    st = dict(x=hcopy(S.x), m=hcopy(S.m), denom=hcopy(S.denom), eps=np.zeros(d, np.float32))
+    c16 = np.zeros((n, L.ld), np.uint16)
+    wsp = np.zeros((n, 1), np.float32)
+    carry = np.zeros(d, bool)
+    for step, g in enumerate(gs):
+        S.step_deferred16(B1, LR, g=g)
+        t.cuda.synchronize()
+        gh = g.detach().cpu().numpy()
+
+        def worker(i):
+            return oracle.compress_deferred16(gh[i:i + 1], st["m"], c16[i:i + 1], kind,
+                                              wsp[i:i + 1], w.wseg, B1)
+
+        say(f"  step {step + 1}: oracle worker pass")
+        with ThreadPoolExecutor(4) as ex:
+            res = list(ex.map(worker, range(n)))
+        del gh
+        wb = np.concatenate([r[0] for r in res])
+        ws = np.concatenate([r[1] for r in res])
+        wsp = ws
+        say(f"  step {step + 1}: oracle server pass and update")
+        a = oracle.server_average(wb, ws, w.wseg, st["eps"])
+        sb, ss = oracle.server_reduce_recompress(wb, ws, w.wseg, w.sseg, st["eps"])
+        oracle.decompress_update(sb, ss, w.sseg, st["denom"], st["m"], st["x"], LR)
+        assert_close(to_host(S.wscale), ws, f"worker scales, step {step + 1}")
+        assert_close(to_host(S.sscale), ss, f"server scales, step {step + 1}")
+        exempt = carry.copy()
+        gw = to_host(S.wbits, np.uint64)
+        got16 = host16(S.c16)
+        flips = 0
+        for i in range(n):
+            ks = np.nonzero(np.unpackbits((gw[i] ^ wb[i]).view(np.uint8), bitorder="little"))[0]
+            ks = ks[ks < d]
+            if ks.size:
+                cv = np.abs(oracle.decode16(c16[i, ks], kind).astype(np.float64))
+                bad = ks[~((cv < 1e-6 * float(ws[i, 0])) | carry[ks])]
+                assert bad.size == 0, f"worker {i}: sign differs at {bad[:4]} where |c| >= 1e-6 s"
+                exempt[ks] = True
+                flips += ks.size
+            diff = np.nonzero((got16[i, :d] != c16[i, :d]) & ~exempt)[0]
+            assert diff.size <= 1e-3 * d, f"c16 of worker {i}: {diff.size} elements differ"
+            assert_close(oracle.decode16(got16[i, diff], kind), oracle.decode16(c16[i, diff], kind),
+                         f"c16 of worker {i}", rtol=ULP_REL[kind])
+        del got16
+        ks = np.nonzero(np.unpackbits((to_host(S.sbits, np.uint64) ^ sb).view(np.uint8),
+                                      bitorder="little"))[0]
+        ks = ks[ks < d]
+        if ks.size:
+            s_k = ss[np.searchsorted(w.sseg, ks, side="right") - 1].astype(np.float64)
+            near = np.abs(a[ks].astype(np.float64)) < 1e-6 * s_k
+            bad = ks[~(near | exempt[ks])]
+            assert bad.size == 0, f"server sign differs at {bad[:4]} where |a| >= 1e-6 s_bar"
+            exempt[ks] = True
+        keep = ~exempt
+        eps = t.empty_like(S.eps)
+        oba.deferred_errors(L, None, None, S.eps, S.sscale, None, eps)
+        for nm, got in (("eps", eps), ("m", S.momentum()), ("x", S.x)):
+            assert_close(to_host(got)[keep], st[nm][keep], f"{nm}, step {step + 1}")
+        del eps
+        S.m_implicit = True
+        carry = exempt
+        say(f"  step {step + 1} matches: {flips} worker and {ks.size} server signs differ at "
+            f"near-zero values, {int(exempt.sum())} coordinates exempt")
+    del gs, S
+    L.close()
+    t.cuda.empty_cache()
