@@ -54,6 +54,8 @@ SIGNATURES = {
     "oba_adam_warmup_step_listed": (_I, [_P, _P, _P, _P, _D, _D, _D, _D, _D, _D, _P, _P, _SZ,
                                          _P]),
     "oba_compress_deferred_listed": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _D, _P, _SZ, _P]),
+    "oba_compress_deferred16_listed": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _D, _P, _SZ,
+                                            _P]),
     "oba_decompress_update_listed": (_I, [_P, _P, _P, _P, _P, _P, _D, _P]),
     "oba_step_small": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _D, _D, _P]),
     "oba_timing_enable": (_I, [_I, _I32]),
@@ -452,6 +454,28 @@ def compress_deferred_listed(L: Layout, TLs: TensorList, m, c, wbits, wscale, be
         _ptr(wscale, "wscale", f32, (L.n, L.n_wseg)), beta1,
         ctypes.c_void_p(L.ws.data_ptr()), L.ws_bytes, _stream(stream))
     _check(rc, "oba_compress_deferred_listed")
+
+
+def compress_deferred16_listed(L: Layout, TLs: TensorList, m, c16, wbits, wscale, beta1,
+                               sbits_prev=None, sscale_prev=None, stream=None):
+    """compress_deferred16 on the listed gradients (c16 [n][ld] float16 or
+    bfloat16, flat)."""
+    import torch
+
+    f32 = (torch.float32,)
+    P = ctypes.c_void_p
+    mp = _ptr(m, "m", f32, (L.d,)) if m is not None else P(None)
+    bp = (_ptr(sbits_prev, "sbits_prev", (torch.int64,), (L.W,)) if sbits_prev is not None
+          else P(None))
+    sp = (_ptr(sscale_prev, "sscale_prev", f32, (L.n_sseg,)) if sscale_prev is not None
+          else P(None))
+    rc = lib().oba_compress_deferred16_listed(
+        L.handle, TLs.handle, mp, bp, sp,
+        _ptr(c16, "c16", (torch.float16, torch.bfloat16), (L.n, L.ld)), _gdtype(c16),
+        _ptr(wbits, "wbits", (torch.int64,), (L.n, L.W)),
+        _ptr(wscale, "wscale", f32, (L.n, L.n_wseg)), beta1,
+        ctypes.c_void_p(L.ws.data_ptr()), L.ws_bytes, _stream(stream))
+    _check(rc, "oba_compress_deferred16_listed")
 
 
 def decompress_update_listed(L: Layout, TLs: TensorList, sbits, sscale, denom, m, lr,

@@ -743,6 +743,45 @@ int oba_compress_deferred_listed(oba_layout L, oba_tensors H, const float* m,
                 [&] { oba::launch_finalize(part, G.n, L->sig_c, wscale, stream); });
 }
 
+int oba_compress_deferred16_listed(oba_layout L, oba_tensors H, const float* m,
+                                   const uint64_t* sbits_prev, const float* sscale_prev, void* c,
+                                   int c_dtype, uint64_t* wbits, float* wscale, double beta1,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  OBA_TRY(check_layout(L));
+  if (!H || H->device != L->device || H->n != L->plan.n) return OBA_EINVAL;
+  if (c_dtype != OBA_F16 && c_dtype != OBA_BF16) return OBA_EINVAL;
+  if (!beta_ok(beta1)) return OBA_EINVAL;
+  const bool implicit_m = !m;
+  if (implicit_m != (sbits_prev != nullptr) || implicit_m != (sscale_prev != nullptr))
+    return OBA_EINVAL;
+  if (implicit_m) {
+    OBA_TRY(check_buf(sbits_prev, 8));
+    OBA_TRY(check_buf(sscale_prev, 4));
+  } else {
+    OBA_TRY(check_buf(m, 16));
+  }
+  OBA_TRY(check_buf(c, 8));
+  OBA_TRY(check_buf(wbits, 8));
+  OBA_TRY(check_buf(wscale, 4));
+  OBA_TRY(check_buf(ws, 8));
+  if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
+  // the grid of oba_compress_deferred16, with its block table of the tensors
+  const bool sg = OBA_S16_GRID != 0;
+  const oba::Geo G = sg ? L->geo : L->geo_c;
+  const oba::SegDev& sig = sg ? L->sig : L->sig_c;
+  double* part = static_cast<double*>(ws);
+  const float b1 = (float)beta1, omb1 = (float)(1.0 - beta1);
+  uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
+  const oba::MomSrc ms{reinterpret_cast<const uint8_t*>(sbits_prev), sscale_prev,
+                       sg ? L->tau : L->tau_c};
+  OBA_TRY(launch("compress_deferred16", stream, [&] {
+    oba::launch_compress_deferred16_listed(G, sg ? H->tl_s : H->tl_c, H->g_dtype, m, c, c_dtype,
+                                           wbytes, sig, part, wscale, b1, omb1, ms, stream);
+  }));
+  return launch("finalize_scales", stream,
+                [&] { oba::launch_finalize(part, G.n, sig, wscale, stream); });
+}
+
 int oba_decompress_update_listed(oba_layout L, oba_tensors H, const uint64_t* sbits,
                                  const float* sscale, const float* denom, float* m, double lr,
                                  hipStream_t stream) {

@@ -393,6 +393,27 @@ void launch_compress_deferred16(const Geo& G, const void* g, int gdt, const floa
   }
 }
 
+void launch_compress_deferred16_listed(const Geo& G, const TList& tl, int gdt, const float* m,
+                                       void* c, int cdt, uint8_t* wbytes, const SegDev& sig,
+                                       double* part, const float* wscale_prev, float b1,
+                                       float omb1, const MomSrc& ms, hipStream_t st) {
+  if (cdt == kGradBF16) {
+    if (ms.sbytes)
+      launch_cmp_t<kDeferredM, true, bf16_bits>(G, nullptr, gdt, nullptr, c, wbytes, sig, part,
+                                                wscale_prev, b1, omb1, ms, st, tl);
+    else
+      launch_cmp_t<kDeferred, true, bf16_bits>(G, nullptr, gdt, m, c, wbytes, sig, part,
+                                               wscale_prev, b1, omb1, ms, st, tl);
+  } else {
+    if (ms.sbytes)
+      launch_cmp_t<kDeferredM, true, uint16_t>(G, nullptr, gdt, nullptr, c, wbytes, sig, part,
+                                               wscale_prev, b1, omb1, ms, st, tl);
+    else
+      launch_cmp_t<kDeferred, true, uint16_t>(G, nullptr, gdt, m, c, wbytes, sig, part,
+                                              wscale_prev, b1, omb1, ms, st, tl);
+  }
+}
+
 void launch_compress_deferred_listed(const Geo& G, const TList& tl, int gdt, const float* m,
                                      float* c, uint8_t* wbytes, const SegDev& sig, double* part,
                                      const float* wscale_prev, float b1, float omb1,

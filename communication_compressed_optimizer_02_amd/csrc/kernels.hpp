@@ -141,6 +141,10 @@ void launch_compress_deferred16(const Geo& G, const void* g, int gdt, const floa
                                 int cdt, uint8_t* wbytes, const SegDev& sig, double* part,
                                 const float* wscale_prev, float b1, float omb1, const MomSrc& ms,
                                 hipStream_t st);
+void launch_compress_deferred16_listed(const Geo& G, const TList& tl, int gdt, const float* m,
+                                       void* c, int cdt, uint8_t* wbytes, const SegDev& sig,
+                                       double* part, const float* wscale_prev, float b1,
+                                       float omb1, const MomSrc& ms, hipStream_t st);
 void launch_server_deferred(const Geo& G, const uint8_t* wbytes, const float* wscale, float* a,
                             uint8_t* sbytes, const SegDev& sig, const SegDev& tau, double* part,
                             const float* sscale_prev, hipStream_t st);

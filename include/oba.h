@@ -333,6 +333,13 @@ int oba_adam_warmup_step_listed(oba_layout layout, oba_tensors tensors, float* m
                                 double bc2, double* vnorm, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
 
+/* oba_compress_deferred16 on the listed gradients: c (16-bit, c_dtype) and
+ * everything else as there. */
+int oba_compress_deferred16_listed(oba_layout layout, oba_tensors tensors, const float* m,
+                                   const uint64_t* sbits_prev, const float* sscale_prev, void* c,
+                                   int c_dtype, uint64_t* wbits, float* wscale, double beta1,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* oba_compress_deferred on the listed gradients (same momentum sources). */
 int oba_compress_deferred_listed(oba_layout layout, oba_tensors tensors, const float* m,
                                  const uint64_t* sbits_prev, const float* sscale_prev, float* c,

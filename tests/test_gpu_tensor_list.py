@@ -108,6 +108,60 @@ def test_listed_path_is_bitwise_the_flat_path(lengths, n, gdt):
     L.close()
 
 
+@pytest.mark.parametrize("lengths,n,gdt,kind", [
+    ([8, 4, 2048, 2052, 1600, 12], 3, "f16", "f16"),
+    ([1600] * 7 + [4800, 12, 100_000, 4], 8, "f32", "bf16"),
+    ("random", 5, "bf16", "bf16"),
+])
+def test_listed_state16_is_bitwise_the_flat_state16(lengths, n, gdt, kind):
+    """The 16-bit-state worker pass on listed gradients equals the flat one
+    bit for bit (stored c~, messages, scales, x), from a drawn state, over
+    four steps (the first reads m, the rest rebuild it)."""
+    t = torch()
+    rng = np.random.default_rng(31)
+    if lengths == "random":
+        lengths = [4 * int(k) for k in rng.integers(1, 40_000, size=57)]
+    d = sum(lengths)
+    say(f"[tensor list, 16-bit state] T={len(lengths)} d={d} n={n} g={gdt} c={kind}")
+    L = oba.Layout(d, n, synth.whole(d), cut_table(rng, d, 3))
+    gen = synth.device_generator(d + 5)
+    F = oba.State(L, gdt)
+    F.x.normal_(0.0, 0.02, generator=gen)
+    F.m.normal_(0.0, 1e-3, generator=gen)
+    F.denom.uniform_(1e-3, 2e-3, generator=gen)
+    m0 = F.m.clone()
+    F.start_state16(kind)
+    xs = split(F.x, lengths)
+    gs = [[t.empty(k, dtype=F.g.dtype, device="cuda") for k in lengths] for _ in range(n)]
+    TL = oba.TensorList(L, xs, gs)
+    c16 = t.zeros_like(F.c16)
+    M = {nm: t.zeros_like(getattr(F, nm)) for nm in ("eps", "wbits", "wscale", "sbits",
+                                                      "sscale")}
+    for step in range(4):
+        F.g[:, :d].normal_(0.0, 1e-3, generator=gen)
+        for i in range(n):
+            at = 0
+            for k, g in zip(lengths, gs[i]):
+                g.copy_(F.g[i, at:at + k])
+                at += k
+        F.step_deferred16(B1, LR)
+        if step == 0:
+            oba.compress_deferred16_listed(L, TL, m0, c16, M["wbits"], M["wscale"], B1)
+        else:
+            oba.compress_deferred16_listed(L, TL, None, c16, M["wbits"], M["wscale"], B1,
+                                           M["sbits"], M["sscale"])
+        oba.server_reduce_recompress_deferred(L, M["wbits"], M["wscale"], M["eps"], M["sbits"],
+                                              M["sscale"])
+        oba.decompress_update_listed(L, TL, M["sbits"], M["sscale"], F.denom, None, LR)
+        t.cuda.synchronize()
+        for nm in ("wbits", "wscale", "sbits", "sscale", "eps"):
+            same(getattr(F, nm), M[nm], f"{nm}, step {step}")
+        same(F.c16.view(t.int16), c16.view(t.int16), f"c16, step {step}")
+        same(F.x, t.cat(xs), f"x, step {step}")
+    TL.close()
+    L.close()
+
+
 def test_listed_path_rejects_bad_tensors():
     t = torch()
     L = oba.Layout(16, 2, synth.whole(16), synth.even_shards(16, 2))
