@@ -63,14 +63,16 @@ class Problem:
 
 def run(d, n, steps, warmup, seed=4, every=10, lr=synth.LR, beta1=synth.BETA1,
         beta2=synth.BETA2, eta=synth.ETA, compressed=True, bias_correction=False, log=None,
-        auto_freeze=None, info=None, local_momentum=False):
+        auto_freeze=None, info=None, local_momentum=False, state16=None):
     """Returns (losses {step: f}, optimizer ms per step, gradient ms per step).
     bias_correction: Kingma-Ba factors 1-b^t in the warm-up (and in the
     frozen variance); off = the bare recurrences.  auto_freeze = (window,
     rtol): the warm-up ends when the variance norm ||v/bc2|| levels off
     (library plateau test), at most at step `warmup`; info["freeze_step"]
     receives the last warm-up step.  local_momentum: every worker keeps its
-    own momentum in the compression stage (the broadcast only moves x)."""
+    own momentum in the compression stage (the broadcast only moves x).
+    state16 ("f16" or "bf16"): the workers' compensated momenta are held in
+    that 16-bit format in the compression stage."""
     import torch
 
     P = Problem(d, n, seed)
@@ -99,9 +101,13 @@ def run(d, n, steps, warmup, seed=4, every=10, lr=synth.LR, beta1=synth.BETA1,
                 S.freeze(eta, bc2)
                 if local_momentum:
                     S.start_local_momentum()
+                if state16:
+                    S.start_state16(state16)
                 frozen_at = t
         elif local_momentum:
             S.step_local(beta1, lr)
+        elif state16:
+            S.step_deferred16(beta1, lr)
         else:
             S.step_deferred(beta1, lr)
         e[2].record()
@@ -127,6 +133,8 @@ def main():
     ap.add_argument("--seed", type=int, default=4)
     ap.add_argument("--local-momentum", action="store_true",
                     help="per-worker momentum in the compression stage")
+    ap.add_argument("--state16", choices=["f16", "bf16"],
+                    help="hold the workers' compensated momenta in this 16-bit format")
     ap.add_argument("--auto-freeze", nargs=2, type=float, metavar=("WINDOW", "RTOL"),
                     help="end the warm-up when the variance norm levels off (at most at "
                          "--warmup), instead of at --warmup")
@@ -139,7 +147,8 @@ def main():
 
     marks = [m for m in (args.warmup, 500, 1000, args.steps) if 0 < m <= args.steps]
     out = {"workload": "quadratic", "d": args.d, "n_workers": args.n, "steps": args.steps,
-           "warmup": args.warmup, "momentum": "per-worker" if args.local_momentum else "shared"}
+           "warmup": args.warmup, "momentum": "per-worker" if args.local_momentum else "shared",
+           "worker_state": args.state16 or "f32"}
     t0 = time.time()
     for name, bc in (("bare", False), ("bias_corrected", True)):
         log(f"[quadratic] {name} warm-up: 1-bit Adam, d={args.d} n={args.n} "
@@ -147,7 +156,7 @@ def main():
         info = {}
         f1, opt1, gr1 = run(args.d, args.n, args.steps, args.warmup, args.seed,
                             bias_correction=bc, log=log, auto_freeze=auto, info=info,
-                            local_momentum=local)
+                            local_momentum=local, state16=args.state16)
         log(f"[quadratic] {name} warm-up: Adam baseline ({time.time() - t0:.0f} s)")
         fa, opta, _ = run(args.d, args.n, args.steps, args.warmup, args.seed, compressed=False,
                           bias_correction=bc, log=log)
