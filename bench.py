@@ -438,7 +438,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the n data-parallel workers are simulated as n "
-              "buffers on that GPU; runs over several GPUs are not part of this build.",
+              "buffers on that GPU; a run over several GPUs is not implemented.",
               file=sys.stderr)
         sys.exit(2)
 

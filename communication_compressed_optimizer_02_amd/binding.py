@@ -593,6 +593,7 @@ class State:
 
     def step(self, beta1, lr, g=None):
         """One compression step: compress -> server -> decompress+update."""
+        self._rows32()
         self._explicit_m()
         compress(self.L, self.g if g is None else g, self.m, self.delta, self.wbits, self.wscale,
                  beta1)
@@ -613,6 +614,7 @@ class State:
     def step_local(self, beta1, lr, g=None):
         """A compression step with per-worker momentum (deferred layout): the
         broadcast m_hat moves x; each worker keeps its own m_i."""
+        self._rows32()
         compress_deferred_local(self.L, self.g if g is None else g, self.m_local, self.delta,
                                 self.wbits, self.wscale, beta1)
         server_reduce_recompress_deferred(self.L, self.wbits, self.wscale, self.eps, self.sbits,
@@ -621,6 +623,7 @@ class State:
 
     def step_small(self, beta1, lr, g=None, implicit_m=True):
         """step_deferred in one launch (layouts of at most 65536 coordinates)."""
+        self._rows32()
         step_small(self.L, self.g if g is None else g, None if self.m_implicit else self.m,
                    self.delta, self.wbits, self.wscale, self.eps, self.sbits, self.sscale,
                    self.denom, None if implicit_m else self.m, self.x, beta1, lr)
@@ -651,11 +654,17 @@ class State:
         decompress_update(self.L, self.sbits, self.sscale, self.denom, None, self.x, lr)
         self.m_implicit = True
 
+    def _rows32(self):
+        if self.delta is None:
+            raise RuntimeError("the binary32 worker rows were released by start_state16(); "
+                               "use step_deferred16() or a new State")
+
     def step_deferred(self, beta1, lr, g=None, implicit_m=True):
         """The same step in the deferred-residual layout: `delta` holds the
         last c and `eps` the last a (see oba_compress_deferred).  With
         implicit_m the update does not store m and the next step rebuilds it
         from the server message; momentum() writes it out."""
+        self._rows32()
         g = self.g if g is None else g
         if self.m_implicit:
             compress_deferred(self.L, g, None, self.delta, self.wbits, self.wscale, beta1,
