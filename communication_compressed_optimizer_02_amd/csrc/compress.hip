@@ -148,6 +148,10 @@ __device__ __forceinline__ void compress_body(Geo G, int32_t i0, const GT* __res
     // workers in batches of NBB: all loads of a batch, then its arithmetic
     // and stores (NBB < NB trades loads in flight per wave for occupancy)
     constexpr int kBatch = __is_same(CT, float) ? kWorkerBatch : kWorkerBatch16;
+    // buffer-resource loads and stores in the deferred passes (the explicit
+    // passes keep the plain form: their read-only norm pass ran 1.6x slower
+    // through buffers)
+    constexpr bool kBuf = OBA_BUF != 0 && MODE >= kDeferred;
     constexpr int NBB = NB < kBatch ? NB : kBatch;
 #pragma unroll
     for (int ib = 0; ib < NB; ib += NBB) {
@@ -162,9 +166,14 @@ __device__ __forceinline__ void compress_body(Geo G, int32_t i0, const GT* __res
           const int64_t row = (int64_t)(i0 + ib + u) * G.ld;
           if constexpr (TL)
             load_listed<GT>(tl, i0 + ib + u, lt, full, gv[u]);
+          else if constexpr (kBuf)
+            load_full_buf(g + row, lo, gv[u]);
           else
             load_full(g + row, q, gv[u]);
-          load_full(delta + row, q, c[u]);
+          if constexpr (kBuf)
+            load_full_buf(delta + row, lo, c[u]);
+          else
+            load_full(delta + row, q, c[u]);
           if (MODE == kDeferredLocal) load_full(m + row, q, ml[u]);
         }
       } else {
@@ -220,7 +229,12 @@ __device__ __forceinline__ void compress_body(Geo G, int32_t i0, const GT* __res
           round_to_row<CT>(c[u], h16[u]);  // a 16-bit state: c as the row holds it
         }
         if (MODE != kNorm) store_sign_bits(wbytes + (int64_t)(i0 + i) * rowbytes, q, sign_bits(c[u]), rowbytes);
-        if (MODE >= kDeferred) store_row(delta + row, q, G.d, full, c[u], h16[u]);
+        if (MODE >= kDeferred) {
+          if (kBuf && full)
+            store_full_buf(delta + row, lo, c[u], h16[u]);
+          else
+            store_row(delta + row, q, G.d, full, c[u], h16[u]);
+        }
         fs[i] = (MODE != kApply) ? sumsq8(c[u]) : 0.0;
         if (MODE == kApply) {
 #pragma unroll

@@ -379,6 +379,94 @@ __device__ __forceinline__ void store_row(T16* __restrict__ p, const Quads& q, i
   }
 }
 
+// ---- full spans through buffer resources ------------------------------------
+// OBA_BUF: a full span of one row is read or written through a buffer
+// resource whose base is the span's first element (block-uniform, scalar
+// registers) and whose size is the span's bytes; each lane adds a 32-bit
+// byte offset, so no 64-bit address is formed per lane and one offset
+// register serves every row of the same element size.  An access past the
+// span's bytes would read 0 and write nothing (the hardware's range check).
+#ifndef OBA_BUF
+#define OBA_BUF 1
+#endif
+// the same for the update and the warm-up step
+#ifndef OBA_BUF_MISC
+#define OBA_BUF_MISC 0
+#endif
+
+constexpr int kBufRsrcWord3 = 0x00020000;  // raw (untyped) buffer, gfx9 family
+constexpr int kBufLoadAux = OBA_NT_LOADS ? 2 : 0;   // nt
+constexpr int kBufStoreAux = OBA_NT_STORES ? 2 : 0;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const T* row, int64_t lo) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(row + lo), (short)0,
+                                           (int)(kSpan * sizeof(T)), kBufRsrcWord3);
+}
+
+__device__ __forceinline__ void load_full_buf(const float* row, int64_t lo, float (&v)[8]) {
+  const __amdgpu_buffer_rsrc_t r = span_rsrc(row, lo);
+  const f32x4 a = __builtin_bit_cast(
+      f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16u * threadIdx.x, 0, kBufLoadAux));
+  const f32x4 b = __builtin_bit_cast(
+      f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16u * (kBlock + threadIdx.x), 0, kBufLoadAux));
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <typename T16>
+__device__ __forceinline__ void load_full_buf(const T16* row, int64_t lo, float (&v)[8]) {
+  const __amdgpu_buffer_rsrc_t r = span_rsrc(row, lo);
+  const u32x2 a = __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, 8u * threadIdx.x, 0, kBufLoadAux));
+  const u32x2 b = __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, 8u * (kBlock + threadIdx.x), 0, kBufLoadAux));
+  const T16* tag = nullptr;
+  v[0] = lo16(tag, a.x); v[1] = hi16(tag, a.x); v[2] = lo16(tag, a.y); v[3] = hi16(tag, a.y);
+  v[4] = lo16(tag, b.x); v[5] = hi16(tag, b.x); v[6] = lo16(tag, b.y); v[7] = hi16(tag, b.y);
+}
+
+__device__ __forceinline__ void store_full_buf(float* row, int64_t lo, const float (&v)[8],
+                                               const uint32_t (&)[4]) {
+  const __amdgpu_buffer_rsrc_t r = span_rsrc(row, lo);
+  __builtin_amdgcn_raw_buffer_store_b128(
+      __builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]}), r, 16u * threadIdx.x, 0,
+      kBufStoreAux);
+  __builtin_amdgcn_raw_buffer_store_b128(
+      __builtin_bit_cast(u32x4, f32x4{v[4], v[5], v[6], v[7]}), r, 16u * (kBlock + threadIdx.x), 0,
+      kBufStoreAux);
+}
+
+template <typename T16>
+__device__ __forceinline__ void store_full_buf(T16* row, int64_t lo, const float (&)[8],
+                                               const uint32_t (&h)[4]) {
+  const __amdgpu_buffer_rsrc_t r = span_rsrc(row, lo);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{h[0], h[1]}, r, 8u * threadIdx.x, 0, kBufStoreAux);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{h[2], h[3]}, r, 8u * (kBlock + threadIdx.x), 0,
+                                        kBufStoreAux);
+}
+
+// Full span: buffer form; otherwise the checked loads of load8.
+template <bool BUF, typename T>
+__device__ __forceinline__ void load8b(const T* __restrict__ p, const Quads& q, int64_t lo,
+                                       int64_t d, bool full, float (&v)[8]) {
+  if (BUF && full)
+    load_full_buf(p, lo, v);
+  else
+    load8(p, q, d, full, v);
+}
+
+template <bool BUF>
+__device__ __forceinline__ void store8b(float* __restrict__ p, const Quads& q, int64_t lo,
+                                        int64_t d, bool full, const float (&v)[8]) {
+  if (BUF && full) {
+    const uint32_t none[4] = {0, 0, 0, 0};
+    store_full_buf(p, lo, v, none);
+  } else {
+    store8(p, q, d, full, v);
+  }
+}
 // c = (b1*m + (1-b1)*g) + delta: two products, then two adds (no contraction)
 __device__ __forceinline__ float compensate(float b1, float omb1, float m, float g, float dl) {
   const float p = b1 * m + omb1 * g;

@@ -41,11 +41,11 @@ __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
       lt = lane_tensors(tl, tcur, q, min(lo + kSpan, G.d), G.d);
     }
     if (UPDATE_X) {
-      load8(denom, q, G.d, full, dv);
+      load8b<OBA_BUF_MISC != 0>(denom, q, lo, G.d, full, dv);
       if constexpr (TL)
         load_listed_x(tl, lt, full, xv);
       else
-        load8(x, q, G.d, full, xv);
+        load8b<OBA_BUF_MISC != 0>(x, q, lo, G.d, full, xv);
     }
     if (hi <= p_hi) {
       const float s_ = sscale[tau.pseg[p]];
@@ -62,12 +62,12 @@ __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
       mh[j] = ((bits >> j) & 1u) ? -sv[j] : sv[j];
       if (UPDATE_X) xv[j] = xv[j] - (lr * mh[j]) / dv[j];
     }
-    if (WRITE_M) store8(m, q, G.d, full, mh);
+    if (WRITE_M) store8b<OBA_BUF_MISC != 0>(m, q, lo, G.d, full, mh);
     if (UPDATE_X) {
       if constexpr (TL)
         store_listed_x(tl, lt, full, xv);
       else
-        store8(x, q, G.d, full, xv);
+        store8b<OBA_BUF_MISC != 0>(x, q, lo, G.d, full, xv);
     }
     while (p < p_end && p_hi <= hi) {
       if (++p < p_end) p_hi = tau.phi[p];

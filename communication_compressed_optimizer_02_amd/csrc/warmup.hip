@@ -39,12 +39,13 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
       tcur_advance(tl, tcur, lo);
       lt = lane_tensors(tl, tcur, q, min(lo + kSpan, G.d), G.d);
     }
-    load8(m, q, G.d, full, mv);
-    load8(v, q, G.d, full, vv);
+    constexpr bool BUF = OBA_BUF_MISC != 0;
+    load8b<BUF>(m, q, lo, G.d, full, mv);
+    load8b<BUF>(v, q, lo, G.d, full, vv);
     if constexpr (TL)
       load_listed_x(tl, lt, full, xv);
     else
-      load8(x, q, G.d, full, xv);
+      load8b<BUF>(x, q, lo, G.d, full, xv);
 #pragma unroll
     for (int j = 0; j < 8; ++j) sum[j] = 0.0f;
     for (int32_t i0 = 0; i0 < G.n; i0 += NB) {  // one pass when n <= NB
@@ -55,7 +56,7 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
         if constexpr (TL)
           load_listed<GT>(tl, min(i0 + u, G.n - 1), lt, full, gv[u]);
         else
-          load8(g + (int64_t)min(i0 + u, G.n - 1) * G.ld, q, G.d, full, gv[u]);
+          load8b<BUF>(g + (int64_t)min(i0 + u, G.n - 1) * G.ld, q, lo, G.d, full, gv[u]);
       }
 #pragma unroll
       for (int u = 0; u < NB; ++u)
@@ -73,12 +74,12 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
       vv[j] = vk;
       xv[j] = xv[j] - (C.lr * (mk / C.bc1)) / (__builtin_sqrtf(vk / C.bc2) + C.eta);
     }
-    store8(m, q, G.d, full, mv);
-    store8(v, q, G.d, full, vv);
+    store8b<BUF>(m, q, lo, G.d, full, mv);
+    store8b<BUF>(v, q, lo, G.d, full, vv);
     if constexpr (TL)
       store_listed_x(tl, lt, full, xv);
     else
-      store8(x, q, G.d, full, xv);
+      store8b<BUF>(x, q, lo, G.d, full, xv);
     if (NORM) acc[0] += sumsq8(vv);  // coordinates past d read 0 and give v = 0
   }
   if (NORM) flush_rows<1>(acc, 1, part + blockIdx.x, 0, lds);
