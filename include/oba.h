@@ -26,7 +26,8 @@
  * Memory: every pointer named in a call is DEVICE memory of the current HIP
  *   device, except the segment tables of oba_layout_create/validate, which
  *   are HOST arrays copied by the call.  float/half buffers must be 16-byte
- *   aligned, packed words 8-byte aligned, scales 4-byte aligned.
+ *   aligned (the 16-bit state rows of oba_compress_deferred16: 8-byte),
+ *   packed words 8-byte aligned, scales 4-byte aligned.
  * Packed signs: bit j of word w is coordinate 64*w+j (least significant bit
  *   first); bit 1 = negative, bit 0 = non-negative (sign(0) = +1, also for
  *   -0.0); bits past d in the last word are written as 0.
@@ -75,7 +76,9 @@ enum {
 };
 
 /* gradient dtype: binary32, binary16, or bfloat16 (the upper half of a
- * binary32; decoded exactly).  All state and arithmetic stay binary32. */
+ * binary32; decoded exactly).  All arithmetic is binary32 and so is all
+ * state, except the workers' compensated vectors of the 16-bit-state pass
+ * (oba_compress_deferred16), whose format is OBA_F16 or OBA_BF16. */
 enum { OBA_F32 = 0, OBA_F16 = 1, OBA_BF16 = 2 };
 
 typedef struct oba_layout_s* oba_layout;
