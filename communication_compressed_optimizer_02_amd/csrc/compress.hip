@@ -322,9 +322,16 @@ static void launch_cmp(const Geo& G, int32_t i0, int groups, const void* g, cons
 #ifndef OBA_IMPLICIT_NB
 #define OBA_IMPLICIT_NB 4
 #endif
+// workers per block of the 16-bit-state pass (its rows carry fewer bytes per
+// worker, so a block can hold more workers' loads), a tuning knob
+#ifndef OBA_IMPLICIT_NB16
+#define OBA_IMPLICIT_NB16 4
+#endif
 constexpr int kMaxNB = OBA_MAX_NB;
+constexpr int kImplicitNB16 = OBA_IMPLICIT_NB16;
 constexpr int kImplicitNB = OBA_IMPLICIT_NB;
-static_assert(kMaxNB >= 1 && kMaxNB <= 8 && kImplicitNB >= 1 && kImplicitNB <= 8,
+static_assert(kMaxNB >= 1 && kMaxNB <= 8 && kImplicitNB >= 1 && kImplicitNB <= 8 &&
+                  kImplicitNB16 >= 1 && kImplicitNB16 <= 8,
               "worker groups hold 1 to 8 workers");
 
 template <typename GT, typename CT, int MODE, bool TL>
@@ -332,7 +339,9 @@ static void launch_cmp_n(const Geo& G, const void* g, const float* m, void* delt
                          uint8_t* wbytes, const SegDev& sig, double* part, const float* wscale,
                          float b1, float omb1, const MomSrc& ms, const TList& tl,
                          hipStream_t st) {
-  constexpr int GROUP = (MODE == kDeferredM || MODE == kDeferredLocal) ? kImplicitNB : kMaxNB;
+  constexpr int GROUP = !__is_same(CT, float)                       ? kImplicitNB16
+                        : (MODE == kDeferredM || MODE == kDeferredLocal) ? kImplicitNB
+                                                                         : kMaxNB;
   const int full = G.n / GROUP, rem = G.n % GROUP, i0 = full * GROUP;
 #define OBA_CMP(NB_, I0, GROUPS) \
   launch_cmp<GT, CT, NB_, MODE, TL>(G, I0, GROUPS, g, m, delta, wbytes, sig, part, wscale, b1, omb1, \
