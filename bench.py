@@ -568,6 +568,8 @@ def main():
     out["one_gpu_share"] = one_gpu_share(w, torch, oba, synth, args.steps, args.warmup)
     torch.cuda.empty_cache()
     out["copy_reference"] = copy_reference(torch)
+    # the dominant kernel against what a plain device copy reaches on this machine
+    out["roofline"]["frac_of_copy"] = round(achieved / out["copy_reference"]["GBps"], 4)
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(w, torch, synth, min(args.cpu_sample, w.d))
