@@ -425,8 +425,16 @@ class TensorList:
             pass
 
 
+def _same_layout(L: Layout, TLs: TensorList):
+    """A tensor list's device tables belong to the layout it was made with
+    (the library refuses any other with OBA_EINVAL as well)."""
+    if TLs.L is not L:
+        raise ValueError("the tensor list was made for another layout")
+
+
 def adam_warmup_step_listed(L: Layout, TLs: TensorList, m, v, lr, beta1, beta2, eta, bc1=1.0,
                             bc2=1.0, vnorm=None, stream=None):
+    _same_layout(L, TLs)
     import torch
 
     f32 = (torch.float32,)
@@ -439,6 +447,7 @@ def adam_warmup_step_listed(L: Layout, TLs: TensorList, m, v, lr, beta1, beta2, 
 
 def compress_deferred_listed(L: Layout, TLs: TensorList, m, c, wbits, wscale, beta1,
                              sbits_prev=None, sscale_prev=None, stream=None):
+    _same_layout(L, TLs)
     import torch
 
     f32 = (torch.float32,)
@@ -460,6 +469,7 @@ def compress_deferred16_listed(L: Layout, TLs: TensorList, m, c16, wbits, wscale
                                sbits_prev=None, sscale_prev=None, stream=None):
     """compress_deferred16 on the listed gradients (c16 [n][ld] float16 or
     bfloat16, flat)."""
+    _same_layout(L, TLs)
     import torch
 
     f32 = (torch.float32,)
@@ -480,6 +490,7 @@ def compress_deferred16_listed(L: Layout, TLs: TensorList, m, c16, wbits, wscale
 
 def decompress_update_listed(L: Layout, TLs: TensorList, sbits, sscale, denom, m, lr,
                              stream=None):
+    _same_layout(L, TLs)
     import torch
 
     f32 = (torch.float32,)

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 #include <new>
 #include <string>
@@ -29,6 +30,7 @@
 struct oba_layout_s {
   oba::Plan plan;
   int device = -1;
+  uint64_t serial = 0;  // unique per handle made by this process (never reused)
   void* dev_tables = nullptr;
   oba::SegDev sig_c{};  // worker segments, compress grid
   oba::SegDev sig{};    // worker segments, server grid
@@ -46,6 +48,10 @@ struct oba_tensors_s {
   int g_dtype = OBA_F32;
   int32_t T = 0;
   int32_t n = 0;
+  // the layout the block tables were built for: its serial, d and grids
+  uint64_t layout_serial = 0;
+  int64_t d = 0;
+  int32_t nblk_c = 0, nblk_w = 0, nblk = 0;
   void* dev = nullptr;  // one allocation holding every table below
   oba::TList tl_c{};    // block table of the compress grid
   oba::TList tl_w{};    // block table of the update grid
@@ -55,6 +61,7 @@ struct oba_tensors_s {
 namespace {
 
 thread_local char g_hip_msg[256] = "HIP error";
+std::atomic<uint64_t> g_layout_serial{0};
 
 int hip_fail(hipError_t e, const char* what) {
   std::snprintf(g_hip_msg, sizeof(g_hip_msg), "HIP error in %s: %s", what, hipGetErrorString(e));
@@ -130,6 +137,16 @@ int check_buf(const void* p, uintptr_t align) {
   return OBA_OK;
 }
 
+// A tensor-list handle is valid only with the layout it was built for: its
+// per-block tables index that layout's grids.
+int check_tensors(oba_layout L, oba_tensors H) {
+  if (!H || H->device != L->device || H->layout_serial != L->serial || H->n != L->plan.n ||
+      H->d != L->plan.d || H->nblk_c != L->plan.nblk_c || H->nblk_w != L->plan.nblk_w ||
+      H->nblk != L->plan.nblk)
+    return OBA_EINVAL;
+  return OBA_OK;
+}
+
 bool is_finite(double x) { return std::isfinite(x); }
 bool gdtype_ok(int t) { return t == OBA_F32 || t == OBA_F16 || t == OBA_BF16; }
 bool beta_ok(double b) { return is_finite(b) && b >= 0.0 && b < 1.0; }
@@ -175,6 +192,7 @@ int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const i
     return rc;
   }
   const oba::Plan& P = L->plan;
+  L->serial = ++g_layout_serial;
   hipError_t e = hipGetDevice(&L->device);
   if (e != hipSuccess) {
     delete L;
@@ -641,6 +659,11 @@ int oba_tensors_create(oba_tensors* out, oba_layout L, int32_t n_tensors,
   H->g_dtype = g_dtype;
   H->T = T;
   H->n = n;
+  H->layout_serial = L->serial;
+  H->d = P.d;
+  H->nblk_c = P.nblk_c;
+  H->nblk_w = P.nblk_w;
+  H->nblk = P.nblk;
   hipError_t e = hipMalloc(&H->dev, bytes);
   if (e != hipSuccess) {
     delete H;
@@ -688,7 +711,7 @@ int oba_adam_warmup_step_listed(oba_layout L, oba_tensors H, float* m, float* v,
                                 double beta1, double beta2, double eta, double bc1, double bc2,
                                 double* vnorm, void* ws, size_t ws_bytes, hipStream_t stream) {
   OBA_TRY(check_layout(L));
-  if (!H || H->device != L->device || H->n != L->plan.n) return OBA_EINVAL;
+  OBA_TRY(check_tensors(L, H));
   if (!is_finite(lr) || !beta_ok(beta1) || !beta_ok(beta2) || !is_finite(eta) || eta < 0.0 ||
       !is_finite(bc1) || bc1 <= 0.0 || !is_finite(bc2) || bc2 <= 0.0)
     return OBA_EINVAL;
@@ -714,7 +737,7 @@ int oba_compress_deferred_listed(oba_layout L, oba_tensors H, const float* m,
                                  uint64_t* wbits, float* wscale, double beta1, void* ws,
                                  size_t ws_bytes, hipStream_t stream) {
   OBA_TRY(check_layout(L));
-  if (!H || H->device != L->device || H->n != L->plan.n) return OBA_EINVAL;
+  OBA_TRY(check_tensors(L, H));
   if (!beta_ok(beta1)) return OBA_EINVAL;
   const bool implicit_m = !m;
   if (implicit_m != (sbits_prev != nullptr) || implicit_m != (sscale_prev != nullptr))
@@ -748,7 +771,7 @@ int oba_compress_deferred16_listed(oba_layout L, oba_tensors H, const float* m,
                                    int c_dtype, uint64_t* wbits, float* wscale, double beta1,
                                    void* ws, size_t ws_bytes, hipStream_t stream) {
   OBA_TRY(check_layout(L));
-  if (!H || H->device != L->device || H->n != L->plan.n) return OBA_EINVAL;
+  OBA_TRY(check_tensors(L, H));
   if (c_dtype != OBA_F16 && c_dtype != OBA_BF16) return OBA_EINVAL;
   if (!beta_ok(beta1)) return OBA_EINVAL;
   const bool implicit_m = !m;
@@ -786,7 +809,7 @@ int oba_decompress_update_listed(oba_layout L, oba_tensors H, const uint64_t* sb
                                  const float* sscale, const float* denom, float* m, double lr,
                                  hipStream_t stream) {
   OBA_TRY(check_layout(L));
-  if (!H || H->device != L->device || H->n != L->plan.n) return OBA_EINVAL;
+  OBA_TRY(check_tensors(L, H));
   if (!is_finite(lr)) return OBA_EINVAL;
   OBA_TRY(check_buf(sbits, 8));
   OBA_TRY(check_buf(sscale, 4));

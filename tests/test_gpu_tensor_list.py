@@ -3,6 +3,7 @@ parameters and the workers' gradients live in separate tensors; every other
 buffer stays flat.  The listed kernels perform the flat kernels' arithmetic
 on other addresses, so from the same inputs they must give bitwise the flat
 path's results."""
+import ctypes
 import sys
 
 import numpy as np
@@ -175,13 +176,39 @@ def test_listed_path_rejects_bad_tensors():
     with pytest.raises(oba.ObaError):
         oba.TensorList(L, [odd, x[1]], g)
     TL = oba.TensorList(L, x, g)
-    L2 = oba.Layout(16, 3, synth.whole(16), synth.even_shards(16, 3))
-    m = t.zeros(16, device="cuda")
-    with pytest.raises(oba.ObaError):  # handle made for another worker count
-        oba.adam_warmup_step_listed(L2, TL, m, m.clone(), LR, B1, B2, ETA)
+    # another layout: another worker count, or the same n and another d (its
+    # grids differ, so the handle's block tables would index past them).  The
+    # binding refuses first; the library itself refuses too, on the host,
+    # before any launch.
+    for L2 in (oba.Layout(16, 3, synth.whole(16), synth.even_shards(16, 3)),
+               oba.Layout(4096, 2, synth.whole(4096), synth.even_shards(4096, 2)),
+               oba.Layout(16, 2, synth.whole(16), synth.even_shards(16, 2))):
+        m = t.zeros(L2.d, device="cuda")
+        with pytest.raises(ValueError):
+            oba.adam_warmup_step_listed(L2, TL, m, m.clone(), LR, B1, B2, ETA)
+        sb = t.zeros(L2.W, dtype=t.int64, device="cuda")
+        ss = t.ones(L2.n_sseg, device="cuda")
+        c = t.zeros((L2.n, L2.ld), device="cuda")
+        wb = t.zeros((L2.n, L2.W), dtype=t.int64, device="cuda")
+        wsc = t.zeros((L2.n, L2.n_wseg), device="cuda")
+        P = ctypes.c_void_p
+        lib, st = oba.lib(), P(t.cuda.current_stream().cuda_stream)
+        ws = P(L2.ws.data_ptr())
+        rcs = [
+            lib.oba_adam_warmup_step_listed(L2.handle, TL.handle, P(m.data_ptr()),
+                                            P(m.data_ptr() + 0), LR, B1, B2, ETA, 1.0, 1.0,
+                                            P(None), ws, L2.ws_bytes, st),
+            lib.oba_compress_deferred_listed(L2.handle, TL.handle, P(m.data_ptr()), P(None),
+                                             P(None), P(c.data_ptr()), P(wb.data_ptr()),
+                                             P(wsc.data_ptr()), B1, ws, L2.ws_bytes, st),
+            lib.oba_decompress_update_listed(L2.handle, TL.handle, P(sb.data_ptr()),
+                                             P(ss.data_ptr()), P(m.data_ptr()), P(None), LR, st),
+        ]
+        assert rcs == [-1, -1, -1], rcs  # OBA_EINVAL
+        L2.close()
+    t.cuda.synchronize()
     TL.close()
     L.close()
-    L2.close()
 
 
 def test_gpt2_xl_tensor_list_full_size():
