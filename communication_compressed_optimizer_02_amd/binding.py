@@ -44,6 +44,7 @@ SIGNATURES = {
     "oba_decompress_update": (_I, [_P, _P, _P, _P, _P, _P, _D, _P]),
     "oba_server_momentum": (_I, [_P, _P, _P, _P, _P]),
     "oba_compress_deferred": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _D, _P, _SZ, _P]),
+    "oba_compress_deferred_noalloc": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _D, _P]),
     "oba_compress_deferred16": (_I, [_P, _P, _I, _P, _P, _P, _P, _I, _P, _P, _D, _P, _SZ,
                                      _P]),
     "oba_compress_deferred_local": (_I, [_P, _P, _I, _P, _P, _P, _P, _D, _P, _SZ, _P]),
@@ -309,6 +310,27 @@ def compress_deferred(L: Layout, g, m, c, wbits, wscale, beta1, sbits_prev=None,
         _ptr(wscale, "wscale", f32, (L.n, L.n_wseg)), beta1,
         ctypes.c_void_p(L.ws.data_ptr()), L.ws_bytes, _stream(stream))
     _check(rc, "oba_compress_deferred")
+
+
+def compress_deferred_noalloc(L: Layout, g, m, c, wbits, wscale, beta1, sbits_prev=None,
+                              sscale_prev=None, stream=None):
+    """compress_deferred without a workspace: the library's fixed device
+    scratch holds the partial sums (for callers that cannot allocate)."""
+    import torch
+
+    f32 = (torch.float32,)
+    P = ctypes.c_void_p
+    mp = _ptr(m, "m", f32, (L.d,)) if m is not None else P(None)
+    bp = (_ptr(sbits_prev, "sbits_prev", (torch.int64,), (L.W,)) if sbits_prev is not None
+          else P(None))
+    sp = (_ptr(sscale_prev, "sscale_prev", f32, (L.n_sseg,)) if sscale_prev is not None
+          else P(None))
+    rc = lib().oba_compress_deferred_noalloc(
+        L.handle, _ptr(g, "g", _gtypes(), (L.n, L.ld)), _gdtype(g),
+        mp, bp, sp, _ptr(c, "c", f32, (L.n, L.ld)),
+        _ptr(wbits, "wbits", (torch.int64,), (L.n, L.W)),
+        _ptr(wscale, "wscale", f32, (L.n, L.n_wseg)), beta1, _stream(stream))
+    _check(rc, "oba_compress_deferred_noalloc")
 
 
 def compress_deferred16(L: Layout, g, m, c16, wbits, wscale, beta1, sbits_prev=None,

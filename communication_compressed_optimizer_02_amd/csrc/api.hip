@@ -58,6 +58,10 @@ struct oba_tensors_s {
   oba::TList tl_s{};    // block table of the server grid
 };
 
+// The fixed device scratch of oba_compress_deferred_noalloc (see below).
+static_assert(OBA_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) double scratch[OBA_NOALLOC_SCRATCH_BYTES / sizeof(double)];
+
 namespace {
 
 thread_local char g_hip_msg[256] = "HIP error";
@@ -119,6 +123,30 @@ int launch(const char* name, hipStream_t st, F&& fn) {
   return OBA_OK;
 }
 
+// ---- fixed device scratch (oba_compress_deferred_noalloc) -----------------
+// The binary64 partial sums of the worker pass, for callers that cannot
+// allocate.  Each GPU holds its own copy of the array until the process ends.
+// Host code never uses the array's name as an address: the device address of
+// each GPU's copy is looked up once per device, when the first layout is
+// created on it, and kept below.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (device `dev` must be current).
+int scratch_on(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return OBA_EINVAL;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress (scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return OBA_OK;
+}
+
 // ---- argument checks ------------------------------------------------------
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -172,6 +200,9 @@ const char* oba_status_string(int status) {
     case OBA_EWORKSPACE: return "workspace smaller than oba_workspace_bytes()";
     case OBA_EHIP: return g_hip_msg;
     case OBA_ENOMEM: return "allocation failed";
+    case OBA_ESCRATCH:
+      return "the layout needs more than the fixed device scratch of "
+             "oba_compress_deferred_noalloc (OBA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -197,6 +228,14 @@ int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const i
   if (e != hipSuccess) {
     delete L;
     return hip_fail(e, "hipGetDevice");
+  }
+  {  // set-up of this device's fixed scratch (once per device)
+    void* sp = nullptr;
+    rc = scratch_on(L->device, &sp);
+    if (rc) {
+      delete L;
+      return rc;
+    }
   }
   // one device allocation: int64 arrays first, then int32 arrays
   std::vector<int64_t> h64;
@@ -424,10 +463,15 @@ int oba_server_reduce_recompress(oba_layout L, const uint64_t* wbits, const floa
                 [&] { oba::launch_residual(G, eps, 0, eps, 0, 1, sscale, L->tau, stream); });
 }
 
-int oba_compress_deferred(oba_layout L, const void* g, int g_dtype, const float* m,
-                          const uint64_t* sbits_prev, const float* sscale_prev, float* c,
-                          uint64_t* wbits, float* wscale, double beta1, void* ws, size_t ws_bytes,
-                          hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// oba_compress_deferred with its binary64 partials at `part` (workspace or
+// the fixed scratch), after the checks common to both entry points.
+int compress_deferred_checks(oba_layout L, const void* g, int g_dtype, const float* m,
+                             const uint64_t* sbits_prev, const float* sscale_prev, float* c,
+                             uint64_t* wbits, float* wscale, double beta1) {
   OBA_TRY(check_layout(L));
   if (!gdtype_ok(g_dtype)) return OBA_EINVAL;
   if (!beta_ok(beta1)) return OBA_EINVAL;
@@ -445,10 +489,14 @@ int oba_compress_deferred(oba_layout L, const void* g, int g_dtype, const float*
   OBA_TRY(check_buf(c, 16));
   OBA_TRY(check_buf(wbits, 8));
   OBA_TRY(check_buf(wscale, 4));
-  OBA_TRY(check_buf(ws, 8));
-  if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
+  return OBA_OK;
+}
+
+int compress_deferred_run(oba_layout L, const void* g, int g_dtype, const float* m,
+                          const uint64_t* sbits_prev, const float* sscale_prev, float* c,
+                          uint64_t* wbits, float* wscale, double beta1, double* part,
+                          hipStream_t stream) {
   const oba::Geo G = L->geo_c;
-  double* part = static_cast<double*>(ws);
   const float b1 = (float)beta1, omb1 = (float)(1.0 - beta1);
   uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
   const oba::MomSrc ms{reinterpret_cast<const uint8_t*>(sbits_prev), sscale_prev, L->tau_c};
@@ -458,6 +506,42 @@ int oba_compress_deferred(oba_layout L, const void* g, int g_dtype, const float*
   }));
   return launch("finalize_scales", stream,
                 [&] { oba::launch_finalize(part, G.n, L->sig_c, wscale, stream); });
+}
+
+}  // namespace
+
+extern "C" {
+
+int oba_compress_deferred(oba_layout L, const void* g, int g_dtype, const float* m,
+                          const uint64_t* sbits_prev, const float* sscale_prev, float* c,
+                          uint64_t* wbits, float* wscale, double beta1, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  OBA_TRY(compress_deferred_checks(L, g, g_dtype, m, sbits_prev, sscale_prev, c, wbits, wscale,
+                                   beta1));
+  if (L->geo.d == 0) return OBA_OK;
+  OBA_TRY(check_buf(ws, 8));
+  if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
+  return compress_deferred_run(L, g, g_dtype, m, sbits_prev, sscale_prev, c, wbits, wscale,
+                               beta1, static_cast<double*>(ws), stream);
+}
+
+int oba_compress_deferred_noalloc(oba_layout L, const void* g, int g_dtype, const float* m,
+                                  const uint64_t* sbits_prev, const float* sscale_prev, float* c,
+                                  uint64_t* wbits, float* wscale, double beta1,
+                                  hipStream_t stream) {
+  OBA_TRY(check_layout(L));
+  // the partials of the compress grid, [n][pieces] (and [n][items]), must fit
+  // the fixed scratch; refused before the buffers are looked at
+  if (L->geo.d > 0 &&
+      oba::partial_bytes(L->sig_c, L->plan.n) > (size_t)OBA_NOALLOC_SCRATCH_BYTES)
+    return OBA_ESCRATCH;
+  OBA_TRY(compress_deferred_checks(L, g, g_dtype, m, sbits_prev, sscale_prev, c, wbits, wscale,
+                                   beta1));
+  if (L->geo.d == 0) return OBA_OK;
+  void* sp = nullptr;
+  OBA_TRY(scratch_on(L->device, &sp));  // resolved when the layout was created
+  return compress_deferred_run(L, g, g_dtype, m, sbits_prev, sscale_prev, c, wbits, wscale,
+                               beta1, static_cast<double*>(sp), stream);
 }
 
 int oba_compress_deferred16(oba_layout L, const void* g, int g_dtype, const float* m,

@@ -72,7 +72,8 @@ enum {
   OBA_ESEG = -3,       /* a segment table is not 0 = o_0 < o_1 < ... < o_k = d */
   OBA_EWORKSPACE = -4, /* workspace smaller than oba_workspace_bytes() */
   OBA_EHIP = -5,       /* a HIP call failed (see oba_status_string) */
-  OBA_ENOMEM = -6      /* host or device allocation of the layout failed */
+  OBA_ENOMEM = -6,     /* host or device allocation of the layout failed */
+  OBA_ESCRATCH = -7    /* the layout needs more than OBA_NOALLOC_SCRATCH_BYTES */
 };
 
 /* gradient dtype: binary32, binary16, or bfloat16 (the upper half of a
@@ -253,6 +254,26 @@ int oba_compress_deferred(oba_layout layout, const void* g, int g_dtype, const f
                           const uint64_t* sbits_prev, const float* sscale_prev, float* c,
                           uint64_t* wbits, float* wscale, double beta1, void* ws, size_t ws_bytes,
                           hipStream_t stream);
+
+/* oba_compress_deferred for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same checks, kernels and results (bit for bit), but no
+ * workspace argument: the worker pass's binary64 partial sums go to a fixed
+ * device array of OBA_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on, until the process ends.  The call allocates nothing and
+ * records no memset (no part of the array needs to start at zero: every
+ * partial is written before it is read).  OBA_ESCRATCH if the layout's
+ * partials, n * (worker pieces + items) binary64 values, exceed the array (a
+ * layout whose oba_workspace_bytes() is at most OBA_NOALLOC_SCRATCH_BYTES
+ * always fits: 10.5 MB at 336M parameters and 8 workers).  All calls on one
+ * GPU share its array: two such calls that can run at the same time (two
+ * streams) race.  The array's device address is looked up when the first
+ * layout is created on a device. */
+#define OBA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int oba_compress_deferred_noalloc(oba_layout layout, const void* g, int g_dtype, const float* m,
+                                  const uint64_t* sbits_prev, const float* sscale_prev, float* c,
+                                  uint64_t* wbits, float* wscale, double beta1,
+                                  hipStream_t stream);
 
 /* Per-worker momentum (the other reading of [Tang] 4.3: every worker keeps
  * its own momentum and the broadcast m_hat only moves x), in the deferred

@@ -36,9 +36,10 @@ def test_library_exports_every_declared_entry_point():
 
 
 def test_status_strings():
-    for rc in (0, -1, -2, -3, -4, -5, -6):
+    for rc in (0, -1, -2, -3, -4, -5, -6, -7):
         assert binding.status_string(rc)
     assert "segment" in binding.status_string(-3)
+    assert "scratch" in binding.status_string(-7)
 
 
 @pytest.mark.parametrize("case,expect", [
