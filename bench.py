@@ -121,6 +121,20 @@ def traffic_from_profiles(workload, kernel, field="hbm_bytes_per_launch"):
     return float(val.group(1))
 
 
+def trace_from_profiles(workload):
+    """The dominant kernel's average launch time (ms) in the committed
+    rocprofv3 kernel trace, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    val = re.search(r"trace_avg_us:\s*([0-9.]+)", text)
+    if not src or not val or src.group(1) != source_hash():
+        return None
+    return float(val.group(1)) / 1e3
+
+
 def make_state(w, torch, oba, synth, warmup_timing=None):
     """The workload's state after its warm-up (Adam steps with the fused
     variance norm, as a run watching for the plateau makes them) and the
@@ -163,60 +177,168 @@ def make_state(w, torch, oba, synth, warmup_timing=None):
     return L, S, (g_a, g_b)
 
 
-def cpu_baseline(w, torch, synth, d_sample):
-    """The oracle (plain C) on a bounded sample of the same workload: one
-    compression step over d_sample coordinates for all n workers, timed
-    twice from the same state -- once as one call per pass on one thread,
-    once with the n workers' compressions (independent of each other) in n
-    threads, the server pass and the update then on one thread.  The sample
-    is drawn with the workload's device generators and copied to the host
-    (drawing it with numpy would take longer than the timed oracle run)."""
+def host_info():
+    """Cores in this process's affinity mask, the CPU model, available RAM."""
+    aff = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    avail = None
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemAvailable:"):
+                    avail = int(line.split()[1]) * 1024
+                    break
+    except OSError:
+        pass
+    return aff, model, avail
+
+
+def oracle_state(w, torch, synth, d, seed):
+    """A compression-stage state and one gradient set of workload w at size
+    d, drawn with the workload's device generators and copied to the host
+    (drawing it with numpy would take longer than the oracle run)."""
+    import numpy as np
+
+    import oracle
+
+    ws = synth.scaled(w, d) if w.name != "gpt2_xl" else None
+    gen = synth.device_generator(seed)
+    zero = synth.device_zero_mask(gen, d) if w.name == "bert_large" else None
+    g = torch.empty((w.n, d), dtype=torch.float16 if w.g_dtype == "f16" else torch.float32,
+                    device="cuda")
+    synth.device_grads(gen, ws, g, zero)
+    del zero
+
+    def normal(shape, std):
+        return torch.empty(shape, device="cuda").normal_(0.0, std, generator=gen).cpu().numpy()
+
+    st = {"x": normal(d, 0.02), "m": normal(d, 1e-3), "delta": normal((w.n, d), 1e-4),
+          "eps": normal(d, 1e-4)}
+    v = normal(d, 1e-3) ** 2
+    st["denom"] = oracle.freeze_variance(np.ascontiguousarray(v, dtype=np.float32), synth.ETA)
+    del v
+    g_h = g.cpu().numpy()
+    del g
+    torch.cuda.empty_cache()
+    return ws, st, g_h
+
+
+def oracle_step_threads(st, g, wseg, sseg, beta1, lr, threads):
+    """One oracle step (compress, server, update) with its independent calls
+    on `threads` threads: one compression per worker row; when the worker
+    scale is one per worker and every server segment starts on a word, one
+    server call per server segment; the update over word-aligned ranges.
+    The oracle's code is unchanged: each call is the one the single-threaded
+    step makes, on its own part of the arrays."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
 
     import oracle
 
-    ws = synth.scaled(w, d_sample)
-    gen = synth.device_generator(w.seed + 1000)
-    dev = "cuda"
-    zero = synth.device_zero_mask(gen, ws.d) if w.name == "bert_large" else None
-    g = torch.empty((ws.n, ws.d), dtype=torch.float16 if ws.g_dtype == "f16" else torch.float32,
-                    device=dev)
-    synth.device_grads(gen, ws, g, zero)
-
-    def normal(shape, std):
-        return torch.empty(shape, device=dev).normal_(0.0, std, generator=gen).cpu().numpy()
-
-    st = {"x": normal(ws.d, 0.02), "m": normal(ws.d, 1e-3), "delta": normal((ws.n, ws.d), 1e-4),
-          "eps": normal(ws.d, 1e-4)}
-    v = normal(ws.d, 1e-3) ** 2
-    st["denom"] = oracle.freeze_variance(np.ascontiguousarray(v, dtype=np.float32), synth.ETA)
-    g = g.cpu().numpy()
-    st2 = {k: a.copy() for k, a in st.items()}
-    t0 = time.perf_counter()
-    oracle.step(st, g, ws.wseg, ws.sseg, synth.BETA1, synth.LR)
-    dt1 = time.perf_counter() - t0
-    threads = max(1, min(ws.n, len(os.sched_getaffinity(0))))
-
-    def worker(i):
-        return oracle.compress(g[i:i + 1], st2["m"], st2["delta"][i:i + 1], ws.wseg, synth.BETA1)
-
-    t0 = time.perf_counter()
+    n, d = g.shape
     with ThreadPoolExecutor(threads) as ex:
-        res = list(ex.map(worker, range(ws.n)))
-    wb = np.concatenate([r[0] for r in res])
-    wsc = np.concatenate([r[1] for r in res])
-    sb, ss = oracle.server_reduce_recompress(wb, wsc, ws.wseg, ws.sseg, st2["eps"])
-    oracle.decompress_update(sb, ss, ws.sseg, st2["denom"], st2["m"], st2["x"], synth.LR)
-    dt = time.perf_counter() - t0
-    assert np.array_equal(st["x"].view(np.uint32), st2["x"].view(np.uint32))
-    return {"value": ws.d / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
-            "sample": f"one compression step (compress, server, update) of the {w.name} recipe "
-                      f"at d={ws.d:,}, n={ws.n}, {ws.g_dtype} gradients: {dt:.2f} s with the "
-                      f"{ws.n} workers' compressions on {threads} threads, {dt1:.2f} s on 1 "
-                      f"thread",
-            "single_thread_value": ws.d / dt1}
+        res = list(ex.map(lambda i: oracle.compress(g[i:i + 1], st["m"], st["delta"][i:i + 1],
+                                                    wseg, beta1), range(n)))
+        wb = np.concatenate([r[0] for r in res])
+        ws = np.concatenate([r[1] for r in res])
+        del res
+        ns = len(sseg) - 1
+        if len(wseg) == 2 and all(int(o) % 64 == 0 for o in sseg[:-1]) and threads > 1:
+            def server(j):
+                lo, hi = int(sseg[j]), int(sseg[j + 1])
+                part = np.ascontiguousarray(wb[:, lo // 64:(hi + 63) // 64])
+                loc = np.array([0, hi - lo], np.int64)
+                return oracle.server_reduce_recompress(part, ws, loc, loc, st["eps"][lo:hi])
+
+            parts = list(ex.map(server, range(ns)))
+            sb = np.concatenate([p_[0] for p_ in parts])
+            ss = np.concatenate([p_[1] for p_ in parts])
+        else:
+            sb, ss = oracle.server_reduce_recompress(wb, ws, wseg, sseg, st["eps"])
+        cuts = sorted({min(d, (d * k // threads) // 64 * 64) for k in range(threads + 1)} | {d})
+        list(ex.map(lambda k: oracle.decompress_update(sb, ss, sseg, st["denom"], st["m"],
+                                                       st["x"], lr, cuts[k], cuts[k + 1]),
+                    range(len(cuts) - 1)))
+    return wb, ws, sb, ss
+
+
+def cpu_baseline(w, torch, synth, d_cap, single_thread=True):
+    """The oracle (plain C) timed on this host's cores: one compression step
+    of the workload (compress, server, update) at its full d when host memory
+    allows (else the largest d that fits, stated), its independent calls on
+    up to 16 threads, median of 3 runs from the same state; then the same
+    step at the bert_base shape on one thread, median of 3."""
+    import numpy as np
+
+    import oracle
+
+    aff, model, avail = host_info()
+    threads = max(1, min(aff, 16))
+    gb = 2 if w.g_dtype == "f16" else 4
+    per_coord = w.n * (gb + 8) + 24  # g, two copies of delta, m, x, eps, denom (host)
+    d = min(w.d, d_cap)
+    if avail is not None:
+        d = min(d, int(0.5 * avail / per_coord) // 2048 * 2048)
+    d = max(d, 1 << 20)
+    log(f"[bench] CPU oracle: d={d:,} of {w.d:,}, {threads} threads of {aff}")
+    ws, st0, g = oracle_state(w, torch, synth, d, w.seed + 1000)
+
+    # the threaded split computes the single-threaded step exactly (small check)
+    k = min(d, 1 << 20)
+    small = synth.scaled(w, k)
+    a = {nm: np.ascontiguousarray(v[..., :k]) for nm, v in st0.items()}
+    b = {nm: v.copy() for nm, v in a.items()}
+    gk = np.ascontiguousarray(g[:, :k])
+    oracle.step(a, gk, small.wseg, small.sseg, synth.BETA1, synth.LR)
+    oracle_step_threads(b, gk, small.wseg, small.sseg, synth.BETA1, synth.LR, threads)
+    for nm in ("x", "m", "delta", "eps"):
+        assert np.array_equal(a[nm].view(np.uint32), b[nm].view(np.uint32)), nm
+    del a, b, gk
+
+    runs = []
+    for _ in range(3):
+        st = {nm: v.copy() for nm, v in st0.items()}
+        t0 = time.perf_counter()
+        oracle_step_threads(st, g, ws.wseg, ws.sseg, synth.BETA1, synth.LR, threads)
+        runs.append(time.perf_counter() - t0)
+        del st
+    del st0, g
+    med = sorted(runs)[1]
+    out = {"value": d / med, "unit": "params/s", "cores": threads, "kind": "oracle",
+           "sample": f"one compression step (compress, server, update) of the {w.name} recipe "
+                     f"at d={d:,} (the workload's d={w.d:,}"
+                     + ("" if d == w.d else f"; params/s measured at the smaller d") +
+                     f"), n={w.n}, {w.g_dtype} gradients; independent oracle calls on "
+                     f"{threads} threads; median of 3 runs",
+           "threads": threads, "affinity_cores": aff, "cpu_model": model,
+           "runs_s": [round(r, 3) for r in runs], "median_s": round(med, 3), "d": d}
+    if single_thread:
+        wb = synth.workload("bert_base")
+        d1 = wb.d if avail is None else min(wb.d, int(0.5 * avail / (wb.n * 12 + 24)))
+        log(f"[bench] CPU oracle, one thread: bert_base d={d1:,}")
+        ws1, st0, g = oracle_state(wb, torch, synth, d1, wb.seed + 1000)
+        runs = []
+        for _ in range(3):
+            st = {nm: v.copy() for nm, v in st0.items()}
+            t0 = time.perf_counter()
+            oracle.step(st, g, ws1.wseg, ws1.sseg, synth.BETA1, synth.LR)
+            runs.append(time.perf_counter() - t0)
+            del st
+        med1 = sorted(runs)[1]
+        out["single_thread"] = {"workload": wb.name, "d": d1, "n": wb.n, "grad_dtype": wb.g_dtype,
+                                "runs_s": [round(r, 3) for r in runs], "median_s": round(med1, 3),
+                                "value": d1 / med1, "unit": "params/s", "threads": 1}
+        del st0, g
+    return out
 
 
 def run_graph(S, gsets, args, torch, synth):
@@ -404,23 +526,389 @@ def one_gpu_share(w, torch, oba, synth, steps, warmup):
                      f"{n} workers' messages, update over d"}
 
 
-def copy_reference(torch, nbytes=1 << 31, reps=5):
-    """Device-to-device copy of nbytes (read nbytes + write nbytes), the
-    plain streaming kernel that calibrates what HBM delivers on this machine."""
-    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-    b = torch.empty_like(a)
-    b.copy_(a)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        b.copy_(a)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    del a, b
-    return {"bytes_moved": 2 * nbytes, "avg_ms": round(ms, 4),
-            "GBps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+# Streaming probes of libhbmstream.so (calib/hbm_stream.hip): name -> (shape,
+# groups).  The worker-pass shapes take the workload's n workers in groups of
+# 4, as the deferred worker pass does; the others are fixed row counts.
+PROBES = {"read": (0, 1), "write": (1, 1), "copy": (2, 1), "worker_g16": (3, None),
+          "worker_g32": (4, None), "state16": (5, None), "warmup_g16": (6, 1),
+          "update": (7, 1), "in_place": (8, 1)}
+# the probe of the same access shape as each kernel of the headline step
+PROBE_OF = {("compress_deferred", "f16"): "worker_g16", ("compress_deferred", "f32"): "worker_g32",
+            ("compress_deferred16", "f16"): "state16", ("decompress_update", None): "update",
+            ("server_deferred", None): "in_place", ("adam_warmup", "f16"): "warmup_g16"}
+
+
+def probe_lib():
+    import ctypes
+
+    path = os.path.join(ROOT, "communication_compressed_optimizer_02_amd", "libhbmstream.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build first (__graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    P, I, I32, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64
+    lib.hbm_stream_shape.restype = I
+    lib.hbm_stream_shape.argtypes = [I, ctypes.POINTER(I32)]
+    lib.hbm_stream_launch.restype = I
+    lib.hbm_stream_launch.argtypes = [I, I, P, P, I64, I64, I32, I32, P, P]
+    return lib
+
+
+PROBE_BPC = (0, 2, 3, 4, 5, 6)  # resident blocks per CU tried (0: as registers allow)
+
+
+def hbm_ceiling(torch, w, reps=5):
+    """What this HBM delivers for each access shape of the method's kernels,
+    measured here with the streaming probes (no arithmetic) at the
+    workload's size, on random data (constant data streams faster on this
+    part): bytes moved per launch / mean launch time (HIP events on the
+    launch stream), the best over the global and buffer-resource forms and
+    over occupancy caps of PROBE_BPC blocks per CU."""
+    import ctypes
+
+    lib = probe_lib()
+    spans = w.d // 2048
+    ld = spans * 2048
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(1, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 3000)
+    out = {}
+    for name, (shape, groups) in PROBES.items():
+        if groups is None:
+            if w.n % 4:
+                continue
+            groups = w.n // 4
+        na, ab, nb, bb, bmode = _probe_shapes()[name]
+        a = torch.empty(max(1, groups * na * ld * ab // 4), device="cuda")
+        b = torch.empty(max(1, groups * nb * ld * bb // 4), device="cuda")
+        a.uniform_(0.5, 1.0, generator=gen)
+        b.uniform_(0.5, 1.0, generator=gen)
+        nbytes = groups * ld * (na * ab + nb * bb * (2 if bmode == 2 else 1))
+        res = {"bytes_per_launch": nbytes, "GBps": 0.0}
+        for buf in (0, 1):
+            for bpc in PROBE_BPC:
+                def go():
+                    return lib.hbm_stream_launch(shape, buf, ctypes.c_void_p(a.data_ptr()),
+                                                 ctypes.c_void_p(b.data_ptr()), ld, spans,
+                                                 groups, bpc, ctypes.c_void_p(sink.data_ptr()),
+                                                 ctypes.c_void_p(stream.cuda_stream))
+                if go() != 0:  # an occupancy cap this device cannot express
+                    continue
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    go()
+                e1.record()
+                torch.cuda.synchronize()
+                gbs = round(nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 1)
+                res[f"{'buffer' if buf else 'global'}_bpc{bpc}"] = gbs
+                if gbs > res["GBps"]:
+                    res["GBps"] = gbs
+                    res["best"] = f"{'buffer' if buf else 'global'}, " + (
+                        f"{bpc} blocks per CU" if bpc else "occupancy as registers allow")
+        out[name] = res
+        del a, b
+        torch.cuda.empty_cache()
+    return {"probes": out, "rows": ld,
+            "note": "streaming probes (calib/hbm_stream.hip) in the kernels' lane layout, "
+                    "non-temporal, all loads of a block before its stores, random data; GBps = "
+                    "the best over load forms and occupancy caps"}
+
+
+# ---- profile summaries (profiles/*.md) from raw rocprofv3 output -----------
+# The profiled commands, run from the repository root on the GPU box (each
+# counter pass on its own run, as rocprofv3 collects one pass per run).
+PROFILE_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof/trace -o run -f csv -- "
+             "python3 -u bench.py --steps 5 --warmup 1 --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex oba:: -d gpurun_out/prof/fetch "
+             "-o run -f csv -- python3 -u bench.py --steps 2 --warmup 0 --no-cpu-baseline",
+    "write": "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex oba:: -d gpurun_out/prof/write "
+             "-o run -f csv -- python3 -u bench.py --steps 2 --warmup 0 --no-cpu-baseline",
+    "occ": "rocprofv3 --pmc OccupancyPercent MeanOccupancyPerCU SQ_WAVES --kernel-include-regex "
+           "oba:: -d gpurun_out/prof/occ -o run -f csv -- python3 -u bench.py --steps 2 "
+           "--warmup 0 --no-cpu-baseline",
+}
+CU_NUM = 256
+
+
+def _short(name):
+    name = re.sub(r"^void ", "", name)
+    name = name.replace("oba::(anonymous namespace)::", "oba::")
+    return name.split("(", 1)[0].strip()
+
+
+_SHAPES = {}
+
+
+def _probe_shapes():
+    """Probe name -> (rows of A, bytes, rows of B, bytes, B mode) per group."""
+    if not _SHAPES:
+        import ctypes
+
+        lib = probe_lib()
+        info = (ctypes.c_int32 * 5)()
+        for nm, (shape, _) in PROBES.items():
+            assert lib.hbm_stream_shape(shape, info) == 0
+            _SHAPES[nm] = tuple(info)
+    return _SHAPES
+
+
+def _role(short, n=None):
+    """What a kernel of the bench run is, from its template arguments; with
+    the workload's worker count n, a worker or server pass whose group size
+    does not fit n (the one-GPU share's single worker) is "other"."""
+    m = re.match(r"oba::k_compress(16)?<[^,]+, [^,]+, (\d+), (\d), (true|false)>", short)
+    if m:
+        mode = int(m.group(3))
+        base = {1: "compress_p1", 2: "compress_p2", 3: "compress_deferred (first step, m read)",
+                4: "compress_deferred", 5: "compress_deferred_local"}[mode]
+        if m.group(1):
+            base = base.replace("compress_deferred", "compress_deferred16")
+        group = min(n, 4) if (mode in (4, 5) or m.group(1)) else min(n, 8) if n else None
+        if n and int(m.group(2)) != group:
+            return "other (one-GPU share)"
+        return base
+    m = re.match(r"oba::k_server_p1<(\d+), (true|false)>", short)
+    if m:
+        if n and int(m.group(1)) != min(n, 8):
+            return "other (one-GPU share)"
+        return "server_deferred" if m.group(2) == "true" else "server_p1"
+    m = re.match(r"oba::k_decompress_update<(true|false), (true|false), (true|false)>", short)
+    if m:
+        return {("false", "true"): "decompress_update", ("true", "true"):
+                "decompress_update (m written)", ("true", "false"): "server_momentum"}.get(
+                    (m.group(1), m.group(2)), "")
+    m = re.match(r"oba::k_stream<([^,]+), ([^,]+), (\d+), (\d+), (\d), (true|false)>", short)
+    if m:
+        ta, tb = (2 if "short" in x else 4 for x in (m.group(1), m.group(2)))
+        key = (int(m.group(3)), ta, int(m.group(4)), tb, int(m.group(5)))
+        for nm, shp in _probe_shapes().items():
+            if shp == key:
+                return f"probe {nm} ({'buffer' if m.group(6) == 'true' else 'global'})"
+        return "probe"
+    for pat, r in (("oba::k_residual", "server_p2"), ("oba::k_adam_warmup", "adam_warmup"),
+                   ("oba::k_freeze", "freeze"), ("oba::k_norm_finalize", "variance norm sum"),
+                   ("oba::k_finalize_scales", "scale sums"), ("oba::k_sum_items", "scale sums")):
+        if short.startswith(pat):
+            return r
+    return ""
+
+
+def _alg_bytes(w):
+    """Algorithmic bytes per launch of each role at the workload's shape."""
+    gb = 2 if w.g_dtype == "f16" else 4
+    n, d = w.n, w.d
+    per = {}
+    for sch in ("deferred", "explicit", "local", "state16"):
+        per.update(gbytes(w, sch))
+    per["compress_deferred (first step, m read)"] = 4 + n * (gb + 4) + 4 * n + n / 8
+    per["compress_deferred16 (first step, m read)"] = 4 + n * (gb + 2) + 2 * n + n / 8
+    per["decompress_update (m written)"] = 1 / 8 + 16
+    per["server_momentum"] = 1 / 8 + 4
+    per["adam_warmup"] = n * gb + 24
+    per["freeze"] = 8
+    out = {k: v * d for k, v in per.items()}
+    ld = (d // 2048) * 2048
+    for nm, (shape, groups) in PROBES.items():
+        na, ab, nb, bb, mode = _probe_shapes()[nm]
+        g = groups if groups is not None else n // 4
+        for form in ("global", "buffer"):
+            out[f"probe {nm} ({form})"] = g * ld * (na * ab + nb * bb * (2 if mode == 2 else 1))
+    return out
+
+
+def _per_dispatch(path, counter, n=None):
+    """(role, short name, grid) -> list of the counter's values per dispatch."""
+    import collections
+    import csv
+
+    acc = collections.defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter or "oba::" not in r["Kernel_Name"]:
+                continue
+            sh = _short(r["Kernel_Name"])
+            acc[(_role(sh, n), sh, int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+    return acc
+
+
+def _largest_grids(keys):
+    """The grid of each short name's largest launches (the workload's own
+    shape; smaller grids of the same kernel are other launches)."""
+    big = {}
+    for _, sh, g in keys:
+        big[sh] = max(big.get(sh, 0), g)
+    return big
+
+
+def summarize_profiles(raw, out_dir, workload="bert_large"):
+    """Write the profile summaries from rocprofv3's raw CSVs under `raw`
+    (trace/, fetch/, write/, occ/) and the two bench JSON lines there
+    (bench.json: the unprofiled default run; trace_bench.json: the traced
+    run)."""
+    import csv
+    import glob
+
+    from communication_compressed_optimizer_02_amd import synth
+
+    w = synth.workload(workload)
+    alg = _alg_bytes(w)
+    one = lambda pat: sorted(glob.glob(os.path.join(raw, pat)))[0]  # noqa: E731
+    src = source_hash()
+    written = []
+
+    def jline(name):
+        with open(os.path.join(raw, name)) as f:
+            return json.loads([x for x in f if x.startswith("{")][-1])
+
+    # ---- traffic: FETCH_SIZE and WRITE_SIZE, calibrated on the copy probe
+    fetch = _per_dispatch(one("fetch/*counter_collection.csv"), "FETCH_SIZE", w.n)
+    write = _per_dispatch(one("write/*counter_collection.csv"), "WRITE_SIZE", w.n)
+    cal = "probe copy (global)"
+    cf = [v for k, vs in fetch.items() if k[0] == cal for v in vs]
+    cw = [v for k, vs in write.items() if k[0] == cal for v in vs]
+    half = alg[cal] / 2  # the copy reads and writes the same bytes
+    ff = half / (sum(cf) / len(cf) * 1024)
+    fw = half / (sum(cw) / len(cw) * 1024)
+    big = _largest_grids(fetch)
+    rows, dom, step = [], None, 0.0
+    for key in sorted(fetch, key=lambda k: (k[0] or "~", k[1], k[2])):
+        role, sh, grid = key
+        fv = sum(fetch[key]) / len(fetch[key]) * 1024 * ff
+        wl = write.get(key, [0.0])
+        wv = sum(wl) / len(wl) * 1024 * fw
+        main = grid == big[sh]
+        a = alg.get(role) if main else None
+        rows.append((sh, grid, role if main else f"{role}, other shape", fv, wv, a))
+        if main and role == "compress_deferred":
+            dom = fv + wv
+        if main and role in ("compress_deferred", "server_deferred", "decompress_update"):
+            step += fv + wv
+    L = [f"# HBM traffic per launch (rocprofv3 counters), {w.name} workload", "",
+         f"Workload: d = {w.d:,}, n = {w.n}, {w.g_dtype} gradients; one MI355X.", "",
+         "Commands (repository root, GPU box; one counter per run):", "",
+         "    " + PROFILE_CMDS["fetch"], "    " + PROFILE_CMDS["write"], "",
+         "Summary written by `python bench.py --summarize-profiles gpurun_out/prof` from those",
+         "runs' counter_collection.csv files.", "",
+         "Calibration: the copy probe (`k_stream<float, float, 4, 4, 1, false>`, global form) reads",
+         f"and writes {half / 1e9:.3f} GB per launch; it reads FETCH_SIZE = "
+         f"{sum(cf) / len(cf) * 1024 / 1e9:.3f} GB and WRITE_SIZE =",
+         f"{sum(cw) / len(cw) * 1024 / 1e9:.3f} GB, so FETCH_SIZE is scaled by {ff:.3f} and "
+         f"WRITE_SIZE by {fw:.3f}.", "",
+         "| kernel | grid (threads) | role | read GB | write GB | traffic GB | algorithmic GB | "
+         "traffic / algorithmic |", "|---|---|---|---|---|---|---|---|"]
+    for sh, grid, role, fv, wv, a in rows:
+        r = f"{(fv + wv) / a:.4f}" if a else "—"
+        ag = f"{a / 1e9:.3f}" if a else "—"
+        L.append(f"| `{sh}` | {grid} | {role or '—'} | {fv / 1e9:.3f} | {wv / 1e9:.3f} | "
+                 f"{(fv + wv) / 1e9:.3f} | {ag} | {r} |")
+    L += ["", "Algorithmic bytes: every buffer a kernel must touch, once per direction "
+          "(bench.py `gbytes`); a probe's are the rows it streams.  A ratio near 1 means no "
+          "re-reads or partial-line waste.", "",
+          "Dominant kernel (compress_deferred):", f"hbm_bytes_per_launch: {dom:.0f}",
+          "Headline step (three streaming kernels):", f"step_hbm_bytes: {step:.0f}",
+          f"kernel_source_sha256: {src}"]
+    path = os.path.join(out_dir, f"compress_deferred_{w.name}_pmc.md")
+    with open(path, "w") as f:
+        f.write("\n".join(L) + "\n")
+    written.append(path)
+
+    # ---- occupancy
+    occ_files = glob.glob(os.path.join(raw, "occ/*counter_collection.csv"))
+    if occ_files:
+        occ = {c: _per_dispatch(occ_files[0], c, w.n)
+               for c in ("OccupancyPercent", "MeanOccupancyPerCU", "SQ_WAVES")}
+        keys = set().union(*[set(v) for v in occ.values()])
+        big = _largest_grids(keys)
+        L = [f"# Occupancy per kernel (rocprofv3 counters), {w.name} workload", "",
+             "Command (repository root, GPU box):", "", "    " + PROFILE_CMDS["occ"], "",
+             "Summary written by `python bench.py --summarize-profiles gpurun_out/prof`.",
+             "OccupancyPercent = 400 * SQ_WAVE_CYCLES / GRBM_GUI_ACTIVE / CU_NUM / 32 (rocprofv3's",
+             "derived counter for gfx950): resident waves as a share of 32 per CU (8 per SIMD);",
+             "waves per SIMD below = OccupancyPercent * 8 / 100, the mean over the dispatch,",
+             "including its ramp-up and drain.  MeanOccupancyPerCU: the same from SQ_LEVEL_WAVES.",
+             "", "| kernel | grid | role | waves per SIMD | OccupancyPercent | MeanOccupancyPerCU "
+             "| waves launched |", "|---|---|---|---|---|---|---|"]
+        for key in sorted(keys, key=lambda k: (k[0] or "~", k[1], k[2])):
+            role, sh, grid = key
+            if grid != big[sh]:
+                continue
+            val = {c: (sum(occ[c][key]) / len(occ[c][key]) if occ[c].get(key) else None)
+                   for c in occ}
+            op = val["OccupancyPercent"]
+            L.append(f"| `{sh}` | {grid} | {role or '—'} | "
+                     f"{op * 8 / 100:.2f} | {op:.1f} | " if op is not None else
+                     f"| `{sh}` | {grid} | {role or '—'} | — | — | ")
+            L[-1] += (f"{val['MeanOccupancyPerCU']:.2f} | " if val["MeanOccupancyPerCU"]
+                      is not None else "— | ")
+            L[-1] += f"{val['SQ_WAVES']:.0f} |" if val["SQ_WAVES"] is not None else "— |"
+        L += ["", f"kernel_source_sha256: {src}"]
+        path = os.path.join(out_dir, f"occupancy_{w.name}.md")
+        with open(path, "w") as f:
+            f.write("\n".join(L) + "\n")
+        written.append(path)
+
+    # ---- kernel trace
+    stats = []
+    with open(one("trace/*kernel_stats.csv")) as f:
+        stats = [r for r in csv.DictReader(f) if "oba::" in r["Name"]]
+    shapes = {}
+    with open(one("trace/*kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            if "oba::" not in r["Kernel_Name"]:
+                continue
+            sh = _short(r["Kernel_Name"])
+            key = (sh, int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]))
+            ent = shapes.setdefault(key, {"t": [], "vgpr": r["VGPR_Count"],
+                                          "agpr": r["Accum_VGPR_Count"], "sgpr": r["SGPR_Count"],
+                                          "lds": r["LDS_Block_Size"],
+                                          "scratch": r["Scratch_Size"]})
+            ent["t"].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    jp, jb = jline("trace_bench.json"), jline("bench.json")
+    big = {}
+    for sh, g in shapes:
+        big[sh] = max(big.get(sh, 0), g)
+    T = [f"# Kernel trace: the 1-bit Adam compression step, {w.name} workload", "",
+         f"Workload: d = {w.d:,} binary32 parameters, n = {w.n} simulated workers, {w.g_dtype} "
+         "gradients, 1 worker segment, n server segments; one MI355X (gfx950).", "",
+         "Command (repository root, GPU box):", "", "    " + PROFILE_CMDS["trace"], "",
+         "Summary written by `python bench.py --summarize-profiles gpurun_out/prof`.", "",
+         "Covers the warm-up and freeze, 1 untimed and 5 timed steps of each schedule "
+         "(deferred, explicit, per-worker momentum, 16-bit state), the graph replays, the "
+         "one-GPU-share run and the HBM streaming probes.  bench.py's own HIP-event timing of the "
+         "dominant kernel (`compress_deferred`): "
+         f"{jp['kernels']['compress_deferred']['avg_ms'] * 1e3:.1f} µs in this traced run, "
+         f"{jb['kernels']['compress_deferred']['avg_ms'] * 1e3:.1f} µs in the unprofiled "
+         "default run on the same box (`python bench.py`).", "",
+         "The VGPR column is rocprofv3's: it counts the kernel descriptor's register granules "
+         "in units of 4, while gfx950 allocates wave64 VGPRs in granules of 8, so the allocated "
+         "count is twice its value rounded up to 8 (84 -> 168).  The compiler's own counts and "
+         "occupancy are in kernel_resources_gfx950.md.", "",
+         "| kernel | grid (threads) | role | launches | avg µs | min µs | max µs | VGPR (rocprof) "
+         "| SGPR | LDS B | scratch B |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for (sh, g), ent in sorted(shapes.items(), key=lambda kv: -sum(kv[1]["t"])):
+        t = ent["t"]
+        role = _role(sh, w.n) if g == big[sh] else f"{_role(sh, w.n)}, other shape"
+        T.append(f"| `{sh}` | {g} | {role or '—'} | {len(t)} | {sum(t) / len(t):.1f} | "
+                 f"{min(t):.1f} | {max(t):.1f} | {ent['vgpr']} | {ent['sgpr']} | {ent['lds']} | "
+                 f"{ent['scratch']} |")
+    T += ["", "Per kernel name (rocprofv3 --stats):", "",
+          "| kernel | calls | avg µs | min µs | max µs |", "|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        T.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                 f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    dom_t = [v for (sh, g), e in shapes.items() if g == big[sh]
+             and _role(sh, w.n) == "compress_deferred" for v in e["t"]]
+    T += ["", "Dominant kernel (compress_deferred), trace average per launch:",
+          f"trace_avg_us: {sum(dom_t) / len(dom_t):.1f}", f"kernel_source_sha256: {src}"]
+    path = os.path.join(out_dir, f"kernel_trace_{w.name}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(T) + "\n")
+    written.append(path)
+    return written
 
 
 def main():
@@ -434,8 +922,18 @@ def main():
     ap.add_argument("--tensor-list", action="store_true",
                     help="also time the deferred step with x and the gradients as the model's "
                          "separate tensors (gpt2_xl: its 388 tensors)")
-    ap.add_argument("--cpu-sample", type=int, default=128_000_000)
+    ap.add_argument("--cpu-sample", type=int, default=336_000_000,
+                    help="largest d of the CPU oracle's timed step")
+    ap.add_argument("--no-single-thread", action="store_true",
+                    help="skip the one-thread oracle run at the bert_base shape")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/*.md from the raw rocprofv3 output under DIR and exit")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        for p_ in summarize_profiles(args.summarize_profiles, os.path.join(ROOT, "profiles"),
+                                     args.workload):
+            print(p_)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the n data-parallel workers are simulated as n "
               "buffers on that GPU; a run over several GPUs is not implemented.",
@@ -536,7 +1034,9 @@ def main():
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": dom_bytes,
-                     "avg_launch_ms": round(dom_ms, 4)},
+                     "avg_launch_ms": round(dom_ms, 4), "timing": "HIP events on the launch "
+                     "stream around each launch of the timed steps",
+                     "profile_trace_avg_ms": trace_from_profiles(w.name)},
         "kernels": kernels,
         "graph_replay": {"ms_per_step": graph_ms, "value": w.d / (graph_ms * 1e-3),
                          "note": "the headline step captured in HIP graphs and replayed"},
@@ -567,12 +1067,27 @@ def main():
     log("[bench] one-GPU share")
     out["one_gpu_share"] = one_gpu_share(w, torch, oba, synth, args.steps, args.warmup)
     torch.cuda.empty_cache()
-    out["copy_reference"] = copy_reference(torch)
-    # the dominant kernel against what a plain device copy reaches on this machine
-    out["roofline"]["frac_of_copy"] = round(achieved / out["copy_reference"]["GBps"], 4)
-    if not args.no_cpu_baseline:
+    log("[bench] HBM streaming probes")
+    ceil = hbm_ceiling(torch, w)
+    out["hbm_ceiling"] = ceil
+    # the dominant kernel against the probe of its own access shape
+    probe = PROBE_OF.get((dom, w.g_dtype)) or PROBE_OF.get((dom, None))
+    if probe in ceil["probes"]:
+        c = ceil["probes"][probe]["GBps"]
+        out["roofline"].update({"ceiling_probe": probe, "ceiling_GBps": c,
+                                "frac_of_ceiling": round(achieved / c, 4)})
+    for kernels in (out["kernels"], out["state16_schedule"]["kernels"]):
+        for k, ent in kernels.items():
+            pr = PROBE_OF.get((k, w.g_dtype)) or PROBE_OF.get((k, None))
+            if pr in ceil["probes"] and "alg_GBps" in ent:
+                ent["frac_of_ceiling"] = round(ent["alg_GBps"] / ceil["probes"][pr]["GBps"], 4)
+    pr = PROBE_OF.get(("adam_warmup", w.g_dtype))
+    if warm and pr in ceil["probes"] and w.n == 8:
+        warm["frac_of_ceiling"] = round(warm["alg_GBps"] / ceil["probes"][pr]["GBps"], 4)
+    if not args.no_cpu_baseline and w.name != "gpt2_xl":
         log("[bench] CPU oracle baseline")
-        out["cpu_baseline"] = cpu_baseline(w, torch, synth, min(args.cpu_sample, w.d))
+        out["cpu_baseline"] = cpu_baseline(w, torch, synth, args.cpu_sample,
+                                           single_thread=not args.no_single_thread)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -26,6 +26,11 @@
 #ifndef OBA_S16_GRID
 #define OBA_S16_GRID 1
 #endif
+// Grid of the warm-up step: 1 = the update grid (one span per block), 0 = the
+// server grid; a tuning knob.
+#ifndef OBA_WARM_SPAN1
+#define OBA_WARM_SPAN1 1
+#endif
 
 struct oba_layout_s {
   oba::Plan plan;
@@ -314,7 +319,8 @@ int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const i
   L->geo_w = geo(P.nblk_w);
   L->geo_c = geo(P.nblk_c);
   L->geo = geo(P.nblk);
-  L->ws_worker = std::max(oba::partial_bytes(L->sig_c, P.n), oba::partial_bytes(L->sig, P.n));
+  L->ws_worker = std::max({oba::partial_bytes(L->sig_c, P.n), oba::partial_bytes(L->sig, P.n),
+                           ((size_t)std::max(P.nblk_w, P.nblk) * 8 + 255) / 256 * 256});
   L->ws_server = oba::partial_bytes(L->tau, 1);
   *out = L;
   return OBA_OK;
@@ -362,10 +368,12 @@ int warmup(oba_layout L, const void* g, int g_dtype, float* x, float* m, float* 
   OBA_TRY(check_buf(v, 16));
   oba::AdamCoef C{(float)lr, (float)beta1, (float)(1.0 - beta1), (float)beta2,
                   (float)(1.0 - beta2), (float)eta, (float)bc1, (float)bc2};
-  // several spans per block: the one-span grid measured 1 % slower here
-  const oba::Geo G = L->geo;
-  // the block partials fit the worker part of the workspace (its pieces
-  // outnumber the blocks of this grid)
+  // one span per block (the update grid) with two resident blocks per CU:
+  // 2.51 -> 2.31 ms at bert_large (same-box A/B; the server grid's four spans
+  // per block with the same cap, 2.51 ms)
+  const oba::Geo G = OBA_WARM_SPAN1 ? L->geo_w : L->geo;
+  // one binary64 partial per block of G: the worker part of the workspace is
+  // sized for them
   double* part = static_cast<double*>(ws);
   return launch("adam_warmup", stream, [&] {
     oba::launch_adam_warmup(G, g, g_dtype, x, m, v, C, part, vnorm, stream);
@@ -808,11 +816,12 @@ int oba_adam_warmup_step_listed(oba_layout L, oba_tensors H, float* m, float* v,
   }
   oba::AdamCoef C{(float)lr, (float)beta1, (float)(1.0 - beta1), (float)beta2,
                   (float)(1.0 - beta2), (float)eta, (float)bc1, (float)bc2};
-  const oba::Geo G = L->geo;
+  // the grid of oba_adam_warmup_step, with its block table of the tensors
+  const oba::Geo G = OBA_WARM_SPAN1 ? L->geo_w : L->geo;
   double* part = static_cast<double*>(ws);
   return launch("adam_warmup", stream, [&] {
-    oba::launch_adam_warmup_listed(G, H->tl_s, H->g_dtype, m, v, C, part, vnorm,
-                                   stream);
+    oba::launch_adam_warmup_listed(G, OBA_WARM_SPAN1 ? H->tl_w : H->tl_s, H->g_dtype, m, v, C,
+                                   part, vnorm, stream);
   });
 }
 

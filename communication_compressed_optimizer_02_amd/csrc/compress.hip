@@ -3,8 +3,10 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "device.hpp"
+#include "occupancy.hpp"
 
 namespace oba {
 
@@ -276,6 +278,268 @@ __device__ __forceinline__ void compress_body(Geo G, int32_t i0, const GT* __res
   }
 }
 
+// The same pass for blocks of several spans (the grid of the 16-bit-state
+// pass): the block's piece cursors and each worker's scale stay in registers
+// (reloaded only when a piece ends, with the next piece peeked before the
+// span's stores), and a span's arithmetic has a fast path for spans inside
+// one piece apart from the general one.  In compress_body a table load issued
+// after a worker's or a span's stores is waited for before the next worker or
+// span proceeds, which waits for those stores too (one counter tracks loads
+// and stores in issue order): 16-bit-state pass 3.27 -> 2.87 ms at bert_large.
+// The binary32 pass at one span per block measured 1-5 % slower in this form
+// (same-box A/B), so it keeps compress_body.
+template <typename GT, typename CT, int NB, int MODE, bool TL>
+__device__ __forceinline__ void compress_body_spans(Geo G, int32_t i0, const GT* __restrict__ g,
+                                              float* __restrict__ m,  // read; written by kDeferredLocal
+                                              CT* __restrict__ delta,
+                                              uint8_t* __restrict__ wbytes, SegDev sig,
+                                              double* __restrict__ part,
+                                              const float* __restrict__ wscale, float b1,
+                                              float omb1, MomSrc ms, TList tl) {
+  __shared__ double lds[kWaves * NB];
+  const int32_t b = blockIdx.x;
+  i0 += blockIdx.y * NB;  // this block's workers: [i0, i0 + NB)
+  const int64_t s_lo = dspan(G, b), s_hi = dspan(G, b + 1);
+  static_assert(!TL || MODE >= kDeferred, "tensor lists: deferred passes only");
+  static_assert(__is_same(CT, float) || MODE == kDeferred || MODE == kDeferredM,
+                "16-bit state rows: the deferred passes with the shared momentum only");
+  TCur tcur{};  // tensor cursor (tensor lists)
+  if constexpr (TL) tcur = tcur_start(tl, b);
+  // worker pieces; each worker's scale of the current piece's segment, kept
+  // in registers and reloaded only when the piece changes (a reload per
+  // worker would be a load after the previous worker's stores)
+  PCur pc = pcur_start(sig, b);
+  float sw[NB];
+  auto load_scales = [&]() {
+    if (MODE != kNorm) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) sw[i] = wscale[(int64_t)(i0 + i) * sig.n_seg + pc.js];
+    }
+  };
+  load_scales();
+  // kDeferredM: cursor over the server segments (on this grid) and sbar of
+  // the current one
+  PCur tc{};
+  float sbar = 0.0f;
+  if (MODE == kDeferredM) {
+    tc = pcur_start(ms.tau, b);
+    sbar = ms.sscale[tc.js];
+  }
+  const int64_t rowbytes = G.W * 8;
+  double acc[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) acc[i] = 0.0;
+
+  // a block inside one worker piece (and one server piece) has every full
+  // span inside it: known from the block's piece range alone
+  const bool one_piece = pc.end - pc.p == 1;
+  const bool one_tpiece = MODE != kDeferredM || tc.end - tc.p == 1;
+  for (int64_t s = s_lo; s < s_hi; ++s) {
+    const int64_t lo = s * kSpan;
+    const int64_t hi = min(lo + kSpan, G.d);
+    const Quads q = quads(lo);
+    const bool full = lo + kSpan <= G.d;
+    int32_t jseg[8];
+    LaneT lt{};
+    if constexpr (TL) {
+      tcur_advance(tl, tcur, lo);
+      lt = lane_tensors(tl, tcur, q, min(lo + kSpan, G.d), G.d);
+    }
+    // every load of the span first (all NB workers), then the arithmetic
+    float mv[8];
+    uint32_t mbits = 0;  // kDeferredM: the last server message's sign bits
+    if (MODE == kDeferredM) {
+      mbits = full ? load_sign_bits<true, OBA_PAIRS_CMP>(ms.sbytes, q, G.d)
+                   : load_sign_bits<false, OBA_PAIRS_CMP>(ms.sbytes, q, G.d);
+    } else if (MODE == kDeferredLocal) {  // per-worker rows, loaded with g below
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mv[j] = 0.0f;
+    } else if (full) {
+      load_full(m, q, mv);
+    } else {
+      load_tail(m, q, G.d, mv);
+    }
+    // the next pieces, used after the span's stores (blocks of several spans)
+    PNext pnx{}, tnx{};
+    if (s + 1 < s_hi) {
+      pnx = pcur_peek(pc, sig);
+      if (MODE == kDeferredM) tnx = pcur_peek(tc, ms.tau);
+    }
+    double fs[NB];
+    bool uniform = true;  // span inside the current piece
+    // workers in batches of NBB: all loads of a batch, then its arithmetic
+    // and stores (NBB < NB trades loads in flight per wave for occupancy)
+    constexpr int kBatch = __is_same(CT, float) ? kWorkerBatch : kWorkerBatch16;
+    // buffer-resource loads and stores in the deferred passes (the explicit
+    // passes keep the plain form: their read-only norm pass ran 1.6x slower
+    // through buffers)
+    constexpr bool kBuf = OBA_BUF != 0 && MODE >= kDeferred;
+    constexpr int NBB = NB < kBatch ? NB : kBatch;
+#pragma unroll
+    for (int ib = 0; ib < NB; ib += NBB) {
+      constexpr int NBL = MODE == kDeferredLocal ? NBB : 1;  // per-worker m rows
+      float gv[NBB][8], c[NBB][8], ml[NBL][8];
+      uint32_t h16[NBB][4];  // a 16-bit state row's patterns
+      // ib + u < NB is decided at compile time: a last batch may be partial
+      if (full) {
+#pragma unroll
+        for (int u = 0; u < NBB; ++u) {
+          if (ib + u >= NB) break;
+          const int64_t row = (int64_t)(i0 + ib + u) * G.ld;
+          if constexpr (TL)
+            load_listed<GT>(tl, i0 + ib + u, lt, true, gv[u]);
+          else if constexpr (kBuf)
+            load_full_buf(g + row, lo, gv[u]);
+          else
+            load_full(g + row, q, gv[u]);
+          if constexpr (kBuf)
+            load_full_buf(delta + row, lo, c[u]);
+          else
+            load_full(delta + row, q, c[u]);
+          if (MODE == kDeferredLocal) load_full(m + row, q, ml[u]);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < NBB; ++u) {
+          if (ib + u >= NB) break;
+          const int64_t row = (int64_t)(i0 + ib + u) * G.ld;
+          if constexpr (TL)
+            load_listed<GT>(tl, i0 + ib + u, lt, false, gv[u]);
+          else
+            load_tail(g + row, q, G.d, gv[u]);
+          load_tail(delta + row, q, G.d, c[u]);
+          if (MODE == kDeferredLocal) load_tail(m + row, q, G.d, ml[u]);
+        }
+      }
+      // The batch's arithmetic and stores.  FAST (a full span inside one
+      // worker piece and, for the implicit momentum, one server piece --
+      // nearly every span) takes the scales from registers; the general path
+      // looks each coordinate's segment up.  Kept apart, so that no load of
+      // the general path is pending where the fast path continues (a wait
+      // for it there would also wait for the stores issued before it: one
+      // counter tracks loads and stores in issue order).
+      auto work = [&](auto fast_tag) {
+        constexpr bool FAST = decltype(fast_tag)::value;
+        if (ib == 0) {
+          if (!FAST && MODE != kNorm && !uniform) lane_segs(sig.off, pc.js, q, G.d, jseg);
+          if (MODE == kDeferredM) {  // m = sbar*sign from the last server message
+            float sb[8];
+            if (FAST || hi <= tc.hi) {
+#pragma unroll
+              for (int j = 0; j < 8; ++j) sb[j] = sbar;
+            } else {
+              int32_t jt[8];
+              lane_segs(ms.tau.off, tc.js, q, G.d, jt);
+#pragma unroll
+              for (int j = 0; j < 8; ++j) sb[j] = ms.sscale[jt[j]];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              mv[j] = (!FAST && !full && coord(q, j) >= G.d)
+                          ? 0.0f
+                          : (((mbits >> j) & 1u) ? -sb[j] : sb[j]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < NBB; ++u) {
+          const int i = ib + u;
+          if (i >= NB) break;
+          const int64_t row = (int64_t)(i0 + i) * G.ld;
+          float sv[8];
+          if (MODE != kNorm) {
+            if (FAST || uniform) {
+#pragma unroll
+              for (int j = 0; j < 8; ++j) sv[j] = sw[i];
+            } else {
+              const float* sc = wscale + (int64_t)(i0 + i) * sig.n_seg;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) sv[j] = sc[jseg[j]];
+            }
+          }
+          if (MODE >= kDeferred) {  // c[u] holds c' of the last step
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[u][j] = residual(c[u][j], sv[j]);
+            if (!FAST && !full) {  // coordinates past d read as 0 and must stay 0 (no bit, no c^2)
+#pragma unroll
+              for (int j = 0; j < 8; ++j)
+                if (coord(q, j) >= G.d) c[u][j] = 0.0f;
+            }
+          }
+          if (MODE == kDeferredLocal) {
+            // the same two products and two adds as compensate(), m_i kept
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              ml[u][j] = b1 * ml[u][j] + omb1 * gv[u][j];
+              c[u][j] = ml[u][j] + c[u][j];
+            }
+            store8(m + row, q, G.d, FAST || full, ml[u]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[u][j] = compensate(b1, omb1, mv[j], gv[u][j], c[u][j]);
+            round_to_row<CT>(c[u], h16[u]);  // a 16-bit state: c as the row holds it
+          }
+          if (MODE != kNorm) store_sign_bits(wbytes + (int64_t)(i0 + i) * rowbytes, q, sign_bits(c[u]), rowbytes);
+          if (MODE >= kDeferred) {
+            if (kBuf && (FAST || full))
+              store_full_buf(delta + row, lo, c[u], h16[u]);
+            else
+              store_row(delta + row, q, G.d, FAST || full, c[u], h16[u]);
+          }
+          fs[i] = (MODE != kApply) ? sumsq8(c[u]) : 0.0;
+          if (MODE == kApply) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[u][j] = residual(c[u][j], sv[j]);
+            store_row(delta + row, q, G.d, FAST || full, c[u], h16[u]);
+          }
+        }
+      };
+      if (ib == 0) uniform = one_piece || hi <= pc.hi;
+      if (full && uniform && (one_tpiece || hi <= tc.hi))
+        work(std::true_type{});
+      else
+        work(std::false_type{});
+    }
+    const int32_t p0 = pc.p;
+    if (MODE == kApply) {
+      pcur_advance(pc, sig, pnx, hi);
+    } else if (uniform) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) acc[i] += fs[i];
+      if (hi == pc.hi) {
+        flush_rows<NB>(acc, NB, part + (int64_t)i0 * sig.n_pieces + pc.p, sig.n_pieces, lds);
+        pcur_advance(pc, sig, pnx, hi);
+      }
+    } else {  // span crosses piece boundaries: sum this lane's c piece by piece
+      int64_t cur = lo;
+      while (cur < hi) {
+        const int64_t e = min(pc.hi, hi);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const int64_t row = (int64_t)(i0 + i) * G.ld;
+          if constexpr (MODE >= kDeferred)
+            acc[i] += sumsq_range(delta + row, q, cur, e);  // c was stored there
+          else
+            acc[i] += sumsq_range_c(m, g + row, delta + row, b1, omb1, q, cur, e);
+        }
+        if (pc.hi <= hi) {
+          flush_rows<NB>(acc, NB, part + (int64_t)i0 * sig.n_pieces + pc.p, sig.n_pieces, lds);
+          if (++pc.p < pc.end) {  // the rare path: load the next piece here
+            pc.hi = uni(sig.phi[pc.p]);
+            pc.js = uni(sig.pseg[pc.p]);
+          }
+        }
+        cur = e;
+      }
+    }
+    if (pc.p != p0 && pc.p < pc.end) load_scales();  // used from the next span on
+    if (MODE == kDeferredM) {
+      const int32_t t0 = tc.p;
+      pcur_advance(tc, ms.tau, tnx, hi);
+      if (tc.p != t0 && tc.p < tc.end) sbar = ms.sscale[tc.js];
+    }
+  }
+}
+
 template <typename GT, typename CT, int NB, int MODE, bool TL>
 __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(
     Geo G, int32_t i0, const GT* __restrict__ g, float* __restrict__ m, CT* __restrict__ delta,
@@ -291,25 +555,40 @@ __global__ __launch_bounds__(kBlock) OBA_CMP16_ATTR void k_compress16(
     Geo G, int32_t i0, const GT* __restrict__ g, float* __restrict__ m, CT* __restrict__ delta,
     uint8_t* __restrict__ wbytes, SegDev sig, double* __restrict__ part,
     const float* __restrict__ wscale, float b1, float omb1, MomSrc ms, TList tl) {
-  compress_body<GT, CT, NB, MODE, TL>(G, i0, g, m, delta, wbytes, sig, part, wscale, b1, omb1,
-                                      ms, tl);
+  compress_body_spans<GT, CT, NB, MODE, TL>(G, i0, g, m, delta, wbytes, sig, part, wscale, b1,
+                                            omb1, ms, tl);
 }
 
 // ---- launchers ----------------------------------------------------------------
+
+// Occupancy caps (blocks per CU, 0: none) of the deferred worker passes with
+// binary32 and with 16-bit state rows, tuning knobs (2 blocks: binary32 pass
+// 4.55 -> 5.39 ms, 16-bit pass equal at bert_large; none kept).
+#ifndef OBA_CMP_BPC
+#define OBA_CMP_BPC 0
+#endif
+#ifndef OBA_CMP16_BPC
+#define OBA_CMP16_BPC 0
+#endif
 
 template <typename GT, typename CT, int NB, int MODE, bool TL>
 static void launch_cmp(const Geo& G, int32_t i0, int groups, const void* g, const float* m,
                        void* delta, uint8_t* wbytes, const SegDev& sig, double* part,
                        const float* wscale, float b1, float omb1, const MomSrc& ms,
                        const TList& tl, hipStream_t st) {
-  if constexpr (__is_same(CT, float))
-    hipLaunchKernelGGL((k_compress<GT, CT, NB, MODE, TL>), dim3(G.nblk, groups), dim3(kBlock), 0,
-                       st, G, i0, static_cast<const GT*>(g), const_cast<float*>(m),
+  if constexpr (__is_same(CT, float)) {
+    const size_t lds = MODE >= kDeferred ? occupancy_lds(OBA_CMP_BPC) : 0;
+    allow_lds(reinterpret_cast<const void*>(&k_compress<GT, CT, NB, MODE, TL>), lds);
+    hipLaunchKernelGGL((k_compress<GT, CT, NB, MODE, TL>), dim3(G.nblk, groups), dim3(kBlock),
+                       lds, st, G, i0, static_cast<const GT*>(g), const_cast<float*>(m),
                        static_cast<CT*>(delta), wbytes, sig, part, wscale, b1, omb1, ms, tl);
-  else
+  } else {
+    const size_t lds = occupancy_lds(OBA_CMP16_BPC);
+    allow_lds(reinterpret_cast<const void*>(&k_compress16<GT, CT, NB, MODE, TL>), lds);
     hipLaunchKernelGGL((k_compress16<GT, CT, NB, MODE, TL>), dim3(G.nblk, groups), dim3(kBlock),
-                       0, st, G, i0, static_cast<const GT*>(g), const_cast<float*>(m),
+                       lds, st, G, i0, static_cast<const GT*>(g), const_cast<float*>(m),
                        static_cast<CT*>(delta), wbytes, sig, part, wscale, b1, omb1, ms, tl);
+  }
 }
 
 // Groups of GROUP workers per block, then one launch for the remainder.  A

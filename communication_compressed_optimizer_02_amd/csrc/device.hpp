@@ -573,6 +573,66 @@ __device__ __forceinline__ int64_t dspan(const Geo& G, int32_t b) {
   return (int64_t)b * G.q + min(b, G.r);
 }
 
+// A block's cursor over the pieces of one segment table: the current piece,
+// its end and its segment.  A span peeks at the next piece (pcur_peek) before
+// its own loads and steps with that (pcur_step) after its stores.  A table
+// load issued after the stores and used by the next span would make that span
+// wait for the stores to complete before its own loads go out (one counter
+// tracks loads and stores in issue order), and so would a loaded value carried
+// from one span to the next in another register.
+struct PCur {
+  int32_t p, end;  // current piece; one past the block's last piece
+  int64_t hi;      // end of piece p
+  int32_t js;      // segment of piece p
+};
+struct PNext {
+  int64_t hi;
+  int32_t js;
+};
+
+// Block-uniform values kept in scalar registers: a cursor value taken
+// through a lane read is complete where it is taken, so no later join of
+// paths has to wait for the load that produced it.
+__device__ __forceinline__ int32_t uni(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uni(int64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ PCur pcur_start(const SegDev& T, int32_t b) {
+  PCur c;
+  c.p = uni(T.blk_first[b]);
+  c.end = uni(T.blk_first[b + 1]);
+  c.hi = uni(T.phi[c.p]);
+  c.js = uni(T.pseg[c.p]);
+  return c;
+}
+
+// The piece after the current one (the current one if it is the block's last).
+__device__ __forceinline__ PNext pcur_peek(const PCur& c, const SegDev& T) {
+  const int32_t q = min(c.p + 1, c.end - 1);
+  return {T.phi[q], T.pseg[q]};
+}
+
+// Step past every piece that ends at or before hi: the first step takes the
+// peeked piece, further ones (pieces shorter than a span) load theirs.
+__device__ __forceinline__ void pcur_advance(PCur& c, const SegDev& T, const PNext& nx,
+                                             int64_t hi) {
+  if (c.p < c.end && c.hi <= hi) {
+    if (++c.p < c.end) {
+      c.hi = uni(nx.hi);
+      c.js = uni(nx.js);
+    }
+    while (c.p < c.end && c.hi <= hi) {
+      if (++c.p < c.end) {
+        c.hi = uni(T.phi[c.p]);
+        c.js = uni(T.pseg[c.p]);
+      }
+    }
+  }
+}
+
 // Segment of coordinate k, walking forward from segment j0 (k >= off[j0]).
 __device__ __forceinline__ int32_t seg_walk(const int64_t* __restrict__ off, int32_t j0,
                                             int64_t k) {

@@ -5,6 +5,7 @@
 #include <cstdint>
 
 #include "device.hpp"
+#include "occupancy.hpp"
 
 namespace oba {
 
@@ -240,13 +241,24 @@ void launch_residual(const Geo& G, const float* src, int64_t src_ld, float* dst,
                      dst_ld, scale, T);
 }
 
+// Occupancy cap of the deferred server pass (blocks per CU, 0: none), a
+// tuning knob (3 blocks: 0.53 -> 0.71 ms, 4: 0.60 ms at bert_large; none
+// kept).
+#ifndef OBA_SRV_BPC
+#define OBA_SRV_BPC 0
+#endif
+
 template <bool DEFERRED>
 static void launch_server_t(const Geo& G, const uint8_t* wbytes, const float* wscale, float* eps,
                             uint8_t* sbytes, const SegDev& sig, const SegDev& tau, double* part,
                             const float* sscale_prev, hipStream_t st) {
-#define OBA_SERVER_LAUNCH(NB)                                                                  \
-  hipLaunchKernelGGL((k_server_p1<NB, DEFERRED>), dim3(G.nblk), dim3(kBlock), 0, st, G, wbytes, \
-                     wscale, eps, sbytes, sig, tau, part, sscale_prev)
+  const size_t lds = DEFERRED ? occupancy_lds(OBA_SRV_BPC) : 0;
+#define OBA_SERVER_LAUNCH(NB)                                                                   \
+  do {                                                                                          \
+    allow_lds(reinterpret_cast<const void*>(&k_server_p1<NB, DEFERRED>), lds);                 \
+    hipLaunchKernelGGL((k_server_p1<NB, DEFERRED>), dim3(G.nblk), dim3(kBlock), lds, st, G,    \
+                       wbytes, wscale, eps, sbytes, sig, tau, part, sscale_prev);               \
+  } while (0)
   switch (G.n) {
     case 1: OBA_SERVER_LAUNCH(1); break;
     case 2: OBA_SERVER_LAUNCH(2); break;

@@ -5,6 +5,7 @@
 #include <cstdint>
 
 #include "device.hpp"
+#include "occupancy.hpp"
 
 namespace oba {
 
@@ -14,6 +15,72 @@ namespace oba {
 // are loaded together (NB = n for n <= 8; larger n loops over groups of 8),
 // after m, v and x, so that all of a span's loads are in flight at once.
 // ===========================================================================
+
+// A span's loads: m, v, x, then the gradient rows, summed in worker order.
+// FULL (the span lies inside [0, d)) takes unchecked vector loads; the tail
+// span checks every element.  The whole span is one branch: with a branch per
+// row, each row's loads (16-bit rows are decoded as they arrive) would wait
+// before the next row is requested, leaving one row in flight per wave.
+template <bool FULL, typename GT, int NB, bool TL>
+__device__ __forceinline__ void warm_span_loads(const Geo& G, const GT* __restrict__ g,
+                                                const float* __restrict__ x,
+                                                const float* __restrict__ m,
+                                                const float* __restrict__ v, const TList& tl,
+                                                const LaneT& lt, const Quads& q, int64_t lo,
+                                                float (&mv)[8], float (&vv)[8], float (&xv)[8],
+                                                float (&sum)[8]) {
+  constexpr bool BUF = OBA_BUF_MISC != 0;
+  if constexpr (FULL) {
+    if constexpr (BUF) {
+      load_full_buf(m, lo, mv);
+      load_full_buf(v, lo, vv);
+    } else {
+      load_full(m, q, mv);
+      load_full(v, q, vv);
+    }
+    if constexpr (TL)
+      load_listed_x_q<false>(tl, lt, xv);
+    else if constexpr (BUF)
+      load_full_buf(x, lo, xv);
+    else
+      load_full(x, q, xv);
+  } else {
+    load_tail(m, q, G.d, mv);
+    load_tail(v, q, G.d, vv);
+    if constexpr (TL)
+      load_listed_x_q<true>(tl, lt, xv);
+    else
+      load_tail(x, q, G.d, xv);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sum[j] = 0.0f;
+  // rows past n are clamped to a valid row and their terms skipped
+  auto group = [&](int32_t i0) {
+    float gv[NB][8];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int64_t row = min(i0 + u, G.n - 1);
+      if constexpr (TL)
+        load_listed_q<!FULL, GT>(tl, row, lt, gv[u]);
+      else if constexpr (FULL)
+        load_full(g + row * G.ld, q, gv[u]);
+      else
+        load_tail(g + row * G.ld, q, G.d, gv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      if (i0 + u < G.n) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sum[j] = sum[j] + gv[u][j];
+      }
+  };
+  if (G.n <= NB) {
+    group(0);  // straight-line: a loop here would wait for every load at its head
+  } else {
+    for (int32_t i0 = 0; i0 < G.n; i0 += NB) group(i0);
+  }
+}
+
 template <typename GT, int NB, bool NORM, bool TL>
 __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restrict__ g,
                                                         float* __restrict__ x,
@@ -39,32 +106,10 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
       tcur_advance(tl, tcur, lo);
       lt = lane_tensors(tl, tcur, q, min(lo + kSpan, G.d), G.d);
     }
-    constexpr bool BUF = OBA_BUF_MISC != 0;
-    load8b<BUF>(m, q, lo, G.d, full, mv);
-    load8b<BUF>(v, q, lo, G.d, full, vv);
-    if constexpr (TL)
-      load_listed_x(tl, lt, full, xv);
+    if (full)
+      warm_span_loads<true, GT, NB, TL>(G, g, x, m, v, tl, lt, q, lo, mv, vv, xv, sum);
     else
-      load8b<BUF>(x, q, lo, G.d, full, xv);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sum[j] = 0.0f;
-    for (int32_t i0 = 0; i0 < G.n; i0 += NB) {  // one pass when n <= NB
-      // rows past n are clamped to a valid row and their terms skipped
-      float gv[NB][8];
-#pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        if constexpr (TL)
-          load_listed<GT>(tl, min(i0 + u, G.n - 1), lt, full, gv[u]);
-        else
-          load8b<BUF>(g + (int64_t)min(i0 + u, G.n - 1) * G.ld, q, lo, G.d, full, gv[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < NB; ++u)
-        if (i0 + u < G.n) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) sum[j] = sum[j] + gv[u][j];
-        }
-    }
+      warm_span_loads<false, GT, NB, TL>(G, g, x, m, v, tl, lt, q, lo, mv, vv, xv, sum);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float gb = pow2 ? sum[j] * inv_n : sum[j] / nf;  // identical for n = 2^k
@@ -74,6 +119,7 @@ __global__ __launch_bounds__(kBlock) void k_adam_warmup(Geo G, const GT* __restr
       vv[j] = vk;
       xv[j] = xv[j] - (C.lr * (mk / C.bc1)) / (__builtin_sqrtf(vk / C.bc2) + C.eta);
     }
+    constexpr bool BUF = OBA_BUF_MISC != 0;
     store8b<BUF>(m, q, lo, G.d, full, mv);
     store8b<BUF>(v, q, lo, G.d, full, vv);
     if constexpr (TL)
@@ -128,12 +174,23 @@ __global__ __launch_bounds__(kBlock) void k_freeze(Geo G, const float* __restric
 
 void launch_norm_finalize(const double* part, int32_t n, double* out, hipStream_t st);
 
+// Occupancy cap of the warm-up step (blocks per CU, 0: none), a tuning knob:
+// with one span per block, 2 blocks per CU took the step from 2.42 to 2.31 ms
+// at bert_large (3: 2.37 ms; same-box A/B); loading the gradient rows before
+// m, v, x was slower (2.63 vs 2.49 ms on the server grid).
+#ifndef OBA_WARM_BPC
+#define OBA_WARM_BPC 2
+#endif
 template <typename GT, bool NORM, bool TL>
 static void launch_warmup_nb(const Geo& G, const void* g, float* x, float* m, float* v,
                              const AdamCoef& C, double* part, const TList& tl, hipStream_t st) {
-#define OBA_WARMUP_LAUNCH(NB)                                                                 \
-  hipLaunchKernelGGL((k_adam_warmup<GT, NB, NORM, TL>), dim3(G.nblk), dim3(kBlock), 0, st, G, \
-                     static_cast<const GT*>(g), x, m, v, C, part, tl)
+  const size_t lds = occupancy_lds(OBA_WARM_BPC);
+#define OBA_WARMUP_LAUNCH(NB)                                                                   \
+  do {                                                                                          \
+    allow_lds(reinterpret_cast<const void*>(&k_adam_warmup<GT, NB, NORM, TL>), lds);           \
+    hipLaunchKernelGGL((k_adam_warmup<GT, NB, NORM, TL>), dim3(G.nblk), dim3(kBlock), lds, st, \
+                       G, static_cast<const GT*>(g), x, m, v, C, part, tl);                     \
+  } while (0)
   switch (G.n) {
     case 1: OBA_WARMUP_LAUNCH(1); break;
     case 2: OBA_WARMUP_LAUNCH(2); break;

@@ -42,6 +42,26 @@ def test_status_strings():
     assert "scratch" in binding.status_string(-7)
 
 
+def test_hbm_probe_library_loads_and_describes_its_shapes():
+    """libhbmstream.so (the streaming probes behind bench.py's HBM ceiling)
+    exports its two calls; the shape table answers on the host and a bad
+    launch is refused on the host (nothing reaches a device)."""
+    import bench
+
+    lib = bench.probe_lib()
+    info = (ctypes.c_int32 * 5)()
+    for name, (shape, _) in bench.PROBES.items():
+        assert lib.hbm_stream_shape(shape, info) == 0, name
+        na, ab, nb, bb, mode = list(info)
+        assert na + nb > 0 and ab in (2, 4) and bb in (2, 4) and mode in (0, 1, 2), name
+    assert lib.hbm_stream_shape(len(bench.PROBES), info) == -1
+    P = ctypes.c_void_p
+    # unknown shape, misaligned buffer, ld too small: refused before any HIP call
+    assert lib.hbm_stream_launch(99, 0, P(16), P(16), 2048, 1, 1, 0, P(16), P(None)) == -1
+    assert lib.hbm_stream_launch(2, 0, P(17), P(16), 2048, 1, 1, 0, P(16), P(None)) == -1
+    assert lib.hbm_stream_launch(2, 0, P(16), P(16), 2040, 1, 1, 0, P(16), P(None)) == -1
+
+
 @pytest.mark.parametrize("case,expect", [
     (dict(d=100, n=2, wseg=[0, 100], sseg=[0, 50, 100]), 0),
     (dict(d=100, n=2, wseg=[0, 100], sseg=[0, 50, 100], ld=104), 0),
