@@ -585,7 +585,8 @@ def hbm_ceiling(torch, w, reps=5):
         b.uniform_(0.5, 1.0, generator=gen)
         nbytes = groups * ld * (na * ab + nb * bb * (2 if bmode == 2 else 1))
         res = {"bytes_per_launch": nbytes, "GBps": 0.0}
-        for buf in (0, 1):
+        forms = (0, 1, 2, 3) if (bmode == 2 and na == nb) else (0, 1)
+        for buf in forms:
             for bpc in PROBE_BPC:
                 def go():
                     return lib.hbm_stream_launch(shape, buf, ctypes.c_void_p(a.data_ptr()),
@@ -603,10 +604,11 @@ def hbm_ceiling(torch, w, reps=5):
                 e1.record()
                 torch.cuda.synchronize()
                 gbs = round(nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 1)
-                res[f"{'buffer' if buf else 'global'}_bpc{bpc}"] = gbs
+                form = ("buffer" if buf & 1 else "global") + (", rows alternating" if buf & 2 else "")
+                res[f"{form}, bpc{bpc}"] = gbs
                 if gbs > res["GBps"]:
                     res["GBps"] = gbs
-                    res["best"] = f"{'buffer' if buf else 'global'}, " + (
+                    res["best"] = f"{form}, " + (
                         f"{bpc} blocks per CU" if bpc else "occupancy as registers allow")
         out[name] = res
         del a, b
@@ -614,7 +616,7 @@ def hbm_ceiling(torch, w, reps=5):
     return {"probes": out, "rows": ld,
             "note": "streaming probes (calib/hbm_stream.hip) in the kernels' lane layout, "
                     "non-temporal, all loads of a block before its stores, random data; GBps = "
-                    "the best over load forms and occupancy caps"}
+                    "the best over load forms, load orders and occupancy caps"}
 
 
 # ---- profile summaries (profiles/*.md) from raw rocprofv3 output -----------
@@ -681,13 +683,16 @@ def _role(short, n=None):
         return {("false", "true"): "decompress_update", ("true", "true"):
                 "decompress_update (m written)", ("true", "false"): "server_momentum"}.get(
                     (m.group(1), m.group(2)), "")
-    m = re.match(r"oba::k_stream<([^,]+), ([^,]+), (\d+), (\d+), (\d), (true|false)>", short)
+    m = re.match(r"oba::k_stream<([^,]+), ([^,]+), (\d+), (\d+), (\d), (true|false), "
+                 r"(true|false)>", short)
     if m:
         ta, tb = (2 if "short" in x else 4 for x in (m.group(1), m.group(2)))
         key = (int(m.group(3)), ta, int(m.group(4)), tb, int(m.group(5)))
+        form = ("buffer" if m.group(6) == "true" else "global") + (
+            ", rows alternating" if m.group(7) == "true" else "")
         for nm, shp in _probe_shapes().items():
             if shp == key:
-                return f"probe {nm} ({'buffer' if m.group(6) == 'true' else 'global'})"
+                return f"probe {nm} ({form})"
         return "probe"
     for pat, r in (("oba::k_residual", "server_p2"), ("oba::k_adam_warmup", "adam_warmup"),
                    ("oba::k_freeze", "freeze"), ("oba::k_norm_finalize", "variance norm sum"),

@@ -25,8 +25,9 @@
 //     a: [groups * rows_a][ld] elements, b: [groups * rows_b][ld] elements,
 //     16-byte aligned; ld % 8 == 0 and ld >= spans * 2048; sink: one float
 //     (written only by a read-only probe, and only in the improbable case
-//     that its loaded values sum to a chosen constant).  buf != 0: buffer
-//     forms.  blocks_per_cu > 0 caps the resident blocks per compute unit
+//     that its loaded values sum to a chosen constant).  buf: bit 0 the
+//     buffer forms, bit 1 the worker passes' load order (A and B rows
+//     alternating; for read-and-write shapes with as many A as B rows).  blocks_per_cu > 0 caps the resident blocks per compute unit
 //     (each block takes 1/blocks_per_cu of the CU's LDS, unused), i.e. the
 //     waves per SIMD, since a block is one wave per SIMD; 0 leaves the cap to
 //     the kernel's registers.  Enqueues one launch on `stream`; returns 0, -1
@@ -63,7 +64,10 @@ __device__ __forceinline__ void probe_store(T* row, const Quads& q, int64_t lo, 
     store_row(row, q, lo + kSpan, true, v, h);
 }
 
-template <typename TA, typename TB, int NA, int NB, int BMODE, bool BUF>
+// ILV (read-and-write shapes with as many A as B rows): the loads alternate
+// A row u, B row u -- the worker passes' order (gradient, then state, worker
+// by worker) -- instead of all A rows, then all B rows.
+template <typename TA, typename TB, int NA, int NB, int BMODE, bool BUF, bool ILV>
 __global__ __launch_bounds__(kBlock) void k_stream(const TA* __restrict__ a, TB* __restrict__ b,
                                                    int64_t ld, float* __restrict__ sink) {
   const int64_t lo = (int64_t)blockIdx.x * kSpan;
@@ -72,11 +76,19 @@ __global__ __launch_bounds__(kBlock) void k_stream(const TA* __restrict__ a, TB*
   TB* br = b + (int64_t)blockIdx.y * NB * ld;
   float va[NA > 0 ? NA : 1][8];
   float vb[NB > 0 ? NB : 1][8];
+  if constexpr (ILV && BMODE == kRmw && NA == NB) {
 #pragma unroll
-  for (int u = 0; u < NA; ++u) probe_load(ar + u * ld, q, lo, BUF, va[u]);
-  if constexpr (BMODE == kRmw) {
+    for (int u = 0; u < NA; ++u) {
+      probe_load(ar + u * ld, q, lo, BUF, va[u]);
+      probe_load(br + u * ld, q, lo, BUF, vb[u]);
+    }
+  } else {
 #pragma unroll
-    for (int u = 0; u < NB; ++u) probe_load(br + u * ld, q, lo, BUF, vb[u]);
+    for (int u = 0; u < NA; ++u) probe_load(ar + u * ld, q, lo, BUF, va[u]);
+    if constexpr (BMODE == kRmw) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) probe_load(br + u * ld, q, lo, BUF, vb[u]);
+    }
   }
   if constexpr (BMODE == kNone) {
     float s = 0.0f;
@@ -119,24 +131,33 @@ constexpr Shape kShapes[] = {
 };
 constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 
-template <typename TA, typename TB, int NA, int NB, int BMODE>
-int launch_t(bool buf, const void* a, void* b, int64_t ld, int64_t spans, int32_t groups,
-             size_t lds, float* sink, hipStream_t st) {
+template <typename TA, typename TB, int NA, int NB, int BMODE, bool ILV>
+int launch_t2(bool buf, const void* a, void* b, int64_t ld, int64_t spans, int32_t groups,
+              size_t lds, float* sink, hipStream_t st) {
   const dim3 grid((unsigned)spans, (unsigned)groups);
   const TA* pa = static_cast<const TA*>(a);
   TB* pb = static_cast<TB*>(b);
-  const void* fn = buf ? reinterpret_cast<const void*>(&k_stream<TA, TB, NA, NB, BMODE, true>)
-                       : reinterpret_cast<const void*>(&k_stream<TA, TB, NA, NB, BMODE, false>);
+  const void* fn =
+      buf ? reinterpret_cast<const void*>(&k_stream<TA, TB, NA, NB, BMODE, true, ILV>)
+          : reinterpret_cast<const void*>(&k_stream<TA, TB, NA, NB, BMODE, false, ILV>);
   if (lds > 0 &&
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return -5;
   if (buf)
-    hipLaunchKernelGGL((k_stream<TA, TB, NA, NB, BMODE, true>), grid, dim3(kBlock), lds, st, pa,
-                       pb, ld, sink);
+    hipLaunchKernelGGL((k_stream<TA, TB, NA, NB, BMODE, true, ILV>), grid, dim3(kBlock), lds, st,
+                       pa, pb, ld, sink);
   else
-    hipLaunchKernelGGL((k_stream<TA, TB, NA, NB, BMODE, false>), grid, dim3(kBlock), lds, st, pa,
-                       pb, ld, sink);
+    hipLaunchKernelGGL((k_stream<TA, TB, NA, NB, BMODE, false, ILV>), grid, dim3(kBlock), lds,
+                       st, pa, pb, ld, sink);
   return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+template <typename TA, typename TB, int NA, int NB, int BMODE>
+int launch_t(int buf, const void* a, void* b, int64_t ld, int64_t spans, int32_t groups,
+             size_t lds, float* sink, hipStream_t st) {
+  if (buf & 2)
+    return launch_t2<TA, TB, NA, NB, BMODE, true>(buf & 1, a, b, ld, spans, groups, lds, sink, st);
+  return launch_t2<TA, TB, NA, NB, BMODE, false>(buf & 1, a, b, ld, spans, groups, lds, sink, st);
 }
 
 }  // namespace
@@ -178,7 +199,8 @@ int hbm_stream_launch(int shape, int buf, const void* a, void* b, int64_t ld, in
     lds = (size_t)(per_cu / blocks_per_cu) / 512 * 512;
     if (lds == 0 || (int)lds > per_block) return -1;
   }
-  const bool bf = buf != 0;
+  if (buf < 0 || buf > 3) return -1;
+  const int bf = buf;
   switch (shape) {
     case 0: return launch_t<float, float, 8, 0, kNone>(bf, a, b, ld, spans, groups, lds, sink, st);
     case 1: return launch_t<float, float, 0, 8, kWrite>(bf, a, b, ld, spans, groups, lds, sink, st);

@@ -321,7 +321,7 @@ int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const i
   L->geo = geo(P.nblk);
   L->ws_worker = std::max({oba::partial_bytes(L->sig_c, P.n), oba::partial_bytes(L->sig, P.n),
                            ((size_t)std::max(P.nblk_w, P.nblk) * 8 + 255) / 256 * 256});
-  L->ws_server = oba::partial_bytes(L->tau, 1);
+  L->ws_server = std::max(oba::partial_bytes(L->tau, 1), oba::partial_bytes(L->tau_c, 1));
   *out = L;
   return OBA_OK;
 }
@@ -634,17 +634,24 @@ int oba_server_reduce_recompress_deferred(oba_layout L, const uint64_t* wbits,
   OBA_TRY(check_buf(sscale, 4));
   OBA_TRY(check_buf(ws, 8));
   if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
-  const oba::Geo G = L->geo;
+#ifndef OBA_SRV_GRID1
+#define OBA_SRV_GRID1 0
+#endif
+  // grid: the server grid (several spans per block), or (OBA_SRV_GRID1) the
+  // compress grid with its tables
+  const bool g1 = OBA_SRV_GRID1 != 0;
+  const oba::Geo G = g1 ? L->geo_c : L->geo;
+  const oba::SegDev& sig = g1 ? L->sig_c : L->sig;
+  const oba::SegDev& tau = g1 ? L->tau_c : L->tau;
   double* part = reinterpret_cast<double*>(static_cast<char*>(ws) +
                                            ((L->ws_worker + 255) / 256) * 256);
   const uint8_t* wbytes = reinterpret_cast<const uint8_t*>(wbits);
   uint8_t* sbytes = reinterpret_cast<uint8_t*>(sbits);
   OBA_TRY(launch("server_deferred", stream, [&] {
-    oba::launch_server_deferred(G, wbytes, wscale, a, sbytes, L->sig, L->tau, part, sscale,
-                                stream);
+    oba::launch_server_deferred(G, wbytes, wscale, a, sbytes, sig, tau, part, sscale, stream);
   }));
   return launch("finalize_scales", stream,
-                [&] { oba::launch_finalize(part, 1, L->tau, sscale, stream); });
+                [&] { oba::launch_finalize(part, 1, tau, sscale, stream); });
 }
 
 int oba_deferred_errors(oba_layout L, const float* c, const float* wscale, const float* a,

@@ -81,7 +81,15 @@ __global__ __launch_bounds__(kBlock) OBA_SRV_ATTR void k_server_p1(Geo G, const 
   // OBA_SRV_LDS: a span's NB packed rows (256 bytes each) are staged in LDS
   // with 8-byte loads, then each lane reads its two bytes per row there
   // (measured 6 % faster than a byte load per lane and row plus a swap)
-  __shared__ uint2 rows_lds[OBA_SRV_LDS ? NB * 32 : 1];
+  // OBA_SRV_PAIR: two full spans inside one worker and one server piece are
+  // taken together (n <= NB): both spans' packed rows and a' are requested
+  // before either is used, twice the bytes in flight per wave (0.533 -> 0.504
+  // ms at bert_large, same-box A/B; with eight spans per block, 0.59 ms)
+#ifndef OBA_SRV_PAIR
+#define OBA_SRV_PAIR 1
+#endif
+  __shared__ uint2 rows2_lds[2][OBA_SRV_LDS ? NB * 32 : 1];
+  uint2* rows_lds = rows2_lds[0];
   const int32_t b = blockIdx.x;
   const int64_t s_lo = dspan(G, b), s_hi = dspan(G, b + 1);
   const int32_t ps_end = sig.blk_first[b + 1], pt_end = tau.blk_first[b + 1];
@@ -98,6 +106,85 @@ __global__ __launch_bounds__(kBlock) OBA_SRV_ATTR void k_server_p1(Geo G, const 
   double acc[1] = {0.0};
   for (int64_t s = s_lo; s < s_hi; ++s) {
     const int64_t lo = s * kSpan;
+    if (OBA_SRV_PAIR != 0 && OBA_SRV_LDS != 0 && G.n <= NB && s + 1 < s_hi &&
+        lo + 2 * kSpan <= G.d && lo + 2 * kSpan <= ps_hi && lo + 2 * kSpan <= pt_hi) {
+      const int64_t lo1 = lo + kSpan, hi1 = lo1 + kSpan;
+      const Quads q0 = quads(lo), q1 = quads(lo1);
+      const int32_t js0 = js_cur;
+      uint2 rv0 = make_uint2(0u, 0u), rv1 = make_uint2(0u, 0u);
+      if (stager) {
+        const int64_t r = min((int)(threadIdx.x >> 5), G.n - 1);
+        const uint8_t* rb = wbytes + r * rowbytes + 8 * (threadIdx.x & 31);
+        rv0 = *reinterpret_cast<const uint2*>(rb + (lo >> 3));
+        rv1 = *reinterpret_cast<const uint2*>(rb + (lo1 >> 3));
+      }
+      float a0[8], a1[8];
+      load_full(eps, q0, a0);
+      load_full(eps, q1, a1);
+      __syncthreads();  // the previous reads of the staged rows are done
+      if (stager) {
+        rows2_lds[0][threadIdx.x] = rv0;
+        rows2_lds[1][threadIdx.x] = rv1;
+      }
+      __syncthreads();
+      float sw[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) sw[u] = wscale[(int64_t)min(u, G.n - 1) * sig.n_seg + js0];
+      const float sp = DEFERRED ? sscale_prev[jt_cur] : 0.0f;
+      const uint32_t sh = (threadIdx.x & 1) ? 4u : 0u;
+      // the single span's operations, in its order, for each of the two
+      auto one = [&](const uint2* rows, float (&av)[8]) {
+        const uint8_t* lb = reinterpret_cast<const uint8_t*>(rows);
+        float t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[j] = 0.0f;
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          const uint32_t ba = lb[u * 256 + (threadIdx.x >> 1)];
+          const uint32_t bb = lb[u * 256 + 128 + (threadIdx.x >> 1)];
+          const uint32_t bits = ((ba >> sh) & 0xFu) | (((bb >> sh) & 0xFu) << 4);
+          if (u < G.n) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) t[j] = t[j] + (((bits >> j) & 1u) ? -sw[u] : sw[u]);
+          }
+        }
+        if (DEFERRED) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) av[j] = residual(av[j], sp);
+        }
+        if (pow2) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) av[j] = t[j] * inv_n + av[j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) av[j] = t[j] / nf + av[j];
+        }
+      };
+      one(rows2_lds[0], a0);
+      one(rows2_lds[1], a1);
+      store8(eps, q0, G.d, true, a0);
+      store8(eps, q1, G.d, true, a1);
+      store_sign_bits(sbytes, q0, sign_bits(a0), rowbytes);
+      store_sign_bits(sbytes, q1, sign_bits(a1), rowbytes);
+      acc[0] += sumsq8(a0);
+      acc[0] += sumsq8(a1);
+      // no piece ends inside the pair; one may end at its end
+      while (ps < ps_end && ps_hi <= hi1) {
+        if (++ps < ps_end) {
+          ps_hi = sig.phi[ps];
+          js_cur = sig.pseg[ps];
+        }
+      }
+      if (hi1 == pt_hi) {
+        flush_rows<1>(acc, 1, part + pt, 0, lds);
+        if (++pt < pt_end) {
+          pt_hi = tau.phi[pt];
+          jt_cur = tau.pseg[pt];
+        }
+      }
+      ++s;  // the loop's increment passes the second span
+      continue;
+    }
     const int64_t hi = min(lo + kSpan, G.d);
     const Quads q = quads(lo);
     float a[8];

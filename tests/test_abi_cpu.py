@@ -60,6 +60,7 @@ def test_hbm_probe_library_loads_and_describes_its_shapes():
     assert lib.hbm_stream_launch(99, 0, P(16), P(16), 2048, 1, 1, 0, P(16), P(None)) == -1
     assert lib.hbm_stream_launch(2, 0, P(17), P(16), 2048, 1, 1, 0, P(16), P(None)) == -1
     assert lib.hbm_stream_launch(2, 0, P(16), P(16), 2040, 1, 1, 0, P(16), P(None)) == -1
+    assert lib.hbm_stream_launch(2, 4, P(16), P(16), 2048, 1, 1, 0, P(16), P(None)) == -1
 
 
 @pytest.mark.parametrize("case,expect", [

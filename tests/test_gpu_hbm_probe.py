@@ -21,7 +21,8 @@ def say(*a):
 @pytest.mark.parametrize("name,buf,bpc", [("copy", 0, 0), ("copy", 1, 4), ("worker_g16", 0, 0),
                                           ("worker_g16", 1, 3), ("in_place", 1, 0),
                                           ("write", 0, 8), ("state16", 1, 0),
-                                          ("warmup_g16", 0, 0), ("update", 1, 0)])
+                                          ("warmup_g16", 0, 0), ("update", 1, 0),
+                                          ("worker_g16", 2, 0), ("state16", 3, 3)])
 def test_probe_stores_what_its_shape_says(name, buf, bpc):
     t = torch()
     lib = bench.probe_lib()
