@@ -465,13 +465,36 @@ def run_listed(w, S, g_flat, args, torch, oba, synth):
             ent["alg_GBps"] = round(alg[k] * w.d / (tot / cnt * 1e-3) / 1e9, 1)
         kernels[k] = ent
     oba.timing_reset()
+    # the listed warm-up step with the variance norm, on the same tensors
+    # (after the deferred steps: it rewrites x, m and v, which they no longer need)
+    vnorm = torch.zeros(1, dtype=torch.float64, device="cuda")
+
+    def warm():
+        oba.adam_warmup_step_listed(L, TL, S.m, S.v, synth.LR, synth.BETA1, synth.BETA2,
+                                    synth.ETA, vnorm=vnorm)
+
+    for _ in range(max(1, args.warmup)):
+        warm()
+    torch.cuda.synchronize()
+    oba.timing_enable(True, 4 * max(1, args.steps))
+    for _ in range(args.steps):
+        warm()
+    torch.cuda.synchronize()
+    oba.timing_enable(False, 1)
+    tot, cnt = oba.timing_read("adam_warmup")
+    oba.timing_reset()
+    gb = 2 if w.g_dtype == "f16" else 4
+    walg = w.n * gb + 24
+    warm_ent = {"avg_ms": round(tot / cnt, 4) if cnt else None, "steps": cnt,
+                "alg_bytes_per_param": walg,
+                "alg_GBps": round(walg * w.d / (tot / cnt * 1e-3) / 1e9, 1) if cnt else None}
     TL.close()
     del TL
     S.m_implicit = False  # the listed run left S.m stale and sbits/sscale its own
     torch.cuda.empty_cache()
     return {"tensors": len(lengths), "ms_per_step": round(ms, 4), "value": w.d / (ms * 1e-3),
             "step_alg_GBps": round(sum(alg.values()) * w.d / (ms * 1e-3) / 1e9, 1),
-            "kernels": kernels}
+            "kernels": kernels, "warmup_step": warm_ent}
 
 
 def one_gpu_share(w, torch, oba, synth, steps, warmup):

@@ -31,6 +31,9 @@
 #ifndef OBA_WARM_SPAN1
 #define OBA_WARM_SPAN1 1
 #endif
+#ifndef OBA_WARM_SPAN1_TL
+#define OBA_WARM_SPAN1_TL OBA_WARM_SPAN1
+#endif
 
 struct oba_layout_s {
   oba::Plan plan;
@@ -823,11 +826,11 @@ int oba_adam_warmup_step_listed(oba_layout L, oba_tensors H, float* m, float* v,
   }
   oba::AdamCoef C{(float)lr, (float)beta1, (float)(1.0 - beta1), (float)beta2,
                   (float)(1.0 - beta2), (float)eta, (float)bc1, (float)bc2};
-  // the grid of oba_adam_warmup_step, with its block table of the tensors
-  const oba::Geo G = OBA_WARM_SPAN1 ? L->geo_w : L->geo;
+  // a grid of oba_adam_warmup_step, with its block table of the tensors
+  const oba::Geo G = OBA_WARM_SPAN1_TL ? L->geo_w : L->geo;
   double* part = static_cast<double*>(ws);
   return launch("adam_warmup", stream, [&] {
-    oba::launch_adam_warmup_listed(G, OBA_WARM_SPAN1 ? H->tl_w : H->tl_s, H->g_dtype, m, v, C,
+    oba::launch_adam_warmup_listed(G, OBA_WARM_SPAN1_TL ? H->tl_w : H->tl_s, H->g_dtype, m, v, C,
                                    part, vnorm, stream);
   });
 }

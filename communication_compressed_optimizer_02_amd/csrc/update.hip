@@ -84,12 +84,18 @@ __global__ __launch_bounds__(kBlock) void k_decompress_update(Geo G,
 #ifndef OBA_UPD_BPC
 #define OBA_UPD_BPC 3
 #endif
+// The tensor-list update (x read and written in place through the tensor
+// table) runs uncapped: the cap of 3 took it from 3.09 to 4.59 ms at gpt2_xl
+// (388 tensors; 6 blocks per CU: 3.03 ms; same-box A/B).
+#ifndef OBA_UPD_BPC_TL
+#define OBA_UPD_BPC_TL 0
+#endif
 
 template <bool WRITE_M, bool TL>
 static void launch_update_t(const Geo& G, const uint8_t* sbytes, const float* sscale,
                             const float* denom, float* m, float* x, const SegDev& tau, float lr,
                             const TList& tl, hipStream_t st) {
-  const size_t lds = occupancy_lds(OBA_UPD_BPC);
+  const size_t lds = occupancy_lds(TL ? OBA_UPD_BPC_TL : OBA_UPD_BPC);
   allow_lds(reinterpret_cast<const void*>(&k_decompress_update<WRITE_M, true, TL>), lds);
   hipLaunchKernelGGL((k_decompress_update<WRITE_M, true, TL>), dim3(G.nblk), dim3(kBlock), lds,
                      st, G, sbytes, sscale, denom, m, x, tau, lr, tl);

@@ -181,10 +181,16 @@ void launch_norm_finalize(const double* part, int32_t n, double* out, hipStream_
 #ifndef OBA_WARM_BPC
 #define OBA_WARM_BPC 2
 #endif
+// The tensor-list warm-up runs uncapped: the cap of 2 took it from 10.43 to
+// 12.6-12.9 ms at gpt2_xl (388 tensors, n = 4, binary32 gradients; 3 blocks
+// per CU: 10.50 ms; the server grid, uncapped: 10.73 ms; same-box A/B).
+#ifndef OBA_WARM_BPC_TL
+#define OBA_WARM_BPC_TL 0
+#endif
 template <typename GT, bool NORM, bool TL>
 static void launch_warmup_nb(const Geo& G, const void* g, float* x, float* m, float* v,
                              const AdamCoef& C, double* part, const TList& tl, hipStream_t st) {
-  const size_t lds = occupancy_lds(OBA_WARM_BPC);
+  const size_t lds = occupancy_lds(TL ? OBA_WARM_BPC_TL : OBA_WARM_BPC);
 #define OBA_WARMUP_LAUNCH(NB)                                                                   \
   do {                                                                                          \
     allow_lds(reinterpret_cast<const void*>(&k_adam_warmup<GT, NB, NORM, TL>), lds);           \
