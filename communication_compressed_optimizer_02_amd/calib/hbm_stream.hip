@@ -11,8 +11,9 @@
 // touched, written only, or read and written in place) per group; grid.y
 // counts the groups, so a shape with groups of 4 rows and grid.y = 2 is the
 // deferred worker pass's 8 workers in two groups of 4.  All loads of a block
-// are issued before its stores, as in the method's kernels; the values
-// stored depend on the values loaded, so no access can be elided.
+// are issued before its stores, as in the method's kernels; every stored
+// value depends on the values loaded, and every loaded row reaches a stored
+// value (a read-only probe sums all of them), so no access can be elided.
 //
 // C ABI (plain pointers, device memory of the current device):
 //   int hbm_stream_shape(int shape, int32_t out[5]);
@@ -98,12 +99,23 @@ __global__ __launch_bounds__(kBlock) void k_stream(const TA* __restrict__ a, TB*
       for (int j = 0; j < 8; ++j) s = s + va[u][j];
     if (s == 1.25e-37f) sink[0] = s;
   } else {
+    // Row u of B takes the A rows u, u + NB, u + 2 NB, ... (so that every
+    // loaded A row reaches a store and no load can be dropped), or A row
+    // u % NA when there are fewer A rows than B rows.
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float from_a = NA > 0 ? va[u % (NA > 0 ? NA : 1)][j] : (float)j;
-        vb[u][j] = (BMODE == kRmw ? vb[u][j] : 0.0f) + from_a + 1.0f;
+        float acc = BMODE == kRmw ? vb[u][j] : 0.0f;
+        if constexpr (NA == 0) {
+          acc = acc + (float)j;
+        } else if (u >= NA) {
+          acc = acc + va[u % (NA > 0 ? NA : 1)][j];
+        } else {
+#pragma unroll
+          for (int k = u; k < NA; k += NB) acc = acc + va[k][j];
+        }
+        vb[u][j] = acc + 1.0f;
       }
       probe_store(br + u * ld, q, lo, BUF, vb[u]);
     }

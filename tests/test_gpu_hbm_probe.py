@@ -1,7 +1,8 @@
 """GPU check of the streaming probes behind bench.py's HBM ceiling
 (libhbmstream.so): the bytes a probe is credited with are the bytes it moves,
 so its stores must land where and as its shape says (every element of every
-written row, each value a function of the values loaded)."""
+written row, each value a function of the values loaded), and every row it
+loads must reach a stored value (else the compiler may drop that load)."""
 import ctypes
 import sys
 
@@ -22,7 +23,8 @@ def say(*a):
                                           ("worker_g16", 1, 3), ("in_place", 1, 0),
                                           ("write", 0, 8), ("state16", 1, 0),
                                           ("warmup_g16", 0, 0), ("update", 1, 0),
-                                          ("worker_g16", 2, 0), ("state16", 3, 3)])
+                                          ("worker_g16", 2, 0), ("state16", 3, 3),
+                                          ("warmup_g16", 1, 2), ("read", 0, 0)])
 def test_probe_stores_what_its_shape_says(name, buf, bpc):
     t = torch()
     lib = bench.probe_lib()
@@ -50,13 +52,16 @@ def test_probe_stores_what_its_shape_says(name, buf, bpc):
     for gi in range(groups):
         for u in range(nb):
             r = gi * nb + u
-            if na:
-                src = af[gi * na + u % na, :n]
-            else:  # element j (0..7) of the lane's two quads: k % 4, +4 in the upper half
+            acc = b0f[r, :n].clone() if mode == 2 else t.zeros(n, device="cuda")
+            if na == 0:  # element j (0..7) of the lane's two quads: k % 4, +4 in the upper half
                 k = t.arange(n, device="cuda")
-                src = (k.remainder(4) + 4 * (k.remainder(2048) >= 1024).long()).float()
-            want = (b0f[r, :n] if mode == 2 else 0.0) + src + 1.0
-            want = want.to(dt[bb]).float()
+                acc = acc + (k.remainder(4) + 4 * (k.remainder(2048) >= 1024).long()).float()
+            elif u >= na:
+                acc = acc + af[gi * na + u % na, :n]
+            else:  # every A row reaches a stored row: u, u + nb, u + 2 nb, ... in that order
+                for kk in range(u, na, nb):
+                    acc = acc + af[gi * na + kk, :n]
+            want = (acc + 1.0).to(dt[bb]).float()
             assert t.equal(bf[r, :n], want), f"row {r}"
             assert t.equal(bf[r, n:], b0f[r, n:]), f"row {r}: past the spans"
     assert float(sink.item()) == 0.0
