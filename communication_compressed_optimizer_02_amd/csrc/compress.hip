@@ -56,6 +56,13 @@ constexpr int kWorkerBatch = OBA_WORKER_BATCH;
 #define OBA_WORKER_BATCH16 4
 #endif
 constexpr int kWorkerBatch16 = OBA_WORKER_BATCH16;
+// The 16-bit-state pass takes two full spans per iteration where a block lies
+// inside one worker piece and one server piece (1), or one span at a time (0):
+// 2.868/2.845 -> 2.854/2.820 ms at bert_large (same-box A/B, two runs each; the
+// registers stay at 2 waves per SIMD either way).
+#ifndef OBA_CMP16_PAIR
+#define OBA_CMP16_PAIR 1
+#endif
 
 // Optional occupancy targets (waves per SIMD) of the worker pass and of its
 // 16-bit-state instances, tuning knobs.
@@ -334,8 +341,88 @@ __device__ __forceinline__ void compress_body_spans(Geo G, int32_t i0, const GT*
   // span inside it: known from the block's piece range alone
   const bool one_piece = pc.end - pc.p == 1;
   const bool one_tpiece = MODE != kDeferredM || tc.end - tc.p == 1;
+
+  // Two full spans at once, in a block inside one worker piece and one
+  // server piece: both spans' loads are issued before the first span's
+  // arithmetic, so each wave has twice the bytes in flight.  Per coordinate
+  // the operations are those of the one-span fast path below, and each
+  // worker's sums of squares are added span by span in the same order.
+  constexpr bool kPair = OBA_CMP16_PAIR != 0 && !TL && (MODE == kDeferred || MODE == kDeferredM);
+  constexpr bool kBufP = OBA_BUF != 0;
+  // (one span's data per set of named arrays: arrays indexed by the span
+  // would be placed in LDS by the compiler before its loops are unrolled)
+  auto span_loads = [&](int64_t l, const Quads& q, uint32_t& mb, float(&mv)[8],
+                        float(&gv)[NB][8], float(&c)[NB][8]) {
+    if constexpr (MODE == kDeferredM)
+      mb = load_sign_bits<true, OBA_PAIRS_CMP>(ms.sbytes, q, G.d);
+    else
+      load_full(m, q, mv);
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int64_t row = (int64_t)(i0 + u) * G.ld;
+      if constexpr (kBufP) {
+        load_full_buf(g + row, l, gv[u]);
+        load_full_buf(delta + row, l, c[u]);
+      } else {
+        load_full(g + row, q, gv[u]);
+        load_full(delta + row, q, c[u]);
+      }
+    }
+  };
+  auto span_work = [&](int64_t l, const Quads& q, uint32_t mb, float(&mv)[8], float(&gv)[NB][8],
+                       float(&c)[NB][8], double(&fs)[NB]) {
+    if constexpr (MODE == kDeferredM) {  // m = sbar*sign from the last server message
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mv[j] = ((mb >> j) & 1u) ? -sbar : sbar;
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int64_t row = (int64_t)(i0 + u) * G.ld;
+      uint32_t h16[4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[u][j] = residual(c[u][j], sw[u]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[u][j] = compensate(b1, omb1, mv[j], gv[u][j], c[u][j]);
+      round_to_row<CT>(c[u], h16);
+      store_sign_bits(wbytes + (int64_t)(i0 + u) * rowbytes, q, sign_bits(c[u]), rowbytes);
+      if constexpr (kBufP)
+        store_full_buf(delta + row, l, c[u], h16);
+      else
+        store_row(delta + row, q, G.d, true, c[u], h16);
+      fs[u] = sumsq8(c[u]);
+    }
+  };
+  auto two_spans = [&](int64_t lo0) {
+    const int64_t lo1 = lo0 + kSpan;
+    const Quads qa = quads(lo0), qb = quads(lo1);
+    uint32_t mba = 0u, mbb = 0u;
+    float mva[8], mvb[8], ga[NB][8], ca[NB][8], gb[NB][8], cb[NB][8];
+    double fsa[NB], fsb[NB];
+    span_loads(lo0, qa, mba, mva, ga, ca);
+    span_loads(lo1, qb, mbb, mvb, gb, cb);
+    span_work(lo0, qa, mba, mva, ga, ca, fsa);
+    span_work(lo1, qb, mbb, mvb, gb, cb, fsb);
+#pragma unroll
+    for (int u = 0; u < NB; ++u) acc[u] += fsa[u];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) acc[u] += fsb[u];
+    const int64_t hi1 = lo1 + kSpan;
+    if (hi1 == pc.hi) {  // the block's one piece ends here
+      flush_rows<NB>(acc, NB, part + (int64_t)i0 * sig.n_pieces + pc.p, sig.n_pieces, lds);
+      pcur_advance(pc, sig, PNext{pc.hi, pc.js}, hi1);
+    }
+    if (MODE == kDeferredM) pcur_advance(tc, ms.tau, PNext{tc.hi, tc.js}, hi1);
+  };
+
   for (int64_t s = s_lo; s < s_hi; ++s) {
     const int64_t lo = s * kSpan;
+    if constexpr (kPair) {
+      if (one_piece && one_tpiece && s + 1 < s_hi && lo + 2 * kSpan <= G.d) {
+        two_spans(lo);
+        ++s;
+        continue;
+      }
+    }
     const int64_t hi = min(lo + kSpan, G.d);
     const Quads q = quads(lo);
     const bool full = lo + kSpan <= G.d;
