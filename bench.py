@@ -821,7 +821,7 @@ def summarize_profiles(raw, out_dir, workload="bert_large"):
          "    " + PROFILE_CMDS["fetch"], "    " + PROFILE_CMDS["write"], "",
          "Summary written by `python bench.py --summarize-profiles gpurun_out/prof` from those",
          "runs' counter_collection.csv files.", "",
-         "Calibration: the copy probe (`k_stream<float, float, 4, 4, 1, false>`, global form) reads",
+         "Calibration: the copy probe (`k_stream<float, float, 4, 4, 1, false, false>`, global form) reads",
          f"and writes {half / 1e9:.3f} GB per launch; it reads FETCH_SIZE = "
          f"{sum(cf) / len(cf) * 1024 / 1e9:.3f} GB and WRITE_SIZE =",
          f"{sum(cw) / len(cw) * 1024 / 1e9:.3f} GB, so FETCH_SIZE is scaled by {ff:.3f} and "
