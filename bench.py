@@ -552,9 +552,13 @@ def one_gpu_share(w, torch, oba, synth, steps, warmup):
 # Streaming probes of libhbmstream.so (calib/hbm_stream.hip): name -> (shape,
 # groups).  The worker-pass shapes take the workload's n workers in groups of
 # 4, as the deferred worker pass does; the others are fixed row counts.
+# name -> (shape, groups); groups None: the workload's n workers in groups of
+# PROBE_PER[name] (the probe is skipped when that does not divide n)
 PROBES = {"read": (0, 1), "write": (1, 1), "copy": (2, 1), "worker_g16": (3, None),
           "worker_g32": (4, None), "state16": (5, None), "warmup_g16": (6, 1),
-          "update": (7, 1), "in_place": (8, 1)}
+          "update": (7, 1), "in_place": (8, 1), "worker_g16_x1": (9, None),
+          "worker_g16_x2": (10, None), "worker_g16_x8": (11, None)}
+PROBE_PER = {"worker_g16_x1": 1, "worker_g16_x2": 2, "worker_g16_x8": 8}
 # the probe of the same access shape as each kernel of the headline step
 PROBE_OF = {("compress_deferred", "f16"): "worker_g16", ("compress_deferred", "f32"): "worker_g32",
             ("compress_deferred16", "f16"): "state16", ("decompress_update", None): "update",
@@ -598,9 +602,10 @@ def hbm_ceiling(torch, w, reps=5):
     out = {}
     for name, (shape, groups) in PROBES.items():
         if groups is None:
-            if w.n % 4:
+            per = PROBE_PER.get(name, 4)
+            if w.n % per:
                 continue
-            groups = w.n // 4
+            groups = w.n // per
         na, ab, nb, bb, bmode = _probe_shapes()[name]
         a = torch.empty(max(1, groups * na * ld * ab // 4), device="cuda")
         b = torch.empty(max(1, groups * nb * ld * bb // 4), device="cuda")

@@ -140,6 +140,9 @@ constexpr Shape kShapes[] = {
     {8, 2, 3, 4, kRmw},    // 6 warm-up, 8 16-bit gradient rows, m v x in place
     {1, 4, 1, 4, kRmw},    // 7 update: denom read, x in place
     {0, 4, 1, 4, kRmw},    // 8 one row in place (the server pass's a)
+    {1, 2, 1, 4, kRmw},    // 9 shape 3 with one worker per group
+    {2, 2, 2, 4, kRmw},    // 10 shape 3 with two workers per group
+    {8, 2, 8, 4, kRmw},    // 11 shape 3 with eight workers per group
 };
 constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 
@@ -223,7 +226,12 @@ int hbm_stream_launch(int shape, int buf, const void* a, void* b, int64_t ld, in
       return launch_t<uint16_t, uint16_t, 4, 4, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
     case 6: return launch_t<uint16_t, float, 8, 3, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
     case 7: return launch_t<float, float, 1, 1, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
-    default: return launch_t<float, float, 0, 1, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
+    case 8: return launch_t<float, float, 0, 1, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
+    case 9: return launch_t<uint16_t, float, 1, 1, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
+    case 10:
+      return launch_t<uint16_t, float, 2, 2, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
+    default:
+      return launch_t<uint16_t, float, 8, 8, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
   }
 }
 

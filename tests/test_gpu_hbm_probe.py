@@ -24,7 +24,9 @@ def say(*a):
                                           ("write", 0, 8), ("state16", 1, 0),
                                           ("warmup_g16", 0, 0), ("update", 1, 0),
                                           ("worker_g16", 2, 0), ("state16", 3, 3),
-                                          ("warmup_g16", 1, 2), ("read", 0, 0)])
+                                          ("warmup_g16", 1, 2), ("read", 0, 0),
+                                          ("worker_g16_x1", 1, 2), ("worker_g16_x2", 3, 0),
+                                          ("worker_g16_x8", 0, 3)])
 def test_probe_stores_what_its_shape_says(name, buf, bpc):
     t = torch()
     lib = bench.probe_lib()
