@@ -337,6 +337,19 @@ def cpu_baseline(w, torch, synth, d_cap, single_thread=True):
         out["single_thread"] = {"workload": wb.name, "d": d1, "n": wb.n, "grad_dtype": wb.g_dtype,
                                 "runs_s": [round(r, 3) for r in runs], "median_s": round(med1, 3),
                                 "value": d1 / med1, "unit": "params/s", "threads": 1}
+        # the same bert_base step on the threads of the main run
+        runs = []
+        for _ in range(3):
+            st = {nm: v.copy() for nm, v in st0.items()}
+            t0 = time.perf_counter()
+            oracle_step_threads(st, g, ws1.wseg, ws1.sseg, synth.BETA1, synth.LR, threads)
+            runs.append(time.perf_counter() - t0)
+            del st
+        medt = sorted(runs)[1]
+        out["bert_base_threads"] = {"workload": wb.name, "d": d1, "threads": threads,
+                                    "runs_s": [round(r, 3) for r in runs],
+                                    "median_s": round(medt, 3), "value": d1 / medt,
+                                    "unit": "params/s"}
         del st0, g
     return out
 
@@ -1119,8 +1132,10 @@ def main():
         warm["frac_of_ceiling"] = round(warm["alg_GBps"] / ceil["probes"][pr]["GBps"], 4)
     if not args.no_cpu_baseline and w.name != "gpt2_xl":
         log("[bench] CPU oracle baseline")
-        out["cpu_baseline"] = cpu_baseline(w, torch, synth, args.cpu_sample,
-                                           single_thread=not args.no_single_thread)
+        cb = cpu_baseline(w, torch, synth, args.cpu_sample,
+                          single_thread=not args.no_single_thread)
+        cb["gpu_over_cpu"] = round(out["value"] / cb["value"], 1)
+        out["cpu_baseline"] = cb
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
