@@ -664,14 +664,14 @@ def hbm_ceiling(torch, w, reps=5):
 # The profiled commands, run from the repository root on the GPU machine (each
 # counter pass on its own run, as rocprofv3 collects one pass per run).
 PROFILE_CMDS = {
-    "trace": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof/trace -o run -f csv -- "
+    "trace": "rocprofv3 --kernel-trace --stats -d profiles_raw/trace -o run -f csv -- "
              "python3 -u bench.py --steps 5 --warmup 1 --no-cpu-baseline",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex oba:: -d gpurun_out/prof/fetch "
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex oba:: -d profiles_raw/fetch "
              "-o run -f csv -- python3 -u bench.py --steps 2 --warmup 0 --no-cpu-baseline",
-    "write": "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex oba:: -d gpurun_out/prof/write "
+    "write": "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex oba:: -d profiles_raw/write "
              "-o run -f csv -- python3 -u bench.py --steps 2 --warmup 0 --no-cpu-baseline",
     "occ": "rocprofv3 --pmc OccupancyPercent MeanOccupancyPerCU SQ_WAVES --kernel-include-regex "
-           "oba:: -d gpurun_out/prof/occ -o run -f csv -- python3 -u bench.py --steps 2 "
+           "oba:: -d profiles_raw/occ -o run -f csv -- python3 -u bench.py --steps 2 "
            "--warmup 0 --no-cpu-baseline",
 }
 CU_NUM = 256
@@ -760,8 +760,8 @@ def _alg_bytes(w):
     ld = (d // 2048) * 2048
     for nm, (shape, groups) in PROBES.items():
         na, ab, nb, bb, mode = _probe_shapes()[nm]
-        g = groups if groups is not None else n // 4
-        for form in ("global", "buffer"):
+        g = groups if groups is not None else n // PROBE_PER.get(nm, 4)
+        for form in ("global", "buffer", "global, rows alternating", "buffer, rows alternating"):
             out[f"probe {nm} ({form})"] = g * ld * (na * ab + nb * bb * (2 if mode == 2 else 1))
     return out
 
@@ -837,7 +837,7 @@ def summarize_profiles(raw, out_dir, workload="bert_large"):
          f"Workload: d = {w.d:,}, n = {w.n}, {w.g_dtype} gradients; one MI355X.", "",
          "Commands (repository root, GPU box; one counter per run):", "",
          "    " + PROFILE_CMDS["fetch"], "    " + PROFILE_CMDS["write"], "",
-         "Summary written by `python bench.py --summarize-profiles gpurun_out/prof` from those",
+         "Summary written by `python bench.py --summarize-profiles profiles_raw` from those",
          "runs' counter_collection.csv files.", "",
          "Calibration: the copy probe (`k_stream<float, float, 4, 4, 1, false, false>`, global form) reads",
          f"and writes {half / 1e9:.3f} GB per launch; it reads FETCH_SIZE = "
@@ -871,7 +871,7 @@ def summarize_profiles(raw, out_dir, workload="bert_large"):
         big = _largest_grids(keys)
         L = [f"# Occupancy per kernel (rocprofv3 counters), {w.name} workload", "",
              "Command (repository root, GPU box):", "", "    " + PROFILE_CMDS["occ"], "",
-             "Summary written by `python bench.py --summarize-profiles gpurun_out/prof`.",
+             "Summary written by `python bench.py --summarize-profiles profiles_raw`.",
              "OccupancyPercent = 400 * SQ_WAVE_CYCLES / GRBM_GUI_ACTIVE / CU_NUM / 32 (rocprofv3's",
              "derived counter for gfx950): resident waves as a share of 32 per CU (8 per SIMD);",
              "waves per SIMD below = OccupancyPercent * 8 / 100, the mean over the dispatch,",
@@ -921,7 +921,7 @@ def summarize_profiles(raw, out_dir, workload="bert_large"):
          f"Workload: d = {w.d:,} binary32 parameters, n = {w.n} simulated workers, {w.g_dtype} "
          "gradients, 1 worker segment, n server segments; one MI355X (gfx950).", "",
          "Command (repository root, GPU box):", "", "    " + PROFILE_CMDS["trace"], "",
-         "Summary written by `python bench.py --summarize-profiles gpurun_out/prof`.", "",
+         "Summary written by `python bench.py --summarize-profiles profiles_raw`.", "",
          "Covers the warm-up and freeze, 1 untimed and 5 timed steps of each schedule "
          "(deferred, explicit, per-worker momentum, 16-bit state), the graph replays, the "
          "one-GPU-share run and the HBM streaming probes.  bench.py's own HIP-event timing of the "
