@@ -316,7 +316,7 @@ def cpu_baseline(w, torch, synth, d_cap, single_thread=True):
     out = {"value": d / med, "unit": "params/s", "cores": threads, "kind": "oracle",
            "sample": f"one compression step (compress, server, update) of the {w.name} recipe "
                      f"at d={d:,} (the workload's d={w.d:,}"
-                     + ("" if d == w.d else f"; params/s measured at the smaller d") +
+                     + ("" if d == w.d else f"; params/s measured at d={d:,}") +
                      f"), n={w.n}, {w.g_dtype} gradients; independent oracle calls on "
                      f"{threads} threads; median of 3 runs",
            "threads": threads, "affinity_cores": aff, "cpu_model": model,
