@@ -688,16 +688,25 @@ static void launch_cmp(const Geo& G, int32_t i0, int groups, const void* g, cons
 #ifndef OBA_IMPLICIT_NB
 #define OBA_IMPLICIT_NB 4
 #endif
-// workers per block of the 16-bit-state pass (its rows carry fewer bytes per
-// worker, so a block can hold more workers' loads), a tuning knob
+// Workers per block of the 16-bit-state pass with the implicit momentum, a
+// tuning knob: one worker per block (its spans two at a time) took the pass
+// from 2.85 to 2.72 ms at bert_large (two: 2.75 ms; same-box A/B; occupancy
+// caps of 2 or 3 blocks per CU made it slower).  The first step after the
+// freeze reads m, shared by the workers of a block, so it keeps groups of
+// OBA_READ_NB16.
 #ifndef OBA_IMPLICIT_NB16
-#define OBA_IMPLICIT_NB16 4
+#define OBA_IMPLICIT_NB16 1
+#endif
+#ifndef OBA_READ_NB16
+#define OBA_READ_NB16 4
 #endif
 constexpr int kMaxNB = OBA_MAX_NB;
 constexpr int kImplicitNB16 = OBA_IMPLICIT_NB16;
+constexpr int kReadNB16 = OBA_READ_NB16;
 constexpr int kImplicitNB = OBA_IMPLICIT_NB;
 static_assert(kMaxNB >= 1 && kMaxNB <= 8 && kImplicitNB >= 1 && kImplicitNB <= 8 &&
-                  kImplicitNB16 >= 1 && kImplicitNB16 <= 8,
+                  kImplicitNB16 >= 1 && kImplicitNB16 <= 8 && kReadNB16 >= 1 &&
+                  kReadNB16 <= 8,
               "worker groups hold 1 to 8 workers");
 
 template <typename GT, typename CT, int MODE, bool TL>
@@ -705,7 +714,8 @@ static void launch_cmp_n(const Geo& G, const void* g, const float* m, void* delt
                          uint8_t* wbytes, const SegDev& sig, double* part, const float* wscale,
                          float b1, float omb1, const MomSrc& ms, const TList& tl,
                          hipStream_t st) {
-  constexpr int GROUP = !__is_same(CT, float)                       ? kImplicitNB16
+  constexpr int GROUP = !__is_same(CT, float)
+                            ? (MODE == kDeferredM ? kImplicitNB16 : kReadNB16)
                         : (MODE == kDeferredM || MODE == kDeferredLocal) ? kImplicitNB
                                                                          : kMaxNB;
   const int full = G.n / GROUP, rem = G.n % GROUP, i0 = full * GROUP;
