@@ -715,7 +715,7 @@ def _role(short, n=None):
         elif m.group(1):  # the 16-bit pass: one worker per block, m-read step groups of 4
             group = 1 if mode == 4 else min(n, 4)
         else:
-            group = min(n, 4) if mode in (4, 5) else min(n, 8)
+            group = min(n, 4) if mode == 4 else 1 if mode == 5 else min(n, 8)
         if n and int(m.group(2)) != group:
             return "other (one-GPU share)"
         return base

@@ -704,6 +704,13 @@ constexpr int kMaxNB = OBA_MAX_NB;
 constexpr int kImplicitNB16 = OBA_IMPLICIT_NB16;
 constexpr int kReadNB16 = OBA_READ_NB16;
 constexpr int kImplicitNB = OBA_IMPLICIT_NB;
+// Workers per block of the per-worker-momentum pass (three rows per worker),
+// a tuning knob: one worker per block took the pass from 8.38-8.47 to
+// 8.08-8.23 ms at bert_large (two: equal to four; same-box A/B).
+#ifndef OBA_LOCAL_NB
+#define OBA_LOCAL_NB 1
+#endif
+constexpr int kLocalNB = OBA_LOCAL_NB;
 static_assert(kMaxNB >= 1 && kMaxNB <= 8 && kImplicitNB >= 1 && kImplicitNB <= 8 &&
                   kImplicitNB16 >= 1 && kImplicitNB16 <= 8 && kReadNB16 >= 1 &&
                   kReadNB16 <= 8,
@@ -716,7 +723,8 @@ static void launch_cmp_n(const Geo& G, const void* g, const float* m, void* delt
                          hipStream_t st) {
   constexpr int GROUP = !__is_same(CT, float)
                             ? (MODE == kDeferredM ? kImplicitNB16 : kReadNB16)
-                        : (MODE == kDeferredM || MODE == kDeferredLocal) ? kImplicitNB
+                        : MODE == kDeferredM                             ? kImplicitNB
+                        : MODE == kDeferredLocal                         ? kLocalNB
                                                                          : kMaxNB;
   const int full = G.n / GROUP, rem = G.n % GROUP, i0 = full * GROUP;
 #define OBA_CMP(NB_, I0, GROUPS) \
