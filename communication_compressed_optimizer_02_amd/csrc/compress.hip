@@ -721,8 +721,10 @@ static void launch_cmp_n(const Geo& G, const void* g, const float* m, void* delt
                          uint8_t* wbytes, const SegDev& sig, double* part, const float* wscale,
                          float b1, float omb1, const MomSrc& ms, const TList& tl,
                          hipStream_t st) {
+  // (the tensor-list 16-bit pass has no two-span path, without which one
+  // worker per block was slower: it keeps groups of OBA_READ_NB16)
   constexpr int GROUP = !__is_same(CT, float)
-                            ? (MODE == kDeferredM ? kImplicitNB16 : kReadNB16)
+                            ? (MODE == kDeferredM && !TL ? kImplicitNB16 : kReadNB16)
                         : MODE == kDeferredM                             ? kImplicitNB
                         : MODE == kDeferredLocal                         ? kLocalNB
                                                                          : kMaxNB;
