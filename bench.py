@@ -570,10 +570,13 @@ def one_gpu_share(w, torch, oba, synth, steps, warmup):
 PROBES = {"read": (0, 1), "write": (1, 1), "copy": (2, 1), "worker_g16": (3, None),
           "worker_g32": (4, None), "state16": (5, None), "warmup_g16": (6, 1),
           "update": (7, 1), "in_place": (8, 1), "worker_g16_x1": (9, None),
-          "worker_g16_x2": (10, None), "worker_g16_x8": (11, None), "state16_x1": (12, None)}
-PROBE_PER = {"worker_g16_x1": 1, "worker_g16_x2": 2, "worker_g16_x8": 8, "state16_x1": 1}
+          "worker_g16_x2": (10, None), "worker_g16_x8": (11, None), "state16_x1": (12, None),
+          "worker_g32_x1": (13, None)}
+PROBE_PER = {"worker_g16_x1": 1, "worker_g16_x2": 2, "worker_g16_x8": 8, "state16_x1": 1,
+             "worker_g32_x1": 1}
 # the probe of the same access shape as each kernel of the headline step
-PROBE_OF = {("compress_deferred", "f16"): "worker_g16", ("compress_deferred", "f32"): "worker_g32",
+PROBE_OF = {("compress_deferred", "f16"): "worker_g16_x1",
+            ("compress_deferred", "f32"): "worker_g32_x1",
             ("compress_deferred16", "f16"): "state16_x1", ("decompress_update", None): "update",
             ("server_deferred", None): "in_place", ("adam_warmup", "f16"): "warmup_g16"}
 
@@ -715,7 +718,7 @@ def _role(short, n=None):
         elif m.group(1):  # the 16-bit pass: one worker per block, m-read step groups of 4
             group = 1 if mode == 4 else min(n, 4)
         else:
-            group = min(n, 4) if mode == 4 else 1 if mode == 5 else min(n, 8)
+            group = 1 if mode in (4, 5) else min(n, 8)
         if n and int(m.group(2)) != group:
             return "other (one-GPU share)"
         return base

@@ -127,8 +127,10 @@ struct Shape {
 };
 
 // Rows per group.  The deferred worker pass at 8 workers with binary16
-// gradients is shape 3 with two groups; its 16-bit-state form shape 12 with
-// eight groups (shape 5 the same with groups of four); the
+// gradients is shape 9 with eight groups (one worker per block; shape 3 the
+// same with groups of four), with binary32 gradients shape 13; its
+// 16-bit-state form shape 12 with eight groups (shape 5 with groups of
+// four); the
 // warm-up at 8 workers shape 6; the update shape 7; the server pass's a
 // shape 8 (its packed rows, n/8 bytes per coordinate, are left out).
 constexpr Shape kShapes[] = {
@@ -145,6 +147,7 @@ constexpr Shape kShapes[] = {
     {2, 2, 2, 4, kRmw},    // 10 shape 3 with two workers per group
     {8, 2, 8, 4, kRmw},    // 11 shape 3 with eight workers per group
     {1, 2, 1, 2, kRmw},    // 12 shape 5 with one worker per group
+    {1, 4, 1, 4, kRmw},    // 13 shape 4 with one worker per group
 };
 constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 
@@ -234,8 +237,9 @@ int hbm_stream_launch(int shape, int buf, const void* a, void* b, int64_t ld, in
       return launch_t<uint16_t, float, 2, 2, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
     case 11:
       return launch_t<uint16_t, float, 8, 8, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
-    default:
+    case 12:
       return launch_t<uint16_t, uint16_t, 1, 1, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
+    default: return launch_t<float, float, 1, 1, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
   }
 }
 

@@ -46,7 +46,9 @@ struct oba_layout_s {
   oba::SegDev tau_w{};  // server segments, update grid
   oba::SegDev tau_c{};  // server segments, compress grid (implicit momentum)
   oba::Geo geo_w{};     // update grid (one span per block)
-  oba::Geo geo_c{};     // compress grid
+  oba::Geo geo_c{};     // compress grid (deferred worker passes)
+  oba::Geo geo_e{};     // explicit grid (explicit apply, per-worker momentum)
+  oba::SegDev sig_e{};  // worker segments, explicit grid
   oba::Geo geo{};       // server grid
   size_t ws_worker = 0, ws_server = 0;
 };
@@ -265,13 +267,15 @@ int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const i
     o32[4] = h32.size();
     h32.insert(h32.end(), pc.seg_item.begin(), pc.seg_item.end());
   };
-  size_t w64[2], w32[5], v64[2], v32[5], s64[2], s32[5], t64[2], t32[5], c64[2], c32[5];
+  size_t w64[2], w32[5], v64[2], v32[5], s64[2], s32[5], t64[2], t32[5], c64[2], c32[5],
+      e64[2], e32[5];
   try {
     put(P.wp, P.wseg, w64, w32);
     put(P.wp_s, P.wseg, v64, v32);
     put(P.sp, P.sseg, s64, s32);
     put(P.sp_w, P.sseg, t64, t32);
     put(P.sp_c, P.sseg, c64, c32);
+    put(P.wp_e, P.wseg, e64, e32);
   } catch (...) {
     delete L;
     return OBA_ENOMEM;
@@ -315,14 +319,17 @@ int oba_layout_create(oba_layout* out, int64_t d, int32_t n, int64_t ld, const i
   L->tau = view(P.sp, s64, s32, (int32_t)P.sseg.size() - 1);
   L->tau_w = view(P.sp_w, t64, t32, (int32_t)P.sseg.size() - 1);
   L->tau_c = view(P.sp_c, c64, c32, (int32_t)P.sseg.size() - 1);
+  L->sig_e = view(P.wp_e, e64, e32, (int32_t)P.wseg.size() - 1);
   auto geo = [&](int32_t nblk) {  // an empty layout has no blocks
     return oba::Geo{P.d, P.ld, P.W, P.S, P.n, nblk, nblk ? P.S / nblk : 0,
                     nblk ? (int32_t)(P.S % nblk) : 0};
   };
   L->geo_w = geo(P.nblk_w);
   L->geo_c = geo(P.nblk_c);
+  L->geo_e = geo(P.nblk_e);
   L->geo = geo(P.nblk);
   L->ws_worker = std::max({oba::partial_bytes(L->sig_c, P.n), oba::partial_bytes(L->sig, P.n),
+                           oba::partial_bytes(L->sig_e, P.n),
                            ((size_t)std::max(P.nblk_w, P.nblk) * 8 + 255) / 256 * 256});
   L->ws_server = std::max(oba::partial_bytes(L->tau, 1), oba::partial_bytes(L->tau_c, 1));
   *out = L;
@@ -430,7 +437,7 @@ int oba_compress(oba_layout L, const void* g, int g_dtype, const float* m, float
   OBA_TRY(check_buf(wscale, 4));
   OBA_TRY(check_buf(ws, 8));
   if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
-  const oba::Geo G = L->geo_c;
+  const oba::Geo G = L->geo_e;
   double* part = static_cast<double*>(ws);
   const float b1 = (float)beta1, omb1 = (float)(1.0 - beta1);
   uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
@@ -443,7 +450,7 @@ int oba_compress(oba_layout L, const void* g, int g_dtype, const float* m, float
   OBA_TRY(launch("finalize_scales", stream,
                  [&] { oba::launch_finalize(part, G.n, L->sig, wscale, stream); }));
   return launch("compress_p2", stream, [&] {
-    oba::launch_compress_apply(G, g, g_dtype, m, delta, wbytes, L->sig_c, wscale, b1,
+    oba::launch_compress_apply(G, g, g_dtype, m, delta, wbytes, L->sig_e, wscale, b1,
                                omb1, stream);
   });
 }
@@ -612,16 +619,16 @@ int oba_compress_deferred_local(oba_layout L, const void* g, int g_dtype, float*
   OBA_TRY(check_buf(ws, 8));
   if (ws_bytes < oba_workspace_bytes(L)) return OBA_EWORKSPACE;
   if ((const void*)m_local == (const void*)c) return OBA_EINVAL;
-  const oba::Geo G = L->geo_c;
+  const oba::Geo G = L->geo_e;
   double* part = static_cast<double*>(ws);
   const float b1 = (float)beta1, omb1 = (float)(1.0 - beta1);
   uint8_t* wbytes = reinterpret_cast<uint8_t*>(wbits);
   OBA_TRY(launch("compress_deferred_local", stream, [&] {
-    oba::launch_compress_deferred_local(G, g, g_dtype, m_local, c, wbytes, L->sig_c,
+    oba::launch_compress_deferred_local(G, g, g_dtype, m_local, c, wbytes, L->sig_e,
                                         part, wscale, b1, omb1, stream);
   }));
   return launch("finalize_scales", stream,
-                [&] { oba::launch_finalize(part, G.n, L->sig_c, wscale, stream); });
+                [&] { oba::launch_finalize(part, G.n, L->sig_e, wscale, stream); });
 }
 
 int oba_server_reduce_recompress_deferred(oba_layout L, const uint64_t* wbits,

@@ -56,6 +56,16 @@ constexpr int kWorkerBatch = OBA_WORKER_BATCH;
 #define OBA_WORKER_BATCH16 4
 #endif
 constexpr int kWorkerBatch16 = OBA_WORKER_BATCH16;
+// The binary32 deferred worker pass with the implicit momentum in the body of
+// the 16-bit pass (two spans per iteration, cursors in registers) with one
+// worker per block on blocks of two spans (1), or in compress_body with
+// groups of four on the one-span grid (0, with OBA_IMPLICIT_NB=4 and
+// OBA_CMP_SPANS=1): 4.54-4.57 -> 4.46-4.51 ms at bert_large (same-box A/B;
+// four spans per block 4.85 ms, two workers per block 4.68 ms).
+#ifndef OBA_CMP_SPANSBODY
+#define OBA_CMP_SPANSBODY 1
+#endif
+constexpr bool kSpansBody = OBA_CMP_SPANSBODY != 0;
 // The 16-bit-state pass takes two full spans per iteration where a block lies
 // inside one worker piece and one server piece (1), or one span at a time (0):
 // 2.868/2.845 -> 2.854/2.820 ms at bert_large (same-box A/B, two runs each; the
@@ -632,6 +642,11 @@ __global__ __launch_bounds__(kBlock) OBA_CMP_ATTR void k_compress(
     Geo G, int32_t i0, const GT* __restrict__ g, float* __restrict__ m, CT* __restrict__ delta,
     uint8_t* __restrict__ wbytes, SegDev sig, double* __restrict__ part,
     const float* __restrict__ wscale, float b1, float omb1, MomSrc ms, TList tl) {
+  if constexpr (kSpansBody && MODE == kDeferredM && !TL) {
+    compress_body_spans<GT, CT, NB, MODE, TL>(G, i0, g, m, delta, wbytes, sig, part, wscale, b1,
+                                              omb1, ms, tl);
+    return;
+  }
   compress_body<GT, CT, NB, MODE, TL>(G, i0, g, m, delta, wbytes, sig, part, wscale, b1, omb1,
                                       ms, tl);
 }
@@ -686,7 +701,7 @@ static void launch_cmp(const Geo& G, int32_t i0, int groups, const void* g, cons
 #define OBA_MAX_NB 8
 #endif
 #ifndef OBA_IMPLICIT_NB
-#define OBA_IMPLICIT_NB 4
+#define OBA_IMPLICIT_NB 1
 #endif
 // Workers per block of the 16-bit-state pass with the implicit momentum, a
 // tuning knob: one worker per block (its spans two at a time) took the pass
@@ -704,6 +719,12 @@ constexpr int kMaxNB = OBA_MAX_NB;
 constexpr int kImplicitNB16 = OBA_IMPLICIT_NB16;
 constexpr int kReadNB16 = OBA_READ_NB16;
 constexpr int kImplicitNB = OBA_IMPLICIT_NB;
+// the tensor-list form of that pass (compress_body: no two-span path) keeps
+// groups of four
+#ifndef OBA_LISTED_NB
+#define OBA_LISTED_NB 4
+#endif
+constexpr int kListedNB = OBA_LISTED_NB;
 // Workers per block of the per-worker-momentum pass (three rows per worker),
 // a tuning knob: one worker per block took the pass from 8.38-8.47 to
 // 8.08-8.23 ms at bert_large (two: equal to four; same-box A/B).
@@ -725,7 +746,7 @@ static void launch_cmp_n(const Geo& G, const void* g, const float* m, void* delt
   // worker per block was slower: it keeps groups of OBA_READ_NB16)
   constexpr int GROUP = !__is_same(CT, float)
                             ? (MODE == kDeferredM && !TL ? kImplicitNB16 : kReadNB16)
-                        : MODE == kDeferredM                             ? kImplicitNB
+                        : MODE == kDeferredM                  ? (TL ? kListedNB : kImplicitNB)
                         : MODE == kDeferredLocal                         ? kLocalNB
                                                                          : kMaxNB;
   const int full = G.n / GROUP, rem = G.n % GROUP, i0 = full * GROUP;

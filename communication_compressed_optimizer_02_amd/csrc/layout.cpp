@@ -94,6 +94,8 @@ int make_plan(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_w
     P.nblk_w = (int32_t)std::min<int64_t>(P.S, kMaxBlocksWorker);
     const int32_t spc = compress_spans(n);
     P.nblk_c = (int32_t)std::min<int64_t>((P.S + spc - 1) / spc, kMaxBlocksWorker);
+    const int32_t spe = explicit_spans(n);
+    P.nblk_e = (int32_t)std::min<int64_t>((P.S + spe - 1) / spe, kMaxBlocksWorker);
     P.wseg.assign(wseg, wseg + n_wseg + 1);
     P.sseg.assign(sseg, sseg + n_sseg + 1);
     if ((rc = cut(P, P.nblk_c, P.wseg, &P.wp))) return rc;
@@ -101,6 +103,7 @@ int make_plan(int64_t d, int32_t n, int64_t ld, const int64_t* wseg, int32_t n_w
     if ((rc = cut(P, P.nblk, P.sseg, &P.sp))) return rc;
     if ((rc = cut(P, P.nblk_w, P.sseg, &P.sp_w))) return rc;
     if ((rc = cut(P, P.nblk_c, P.sseg, &P.sp_c))) return rc;
+    if ((rc = cut(P, P.nblk_e, P.wseg, &P.wp_e))) return rc;
     *out = std::move(P);
   } catch (...) {
     return kENoMem;

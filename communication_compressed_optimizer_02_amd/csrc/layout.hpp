@@ -38,15 +38,18 @@ constexpr int64_t kSpan = kBlock * kVec;    // coordinates per block pass
 constexpr int kMaxBlocks = OBA_MAX_BLOCKS;
 constexpr int kServerSpans = OBA_SERVER_SPANS;  // least spans per block of the server grid
 constexpr int kMaxBlocksWorker = OBA_MAX_BLOCKS_WORKER;
-// Spans per block of the compress grid: one when a block holds four workers
-// or more; with fewer workers per block a block does too little work per
-// span, and 4/n spans per block measured 16 % faster for one worker.
-// Spans per block of the compress grid for four or more workers, a tuning
-// knob (fewer workers take 4/n, so a block still has about four workers' spans).
+// Spans per block of the compress grid, the grid of the deferred worker
+// passes, a tuning knob: their binary32 form takes one worker per block and a
+// block's two spans at once, so blocks of two spans.
 #ifndef OBA_CMP_SPANS
-#define OBA_CMP_SPANS 1
+#define OBA_CMP_SPANS 2
 #endif
-inline int32_t compress_spans(int32_t n) { return n >= 4 ? OBA_CMP_SPANS : 4 / n; }
+inline int32_t compress_spans(int32_t) { return OBA_CMP_SPANS; }
+// Spans per block of the explicit grid (the explicit apply pass and the
+// per-worker-momentum pass): one when a block holds four workers or more;
+// with fewer workers per block a block does too little work per span, and 4/n
+// spans per block measured 16 % faster for one worker.
+inline int32_t explicit_spans(int32_t n) { return n >= 4 ? 1 : 4 / n; }
 constexpr int32_t kMaxWorkers = 4096;
 
 // A segment cut into more than kSplitAbove pieces has its partials summed in
@@ -70,13 +73,15 @@ struct Plan {
   int32_t n = 0;
   int32_t nblk = 0;    // grid of the server, residual, warm-up, freeze, norm kernels
   int32_t nblk_w = 0;  // grid of the update (one span per block)
-  int32_t nblk_c = 0;  // grid of the worker-side compress kernels
+  int32_t nblk_c = 0;  // grid of the deferred worker passes (compress grid)
+  int32_t nblk_e = 0;  // grid of the explicit apply and per-worker-momentum passes
   std::vector<int64_t> wseg, sseg;  // offsets, n_seg+1 each
   Pieces wp;    // worker segments cut on the compress grid
   Pieces wp_s;  // worker segments cut on the server grid (scale lookups there)
   Pieces sp;    // server segments cut on the server grid
   Pieces sp_w;  // server segments cut on the update grid
   Pieces sp_c;  // server segments cut on the compress grid (implicit momentum)
+  Pieces wp_e;  // worker segments cut on the explicit grid
 };
 
 // Status codes mirror the C ABI (0 ok, negative error).

@@ -1,9 +1,10 @@
 // plan_driver.cpp -- test driver for the host-only piece planner.
 // Usage: plan_driver d n ld n_wseg o_0 .. o_nw n_sseg o_0 .. o_ns
-// Prints "rc <status>", then "G d W S nblk nblk_w nblk_c", then for the
+// Prints "rc <status>", then "G d W S nblk nblk_w nblk_c nblk_e", then for the
 // worker segments on the compress grid, the worker segments on the server
 // grid, the server segments on the server grid, on the update grid and on the
-// compress grid: "T <n_pieces> <n_seg>", one
+// compress grid, and the worker segments on the explicit grid:
+// "T <n_pieces> <n_seg>", one
 // "P lo hi seg" line per piece, "B" + blk_first, "S" + seg_first, "I" +
 // item_q, "J" + seg_item (the last two empty for one-stage sums).  With a
 // tensor list appended ("nt l_0 .. l_{nt-1}"): "TO <status>", then for the
@@ -44,13 +45,14 @@ int main(int argc, char** argv) {
   int rc = oba::make_plan(d, (int32_t)n, ld, w.data(), nw, s.data(), ns, &P);
   std::printf("rc %d\n", rc);
   if (rc) return 0;
-  std::printf("G %lld %lld %lld %d %d %d\n", (long long)P.d, (long long)P.W, (long long)P.S,
-              P.nblk, P.nblk_w, P.nblk_c);
+  std::printf("G %lld %lld %lld %d %d %d %d\n", (long long)P.d, (long long)P.W, (long long)P.S,
+              P.nblk, P.nblk_w, P.nblk_c, P.nblk_e);
   dump(P.wp, nw);
   dump(P.wp_s, nw);
   dump(P.sp, ns);
   dump(P.sp_w, ns);
   dump(P.sp_c, ns);
+  dump(P.wp_e, nw);
   // optional tensor list: nt l_0 .. l_{nt-1}
   if (a < argc) {
     const int nt = (int)next();

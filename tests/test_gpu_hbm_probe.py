@@ -27,7 +27,7 @@ def say(*a):
                                           ("warmup_g16", 1, 2), ("read", 0, 0),
                                           ("worker_g16_x1", 1, 2), ("worker_g16_x2", 3, 0),
                                           ("worker_g16_x8", 0, 3), ("state16_x1", 1, 0),
-                                          ("state16_x1", 2, 3)])
+                                          ("state16_x1", 2, 3), ("worker_g32_x1", 1, 0)])
 def test_probe_stores_what_its_shape_says(name, buf, bpc):
     t = torch()
     lib = bench.probe_lib()

@@ -72,11 +72,11 @@ def test_noalloc_equals_workspace_form_twice_then_smaller():
 
 
 def test_noalloc_refuses_a_layout_beyond_its_scratch():
-    """4096 workers over 4M coordinates need 4096 * 2048 pieces * 8 bytes of
-    partials (64 MiB): refused with OBA_ESCRATCH before any buffer is looked
-    at (null buffers here), so nothing is launched."""
+    """4096 workers over 8M coordinates need 4096 * 2048 pieces (blocks of two
+    spans) * 8 bytes of partials (64 MiB): refused with OBA_ESCRATCH before
+    any buffer is looked at (null buffers here), so nothing is launched."""
     t = torch()
-    d, n = 4 << 20, 4096
+    d, n = 8 << 20, 4096
     L = oba.Layout(d, n, synth.whole(d), synth.whole(d))
     assert oba.lib().oba_workspace_bytes(L.handle) > (32 << 20)
     P = ctypes.c_void_p
