@@ -732,15 +732,13 @@ def _role(short, n=None):
         return {("false", "true"): "decompress_update", ("true", "true"):
                 "decompress_update (m written)", ("true", "false"): "server_momentum"}.get(
                     (m.group(1), m.group(2)), "")
-    m = re.match(r"oba::k_stream<([^,]+), ([^,]+), (\d+), (\d+), (\d), (true|false), "
+    m = re.match(r"oba::k_stream<(\d+), [^,]+, [^,]+, \d+, \d+, \d, (true|false), "
                  r"(true|false)>", short)
-    if m:
-        ta, tb = (2 if "short" in x else 4 for x in (m.group(1), m.group(2)))
-        key = (int(m.group(3)), ta, int(m.group(4)), tb, int(m.group(5)))
-        form = ("buffer" if m.group(6) == "true" else "global") + (
-            ", rows alternating" if m.group(7) == "true" else "")
-        for nm, shp in _probe_shapes().items():
-            if shp == key:
+    if m:  # the first template argument is the probe's shape index
+        form = ("buffer" if m.group(2) == "true" else "global") + (
+            ", rows alternating" if m.group(3) == "true" else "")
+        for nm, (shape, _) in PROBES.items():
+            if shape == int(m.group(1)):
                 return f"probe {nm} ({form})"
         return "probe"
     for pat, r in (("oba::k_residual", "server_p2"), ("oba::k_adam_warmup", "adam_warmup"),
@@ -847,7 +845,7 @@ def summarize_profiles(raw, out_dir, workload="bert_large"):
          "    " + PROFILE_CMDS["fetch"], "    " + PROFILE_CMDS["write"], "",
          "Summary written by `python bench.py --summarize-profiles profiles_raw` from those",
          "runs' counter_collection.csv files.", "",
-         "Calibration: the copy probe (`k_stream<float, float, 4, 4, 1, false, false>`, global form) reads",
+         "Calibration: the copy probe (`k_stream<2, float, float, 4, 4, 1, false, false>`, global form) reads",
          f"and writes {half / 1e9:.3f} GB per launch; it reads FETCH_SIZE = "
          f"{sum(cf) / len(cf) * 1024 / 1e9:.3f} GB and WRITE_SIZE =",
          f"{sum(cw) / len(cw) * 1024 / 1e9:.3f} GB, so FETCH_SIZE is scaled by {ff:.3f} and "

@@ -68,7 +68,9 @@ __device__ __forceinline__ void probe_store(T* row, const Quads& q, int64_t lo, 
 // ILV (read-and-write shapes with as many A as B rows): the loads alternate
 // A row u, B row u -- the worker passes' order (gradient, then state, worker
 // by worker) -- instead of all A rows, then all B rows.
-template <typename TA, typename TB, int NA, int NB, int BMODE, bool BUF, bool ILV>
+// SID: the shape's index, so that every shape is a kernel of its own name
+// (two shapes may have the same rows and differ in their groups)
+template <int SID, typename TA, typename TB, int NA, int NB, int BMODE, bool BUF, bool ILV>
 __global__ __launch_bounds__(kBlock) void k_stream(const TA* __restrict__ a, TB* __restrict__ b,
                                                    int64_t ld, float* __restrict__ sink) {
   const int64_t lo = (int64_t)blockIdx.x * kSpan;
@@ -151,33 +153,35 @@ constexpr Shape kShapes[] = {
 };
 constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 
-template <typename TA, typename TB, int NA, int NB, int BMODE, bool ILV>
+template <int SID, typename TA, typename TB, int NA, int NB, int BMODE, bool ILV>
 int launch_t2(bool buf, const void* a, void* b, int64_t ld, int64_t spans, int32_t groups,
               size_t lds, float* sink, hipStream_t st) {
   const dim3 grid((unsigned)spans, (unsigned)groups);
   const TA* pa = static_cast<const TA*>(a);
   TB* pb = static_cast<TB*>(b);
   const void* fn =
-      buf ? reinterpret_cast<const void*>(&k_stream<TA, TB, NA, NB, BMODE, true, ILV>)
-          : reinterpret_cast<const void*>(&k_stream<TA, TB, NA, NB, BMODE, false, ILV>);
+      buf ? reinterpret_cast<const void*>(&k_stream<SID, TA, TB, NA, NB, BMODE, true, ILV>)
+          : reinterpret_cast<const void*>(&k_stream<SID, TA, TB, NA, NB, BMODE, false, ILV>);
   if (lds > 0 &&
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return -5;
   if (buf)
-    hipLaunchKernelGGL((k_stream<TA, TB, NA, NB, BMODE, true, ILV>), grid, dim3(kBlock), lds, st,
+    hipLaunchKernelGGL((k_stream<SID, TA, TB, NA, NB, BMODE, true, ILV>), grid, dim3(kBlock), lds, st,
                        pa, pb, ld, sink);
   else
-    hipLaunchKernelGGL((k_stream<TA, TB, NA, NB, BMODE, false, ILV>), grid, dim3(kBlock), lds,
+    hipLaunchKernelGGL((k_stream<SID, TA, TB, NA, NB, BMODE, false, ILV>), grid, dim3(kBlock), lds,
                        st, pa, pb, ld, sink);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
-template <typename TA, typename TB, int NA, int NB, int BMODE>
+template <int SID, typename TA, typename TB, int NA, int NB, int BMODE>
 int launch_t(int buf, const void* a, void* b, int64_t ld, int64_t spans, int32_t groups,
              size_t lds, float* sink, hipStream_t st) {
   if (buf & 2)
-    return launch_t2<TA, TB, NA, NB, BMODE, true>(buf & 1, a, b, ld, spans, groups, lds, sink, st);
-  return launch_t2<TA, TB, NA, NB, BMODE, false>(buf & 1, a, b, ld, spans, groups, lds, sink, st);
+    return launch_t2<SID, TA, TB, NA, NB, BMODE, true>(buf & 1, a, b, ld, spans, groups, lds, sink,
+                                                       st);
+  return launch_t2<SID, TA, TB, NA, NB, BMODE, false>(buf & 1, a, b, ld, spans, groups, lds, sink,
+                                                      st);
 }
 
 }  // namespace
@@ -222,24 +226,24 @@ int hbm_stream_launch(int shape, int buf, const void* a, void* b, int64_t ld, in
   if (buf < 0 || buf > 3) return -1;
   const int bf = buf;
   switch (shape) {
-    case 0: return launch_t<float, float, 8, 0, kNone>(bf, a, b, ld, spans, groups, lds, sink, st);
-    case 1: return launch_t<float, float, 0, 8, kWrite>(bf, a, b, ld, spans, groups, lds, sink, st);
-    case 2: return launch_t<float, float, 4, 4, kWrite>(bf, a, b, ld, spans, groups, lds, sink, st);
-    case 3: return launch_t<uint16_t, float, 4, 4, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
-    case 4: return launch_t<float, float, 4, 4, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
+    case 0: return launch_t<0, float, float, 8, 0, kNone>(bf, a, b, ld, spans, groups, lds, sink, st);
+    case 1: return launch_t<1, float, float, 0, 8, kWrite>(bf, a, b, ld, spans, groups, lds, sink, st);
+    case 2: return launch_t<2, float, float, 4, 4, kWrite>(bf, a, b, ld, spans, groups, lds, sink, st);
+    case 3: return launch_t<3, uint16_t, float, 4, 4, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
+    case 4: return launch_t<4, float, float, 4, 4, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
     case 5:
-      return launch_t<uint16_t, uint16_t, 4, 4, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
-    case 6: return launch_t<uint16_t, float, 8, 3, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
-    case 7: return launch_t<float, float, 1, 1, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
-    case 8: return launch_t<float, float, 0, 1, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
-    case 9: return launch_t<uint16_t, float, 1, 1, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
+      return launch_t<5, uint16_t, uint16_t, 4, 4, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
+    case 6: return launch_t<6, uint16_t, float, 8, 3, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
+    case 7: return launch_t<7, float, float, 1, 1, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
+    case 8: return launch_t<8, float, float, 0, 1, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
+    case 9: return launch_t<9, uint16_t, float, 1, 1, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
     case 10:
-      return launch_t<uint16_t, float, 2, 2, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
+      return launch_t<10, uint16_t, float, 2, 2, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
     case 11:
-      return launch_t<uint16_t, float, 8, 8, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
+      return launch_t<11, uint16_t, float, 8, 8, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
     case 12:
-      return launch_t<uint16_t, uint16_t, 1, 1, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
-    default: return launch_t<float, float, 1, 1, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
+      return launch_t<12, uint16_t, uint16_t, 1, 1, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
+    default: return launch_t<13, float, float, 1, 1, kRmw>(bf, a, b, ld, spans, groups, lds, sink, st);
   }
 }
 
